@@ -1,0 +1,37 @@
+"""fp64 CPU oracle for the Transformer-XL relative-attention step.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+baseline leg may import anything here. The product (the HIP library and its
+Python binding) never imports, calls or links this package, and this package
+never imports the product: the two share no code. Inputs come from
+``txl_synth`` (random draws only) or from values the pages print.
+
+Every function is a plain, slow, literal reading of the pages, in float64:
+explicit loops over queries, the mask rule evaluated per key, and the relative
+embedding looked up by distance (no shift trick, no ring buffer, no tiling).
+
+Pages cited (by title and section):
+  [P1] zty624.github.io notes, "Transformer-XL" (sections "Segment-Level
+       Recurrence", "Batched Tensor Contract", "Causal Mask With Memory",
+       "Relative Positional Encoding", "Dimension Walkthrough", "Relative
+       Shift Trick", "Relative Shift Golden Test", "Batched Streams", ...)
+  [P2] wq-win.github.io, "019 Transformer-XL" (section 3 pseudo-code and the
+       worked example of a 4x12 score)
+  [P3] iopencloud.com, "Transformer-XL与长序列建模" (section 2.2, the
+       (q+u)/(q+v) form of the score)
+  [P4] robocikowo.com, "Transformer-XL" (glossary: FIFO memory buffer,
+       four-term score, sinusoidal relative embedding)
+
+Parity status of each function (what pins it is listed in the tests):
+  attention.allow, attention.rel_ids, attention.rel_attn   pinned
+  memory.tail, memory.update_mems, memory.update_rows      pinned
+  stack.layer_norm, stack.gelu                             pinned (torch fp64)
+  stack.sinusoid                                           parity unpinned
+      (the pages only say "sinusoidal"; the formula is a stated reading,
+       checked for internal properties only)
+  stack.layer_forward, stack.segment_step_row, stack.stream
+      layer body (W^O, post-LayerNorm, GELU feed-forward) parity unpinned:
+      the pages fix Q from H and K/V from [mem; H] but not the rest of the
+      layer; the memory plumbing is pinned by the unrolled-recurrence test.
+"""
+from . import attention, memory, stack  # noqa: F401

@@ -1,0 +1,163 @@
+"""fp64 oracle: the relative-position table, one layer, one segment, a stream.
+
+TEST INFRASTRUCTURE (see the package docstring): never imported by the product.
+
+What the pages fix, and what is a stated reading:
+  * Q from the current segment only, K and V from [SG(mem); H] ([P1]
+    "Transformer-XL" notes, sections "Segment-Level Recurrence" and "Batched
+    Tensor Contract"; [P2] "019 Transformer-XL", section 3 pseudo-code).
+  * Layer n reads the memory of layer n-1 and every layer keeps its own
+    memory list [M^(0) ... M^(N)] updated with Tail_M ([P1] "Segment-Level
+    Recurrence"; [P2] section 2 on the dependency moving down one layer per
+    segment).
+  * Rows reset at document boundaries start from an empty memory ([P1]
+    "Training Loop Sketch" sets mems to None on reset; "Batched Streams" makes
+    the flag per row).
+  * R is a sinusoidal embedding of the relative distance projected per head
+    ([P4] "Transformer-XL" glossary entries on the four-term score). The
+    sinusoid's formula is not printed: the reading used here (and stated as
+    parity unpinned) is the concatenated [sin | cos] form with frequencies
+    10000^(-2k/d), k = 0 .. d/2-1.
+  * The rest of the layer is not on the pages. Reading used (parity
+    unpinned): attention output projection W^O, residual, LayerNorm (biased
+    variance, eps 1e-5); feed-forward d -> d_ff -> d with the exact erf GELU,
+    residual, LayerNorm. No biases, no dropout, no absolute positions.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+from scipy.special import erf
+
+from .attention import rel_attn
+from .memory import tail
+
+LN_EPS = 1e-5
+
+
+def sinusoid(dist: np.ndarray, d: int) -> np.ndarray:
+    """Sinusoidal embedding [len(dist), d] of the distances ``dist``.
+
+    emb(delta) = [sin(delta * f_0..f_{d/2-1}) | cos(delta * f_0..f_{d/2-1})],
+    f_k = 10000^(-2k/d). (Reading; the pages only say "sinusoidal".)
+    """
+    assert d % 2 == 0
+    dist = np.asarray(dist, dtype=np.float64)
+    k = np.arange(d // 2, dtype=np.float64)
+    freq = 10000.0 ** (-2.0 * k / d)
+    ang = dist[:, None] * freq[None, :]
+    return np.concatenate([np.sin(ang), np.cos(ang)], axis=1)
+
+
+def rel_pos_table(w_r: np.ndarray, M: int, L: int, H: int, dh: int
+                  ) -> np.ndarray:
+    """R for every head: [H, M+L, dh] with row t holding distance M+L-1-t.
+
+    [P1] "Dimension Walkthrough": R has one row per relative distance, from
+    the farthest memory slot to the current position. Each head projects the
+    sinusoid with its own slice of W_R [d, H*dh] (math orientation).
+    """
+    w_r = np.asarray(w_r, dtype=np.float64)
+    d = w_r.shape[0]
+    dist = np.arange(M + L - 1, -1, -1)
+    s = sinusoid(dist, d)
+    r = s @ w_r
+    return r.reshape(M + L, H, dh).transpose(1, 0, 2).copy()
+
+
+def layer_norm(x: np.ndarray, g: np.ndarray, b: np.ndarray,
+               eps: float = LN_EPS) -> np.ndarray:
+    """LayerNorm over the last axis: biased variance, then gain and shift."""
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * g + b
+
+
+def gelu(x: np.ndarray) -> np.ndarray:
+    """Exact GELU: x * Phi(x) with the Gaussian CDF written through erf."""
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+def _f64(w: Dict[str, object]) -> Dict[str, np.ndarray]:
+    return {k: np.asarray(v, dtype=np.float64) for k, v in w.items()}
+
+
+def layer_forward(h: np.ndarray, mem: np.ndarray, lw: Dict[str, np.ndarray],
+                  r_table: np.ndarray, M: int, H: int, dh: int) -> np.ndarray:
+    """One layer for one batch row.
+
+    h [L, d] is H^(n-1) of the current segment, mem [m, d] (m <= M) the
+    memory of layer n-1, oldest first. r_table is the layer's R for a memory
+    of capacity M ([H, M+L, dh]); with m < M stored states only its last m+L
+    rows (distances m+L-1 .. 0) are used.
+    Weights in math orientation: y = x W with W [in, out].
+    """
+    lw = _f64(lw)
+    h = np.asarray(h, dtype=np.float64)
+    mem = np.asarray(mem, dtype=np.float64)
+    L, d = h.shape
+    m = mem.shape[0]
+    ext = np.concatenate([mem, h], axis=0)           # [SG(mem); H]
+    q = (h @ lw["wq"]).reshape(L, H, dh).transpose(1, 0, 2)[None]
+    k = (ext @ lw["wk"]).reshape(m + L, H, dh).transpose(1, 0, 2)[None]
+    v = (ext @ lw["wv"]).reshape(m + L, H, dh).transpose(1, 0, 2)[None]
+    r = np.asarray(r_table, dtype=np.float64)[:, M - m:, :]
+    att = rel_attn(q, k, v, r, lw["u"], lw["vb"], valid=[m])["out"][0]
+    a = att.transpose(1, 0, 2).reshape(L, H * dh) @ lw["wo"]
+    h1 = layer_norm(h + a, lw["ln1_g"], lw["ln1_b"])
+    f = gelu(h1 @ lw["w1"]) @ lw["w2"]
+    return layer_norm(h1 + f, lw["ln2_g"], lw["ln2_b"])
+
+
+def segment_step_row(tokens: np.ndarray, mems: Sequence[np.ndarray],
+                     emb: np.ndarray, layers: Sequence[Dict[str, np.ndarray]],
+                     r_tables: Sequence[np.ndarray], M: int, H: int, dh: int):
+    """One segment of one batch row through the stack.
+
+    mems is the list [M^(0) ... M^(N)] of that row (arrays [m_n, d]).
+    Returns (hs, new_mems): hs = [H^(0) ... H^(N)] ([L, d] each, H^(0) the
+    embedded tokens) and new_mems[n] = Tail_M([M^(n); H^(n)]).
+    """
+    emb = np.asarray(emb, dtype=np.float64)
+    h = emb[np.asarray(tokens, dtype=np.int64)]
+    hs = [h]
+    for n, lw in enumerate(layers):
+        h = layer_forward(h, mems[n], lw, r_tables[n], M, H, dh)
+        hs.append(h)
+    new_mems = [tail(np.concatenate([np.asarray(mems[n], dtype=np.float64),
+                                     hs[n]], axis=0), M).copy()
+                for n in range(len(layers) + 1)]
+    return hs, new_mems
+
+
+def stream(tokens: np.ndarray, resets: np.ndarray, emb: np.ndarray,
+           layers: Sequence[Dict[str, np.ndarray]],
+           r_tables: Sequence[np.ndarray], M: int, H: int, dh: int,
+           rows: Optional[Sequence[int]] = None) -> List[Dict[int, List[np.ndarray]]]:
+    """Stream consecutive segments through the stack, row by row.
+
+    tokens [S, B, L] ints; resets [S, B] flags. A row whose flag is set (and
+    every row at its first segment) starts from empty memories, as with
+    mems = None in [P1] "Training Loop Sketch". Returns, per segment, a dict
+    row -> [H^(0) ... H^(N)].
+    """
+    tokens = np.asarray(tokens)
+    resets = np.asarray(resets)
+    S, B, _ = tokens.shape
+    rows = list(range(B)) if rows is None else list(rows)
+    d = np.asarray(emb).shape[1]
+    n_mem = len(layers) + 1
+    mems: Dict[int, Optional[List[np.ndarray]]] = {b: None for b in rows}
+    out = []
+    for s in range(S):
+        seg = {}
+        for b in rows:
+            if mems[b] is None or resets[s, b]:
+                mems[b] = [np.zeros((0, d)) for _ in range(n_mem)]
+            hs, mems[b] = segment_step_row(tokens[s, b], mems[b], emb, layers,
+                                           r_tables, M, H, dh)
+            seg[b] = hs
+        out.append(seg)
+    return out
