@@ -1,0 +1,185 @@
+#!/usr/bin/env python3
+"""Throughput of the Transformer-XL relative-attention step on one MI355X.
+
+Workload (a step): one layer of relative-position memory attention plus that
+layer's FIFO memory update, bf16, B=8, H=16, d_h=64 (d=1024), segment L=512,
+memory M=512 fully valid. Inputs are seeded synthetic tensors of that shape,
+resident in HBM before timing starts; the relative-position table R (a
+function of the weights and of M, L only) is built once by the library
+before timing. Each timed step is txl_rel_attn_fwd followed by
+txl_mem_update; the update rotates over 16 ring/segment buffer pairs
+(268 MB) so that it is not served from the 256 MB last-level cache.
+
+Prints one JSON line. `value` is attention TFLOP/s over the whole step
+(algorithmic flops: 6*d_h per visible (query, key) pair, masked pairs not
+counted); per-kernel figures come from HIP events recorded on the launch
+stream around each kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "rel-pos memory attention TFLOP/s (% bf16 MFMA peak) + mem-update GB/s, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+N_RING_SETS = 16
+
+
+def attn_flops(B, H, L, M_eff, d_h):
+    pairs = B * (L * M_eff + L * (L + 1) // 2)
+    return 6.0 * d_h * H * pairs
+
+
+def cpu_baseline(x, cfg, seconds: float):
+    """Time the fp64 oracle on a bounded sample of the same workload: whole
+    (batch row, head) slices, all queries, in order until `seconds` pass."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as oa
+    from oracle import stack as ost
+
+    r = ost.rel_pos_table(x["w_r"].double().numpy(), cfg.M, cfg.L, cfg.H, cfg.d_h)
+    r = r.astype(np.float64)
+    q, k, v = (x[n].double().numpy() for n in ("q", "k", "v"))
+    u, vb = x["u"].double().numpy(), x["vb"].double().numpy()
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for b in range(cfg.B):
+            for h in range(cfg.H):
+                oa.rel_attn(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                            r[h:h + 1], u[h:h + 1], vb[h:h + 1], valid=[cfg.M])
+                done += 1
+                flops += attn_flops(1, 1, cfg.L, cfg.M, cfg.d_h)
+                if time.perf_counter() - t0 >= seconds:
+                    break
+            if time.perf_counter() - t0 >= seconds:
+                break
+    el = time.perf_counter() - t0
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 oracle rel-attn on {done} of {cfg.B * cfg.H} (batch row, head) "
+                      f"slices of the same workload, all {cfg.L} queries each, "
+                      f"{el:.1f} s, 1 thread"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the oracle CPU baseline (0 skips it)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not run "
+              "(the step shards over batch rows with no communication; see DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import txl_synth
+    import transformer_xl_relative_txl_amd as txl
+
+    cfg = txl_synth.ATTN_CONFIGS["C3"]
+    B, H, L, M, dh = cfg.B, cfg.H, cfg.L, cfg.M, cfg.d_h
+    d = H * dh
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = txl_synth.attn_inputs(cfg)
+
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    u, vb = x["u"].to(dev), x["vb"].to(dev)
+    valid = torch.full((B,), M, dtype=torch.int32, device=dev)
+    w_r = x["w_r"].t().contiguous().to(dev)            # output-major [H*d_h, d]
+    r_flat = torch.empty((M + L, H * dh), dtype=torch.bfloat16, device=dev)
+    txl.txl_rel_pos_table(w_r, M, L, H, dh, r_flat)
+    r = r_flat.view(M + L, H, dh).permute(1, 0, 2)      # [H, M+L, d_h] view
+    out = torch.empty_like(q)
+
+    g = torch.Generator("cpu").manual_seed(cfg.seed + 100)
+    rings, segs = [], []
+    for s in range(N_RING_SETS):
+        mem = x["mem"] if s == 0 else torch.randn((B, M, d), generator=g).to(torch.bfloat16)
+        rings.append(txl.TxlMem(mem.to(dev).contiguous(),
+                                torch.full((B,), M, dtype=torch.int32, device=dev), 0))
+        hs = x["h"] if s == 0 else torch.randn((B, L, d), generator=g).to(torch.bfloat16)
+        segs.append(hs.to(dev).contiguous())
+
+    def step(i):
+        txl.txl_rel_attn_fwd(q, k, v, r, u, vb, out, mem_valid=valid)
+        txl.txl_mem_update([rings[i % N_RING_SETS]], [segs[i % N_RING_SETS]])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(K):
+        ev[i][0].record()
+        txl.txl_rel_attn_fwd(q, k, v, r, u, vb, out, mem_valid=valid)
+        ev[i][1].record()
+        txl.txl_mem_update([rings[i % N_RING_SETS]], [segs[i % N_RING_SETS]])
+        ev[i][2].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+
+    step_ms = start.elapsed_time(end) / K
+    attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    mem_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    flops = attn_flops(B, H, L, M, dh)
+    Lp = min(L, M)
+    mem_bytes = 2.0 * B * Lp * d * 2
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    mem_gbps = mem_bytes / (mem_ms * 1e-3) / 1e9
+    value = flops / (step_ms * 1e-3) / 1e12
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "one layer rel-attn + mem update, B=8 H=16 d_h=64 L=512 M=512",
+                   "B": B, "H": H, "d_h": dh, "L": L, "M": M, "valid": M,
+                   "seed": cfg.seed},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "mem_update": {"bound": "hbm", "achieved": round(mem_gbps, 1), "peak": PEAK_HBM_GBPS,
+                       "unit": "GB/s", "frac": round(mem_gbps / PEAK_HBM_GBPS, 4),
+                       "bytes_per_launch": mem_bytes, "ms": round(mem_ms, 5)},
+        "attn_ms": round(attn_ms, 5),
+        "attn_gflop_per_launch": round(flops / 1e9, 3),
+        "wall_s_timed": round(wall, 4),
+    }
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(x, cfg, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

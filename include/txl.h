@@ -1,0 +1,172 @@
+/*
+ * libtxl: the Transformer-XL relative-position memory attention step for
+ * AMD MI355X (gfx950, CDNA4), as a C ABI.
+ *
+ * Pages this library implements (cited by title and section):
+ *   [P1] zty624.github.io notes, "Transformer-XL"
+ *   [P2] wq-win.github.io, "019 Transformer-XL"
+ *   [P3] iopencloud.com, "Transformer-XL与长序列建模"
+ *   [P4] robocikowo.com, "Transformer-XL"
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates no device memory on any call and keeps no pointer after the
+ *     call returns (txl_stack keeps the weight pointers it is given; see there).
+ *   - Every call is asynchronous on the caller's stream. TXL_OK means "all
+ *     work enqueued"; device faults surface at the caller's next sync.
+ *   - Every argument is checked before anything is enqueued: on an error
+ *     nothing has been launched and outputs are untouched. txl_last_error()
+ *     then holds a message (thread-local).
+ *   - Element strides count elements, not bytes; the last dimension of every
+ *     strided tensor is contiguous. Vector loads need every row start to be
+ *     16-byte aligned (base pointers and strides), else TXL_ERR_UNSUPPORTED.
+ *   - "bf16" means bfloat16 storage with fp32 accumulation; conversions to
+ *     bf16 round to nearest even.
+ *   - Keys are in logical order: key index j' in [0, M) is memory (oldest
+ *     first), [M, M+L) is the current segment; key position j = j' - M.
+ */
+#ifndef TXL_H
+#define TXL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TXL_API __attribute__((visibility("default")))
+#define TXL_VERSION 1
+
+typedef enum { TXL_F32 = 0, TXL_BF16 = 1 } txl_dtype;
+
+typedef enum {
+  TXL_OK = 0,
+  TXL_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent shapes */
+  TXL_ERR_UNSUPPORTED = 2, /* valid request this build does not serve (d_h, alignment) */
+  TXL_ERR_WORKSPACE = 3,   /* caller buffer too small */
+  TXL_ERR_HIP = 4          /* a HIP launch failed; see txl_last_error() */
+} txl_status;
+
+/* ------------------------------------------------------------------------
+ * Relative-position table R.
+ * [P1] "Dimension Walkthrough": R has one row per relative distance, from
+ * the farthest memory slot down to distance 0; [P4] glossary: R is a
+ * sinusoidal embedding of the distance i - j, projected per head.
+ *
+ *   r[t, h*d_h + e] = sum_k S(M+L-1-t, k) * w_r[h*d_h + e, k]
+ *   S(delta, k)     = sin(delta * f_k)        for k <  d/2
+ *                     cos(delta * f_{k-d/2})  for k >= d/2,  f_k = 10000^(-2k/d)
+ *
+ * w_r : [H*d_h, d] (output-major, like a torch Linear weight), dtype.
+ * r   : [M+L, H*d_h] row-major, dtype; as the per-head table of
+ *       txl_rel_attn_fwd use r_sh = d_h, r_sl = H*d_h.
+ * The sinusoid is evaluated in fp64, the projection accumulates in fp32.
+ * Depends only on the weights and on (M, L): compute it once per model.
+ * Errors: INVALID_ARG for null pointers, M < 0, L < 1, d odd or < 2,
+ * H < 1, d_h < 1.
+ * ------------------------------------------------------------------------ */
+TXL_API txl_status txl_rel_pos_table(txl_dtype dtype, int32_t M, int32_t L,
+                                     int32_t d, int32_t H, int32_t d_h,
+                                     const void *w_r, void *r,
+                                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Fused relative-position attention over [memory; current segment].
+ *
+ * For batch row b, head h, query i in [0, L) and visible key position j:
+ *   A_ij = (q_i + u_h) . k_j + (q_i + v_h) . R_{i-j}
+ *        ( = q.k + q.R + u.k + v.R, the four terms of [P1] "Relative
+ *          Positional Encoding"; the (q+u)/(q+v) form of [P3] section 2.2 )
+ *   out_i = sum_j softmax_j(A_ij * scale) v_j        ([P1] "Dimension Walkthrough")
+ * with R_{i-j} = r[h, M+L-1-(i-j)] (row t of r holds distance M+L-1-t).
+ * Visible keys ([P1] "Causal Mask With Memory", allow(i, j)):
+ *   memory  -valid_b <= j < 0      (slots beyond the row's valid count, e.g.
+ *                                   after a document reset, are masked)
+ *   current 0 <= j <= i
+ * Masked keys get weight exactly 0 and are never read for V.
+ * The position term is computed in-tile by index arithmetic (no
+ * pad/reshape/slice, [P1] "Relative Shift Trick" replaced).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  txl_dtype dtype;               /* q, k, v, r, u, vb and out share it     */
+  int32_t B, H, L, M, d_h;       /* M >= 0 memory capacity; keys = M + L    */
+  const void *q;                 /* [B, H, L, d_h]                          */
+  int64_t q_sb, q_sh, q_sl;
+  const void *k, *v;             /* [B, H, M+L, d_h], logical key order     */
+  int64_t kv_sb, kv_sh, kv_sl;
+  const void *r;                 /* [H, M+L, d_h], row t <-> distance M+L-1-t */
+  int64_t r_sh, r_sl;
+  const void *u, *vb;            /* [H, d_h] contiguous: content / position bias */
+  const int32_t *mem_valid;      /* [B] device, each in [0, M]; NULL = all M valid */
+  float scale;                   /* 0 => 1/sqrt(d_h)                        */
+  void *out;                     /* [B, H, L, d_h]                          */
+  int64_t o_sb, o_sh, o_sl;
+  float *lse;                    /* [B, H, L] contiguous fp32, natural-log
+                                    log-sum-exp of scaled visible scores; NULL = skip */
+} txl_rel_attn_args;
+
+/* Shapes: d_h must be 64 (else UNSUPPORTED). B == 0 or L == 0: nothing to
+ * do, TXL_OK. mem_valid values outside [0, M] are the caller's error (they
+ * are clamped on the device). fp32 and bf16 are both served; bf16 runs the
+ * MFMA kernel, fp32 a VALU kernel of the same semantics. */
+TXL_API txl_status txl_rel_attn_fwd(const txl_rel_attn_args *a,
+                                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Per-layer FIFO memory as a ring buffer.
+ * [P1] "Segment-Level Recurrence" and "Batched Tensor Contract": after the
+ * step every layer's memory becomes Tail_M([mem; H]) (the last M states;
+ * all of them while fewer; nothing when M = 0). [P4]: a FIFO buffer in GPU
+ * memory whose oldest entries are overwritten.
+ *
+ * Ring layout: data[b, s, :] for slot s in [0, M). `head` (host state) is the
+ * slot that holds the oldest state once the ring is full and the next slot
+ * to be written; logical memory index j' in [0, M) lives in slot
+ * (head + j') mod M. Row b holds valid[b] states: logical indices
+ * [M - valid[b], M). A fresh stream starts with head = 0, valid = 0, and
+ * data filled with finite values (e.g. zeros).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  void *data;        /* [B, M, d] device, dtype                             */
+  int32_t *valid;    /* [B] device                                          */
+  int64_t head;      /* host; updated by txl_mem_update                     */
+  int32_t B, M, d;
+  txl_dtype dtype;
+} txl_mem;
+
+/* Append the segment to every ring: with L' = min(L, M), rows
+ * h[n][b, L-L'+k, :] go to slot (head + k) mod M of ring n, then
+ * head <- (head + L') mod M and valid[b] <- min(M, valid[b] + L).
+ * h: host array of n_mems device pointers, each [B, L, d] contiguous.
+ * All rings in one call must share B, M, d and dtype; one launch covers all.
+ * M == 0 or L == 0: nothing to do. Moves 2*B*L'*d*sizeof(dtype) bytes per ring. */
+TXL_API txl_status txl_mem_update(txl_mem *mems, int32_t n_mems,
+                                  const void *const *h, int32_t L,
+                                  hipStream_t stream);
+
+/* Document boundary ([P1] "Batched Streams": the reset flag is per row):
+ * valid[b] <- 0 in every ring for rows with reset[b] != 0 (reset: [B] uint8
+ * device; NULL resets every row). The masked reading of "clear or mask":
+ * the row then attends exactly as a fresh stream. */
+TXL_API txl_status txl_mem_reset_rows(txl_mem *mems, int32_t n_mems,
+                                      const uint8_t *reset, hipStream_t stream);
+
+/* Copy a ring out in logical order: out[b, j', :] = data[b, (head+j') mod M, :]
+ * (out: [B, M, d] contiguous device). Used to checkpoint a stream or to
+ * compare memories; rows' invalid prefixes are copied as they are. */
+TXL_API txl_status txl_mem_read_logical(const txl_mem *m, void *out,
+                                        hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+TXL_API const char *txl_status_str(txl_status s);
+TXL_API const char *txl_last_error(void);  /* thread-local; "" if none */
+TXL_API int32_t txl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TXL_H */

@@ -1,0 +1,19 @@
+"""libtxl for MI355X: Transformer-XL relative-position memory attention.
+
+The HIP library (libtxl.so, built by ``transformer_xl_relative_txl_amd.build``)
+holds every kernel; this package only marshals torch tensors into its C ABI.
+"""
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    TXL_BF16,
+    TXL_F32,
+    TxlError,
+    TxlMem,
+    lib,
+    txl_mem_read_logical,
+    txl_mem_reset_rows,
+    txl_mem_update,
+    txl_rel_attn_fwd,
+    txl_rel_pos_table,
+    txl_version,
+)

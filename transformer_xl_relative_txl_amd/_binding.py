@@ -1,0 +1,255 @@
+"""ctypes binding of libtxl (include/txl.h): argument marshalling only.
+
+Every function here takes torch tensors that already live on the GPU, turns
+them into the C structs of the header (pointers, sizes, element strides) and
+calls the library on torch's current stream. No arithmetic of the method runs
+in Python. If the library is missing the import fails loudly: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtxl.so")
+
+TXL_F32, TXL_BF16 = 0, 1
+_STATUS = {0: "TXL_OK", 1: "TXL_ERR_INVALID_ARG", 2: "TXL_ERR_UNSUPPORTED",
+           3: "TXL_ERR_WORKSPACE", 4: "TXL_ERR_HIP"}
+
+
+class TxlError(RuntimeError):
+    """A libtxl call returned a status other than TXL_OK."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+        self.status_name = _STATUS.get(status, str(status))
+
+
+class RelAttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int),
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32),
+        ("M", ctypes.c_int32), ("d_h", ctypes.c_int32),
+        ("q", ctypes.c_void_p),
+        ("q_sb", ctypes.c_int64), ("q_sh", ctypes.c_int64), ("q_sl", ctypes.c_int64),
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("kv_sb", ctypes.c_int64), ("kv_sh", ctypes.c_int64), ("kv_sl", ctypes.c_int64),
+        ("r", ctypes.c_void_p),
+        ("r_sh", ctypes.c_int64), ("r_sl", ctypes.c_int64),
+        ("u", ctypes.c_void_p), ("vb", ctypes.c_void_p),
+        ("mem_valid", ctypes.c_void_p),
+        ("scale", ctypes.c_float),
+        ("out", ctypes.c_void_p),
+        ("o_sb", ctypes.c_int64), ("o_sh", ctypes.c_int64), ("o_sl", ctypes.c_int64),
+        ("lse", ctypes.c_void_p),
+    ]
+
+
+class TxlMemStruct(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("valid", ctypes.c_void_p),
+        ("head", ctypes.c_int64),
+        ("B", ctypes.c_int32), ("M", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("dtype", ctypes.c_int),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libtxl.so is not built at {LIB_PATH}; run "
+            "`python -m transformer_xl_relative_txl_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int
+    lib.txl_status_str.argtypes = [st]
+    lib.txl_status_str.restype = ctypes.c_char_p
+    lib.txl_last_error.argtypes = []
+    lib.txl_last_error.restype = ctypes.c_char_p
+    lib.txl_version.argtypes = []
+    lib.txl_version.restype = i32
+    lib.txl_rel_pos_table.argtypes = [st, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.txl_rel_pos_table.restype = st
+    lib.txl_rel_attn_fwd.argtypes = [ctypes.POINTER(RelAttnArgs), vp]
+    lib.txl_rel_attn_fwd.restype = st
+    lib.txl_mem_update.argtypes = [ctypes.POINTER(TxlMemStruct), i32,
+                                   ctypes.POINTER(vp), i32, vp]
+    lib.txl_mem_update.restype = st
+    lib.txl_mem_reset_rows.argtypes = [ctypes.POINTER(TxlMemStruct), i32, vp, vp]
+    lib.txl_mem_reset_rows.restype = st
+    lib.txl_mem_read_logical.argtypes = [ctypes.POINTER(TxlMemStruct), vp, vp]
+    lib.txl_mem_read_logical.restype = st
+    del i64
+    return lib
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded on first use)."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        msg = lib().txl_last_error().decode(errors="replace")
+        raise TxlError(fn, status, msg)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TXL_F32
+    if t.dtype == torch.bfloat16:
+        return TXL_BF16
+    raise TypeError(f"libtxl serves float32 and bfloat16, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+# ----------------------------------------------------------------------------
+def txl_version() -> int:
+    return int(lib().txl_version())
+
+
+def txl_rel_pos_table(w_r: torch.Tensor, M: int, L: int, H: int, d_h: int,
+                      r: torch.Tensor, stream=None) -> torch.Tensor:
+    """R [M+L, H*d_h] from W_R stored output-major [H*d_h, d] (contiguous)."""
+    assert w_r.is_contiguous() and r.is_contiguous()
+    d = w_r.shape[1]
+    _check("txl_rel_pos_table",
+           lib().txl_rel_pos_table(_dtype(w_r), M, L, d, H, d_h, _ptr(w_r), _ptr(r),
+                                   _stream(stream)))
+    return r
+
+
+def txl_rel_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     r: torch.Tensor, u: torch.Tensor, vb: torch.Tensor,
+                     out: torch.Tensor, mem_valid: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, scale: float = 0.0,
+                     stream=None) -> torch.Tensor:
+    """Relative attention. q [B,H,L,d_h]; k, v [B,H,M+L,d_h] (same strides);
+    r [H,M+L,d_h]; u, vb [H,d_h] contiguous; out [B,H,L,d_h]; mem_valid [B]
+    int32; lse [B,H,L] float32. Any element strides with a contiguous last
+    dimension."""
+    B, H, L, d_h = q.shape
+    M = k.shape[2] - L
+    if k.stride() != v.stride():
+        raise ValueError("k and v must share strides")
+    a = RelAttnArgs()
+    a.dtype = _dtype(q)
+    a.B, a.H, a.L, a.M, a.d_h = B, H, L, M, d_h
+    a.q = _ptr(q)
+    a.q_sb, a.q_sh, a.q_sl = q.stride(0), q.stride(1), q.stride(2)
+    a.k, a.v = _ptr(k), _ptr(v)
+    a.kv_sb, a.kv_sh, a.kv_sl = k.stride(0), k.stride(1), k.stride(2)
+    a.r = _ptr(r)
+    a.r_sh, a.r_sl = r.stride(0), r.stride(1)
+    a.u, a.vb = _ptr(u), _ptr(vb)
+    a.mem_valid = _ptr(mem_valid)
+    a.scale = float(scale)
+    a.out = _ptr(out)
+    a.o_sb, a.o_sh, a.o_sl = out.stride(0), out.stride(1), out.stride(2)
+    a.lse = _ptr(lse)
+    _check("txl_rel_attn_fwd", lib().txl_rel_attn_fwd(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+class TxlMem:
+    """One ring-buffer memory: device tensors data [B,M,d] and valid [B]
+    plus the host-side head (the C struct txl_mem)."""
+
+    def __init__(self, data: torch.Tensor, valid: torch.Tensor, head: int = 0):
+        assert data.dim() == 3 and data.is_contiguous()
+        assert valid.dtype == torch.int32 and valid.shape == (data.shape[0],)
+        self.data, self.valid, self.head = data, valid, int(head)
+
+    @classmethod
+    def empty(cls, B: int, M: int, d: int, dtype=torch.bfloat16, device="cuda"):
+        """A fresh stream: zero-filled slots, no valid states, head 0."""
+        return cls(torch.zeros((B, M, d), dtype=dtype, device=device),
+                   torch.zeros((B,), dtype=torch.int32, device=device), 0)
+
+    @property
+    def B(self):
+        return self.data.shape[0]
+
+    @property
+    def M(self):
+        return self.data.shape[1]
+
+    @property
+    def d(self):
+        return self.data.shape[2]
+
+    def _struct(self) -> TxlMemStruct:
+        s = TxlMemStruct()
+        s.data, s.valid, s.head = _ptr(self.data), _ptr(self.valid), self.head
+        s.B, s.M, s.d = self.B, self.M, self.d
+        s.dtype = _dtype(self.data)
+        return s
+
+
+def _structs(mems: Sequence[TxlMem]):
+    arr = (TxlMemStruct * max(1, len(mems)))()
+    for i, m in enumerate(mems):
+        arr[i] = m._struct()
+    return arr
+
+
+def txl_mem_update(mems: Sequence[TxlMem], hs: Sequence[torch.Tensor],
+                   stream=None) -> None:
+    """Append segment hs[n] ([B,L,d] contiguous) to ring mems[n]; heads advance."""
+    assert len(mems) == len(hs)
+    L = hs[0].shape[1] if hs else 0
+    for h in hs:
+        assert h.is_contiguous() and h.shape[1] == L
+    arr = _structs(mems)
+    ptrs = (ctypes.c_void_p * max(1, len(hs)))(*[h.data_ptr() for h in hs])
+    _check("txl_mem_update",
+           lib().txl_mem_update(arr, len(mems), ptrs, L, _stream(stream)))
+    for i, m in enumerate(mems):
+        m.head = int(arr[i].head)
+
+
+def txl_mem_reset_rows(mems: Sequence[TxlMem], reset: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    """valid[b] = 0 in every ring for rows with reset[b] != 0 (uint8 [B]; None = all)."""
+    if reset is not None:
+        assert reset.dtype == torch.uint8
+    arr = _structs(mems)
+    _check("txl_mem_reset_rows",
+           lib().txl_mem_reset_rows(arr, len(mems), _ptr(reset), _stream(stream)))
+
+
+def txl_mem_read_logical(mem: TxlMem, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """Copy the ring out oldest-first into out [B,M,d]."""
+    assert out.is_contiguous()
+    s = mem._struct()
+    _check("txl_mem_read_logical",
+           lib().txl_mem_read_logical(ctypes.byref(s), _ptr(out), _stream(stream)))
+    return out
+
+
+def exported_symbols() -> List[str]:
+    """Names of the C entry points this binding wraps."""
+    return ["txl_rel_pos_table", "txl_rel_attn_fwd", "txl_mem_update",
+            "txl_mem_reset_rows", "txl_mem_read_logical", "txl_status_str",
+            "txl_last_error", "txl_version"]

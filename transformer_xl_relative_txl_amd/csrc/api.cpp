@@ -1,0 +1,213 @@
+// Host layer of libtxl: argument checks, launch dispatch, error reporting.
+// Every public call validates all of its arguments before enqueuing any work,
+// so an error never leaves partial results behind.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "txl.h"
+#include "txl_internal.h"
+
+namespace txl {
+
+static thread_local char g_last_error[512] = "";
+
+txl_status fail(txl_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+txl_status check_launch(const char *what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(TXL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return TXL_OK;
+}
+
+static bool aligned16(const void *p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+static bool stride_ok(int64_t s, size_t es) {
+  return s >= 0 && ((s * static_cast<int64_t>(es)) % 16) == 0;
+}
+static bool dtype_ok(txl_dtype t) { return t == TXL_F32 || t == TXL_BF16; }
+
+static void clear_error() { g_last_error[0] = '\0'; }
+
+}  // namespace txl
+
+using namespace txl;
+
+extern "C" {
+
+TXL_API const char *txl_status_str(txl_status s) {
+  switch (s) {
+    case TXL_OK: return "ok";
+    case TXL_ERR_INVALID_ARG: return "invalid argument";
+    case TXL_ERR_UNSUPPORTED: return "unsupported";
+    case TXL_ERR_WORKSPACE: return "workspace too small";
+    case TXL_ERR_HIP: return "hip error";
+  }
+  return "unknown status";
+}
+
+TXL_API const char *txl_last_error(void) { return g_last_error; }
+
+TXL_API int32_t txl_version(void) { return TXL_VERSION; }
+
+// ---------------------------------------------------------------------------
+TXL_API txl_status txl_rel_pos_table(txl_dtype dtype, int32_t M, int32_t L,
+                                     int32_t d, int32_t H, int32_t d_h,
+                                     const void *w_r, void *r,
+                                     hipStream_t stream) {
+  clear_error();
+  if (!dtype_ok(dtype)) return fail(TXL_ERR_INVALID_ARG, "rel_pos_table: bad dtype");
+  if (M < 0 || L < 1) return fail(TXL_ERR_INVALID_ARG, "rel_pos_table: need M >= 0, L >= 1");
+  if (d < 2 || (d % 2) != 0) return fail(TXL_ERR_INVALID_ARG, "rel_pos_table: d must be even and >= 2");
+  if (H < 1 || d_h < 1) return fail(TXL_ERR_INVALID_ARG, "rel_pos_table: need H >= 1, d_h >= 1");
+  if (!w_r || !r) return fail(TXL_ERR_INVALID_ARG, "rel_pos_table: null pointer");
+  if (static_cast<int64_t>(M) + L > (1 << 30))
+    return fail(TXL_ERR_INVALID_ARG, "rel_pos_table: M + L too large");
+  return launch_rel_pos_table(dtype, M, L, d, H * d_h, w_r, r, stream);
+}
+
+// ---------------------------------------------------------------------------
+TXL_API txl_status txl_rel_attn_fwd(const txl_rel_attn_args *a,
+                                    hipStream_t stream) {
+  clear_error();
+  if (!a) return fail(TXL_ERR_INVALID_ARG, "rel_attn: null args");
+  if (!dtype_ok(a->dtype)) return fail(TXL_ERR_INVALID_ARG, "rel_attn: bad dtype");
+  if (a->B < 0 || a->H < 1 || a->L < 0 || a->M < 0)
+    return fail(TXL_ERR_INVALID_ARG, "rel_attn: need B >= 0, H >= 1, L >= 0, M >= 0");
+  if (a->d_h != 64)
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn: d_h = %d, only 64 is built", a->d_h);
+  if (static_cast<int64_t>(a->M) + a->L > (1 << 30))
+    return fail(TXL_ERR_INVALID_ARG, "rel_attn: M + L too large");
+  if (!(std::isfinite(a->scale)))
+    return fail(TXL_ERR_INVALID_ARG, "rel_attn: scale is not finite");
+  if (a->B == 0 || a->L == 0) return TXL_OK;
+  if (!a->q || !a->k || !a->v || !a->r || !a->u || !a->vb || !a->out)
+    return fail(TXL_ERR_INVALID_ARG, "rel_attn: null tensor pointer");
+  const size_t es = dtype_size(a->dtype);
+  const void *ptrs[] = {a->q, a->k, a->v, a->r, a->u, a->vb, a->out};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return fail(TXL_ERR_UNSUPPORTED, "rel_attn: tensor not 16-byte aligned");
+  const int64_t strides[] = {a->q_sb, a->q_sh, a->q_sl, a->kv_sb, a->kv_sh, a->kv_sl,
+                             a->r_sh, a->r_sl, a->o_sb, a->o_sh, a->o_sl};
+  for (int64_t s : strides)
+    if (!stride_ok(s, es))
+      return fail(TXL_ERR_UNSUPPORTED,
+                  "rel_attn: stride %lld is negative or not a multiple of 16 bytes",
+                  static_cast<long long>(s));
+  if (a->lse && (reinterpret_cast<uintptr_t>(a->lse) & 3u))
+    return fail(TXL_ERR_INVALID_ARG, "rel_attn: lse not 4-byte aligned");
+  if (a->mem_valid && (reinterpret_cast<uintptr_t>(a->mem_valid) & 3u))
+    return fail(TXL_ERR_INVALID_ARG, "rel_attn: mem_valid not 4-byte aligned");
+
+  AttnParams p;
+  p.q = a->q; p.k = a->k; p.v = a->v; p.r = a->r; p.u = a->u; p.vb = a->vb;
+  p.out = a->out; p.lse = a->lse; p.valid = a->mem_valid;
+  p.q_sb = a->q_sb; p.q_sh = a->q_sh; p.q_sl = a->q_sl;
+  p.kv_sb = a->kv_sb; p.kv_sh = a->kv_sh; p.kv_sl = a->kv_sl;
+  p.r_sh = a->r_sh; p.r_sl = a->r_sl;
+  p.o_sb = a->o_sb; p.o_sh = a->o_sh; p.o_sl = a->o_sl;
+  p.B = a->B; p.H = a->H; p.L = a->L; p.M = a->M;
+  p.scale = a->scale != 0.0f ? a->scale : 1.0f / std::sqrt(static_cast<float>(a->d_h));
+  if (a->dtype == TXL_BF16) return launch_rel_attn_mfma(p, stream);
+  return launch_rel_attn_valu(p, a->dtype, stream);
+}
+
+// ---------------------------------------------------------------------------
+static txl_status check_rings(const txl_mem *mems, int32_t n_mems, const char *who) {
+  if (n_mems < 0) return fail(TXL_ERR_INVALID_ARG, "%s: n_mems < 0", who);
+  if (n_mems > 0 && !mems) return fail(TXL_ERR_INVALID_ARG, "%s: null mems", who);
+  for (int i = 0; i < n_mems; ++i) {
+    const txl_mem &m = mems[i];
+    if (!dtype_ok(m.dtype)) return fail(TXL_ERR_INVALID_ARG, "%s: ring %d bad dtype", who, i);
+    if (m.B < 0 || m.M < 0 || m.d < 1)
+      return fail(TXL_ERR_INVALID_ARG, "%s: ring %d needs B >= 0, M >= 0, d >= 1", who, i);
+    if (m.B != mems[0].B || m.M != mems[0].M || m.d != mems[0].d || m.dtype != mems[0].dtype)
+      return fail(TXL_ERR_INVALID_ARG, "%s: rings in one call must share B, M, d, dtype", who);
+    if (m.B > 0 && !m.valid) return fail(TXL_ERR_INVALID_ARG, "%s: ring %d null valid", who, i);
+    if (m.M > 0 && m.B > 0 && !m.data) return fail(TXL_ERR_INVALID_ARG, "%s: ring %d null data", who, i);
+    if (m.M > 0 && (m.head < 0 || m.head >= m.M))
+      return fail(TXL_ERR_INVALID_ARG, "%s: ring %d head %lld outside [0, M)", who, i,
+                  static_cast<long long>(m.head));
+    if (m.valid && (reinterpret_cast<uintptr_t>(m.valid) & 3u))
+      return fail(TXL_ERR_INVALID_ARG, "%s: ring %d valid not 4-byte aligned", who, i);
+  }
+  return TXL_OK;
+}
+
+TXL_API txl_status txl_mem_update(txl_mem *mems, int32_t n_mems,
+                                  const void *const *h, int32_t L,
+                                  hipStream_t stream) {
+  clear_error();
+  txl_status st = check_rings(mems, n_mems, "mem_update");
+  if (st != TXL_OK) return st;
+  if (L < 0) return fail(TXL_ERR_INVALID_ARG, "mem_update: L < 0");
+  if (n_mems == 0 || L == 0 || mems[0].M == 0 || mems[0].B == 0) return TXL_OK;
+  if (!h) return fail(TXL_ERR_INVALID_ARG, "mem_update: null h array");
+  const int64_t row_bytes = static_cast<int64_t>(mems[0].d) * dtype_size(mems[0].dtype);
+  if (row_bytes % 16) return fail(TXL_ERR_UNSUPPORTED, "mem_update: d * sizeof(dtype) must be a multiple of 16");
+  for (int i = 0; i < n_mems; ++i) {
+    if (!h[i]) return fail(TXL_ERR_INVALID_ARG, "mem_update: h[%d] is null", i);
+    if (!aligned16(h[i]) || !aligned16(mems[i].data))
+      return fail(TXL_ERR_UNSUPPORTED, "mem_update: ring %d or h[%d] not 16-byte aligned", i, i);
+  }
+  const int M = mems[0].M;
+  const int Lp = L < M ? L : M;
+  for (int base = 0; base < n_mems; base += kMaxRingsPerLaunch) {
+    const int n = (n_mems - base) < kMaxRingsPerLaunch ? (n_mems - base) : kMaxRingsPerLaunch;
+    RingBatch rb;
+    for (int i = 0; i < n; ++i) {
+      rb.data[i] = mems[base + i].data;
+      rb.valid[i] = mems[base + i].valid;
+      rb.h[i] = h[base + i];
+      rb.head[i] = mems[base + i].head;
+    }
+    st = launch_mem_update(rb, n, mems[0].B, M, L, row_bytes, stream);
+    if (st != TXL_OK) return st;
+  }
+  for (int i = 0; i < n_mems; ++i) mems[i].head = (mems[i].head + Lp) % M;
+  return TXL_OK;
+}
+
+TXL_API txl_status txl_mem_reset_rows(txl_mem *mems, int32_t n_mems,
+                                      const uint8_t *reset, hipStream_t stream) {
+  clear_error();
+  txl_status st = check_rings(mems, n_mems, "mem_reset_rows");
+  if (st != TXL_OK) return st;
+  if (n_mems == 0 || mems[0].B == 0) return TXL_OK;
+  for (int base = 0; base < n_mems; base += kMaxRingsPerLaunch) {
+    const int n = (n_mems - base) < kMaxRingsPerLaunch ? (n_mems - base) : kMaxRingsPerLaunch;
+    int32_t *valid[kMaxRingsPerLaunch];
+    for (int i = 0; i < n; ++i) valid[i] = mems[base + i].valid;
+    st = launch_mem_reset(valid, n, mems[0].B, reset, stream);
+    if (st != TXL_OK) return st;
+  }
+  return TXL_OK;
+}
+
+TXL_API txl_status txl_mem_read_logical(const txl_mem *m, void *out,
+                                        hipStream_t stream) {
+  clear_error();
+  txl_status st = check_rings(m, m ? 1 : 0, "mem_read_logical");
+  if (st != TXL_OK) return st;
+  if (!m) return fail(TXL_ERR_INVALID_ARG, "mem_read_logical: null ring");
+  if (m->M == 0 || m->B == 0) return TXL_OK;
+  if (!out) return fail(TXL_ERR_INVALID_ARG, "mem_read_logical: null out");
+  const int64_t row_bytes = static_cast<int64_t>(m->d) * dtype_size(m->dtype);
+  if (row_bytes % 16) return fail(TXL_ERR_UNSUPPORTED, "mem_read_logical: d * sizeof(dtype) must be a multiple of 16");
+  if (!aligned16(out) || !aligned16(m->data))
+    return fail(TXL_ERR_UNSUPPORTED, "mem_read_logical: not 16-byte aligned");
+  return launch_mem_read_logical(m->data, out, m->B, m->M, m->head, row_bytes, stream);
+}
+
+}  // extern "C"

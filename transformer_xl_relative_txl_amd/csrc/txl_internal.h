@@ -1,0 +1,56 @@
+// Internal declarations shared by the host layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "txl.h"
+
+namespace txl {
+
+// Records a formatted message as the thread's last error and returns `s`.
+txl_status fail(txl_status s, const char *fmt, ...);
+// Maps the last HIP launch error (if any) to TXL_ERR_HIP with its message.
+txl_status check_launch(const char *what);
+
+inline size_t dtype_size(txl_dtype t) { return t == TXL_F32 ? 4 : 2; }
+
+// ---- attention -----------------------------------------------------------
+// Validated launch parameters (strides in elements, scale already resolved).
+struct AttnParams {
+  const void *q, *k, *v, *r, *u, *vb;
+  void *out;
+  float *lse;
+  const int32_t *valid;
+  int64_t q_sb, q_sh, q_sl, kv_sb, kv_sh, kv_sl, r_sh, r_sl, o_sb, o_sh, o_sl;
+  int32_t B, H, L, M;
+  float scale;
+};
+// fp32 / bf16 VALU kernel (one thread per query row).
+txl_status launch_rel_attn_valu(const AttnParams &p, txl_dtype dt,
+                                hipStream_t s);
+// bf16 MFMA kernel.
+txl_status launch_rel_attn_mfma(const AttnParams &p, hipStream_t s);
+
+// ---- memory ring ---------------------------------------------------------
+constexpr int kMaxRingsPerLaunch = 32;
+struct RingBatch {
+  void *data[kMaxRingsPerLaunch];
+  int32_t *valid[kMaxRingsPerLaunch];
+  const void *h[kMaxRingsPerLaunch];
+  int64_t head[kMaxRingsPerLaunch];
+};
+txl_status launch_mem_update(const RingBatch &rb, int n, int B, int M, int L,
+                             int64_t row_bytes, hipStream_t s);
+txl_status launch_mem_reset(int32_t *const *valid, int n, int B,
+                            const uint8_t *reset, hipStream_t s);
+txl_status launch_mem_read_logical(const void *data, void *out, int B, int M,
+                                   int64_t head, int64_t row_bytes,
+                                   hipStream_t s);
+
+// ---- relative-position table ---------------------------------------------
+txl_status launch_rel_pos_table(txl_dtype dt, int M, int L, int d, int HD,
+                                const void *w_r, void *r, hipStream_t s);
+
+}  // namespace txl
