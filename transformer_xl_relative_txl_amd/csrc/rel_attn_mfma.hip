@@ -1,12 +1,326 @@
-// bf16 attention dispatch. The MFMA kernel replaces this forwarding shim.
+// Relative-position attention, bf16 MFMA kernel for gfx950 (CDNA4).
+//
+// For query i and visible key position j ([P1] "Transformer-XL" notes,
+// "Causal Mask With Memory": memory -valid <= j < 0, current 0 <= j <= i):
+//   A_ij = (q_i + u).k_j + (q_i + v).R_{i-j}          ([P1] "Relative Positional
+//          Encoding", regrouped as in [P3] section 2.2)
+//   out_i = sum_j softmax_j(A_ij * scale) v_j         ([P1] "Dimension Walkthrough")
+// R_{i-j} is row t = j' + L - 1 - i of the per-head table (j' = j + M).
+//
+// Design (one workgroup = 4 waves x 32 queries, key tiles of 64):
+//  * Scores are computed transposed, S^T = K (Q')^T with the 32x32x16 bf16
+//    MFMA, Q' = (q+u)*scale*log2(e) held in registers as the B operand. The
+//    accumulator layout of S^T (one query per lane column, keys down the
+//    registers) is exactly the B-operand layout that O^T = V^T P^T needs, so
+//    the probabilities never leave registers.
+//  * The position term uses the same trick with Q'' = (q+v)*scale*log2(e):
+//    band rows R[t] for the wave's distance window are multiplied once each
+//    (64 new rows per key tile, the window slides with the keys), and the
+//    per-query diagonal read (the relative shift, [P1] "Relative Shift
+//    Trick" replaced by index arithmetic) goes through a per-wave LDS ring.
+//    The ring stores band value (u, r) at column (u + r + 1) mod 128 of
+//    query r's row, which turns the skewed read of 4 consecutive keys into
+//    one aligned 16-byte load.
+//  * K and V^T tiles are staged in LDS by the whole workgroup; R rows go
+//    straight from global/L2 into the A operand.
+//  * Online softmax in base 2 (scale folded into Q' and Q''), row max over
+//    the lane's registers plus one exchange with lane^32, row sums kept per
+//    lane and combined once at the end.
+//  * Key tiles run from the row's first valid memory slot to the diagonal;
+//    fully masked tiles are never visited, and only tiles that cross the
+//    diagonal evaluate the mask. Query tiles are scheduled heaviest first
+//    and the (batch, head) index varies fastest, so the tiles of one head
+//    land on the same XCD and share its L2.
 #include <hip/hip_runtime.h>
+
+#include <cmath>
 
 #include "txl_internal.h"
 
 namespace txl {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int DH = 64;         // head dimension served
+constexpr int QW = 32;         // queries per wave (MFMA N)
+constexpr int NW = 4;          // waves per workgroup
+constexpr int BQ = QW * NW;    // queries per workgroup
+constexpr int BK = 64;         // keys per tile
+constexpr int KS = DH + 8;     // K tile row stride (bf16 elements)
+constexpr int VS = BK + 8;     // V^T tile row stride (bf16 elements)
+constexpr int RING = 128;      // band ring columns per query row
+constexpr int RS = RING + 4;   // band ring row stride (floats)
+
+constexpr size_t kLdsK = size_t(BK) * KS * 2;
+constexpr size_t kLdsV = size_t(DH) * VS * 2;
+constexpr size_t kLdsBand = size_t(NW) * QW * RS * 4;
+constexpr size_t kLdsTotal = kLdsK + kLdsV + kLdsBand;
+
+__device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ inline bf16x8 load8(const __bf16 *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+__device__ inline bf16x8 zero8() {
+  bf16x8 z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = static_cast<__bf16>(0.0f);
+  return z;
+}
+
+__global__ __launch_bounds__(256) void rel_attn_mfma_kernel(AttnParams p, int n_qt) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __bf16 *sk = reinterpret_cast<__bf16 *>(smem);
+  __bf16 *svt = reinterpret_cast<__bf16 *>(smem + kLdsK);
+  float *sband = reinterpret_cast<float *>(smem + kLdsK + kLdsV);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int r = lane & 31;   // query within the wave (MFMA column)
+  const int hh = lane >> 5;  // which half of the wave
+
+  // heaviest query tiles first; (batch, head) fastest
+  const int BH = p.B * p.H;
+  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x) / BH;
+  const int bh = static_cast<int>(blockIdx.x) % BH;
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int L = p.L, M = p.M;
+  const int i0 = qt * BQ;
+  const int iw = i0 + wave * QW;
+  const int i = iw + r;
+
+  int valid = p.valid ? p.valid[b] : M;
+  valid = valid < 0 ? 0 : (valid > M ? M : valid);
+  const int j_lo = M - valid;                       // first visible key (logical)
+  const int i_last = (i0 + BQ < L ? i0 + BQ : L) - 1;
+  const int j_end = M + i_last + 1;                 // keys [j_lo, j_end) are staged
+  const int n_tiles = (j_end - j_lo + BK - 1) / BK;
+  const int ML = M + L;
+
+  const __bf16 *qp = static_cast<const __bf16 *>(p.q) + b * p.q_sb + h * p.q_sh;
+  const __bf16 *kp = static_cast<const __bf16 *>(p.k) + b * p.kv_sb + h * p.kv_sh;
+  const __bf16 *vp = static_cast<const __bf16 *>(p.v) + b * p.kv_sb + h * p.kv_sh;
+  const __bf16 *rp = static_cast<const __bf16 *>(p.r) + h * p.r_sh;
+  const __bf16 *up = static_cast<const __bf16 *>(p.u) + h * DH;
+  const __bf16 *vbp = static_cast<const __bf16 *>(p.vb) + h * DH;
+
+  // Q' = (q+u) c and Q'' = (q+v) c as B operands: k-step s holds dims 16s+8hh..+7
+  const float c2 = p.scale * 1.4426950408889634f;
+  bf16x8 qa[4], qb[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int d0 = 16 * s + 8 * hh;
+    const bf16x8 qv = i < L ? load8(qp + static_cast<int64_t>(i) * p.q_sl + d0) : zero8();
+    const bf16x8 uv = load8(up + d0);
+    const bf16x8 vv = load8(vbp + d0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = static_cast<float>(qv[e]);
+      qa[s][e] = static_cast<__bf16>((x + static_cast<float>(uv[e])) * c2);
+      qb[s][e] = static_cast<__bf16>((x + static_cast<float>(vv[e])) * c2);
+    }
+  }
+
+  const bool wave_active = iw < L;
+  f32x16 o_acc[2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) o_acc[db][x] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+  float *band = sband + (wave * QW + r) * RS;  // this lane's query row of the ring
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int j0 = j_lo + kt * BK;
+    __syncthreads();  // the previous tile's K/V^T reads are done
+    // ---- stage K [64 keys][64] ----
+#pragma unroll
+    for (int rep = 0; rep < (BK * DH / 8) / 256; ++rep) {
+      const int cidx = tid + rep * 256;
+      const int row = cidx >> 3, col = (cidx & 7) * 8;
+      const int jj = j0 + row;
+      const bf16x8 val = jj < j_end ? load8(kp + static_cast<int64_t>(jj) * p.kv_sl + col) : zero8();
+      *reinterpret_cast<bf16x8 *>(sk + row * KS + col) = val;
+    }
+    // ---- stage V^T [64 dims][64 keys]: each thread packs two keys ----
+    {
+      // 32-bit word w of a row holds dims 2w (low half) and 2w+1 (high half)
+      const int kq = tid & 31, dc = tid >> 5;
+      const int ja = j0 + 2 * kq, jb = ja + 1;
+      u32x4 wa = {0u, 0u, 0u, 0u}, wb = {0u, 0u, 0u, 0u};
+      if (ja < j_end) wa = *reinterpret_cast<const u32x4 *>(vp + static_cast<int64_t>(ja) * p.kv_sl + 8 * dc);
+      if (jb < j_end) wb = *reinterpret_cast<const u32x4 *>(vp + static_cast<int64_t>(jb) * p.kv_sl + 8 * dc);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t even = (wa[w] & 0xffffu) | (wb[w] << 16);
+        const uint32_t odd = (wa[w] >> 16) | (wb[w] & 0xffff0000u);
+        *reinterpret_cast<uint32_t *>(svt + (8 * dc + 2 * w) * VS + 2 * kq) = even;
+        *reinterpret_cast<uint32_t *>(svt + (8 * dc + 2 * w + 1) * VS + 2 * kq) = odd;
+      }
+    }
+    __syncthreads();
+
+    const bool tile_active = wave_active && (j0 - M <= iw + QW - 1);
+    if (!tile_active) continue;
+
+    // ---- content scores S^T[key][query] = K (Q')^T ----
+    f32x16 s_acc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) s_acc[kb][x] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 a = load8(sk + (kb * 32 + r) * KS + 16 * s + 8 * hh);
+        s_acc[kb] = mfma32(a, qa[s], s_acc[kb]);
+      }
+    }
+
+    // ---- position band: rows u (tile-relative, u = c + 31 - r), t = j0 + u + L - 32 - iw ----
+    for (int bb = (kt == 0 ? 0 : 1); bb < 3; ++bb) {
+      const int t = j0 + 32 * bb + r + L - 32 - iw;
+      const bool t_ok = t >= 0 && t < ML;
+      f32x16 b_acc;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) b_acc[x] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 a = t_ok ? load8(rp + static_cast<int64_t>(t) * p.r_sl + 16 * s + 8 * hh) : zero8();
+        b_acc = mfma32(a, qb[s], b_acc);
+      }
+      // register 4a+c' holds band row u = 32bb + 8a + 4hh + c' for query r
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const int u = 32 * bb + 8 * a4 + 4 * hh + cc;
+          band[(64 * kt + u + r + 1) & (RING - 1)] = b_acc[4 * a4 + cc];
+        }
+    }
+    wave_lds_sync();
+
+    // ---- logits: content + skewed position (log2 units) ----
+    float sv[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int base = (64 * kt + kb * 32 + 8 * a4 + 4 * hh + 32) & (RING - 1);
+        const f32x4 pos = *reinterpret_cast<const f32x4 *>(band + base);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) sv[kb][4 * a4 + cc] = s_acc[kb][4 * a4 + cc] + pos[cc];
+      }
+    // ---- mask: only tiles that reach past the wave's first query ----
+    if (j0 + BK - 1 - M > iw) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const int jj = j0 + kb * 32 + 8 * (x >> 2) + 4 * hh + (x & 3);
+          if (jj - M > i) sv[kb][x] = -INFINITY;
+        }
+    }
+
+    // ---- online softmax ----
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) mt = fmaxf(mt, sv[kb][x]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.0f;
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = __builtin_amdgcn_exp2f(sv[kb][8 * s2 + e] - m_new);
+          psum += pv;
+          pb[kb][s2][e] = static_cast<__bf16>(pv);
+        }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) o_acc[db][x] *= alpha;
+
+    // ---- O^T[d][query] += V^T P^T: k-step (kb, s2) covers keys kb*32 + 16 s2 + {4hh..4hh+3, 8+4hh..8+4hh+3} ----
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const __bf16 *vrow = svt + (db * 32 + r) * VS + kb * 32 + 16 * s2 + 4 * hh;
+          const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vrow);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vrow + 8);
+          bf16x8 a;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[e] = lo[e];
+            a[e + 4] = hi[e];
+          }
+          o_acc[db] = mfma32(a, pb[kb][s2], o_acc[db]);
+        }
+  }
+
+  if (!wave_active) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (i >= L) return;
+  const float inv = 1.0f / l_tot;
+  __bf16 *op = static_cast<__bf16 *>(p.out) + b * p.o_sb + h * p.o_sh + static_cast<int64_t>(i) * p.o_sl;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      bf16x4 o4;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) o4[cc] = static_cast<__bf16>(o_acc[db][4 * a4 + cc] * inv);
+      *reinterpret_cast<bf16x4 *>(op + db * 32 + 8 * a4 + 4 * hh) = o4;
+    }
+  if (p.lse && hh == 0)
+    p.lse[(static_cast<int64_t>(b) * p.H + h) * L + i] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
+}
+
+}  // namespace
 
 txl_status launch_rel_attn_mfma(const AttnParams &p, hipStream_t s) {
-  return launch_rel_attn_valu(p, TXL_BF16, s);
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(rel_attn_mfma_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(kLdsTotal)) != hipSuccess)
+      return fail(TXL_ERR_HIP, "rel_attn: cannot raise the LDS limit to %zu bytes", kLdsTotal);
+    attr_set = true;
+  }
+  const int n_qt = (p.L + BQ - 1) / BQ;
+  const int64_t blocks = static_cast<int64_t>(n_qt) * p.B * p.H;
+  if (blocks > 0x7fffffffLL) return fail(TXL_ERR_UNSUPPORTED, "rel_attn: grid too large");
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(rel_attn_mfma_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256),
+                     kLdsTotal, s, p, n_qt);
+  return check_launch("rel_attn_mfma_kernel");
 }
 
 }  // namespace txl
