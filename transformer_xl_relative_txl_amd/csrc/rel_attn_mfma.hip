@@ -53,12 +53,13 @@ constexpr int BQ = QW * NW;    // queries per workgroup
 constexpr int BK = 64;         // keys per tile
 constexpr int KS = DH + 8;     // K tile row stride (bf16 elements)
 constexpr int VS = BK + 8;     // V^T tile row stride (bf16 elements)
-constexpr int RING = 128;      // band ring columns per query row
-constexpr int RS = RING + 4;   // band ring row stride (floats)
+constexpr int NU = BK + QW;    // band rows per tile: u = c + 31 - r in [0, 95)
+constexpr int US = QW + 2;     // band row stride (floats); odd multiple of 2 -> conflict-free skew
+constexpr float kLazyMax = 8.0f;  // keep the running max until a tile beats it by 2^8
 
 constexpr size_t kLdsK = size_t(BK) * KS * 2;
 constexpr size_t kLdsV = size_t(DH) * VS * 2;
-constexpr size_t kLdsBand = size_t(NW) * QW * RS * 4;
+constexpr size_t kLdsBand = size_t(NW) * NU * US * 4;
 constexpr size_t kLdsTotal = kLdsK + kLdsV + kLdsBand;
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -82,7 +83,57 @@ __device__ inline bf16x8 zero8() {
   return z;
 }
 
-__global__ __launch_bounds__(256) void rel_attn_mfma_kernel(AttnParams p, int n_qt) {
+// Raw buffer loads: the hardware range check returns zeros for rows past the
+// end of a buffer (and for negative offsets), so tile loads need no branches
+// and the compiler can count outstanding loads exactly.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ inline u32x4 bload(rsrc_t rs, int byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0));
+}
+
+// One tile of K (two 16-byte chunks per thread) and V (two keys x 8 dims
+// per thread), held in registers between the global load and the LDS store.
+struct KVRegs {
+  u32x4 k[2];
+  u32x4 va, vb;
+};
+
+__device__ inline void load_kv(KVRegs &x, rsrc_t krs, rsrc_t vrs, int row_bytes, int j0, int tid) {
+#pragma unroll
+  for (int rep = 0; rep < 2; ++rep) {
+    const int cidx = tid + rep * 256;
+    const int row = cidx >> 3, col = (cidx & 7) * 8;
+    x.k[rep] = bload(krs, (j0 + row) * row_bytes + col * 2);
+  }
+  const int kq = tid & 31, dc = tid >> 5;
+  const int ja = j0 + 2 * kq;
+  x.va = bload(vrs, ja * row_bytes + 16 * dc);
+  x.vb = bload(vrs, (ja + 1) * row_bytes + 16 * dc);
+}
+
+__device__ inline void store_kv(const KVRegs &x, __bf16 *sk, __bf16 *svt, int tid) {
+#pragma unroll
+  for (int rep = 0; rep < 2; ++rep) {
+    const int cidx = tid + rep * 256;
+    const int row = cidx >> 3, col = (cidx & 7) * 8;
+    *reinterpret_cast<u32x4 *>(sk + row * KS + col) = x.k[rep];
+  }
+  // V^T: 32-bit word w of a V row holds dims 2w (low half) and 2w+1 (high half)
+  const int kq = tid & 31, dc = tid >> 5;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t even = (x.va[w] & 0xffffu) | (x.vb[w] << 16);
+    const uint32_t odd = (x.va[w] >> 16) | (x.vb[w] & 0xffff0000u);
+    *reinterpret_cast<uint32_t *>(svt + (8 * dc + 2 * w) * VS + 2 * kq) = even;
+    *reinterpret_cast<uint32_t *>(svt + (8 * dc + 2 * w + 1) * VS + 2 * kq) = odd;
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int n_qt) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __bf16 *sk = reinterpret_cast<__bf16 *>(smem);
   __bf16 *svt = reinterpret_cast<__bf16 *>(smem + kLdsK);
@@ -120,6 +171,16 @@ __global__ __launch_bounds__(256) void rel_attn_mfma_kernel(AttnParams p, int n_
   const __bf16 *up = static_cast<const __bf16 *>(p.u) + h * DH;
   const __bf16 *vbp = static_cast<const __bf16 *>(p.vb) + h * DH;
 
+  // keys [0, j_end) and R rows [0, M+L) are in range; the rest read as zero
+  const int kv_row_bytes = static_cast<int>(p.kv_sl) * 2;
+  const int r_row_bytes = static_cast<int>(p.r_sl) * 2;
+  const rsrc_t krs = make_rsrc(kp, static_cast<uint32_t>((j_end - 1) * kv_row_bytes + 2 * DH));
+  const rsrc_t vrs = make_rsrc(vp, static_cast<uint32_t>((j_end - 1) * kv_row_bytes + 2 * DH));
+  const rsrc_t rrs = make_rsrc(rp, static_cast<uint32_t>((ML - 1) * r_row_bytes + 2 * DH));
+
+  KVRegs nxt;
+  load_kv(nxt, krs, vrs, kv_row_bytes, j_lo, tid);
+
   // Q' = (q+u) c and Q'' = (q+v) c as B operands: k-step s holds dims 16s+8hh..+7
   const float c2 = p.scale * 1.4426950408889634f;
   bf16x8 qa[4], qb[4];
@@ -144,39 +205,31 @@ __global__ __launch_bounds__(256) void rel_attn_mfma_kernel(AttnParams p, int n_
 #pragma unroll
     for (int x = 0; x < 16; ++x) o_acc[db][x] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
-  float *band = sband + (wave * QW + r) * RS;  // this lane's query row of the ring
+  float *band = sband + wave * (NU * US);
+  // band[u][r] for this lane: written at u*US + r, the shifted read of key c
+  // is band[(c + 31 - r)][r]
+  float *band_w = band + 4 * hh * US + r;
+  const float *band_r = band + (31 - r + 4 * hh) * US + r;
 
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int j0 = j_lo + kt * BK;
-    __syncthreads();  // the previous tile's K/V^T reads are done
-    // ---- stage K [64 keys][64] ----
-#pragma unroll
-    for (int rep = 0; rep < (BK * DH / 8) / 256; ++rep) {
-      const int cidx = tid + rep * 256;
-      const int row = cidx >> 3, col = (cidx & 7) * 8;
-      const int jj = j0 + row;
-      const bf16x8 val = jj < j_end ? load8(kp + static_cast<int64_t>(jj) * p.kv_sl + col) : zero8();
-      *reinterpret_cast<bf16x8 *>(sk + row * KS + col) = val;
-    }
-    // ---- stage V^T [64 dims][64 keys]: each thread packs two keys ----
-    {
-      // 32-bit word w of a row holds dims 2w (low half) and 2w+1 (high half)
-      const int kq = tid & 31, dc = tid >> 5;
-      const int ja = j0 + 2 * kq, jb = ja + 1;
-      u32x4 wa = {0u, 0u, 0u, 0u}, wb = {0u, 0u, 0u, 0u};
-      if (ja < j_end) wa = *reinterpret_cast<const u32x4 *>(vp + static_cast<int64_t>(ja) * p.kv_sl + 8 * dc);
-      if (jb < j_end) wb = *reinterpret_cast<const u32x4 *>(vp + static_cast<int64_t>(jb) * p.kv_sl + 8 * dc);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t even = (wa[w] & 0xffffu) | (wb[w] << 16);
-        const uint32_t odd = (wa[w] >> 16) | (wb[w] & 0xffff0000u);
-        *reinterpret_cast<uint32_t *>(svt + (8 * dc + 2 * w) * VS + 2 * kq) = even;
-        *reinterpret_cast<uint32_t *>(svt + (8 * dc + 2 * w + 1) * VS + 2 * kq) = odd;
-      }
-    }
-    __syncthreads();
-
     const bool tile_active = wave_active && (j0 - M <= iw + QW - 1);
+
+    __syncthreads();  // the previous tile's K / V^T reads are done
+    store_kv(nxt, sk, svt, tid);
+    // R rows t = j0 + u + L - 32 - iw of the three band blocks (u = 32bb + r);
+    // issued unconditionally so every wait below has a static count
+    bf16x8 rr[3][4];
+#pragma unroll
+    for (int bb = 0; bb < 3; ++bb) {
+      const int t = j0 + 32 * bb + r + L - 32 - iw;  // may fall outside [0, M+L): zeros
+      const int off = t * r_row_bytes + 16 * hh;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) rr[bb][s] = __builtin_bit_cast(bf16x8, bload(rrs, off + 32 * s));
+    }
+    // next tile (past the last one every row is out of range and reads zero)
+    load_kv(nxt, krs, vrs, kv_row_bytes, j0 + BK, tid);
+    __syncthreads();
     if (!tile_active) continue;
 
     // ---- content scores S^T[key][query] = K (Q')^T ----
@@ -192,39 +245,31 @@ __global__ __launch_bounds__(256) void rel_attn_mfma_kernel(AttnParams p, int n_
       }
     }
 
-    // ---- position band: rows u (tile-relative, u = c + 31 - r), t = j0 + u + L - 32 - iw ----
-    for (int bb = (kt == 0 ? 0 : 1); bb < 3; ++bb) {
-      const int t = j0 + 32 * bb + r + L - 32 - iw;
-      const bool t_ok = t >= 0 && t < ML;
+    // ---- position band P[u][query] = R[t(u)] (Q'')^T, 96 rows ----
+#pragma unroll
+    for (int bb = 0; bb < 3; ++bb) {
       f32x16 b_acc;
 #pragma unroll
       for (int x = 0; x < 16; ++x) b_acc[x] = 0.0f;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 a = t_ok ? load8(rp + static_cast<int64_t>(t) * p.r_sl + 16 * s + 8 * hh) : zero8();
-        b_acc = mfma32(a, qb[s], b_acc);
-      }
-      // register 4a+c' holds band row u = 32bb + 8a + 4hh + c' for query r
+      for (int s = 0; s < 4; ++s) b_acc = mfma32(rr[bb][s], qb[s], b_acc);
+      // register 4a+c' holds band row u = 32bb + 8a + 4hh + c'
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4)
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const int u = 32 * bb + 8 * a4 + 4 * hh + cc;
-          band[(64 * kt + u + r + 1) & (RING - 1)] = b_acc[4 * a4 + cc];
-        }
+        for (int cc = 0; cc < 4; ++cc)
+          band_w[(32 * bb + 8 * a4 + cc) * US] = b_acc[4 * a4 + cc];
     }
     wave_lds_sync();
 
-    // ---- logits: content + skewed position (log2 units) ----
+    // ---- logits: content + shifted position (log2 units) ----
     float sv[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const int base = (64 * kt + kb * 32 + 8 * a4 + 4 * hh + 32) & (RING - 1);
-        const f32x4 pos = *reinterpret_cast<const f32x4 *>(band + base);
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) sv[kb][4 * a4 + cc] = s_acc[kb][4 * a4 + cc] + pos[cc];
+      for (int x = 0; x < 16; ++x) {
+        const int c = kb * 32 + 8 * (x >> 2) + (x & 3);  // + 4hh folded into band_r
+        sv[kb][x] = s_acc[kb][x] + band_r[c * US];
       }
     // ---- mask: only tiles that reach past the wave's first query ----
     if (j0 + BK - 1 - M > iw) {
@@ -237,16 +282,22 @@ __global__ __launch_bounds__(256) void rel_attn_mfma_kernel(AttnParams p, int n_
         }
     }
 
-    // ---- online softmax ----
+    // ---- online softmax (the running max moves only when beaten by 2^8) ----
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int x = 0; x < 16; ++x) mt = fmaxf(mt, sv[kb][x]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    if (mt > m_run + kLazyMax) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
+      m_run = mt;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) o_acc[db][x] *= alpha;
+    }
     float psum = 0.0f;
     bf16x8 pb[2][2];
 #pragma unroll
@@ -255,15 +306,11 @@ __global__ __launch_bounds__(256) void rel_attn_mfma_kernel(AttnParams p, int n_
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(sv[kb][8 * s2 + e] - m_new);
+          const float pv = __builtin_amdgcn_exp2f(sv[kb][8 * s2 + e] - m_run);
           psum += pv;
           pb[kb][s2][e] = static_cast<__bf16>(pv);
         }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) o_acc[db][x] *= alpha;
+    l_run += psum;
 
     // ---- O^T[d][query] += V^T P^T: k-step (kb, s2) covers keys kb*32 + 16 s2 + {4hh..4hh+3, 8+4hh..8+4hh+3} ----
 #pragma unroll
@@ -314,6 +361,13 @@ txl_status launch_rel_attn_mfma(const AttnParams &p, hipStream_t s) {
       return fail(TXL_ERR_HIP, "rel_attn: cannot raise the LDS limit to %zu bytes", kLdsTotal);
     attr_set = true;
   }
+  // buffer loads address rows by 32-bit byte offsets from the (batch, head)
+  // base and rely on rows not overlapping for the out-of-range zero fill
+  if (p.kv_sl < DH || p.r_sl < DH || p.q_sl < DH || p.o_sl < DH)
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn: bf16 row strides must be >= d_h");
+  const int64_t ML = static_cast<int64_t>(p.M) + p.L;
+  if ((ML + BK) * p.kv_sl * 2 >= (int64_t(1) << 31) || (ML + BK + QW) * p.r_sl * 2 >= (int64_t(1) << 31))
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn: key / R rows span more than 2 GiB per head");
   const int n_qt = (p.L + BQ - 1) / BQ;
   const int64_t blocks = static_cast<int64_t>(n_qt) * p.B * p.H;
   if (blocks > 0x7fffffffLL) return fail(TXL_ERR_UNSUPPORTED, "rel_attn: grid too large");
