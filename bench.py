@@ -12,8 +12,9 @@ txl_mem_update; the update rotates over 16 ring/segment buffer pairs
 
 Prints one JSON line. `value` is attention TFLOP/s over the whole step
 (algorithmic flops: 6*d_h per visible (query, key) pair, masked pairs not
-counted); per-kernel figures come from HIP events recorded on the launch
-stream around each kernel.
+counted). Every figure replays a captured HIP graph of K launches between
+two HIP events on the launch stream; per-kernel figures come from graphs that
+hold only that kernel.
 """
 from __future__ import annotations
 
@@ -40,7 +41,8 @@ def attn_flops(B, H, L, M_eff, d_h):
 
 def cpu_baseline(x, cfg, seconds: float):
     """Time the fp64 oracle on a bounded sample of the same workload: whole
-    (batch row, head) slices, all queries, in order until `seconds` pass."""
+    (batch row, head) slices, all queries each, cycling over the slices until
+    `seconds` pass."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -51,23 +53,20 @@ def cpu_baseline(x, cfg, seconds: float):
     r = r.astype(np.float64)
     q, k, v = (x[n].double().numpy() for n in ("q", "k", "v"))
     u, vb = x["u"].double().numpy(), x["vb"].double().numpy()
+    slices = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
     done, flops = 0, 0.0
     t0 = time.perf_counter()
     with threadpool_limits(limits=1):
-        for b in range(cfg.B):
-            for h in range(cfg.H):
-                oa.rel_attn(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
-                            r[h:h + 1], u[h:h + 1], vb[h:h + 1], valid=[cfg.M])
-                done += 1
-                flops += attn_flops(1, 1, cfg.L, cfg.M, cfg.d_h)
-                if time.perf_counter() - t0 >= seconds:
-                    break
-            if time.perf_counter() - t0 >= seconds:
-                break
+        while time.perf_counter() - t0 < seconds:
+            b, h = slices[done % len(slices)]
+            oa.rel_attn(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                        r[h:h + 1], u[h:h + 1], vb[h:h + 1], valid=[cfg.M])
+            done += 1
+            flops += attn_flops(1, 1, cfg.L, cfg.M, cfg.d_h)
     el = time.perf_counter() - t0
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 oracle rel-attn on {done} of {cfg.B * cfg.H} (batch row, head) "
-                      f"slices of the same workload, all {cfg.L} queries each, "
+            "sample": f"fp64 oracle rel-attn on {done} (batch row, head) slices of the same "
+                      f"workload ({cfg.B * cfg.H} slices per step), all {cfg.L} queries each, "
                       f"{el:.1f} s, 1 thread"}
 
 
@@ -115,33 +114,69 @@ def main() -> int:
         hs = x["h"] if s == 0 else torch.randn((B, L, d), generator=g).to(torch.bfloat16)
         segs.append(hs.to(dev).contiguous())
 
-    def step(i):
+    def attn():
         txl.txl_rel_attn_fwd(q, k, v, r, u, vb, out, mem_valid=valid)
+
+    def mem(i):
         txl.txl_mem_update([rings[i % N_RING_SETS]], [segs[i % N_RING_SETS]])
 
     for i in range(args.warmup):
-        step(i)
+        attn()
+        mem(i)
     torch.cuda.synchronize()
 
+    # Each figure replays a captured HIP graph of K launches on this stream:
+    # no host launch gaps inside the timed regions. (A replayed ring update
+    # writes the slots its capture saw; the bytes moved are the same.)
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record()
-    for i in range(K):
-        ev[i][0].record()
-        txl.txl_rel_attn_fwd(q, k, v, r, u, vb, out, mem_valid=valid)
-        ev[i][1].record()
-        txl.txl_mem_update([rings[i % N_RING_SETS]], [segs[i % N_RING_SETS]])
-        ev[i][2].record()
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
 
-    step_ms = start.elapsed_time(end) / K
-    attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    mem_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K):
+                fn(i)
+        return g
+
+    # all layers' rings of the 16-layer stack (d=512, B=16, L=M=384) in one
+    # launch: 17 rings x 12.6 MB, two rotating sets (428 MB)
+    sc = txl_synth.STACK_CONFIGS["C4"]
+    n_rings = sc.n_layer + 1
+    multi = []
+    for _s in range(2):
+        mr = [txl.TxlMem(torch.zeros((sc.B, sc.M, sc.d), dtype=torch.bfloat16, device=dev),
+                         torch.full((sc.B,), sc.M, dtype=torch.int32, device=dev), 0)
+              for _ in range(n_rings)]
+        mh = [torch.randn((sc.B, sc.L, sc.d), generator=g).to(torch.bfloat16).to(dev)
+              for _ in range(n_rings)]
+        multi.append((mr, mh))
+    multi_bytes = 2.0 * n_rings * sc.B * min(sc.L, sc.M) * sc.d * 2
+
+    def mem_multi(i):
+        mr, mh = multi[i % 2]
+        txl.txl_mem_update(mr, mh)
+
+    for i in range(2):
+        mem_multi(i)
+    g_step = capture(lambda i: (attn(), mem(i)))
+    g_attn = capture(lambda i: attn())
+    g_mem = capture(lambda i: mem(i))
+
+    def timed(g):
+        g.replay()  # untimed replay: first-touch and cache state
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t = time.perf_counter()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K, time.perf_counter() - t
+
+    step_ms, wall = timed(g_step)
+    attn_ms = timed(g_attn)[0]
+    mem_ms = timed(g_mem)[0]
+    multi_ms = timed(capture(mem_multi))[0]
+
     flops = attn_flops(B, H, L, M, dh)
     Lp = min(L, M)
     mem_bytes = 2.0 * B * Lp * d * 2
@@ -171,6 +206,11 @@ def main() -> int:
         "mem_update": {"bound": "hbm", "achieved": round(mem_gbps, 1), "peak": PEAK_HBM_GBPS,
                        "unit": "GB/s", "frac": round(mem_gbps / PEAK_HBM_GBPS, 4),
                        "bytes_per_launch": mem_bytes, "ms": round(mem_ms, 5)},
+        "mem_update_all_layers": {
+            "workload": "17 rings [16, 384, 512] bf16, L=384, one launch",
+            "achieved": round(multi_bytes / (multi_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "frac": round(multi_bytes / (multi_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "bytes_per_launch": multi_bytes, "ms": round(multi_ms, 5)},
         "attn_ms": round(attn_ms, 5),
         "attn_gflop_per_launch": round(flops / 1e9, 3),
         "wall_s_timed": round(wall, 4),

@@ -6,9 +6,13 @@
 // only the L' = min(L, M) new rows into the slots that held the oldest ones,
 // so an update moves 2*B*L'*d*s bytes instead of shifting all M rows.
 //
-// All three kernels are plain 16-byte copies: one uint4 per thread, rows
-// contiguous in memory, consecutive threads on consecutive 16-byte chunks of
-// a row, so every wavefront reads and writes whole 1 KiB spans.
+// The copies are HBM-bound: each thread moves one 16-byte chunk of the
+// flattened (ring, row, chunk) space, consecutive threads on consecutive
+// chunks (whole 1 KiB spans per wavefront); the most waves in flight gave the
+// best rate for updates of a few MB, where dispatch and ramp-up are a large
+// part of the time. Row indices are split with multiply-shift division by
+// host-computed magic numbers, and both streams carry non-temporal hints:
+// neither side is reread soon.
 #include <hip/hip_runtime.h>
 
 #include "txl_internal.h"
@@ -16,33 +20,63 @@
 namespace txl {
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kChunks = 1;  // 16-byte chunks per thread (more per thread measured slower)
+
+// floor(n / d) = (umulhi(n, m) + n) >> s for 0 <= n < 2^31, d >= 1
+struct FastDiv {
+  uint32_t d, m, s;
+};
+FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((uint64_t(1) << s) < d) ++s;
+  const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1;
+  return FastDiv{d, static_cast<uint32_t>(m), s};
+}
+__device__ inline uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
+
 struct RingMeta {
   int B, M, L, Lp;
-  int64_t cpr;  // 16-byte chunks per row
+  uint32_t cpr;         // 16-byte chunks per row
+  FastDiv div_cpr, div_lp, div_b;
+  uint32_t total;       // chunks in the launch
 };
 
-__global__ __launch_bounds__(256) void mem_update_kernel(RingBatch rb,
-                                                         RingMeta mt,
-                                                         int64_t total) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (e >= total) return;
-  const int64_t row = e / mt.cpr;  // (ring, b, k) flattened
-  const int64_t c = e - row * mt.cpr;
-  const int k = static_cast<int>(row % mt.Lp);
-  const int64_t rb_ = row / mt.Lp;
-  const int b = static_cast<int>(rb_ % mt.B);
-  const int ring = static_cast<int>(rb_ / mt.B);
-  // source row L - L' + k of segment row b; destination slot (head + k) mod M
-  const int64_t src_row = static_cast<int64_t>(b) * mt.L + (mt.L - mt.Lp + k);
-  const int64_t slot = (rb.head[ring] + k) % mt.M;
-  const int64_t dst_row = static_cast<int64_t>(b) * mt.M + slot;
-  const uint4 *src = reinterpret_cast<const uint4 *>(rb.h[ring]) + src_row * mt.cpr + c;
-  uint4 *dst = reinterpret_cast<uint4 *>(rb.data[ring]) + dst_row * mt.cpr + c;
-  *dst = *src;
-  if (k == 0 && c == 0) {
-    const int v = rb.valid[ring][b] + mt.L;
-    rb.valid[ring][b] = v < mt.M ? v : mt.M;
+__global__ __launch_bounds__(kThreads) void mem_update_kernel(RingBatch rb, RingMeta mt) {
+  const uint32_t base = blockIdx.x * (kThreads * kChunks) + threadIdx.x;
+  u32x4 v[kChunks];
+  u32x4 *dst[kChunks];
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    const uint32_t e = base + j * kThreads;
+    dst[j] = nullptr;
+    if (e >= mt.total) continue;
+    const uint32_t row = fdiv(e, mt.div_cpr);  // (ring, b, k) flattened
+    const uint32_t c = e - row * mt.cpr;
+    const uint32_t rk = fdiv(row, mt.div_lp);
+    const uint32_t k = row - rk * mt.Lp;
+    const uint32_t ring = fdiv(rk, mt.div_b);
+    const uint32_t b = rk - ring * mt.B;
+    // source row L - L' + k of segment row b; destination slot (head + k) mod M
+    const int64_t src_row = static_cast<int64_t>(b) * mt.L + (mt.L - mt.Lp + k);
+    int64_t slot = rb.head[ring] + k;
+    if (slot >= mt.M) slot -= mt.M;
+    const int64_t dst_row = static_cast<int64_t>(b) * mt.M + slot;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(rb.h[ring]) + src_row * mt.cpr + c;
+    dst[j] = reinterpret_cast<u32x4 *>(rb.data[ring]) + dst_row * mt.cpr + c;
+    v[j] = __builtin_nontemporal_load(src);
+    if (k == 0 && c == 0) {
+      const int nv = rb.valid[ring][b] + mt.L;
+      rb.valid[ring][b] = nv < mt.M ? nv : mt.M;
+    }
   }
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j)
+    if (dst[j]) __builtin_nontemporal_store(v[j], dst[j]);
 }
 
 struct ValidPtrs {
@@ -57,17 +91,22 @@ __global__ void mem_reset_kernel(ValidPtrs vp, int n, int B,
   if (reset == nullptr || reset[b] != 0) vp.p[ring][b] = 0;
 }
 
-__global__ __launch_bounds__(256) void mem_read_logical_kernel(
-    const uint4 *data, uint4 *out, int M, int64_t head, int64_t cpr,
-    int64_t total) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (e >= total) return;
-  const int64_t row = e / cpr;  // (b, j') flattened
-  const int64_t c = e - row * cpr;
-  const int64_t b = row / M;
-  const int64_t j = row - b * M;
-  const int64_t slot = (head + j) % M;
-  out[row * cpr + c] = data[(b * M + slot) * cpr + c];
+__global__ __launch_bounds__(kThreads) void mem_read_logical_kernel(
+    const u32x4 *data, u32x4 *out, int M, int64_t head, uint32_t cpr, FastDiv div_cpr,
+    FastDiv div_m, uint32_t total) {
+  const uint32_t base = blockIdx.x * (kThreads * kChunks) + threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    const uint32_t e = base + j * kThreads;
+    if (e >= total) return;
+    const uint32_t row = fdiv(e, div_cpr);  // (b, j') flattened
+    const uint32_t c = e - row * cpr;
+    const uint32_t b = fdiv(row, div_m);
+    const uint32_t jl = row - b * M;
+    int64_t slot = head + jl;
+    if (slot >= M) slot -= M;
+    out[static_cast<int64_t>(row) * cpr + c] = data[(static_cast<int64_t>(b) * M + slot) * cpr + c];
+  }
 }
 
 }  // namespace
@@ -79,13 +118,18 @@ txl_status launch_mem_update(const RingBatch &rb, int n, int B, int M, int L,
   mt.M = M;
   mt.L = L;
   mt.Lp = L < M ? L : M;
-  mt.cpr = row_bytes / 16;
-  const int64_t total = static_cast<int64_t>(n) * B * mt.Lp * mt.cpr;
-  const int64_t blocks = (total + 255) / 256;
-  if (blocks > 0x7fffffffLL) return fail(TXL_ERR_UNSUPPORTED, "mem_update: too many rows");
+  const int64_t cpr = row_bytes / 16;
+  const int64_t total = static_cast<int64_t>(n) * B * mt.Lp * cpr;
+  if (total >= (int64_t(1) << 31)) return fail(TXL_ERR_UNSUPPORTED, "mem_update: more than 2^31 chunks");
+  mt.cpr = static_cast<uint32_t>(cpr);
+  mt.div_cpr = make_fastdiv(mt.cpr);
+  mt.div_lp = make_fastdiv(static_cast<uint32_t>(mt.Lp));
+  mt.div_b = make_fastdiv(static_cast<uint32_t>(B));
+  mt.total = static_cast<uint32_t>(total);
+  const int64_t per_block = kThreads * kChunks;
+  const unsigned blocks = static_cast<unsigned>((total + per_block - 1) / per_block);
   (void)hipGetLastError();
-  hipLaunchKernelGGL(mem_update_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                     rb, mt, total);
+  hipLaunchKernelGGL(mem_update_kernel, dim3(blocks), dim3(kThreads), 0, s, rb, mt);
   return check_launch("mem_update_kernel");
 }
 
@@ -105,12 +149,14 @@ txl_status launch_mem_read_logical(const void *data, void *out, int B, int M,
                                    hipStream_t s) {
   const int64_t cpr = row_bytes / 16;
   const int64_t total = static_cast<int64_t>(B) * M * cpr;
-  const int64_t blocks = (total + 255) / 256;
-  if (blocks > 0x7fffffffLL) return fail(TXL_ERR_UNSUPPORTED, "mem_read_logical: too many rows");
+  if (total >= (int64_t(1) << 31)) return fail(TXL_ERR_UNSUPPORTED, "mem_read_logical: more than 2^31 chunks");
+  const int64_t per_block = kThreads * kChunks;
+  const unsigned blocks = static_cast<unsigned>((total + per_block - 1) / per_block);
   (void)hipGetLastError();
-  hipLaunchKernelGGL(mem_read_logical_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     s, reinterpret_cast<const uint4 *>(data), reinterpret_cast<uint4 *>(out), M,
-                     head, cpr, total);
+  hipLaunchKernelGGL(mem_read_logical_kernel, dim3(blocks), dim3(kThreads), 0, s,
+                     reinterpret_cast<const u32x4 *>(data), reinterpret_cast<u32x4 *>(out), M,
+                     head, static_cast<uint32_t>(cpr), make_fastdiv(static_cast<uint32_t>(cpr)),
+                     make_fastdiv(static_cast<uint32_t>(M)), static_cast<uint32_t>(total));
   return check_launch("mem_read_logical_kernel");
 }
 
