@@ -160,6 +160,68 @@ TXL_API txl_status txl_mem_reset_rows(txl_mem *mems, int32_t n_mems,
 TXL_API txl_status txl_mem_read_logical(const txl_mem *m, void *out,
                                         hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * One segment through an N-layer stack ([P2] "019 Transformer-XL", section 3
+ * pseudo-code; [P1] "Segment-Level Recurrence" and "Training and Inference"):
+ *   H^(0) = Emb[tokens]
+ *   for layer n = 1..N:
+ *     Q = H^(n-1) W^Q,  K, V = [SG(M^(n-1)); H^(n-1)] W^{K,V}
+ *         (memory rows read from ring n-1 in logical order; invalid slots
+ *          are skipped; [P1] "Relation to KV Cache": memory holds hidden
+ *          states and is projected again every segment)
+ *     A = txl_rel_attn_fwd(Q, K, V, R^(n), u^(n), v^(n), valid of ring n-1)
+ *     ring n-1 <- Tail_M([M^(n-1); H^(n-1)])   (after it has been read)
+ *     X = LN1(H^(n-1) + A W^O);  H^(n) = LN2(X + GELU(X W1) W2)
+ *   ring N <- Tail_M([M^(N); H^(N)]);  h_out = H^(N)
+ * The layer body after the attention (W^O, post-LayerNorm, exact-erf GELU
+ * feed-forward, no biases) is not on the pages; it is this library's reading.
+ * R^(n) (txl_rel_pos_table of the layer's W_R for distances M+L-1..0) is
+ * built once by txl_stack_create.
+ *
+ * Weights (dtype bf16, device, output-major like a torch Linear weight):
+ *   wq, wk, wv, wr: [H*d_h, d]   wo: [d, H*d_h]   w1: [d_ff, d]   w2: [d, d_ff]
+ *   u, vb: [H, d_h]   ln1_g, ln1_b, ln2_g, ln2_b: [d]   emb: [vocab, d]
+ * Shapes served: dtype bf16, d_h = 64, d and d_ff multiples of 256, H*d_h a
+ * multiple of 128, d <= 4096. Token ids outside [0, vocab) embed as zeros.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t n_layer, d, n_head, d_h, d_ff, vocab, B, L, M;
+  float ln_eps;      /* 0 => 1e-5 */
+  txl_dtype dtype;
+} txl_stack_config;
+
+typedef struct {
+  const void *wq, *wk, *wv, *wo, *wr, *u, *vb, *ln1_g, *ln1_b, *w1, *w2, *ln2_g, *ln2_b;
+} txl_layer_weights;
+
+typedef struct {
+  const void *emb;
+  const txl_layer_weights *layers;  /* n_layer entries, host array */
+} txl_stack_weights;
+
+typedef struct txl_stack txl_stack; /* opaque host object */
+
+/* Bytes of the caller-owned persistent device buffer that holds R per layer. */
+TXL_API size_t txl_stack_persistent_bytes(const txl_stack_config *c);
+/* Checks the configuration, copies the weight pointer table (the weights
+ * themselves must outlive the stack), builds every layer's R into
+ * `persistent` on `stream`, and returns a host object in *out (free it with
+ * txl_stack_destroy). Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE
+ * (persistent_bytes too small), HIP. */
+TXL_API txl_status txl_stack_create(const txl_stack_config *c, const txl_stack_weights *w,
+                                    void *persistent, size_t persistent_bytes,
+                                    hipStream_t stream, txl_stack **out);
+/* Bytes of the caller-owned scratch device buffer txl_segment_step needs. */
+TXL_API size_t txl_segment_step_workspace_bytes(const txl_stack_config *c);
+/* One segment: tokens [B, L] int32 device; mems: n_layer + 1 rings (each
+ * [B, M, d] of the stack's dtype; heads are advanced); h_out [B, L, d].
+ * Calls with the same workspace must not overlap. Errors: INVALID_ARG,
+ * UNSUPPORTED, WORKSPACE, HIP; on an error nothing has been enqueued. */
+TXL_API txl_status txl_segment_step(txl_stack *st, const int32_t *tokens, txl_mem *mems,
+                                    void *h_out, void *workspace, size_t ws_bytes,
+                                    hipStream_t stream);
+TXL_API void txl_stack_destroy(txl_stack *st);
+
 /* ------------------------------------------------------------------------ */
 TXL_API const char *txl_status_str(txl_status s);
 TXL_API const char *txl_last_error(void);  /* thread-local; "" if none */

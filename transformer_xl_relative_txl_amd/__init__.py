@@ -9,6 +9,7 @@ from ._binding import (  # noqa: F401
     TXL_F32,
     TxlError,
     TxlMem,
+    TxlStack,
     lib,
     txl_mem_read_logical,
     txl_mem_reset_rows,

@@ -61,6 +61,24 @@ class TxlMemStruct(ctypes.Structure):
     ]
 
 
+class StackConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("n_layer", "d", "n_head", "d_h", "d_ff", "vocab", "B", "L", "M")] + [
+        ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int)]
+
+
+LAYER_FIELDS = ("wq", "wk", "wv", "wo", "wr", "u", "vb", "ln1_g", "ln1_b", "w1", "w2",
+                "ln2_g", "ln2_b")
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_FIELDS]
+
+
+class StackWeights(ctypes.Structure):
+    _fields_ = [("emb", ctypes.c_void_p), ("layers", ctypes.POINTER(LayerWeights))]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -85,6 +103,18 @@ def _load() -> ctypes.CDLL:
     lib.txl_mem_reset_rows.restype = st
     lib.txl_mem_read_logical.argtypes = [ctypes.POINTER(TxlMemStruct), vp, vp]
     lib.txl_mem_read_logical.restype = st
+    sz = ctypes.c_size_t
+    lib.txl_stack_persistent_bytes.argtypes = [ctypes.POINTER(StackConfig)]
+    lib.txl_stack_persistent_bytes.restype = sz
+    lib.txl_segment_step_workspace_bytes.argtypes = [ctypes.POINTER(StackConfig)]
+    lib.txl_segment_step_workspace_bytes.restype = sz
+    lib.txl_stack_create.argtypes = [ctypes.POINTER(StackConfig), ctypes.POINTER(StackWeights),
+                                     vp, sz, vp, ctypes.POINTER(vp)]
+    lib.txl_stack_create.restype = st
+    lib.txl_segment_step.argtypes = [vp, vp, ctypes.POINTER(TxlMemStruct), vp, vp, sz, vp]
+    lib.txl_segment_step.restype = st
+    lib.txl_stack_destroy.argtypes = [vp]
+    lib.txl_stack_destroy.restype = None
     del i64
     return lib
 
@@ -248,8 +278,74 @@ def txl_mem_read_logical(mem: TxlMem, out: torch.Tensor, stream=None) -> torch.T
     return out
 
 
+class TxlStack:
+    """An N-layer stack (txl_stack_create): weights are torch tensors in the
+    C layout (bf16, output-major, contiguous); the persistent R buffer and
+    the step workspace are device tensors owned by this object."""
+
+    def __init__(self, *, n_layer: int, d: int, n_head: int, d_h: int, d_ff: int, vocab: int,
+                 B: int, L: int, M: int, emb: torch.Tensor, layers: Sequence[dict],
+                 ln_eps: float = 1e-5, stream=None):
+        self.cfg = StackConfig(n_layer, d, n_head, d_h, d_ff, vocab, B, L, M, ln_eps, TXL_BF16)
+        self._keep = [emb] + [t for lw in layers for t in lw.values()]
+        for t in self._keep:
+            assert t.is_cuda and t.is_contiguous() and t.dtype == torch.bfloat16
+        self._layers = (LayerWeights * n_layer)()
+        for i, lw in enumerate(layers):
+            self._layers[i] = LayerWeights(*[lw[n].data_ptr() for n in LAYER_FIELDS])
+        self._weights = StackWeights(emb.data_ptr(), self._layers)
+        pb = lib().txl_stack_persistent_bytes(ctypes.byref(self.cfg))
+        wb = lib().txl_segment_step_workspace_bytes(ctypes.byref(self.cfg))
+        if pb == 0 or wb == 0:
+            raise TxlError("txl_stack_persistent_bytes", 2,
+                           lib().txl_last_error().decode(errors="replace"))
+        dev = emb.device
+        self.persistent = torch.empty(pb, dtype=torch.uint8, device=dev)
+        self.workspace = torch.empty(wb, dtype=torch.uint8, device=dev)
+        h = ctypes.c_void_p()
+        _check("txl_stack_create",
+               lib().txl_stack_create(ctypes.byref(self.cfg), ctypes.byref(self._weights),
+                                      self.persistent.data_ptr(), pb, _stream(stream),
+                                      ctypes.byref(h)))
+        self._h = h
+
+    def r_table(self, layer: int) -> torch.Tensor:
+        """Layer `layer`'s R as built by the library: [M+L, H*d_h] bf16 view."""
+        c = self.cfg
+        hd = c.n_head * c.d_h
+        per = self.persistent.numel() // c.n_layer
+        raw = self.persistent[layer * per: layer * per + (c.M + c.L) * hd * 2]
+        return raw.view(torch.bfloat16).view(c.M + c.L, hd)
+
+    def step(self, tokens: torch.Tensor, mems: Sequence[TxlMem], h_out: torch.Tensor,
+             stream=None) -> torch.Tensor:
+        """txl_segment_step: tokens [B, L] int32, n_layer + 1 rings, h_out [B, L, d]."""
+        assert tokens.dtype == torch.int32 and tokens.is_contiguous()
+        assert len(mems) == self.cfg.n_layer + 1 and h_out.is_contiguous()
+        arr = _structs(mems)
+        _check("txl_segment_step",
+               lib().txl_segment_step(self._h, tokens.data_ptr(), arr, h_out.data_ptr(),
+                                      self.workspace.data_ptr(), self.workspace.numel(),
+                                      _stream(stream)))
+        for i, m in enumerate(mems):
+            m.head = int(arr[i].head)
+        return h_out
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().txl_stack_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def exported_symbols() -> List[str]:
     """Names of the C entry points this binding wraps."""
     return ["txl_rel_pos_table", "txl_rel_attn_fwd", "txl_mem_update",
-            "txl_mem_reset_rows", "txl_mem_read_logical", "txl_status_str",
-            "txl_last_error", "txl_version"]
+            "txl_mem_reset_rows", "txl_mem_read_logical", "txl_stack_persistent_bytes",
+            "txl_stack_create", "txl_segment_step_workspace_bytes", "txl_segment_step",
+            "txl_stack_destroy", "txl_status_str", "txl_last_error", "txl_version"]

@@ -25,6 +25,8 @@ SOURCES = [
     "mem.hip",
     "rel_attn_valu.hip",
     "rel_attn_mfma.hip",
+    "gemm.hip",
+    "stack.cpp",
 ]
 
 ARCH = "gfx950"

@@ -1,0 +1,276 @@
+// Dense layers of the stack: bf16 MFMA GEMM with fused epilogues, LayerNorm,
+// embedding gather.
+//
+// [P1] "Transformer-XL" notes, "Segment-Level Recurrence": Q comes from the
+// current segment, K and V from [SG(mem); H]; [P1] "Relation to KV Cache":
+// the memory holds hidden states before projection, so each segment projects
+// its memory again. The K/V GEMM therefore reads its A rows straight from the
+// ring (in logical order, oldest first) and from the segment, never building
+// [mem; H] in memory, and skips row tiles whose memory slots are all invalid.
+//
+// GEMM: C[m, n] = sum_k A[m, k] W[n, k] (W output-major, like a torch Linear
+// weight), 128 x 128 tile per workgroup of 4 waves (2 x 2, each 64 x 64 as
+// 2 x 2 blocks of v_mfma_f32_32x32x16_bf16), K in slabs of 32 staged in LDS,
+// the next slab prefetched into registers during the MFMAs. Tiles are handed
+// out so that the tiles of one XCD are contiguous in row-major order (the
+// hardware deals workgroups to the 8 XCDs round robin), which keeps a row
+// tile's A rows in one L2.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "txl_internal.h"
+
+namespace txl {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 128, BN = 128, BKS = 32;  // tile rows, cols, K slab
+constexpr int AS = BKS + 8;                   // LDS row stride (bf16 elements)
+constexpr int kXcds = 8;
+
+__device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int E>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) __bf16 sa[BM * AS];
+  __shared__ __attribute__((aligned(16))) __bf16 sb[BN * AS];
+
+  // XCD-contiguous tile assignment (a bijection on [0, T))
+  const int T = gridDim.x;
+  const int bid = blockIdx.x;
+  const int x = bid % kXcds, local = bid / kXcds;
+  const int q = T / kXcds, rem = T % kXcds;
+  const int tile = x * q + (x < rem ? x : rem) + local;
+  const int n_tn = p.N / BN;
+  const int tm = tile / n_tn, tn = tile - tm * n_tn;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, g = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // this thread's two A rows and two W rows (16-byte chunk kc of each 32-slab)
+  const int kc = tid & 3;
+  const __bf16 *arow[2];
+  const __bf16 *wrow[2];
+  int any_valid = 0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = (tid >> 2) + 64 * j;
+    const int m = m0 + row;
+    const __bf16 *src = nullptr;
+    if (m < p.rows) {
+      if (!p.gather) {
+        src = p.a + static_cast<int64_t>(m) * p.lda;
+      } else {
+        const int ml = p.memM + p.segL;
+        const int b = m / ml, jl = m - b * ml;
+        if (jl >= p.memM) {
+          src = p.seg + (static_cast<int64_t>(b) * p.segL + (jl - p.memM)) * p.lda;
+        } else {
+          int valid = p.valid[b];
+          valid = valid < 0 ? 0 : (valid > p.memM ? p.memM : valid);
+          if (jl >= p.memM - valid) {
+            int64_t slot = p.head + jl;
+            if (slot >= p.memM) slot -= p.memM;
+            src = p.ring + (static_cast<int64_t>(b) * p.memM + slot) * p.lda;
+          }
+        }
+      }
+    }
+    arow[j] = src;
+    any_valid |= (src != nullptr);
+    const int n = n0 + row;
+    wrow[j] = n < p.n_split ? p.w0 + static_cast<int64_t>(n) * p.K
+                            : p.w1 + static_cast<int64_t>(n - p.n_split) * p.K;
+  }
+  if (p.gather && !__syncthreads_or(any_valid)) return;  // all rows are empty memory slots
+
+  u32x4 av[2], wv[2];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      av[j] = arow[j] ? *reinterpret_cast<const u32x4 *>(arow[j] + k0 + 8 * kc) : u32x4{0u, 0u, 0u, 0u};
+      wv[j] = *reinterpret_cast<const u32x4 *>(wrow[j] + k0 + 8 * kc);
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][jn][e] = 0.0f;
+
+  load(0);
+  for (int k0 = 0; k0 < p.K; k0 += BKS) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = (tid >> 2) + 64 * j;
+      *reinterpret_cast<u32x4 *>(sa + row * AS + 8 * kc) = av[j];
+      *reinterpret_cast<u32x4 *>(sb + row * AS + 8 * kc) = wv[j];
+    }
+    __syncthreads();
+    if (k0 + BKS < p.K) load(k0 + BKS);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const bf16x8 *>(sa + (wm * 64 + i * 32 + r) * AS + 16 * s + 8 * g);
+#pragma unroll
+      for (int jn = 0; jn < 2; ++jn)
+        bfr[jn] = *reinterpret_cast<const bf16x8 *>(sb + (wn * 64 + jn * 32 + r) * AS + 16 * s + 8 * g);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn) acc[i][jn] = mfma32(af[i], bfr[jn], acc[i][jn]);
+    }
+  }
+
+  // epilogue: register 4a+c of block (i, jn) holds C[wm*64 + 32i + 8a + 4g + c][wn*64 + 32jn + r]
+  const bool second = n0 >= p.n_split;
+#pragma unroll
+  for (int jn = 0; jn < 2; ++jn) {
+    const int n = n0 + wn * 64 + jn * 32 + r;
+    const int nc = second ? n - p.n_split : n;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int m = m0 + wm * 64 + i * 32 + 8 * a4 + 4 * g + c;
+          if (m >= p.rows) continue;
+          float v = acc[i][jn][4 * a4 + c];
+          if (E == kEpiResidualF32) {
+            v += static_cast<float>(p.res[static_cast<int64_t>(m) * p.ldres + nc]);
+            static_cast<float *>(second ? p.c1 : p.c0)[static_cast<int64_t>(m) * p.ldc + nc] = v;
+          } else {
+            if (E == kEpiGeluBf16) v = 0.5f * v * (1.0f + erff(v * 0.7071067811865476f));
+            static_cast<__bf16 *>(second ? p.c1 : p.c0)[static_cast<int64_t>(m) * p.ldc + nc] =
+                static_cast<__bf16>(v);
+          }
+        }
+  }
+}
+
+// LayerNorm over rows of fp32 x: y = (x - mean) / sqrt(var + eps) * gamma + beta,
+// biased variance, one wave per row, result rounded to bf16.
+constexpr int kLnMaxChunks = 16;  // 4-float chunks per lane: d <= 4096
+
+__global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict__ x,
+                                                        const __bf16 *__restrict__ gamma,
+                                                        const __bf16 *__restrict__ beta,
+                                                        __bf16 *__restrict__ y, int rows, int d,
+                                                        float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int nch = d / 256;
+  const float *xr = x + static_cast<int64_t>(row) * d;
+  f32x4 v[kLnMaxChunks];
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kLnMaxChunks; ++c) {
+    if (c < nch) {
+      v[c] = *reinterpret_cast<const f32x4 *>(xr + 256 * c + 4 * lane);
+      s += (v[c][0] + v[c][1]) + (v[c][2] + v[c][3]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  const float mean = s / d;
+  float ss = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kLnMaxChunks; ++c) {
+    if (c < nch) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float t = v[c][e] - mean;
+        ss += t * t;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  const float inv = 1.0f / sqrtf(ss / d + eps);
+  __bf16 *yr = y + static_cast<int64_t>(row) * d;
+#pragma unroll
+  for (int c = 0; c < kLnMaxChunks; ++c) {
+    if (c < nch) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int col = 256 * c + 4 * lane + e;
+        yr[col] = static_cast<__bf16>((v[c][e] - mean) * inv * static_cast<float>(gamma[col]) +
+                                      static_cast<float>(beta[col]));
+      }
+    }
+  }
+}
+
+// H0[b, l, :] = emb[tokens[b, l], :]; ids outside [0, vocab) give a zero row.
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ tokens,
+                                                    const u32x4 *__restrict__ emb,
+                                                    u32x4 *__restrict__ out, int vocab,
+                                                    int cpr, int64_t total) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int64_t row = e / cpr;
+  const int c = static_cast<int>(e - row * cpr);
+  const int tok = tokens[row];
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (tok >= 0 && tok < vocab) v = emb[static_cast<int64_t>(tok) * cpr + c];
+  out[e] = v;
+}
+
+}  // namespace
+
+txl_status launch_gemm(const GemmParams &p, int epi, hipStream_t s) {
+  if (p.rows <= 0) return TXL_OK;
+  const int64_t tiles = static_cast<int64_t>((p.rows + BM - 1) / BM) * (p.N / BN);
+  if (tiles > 0x7fffffffLL) return fail(TXL_ERR_UNSUPPORTED, "gemm: too many tiles");
+  (void)hipGetLastError();
+  const dim3 grid(static_cast<unsigned>(tiles)), block(256);
+  if (epi == kEpiStoreBf16)
+    hipLaunchKernelGGL(gemm_kernel<kEpiStoreBf16>, grid, block, 0, s, p);
+  else if (epi == kEpiGeluBf16)
+    hipLaunchKernelGGL(gemm_kernel<kEpiGeluBf16>, grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL(gemm_kernel<kEpiResidualF32>, grid, block, 0, s, p);
+  return check_launch("gemm_kernel");
+}
+
+txl_status launch_layernorm(const float *x, const void *gamma, const void *beta, void *y,
+                            int rows, int d, float eps, hipStream_t s) {
+  if (rows <= 0) return TXL_OK;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(layernorm_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, x,
+                     static_cast<const __bf16 *>(gamma), static_cast<const __bf16 *>(beta),
+                     static_cast<__bf16 *>(y), rows, d, eps);
+  return check_launch("layernorm_kernel");
+}
+
+txl_status launch_embed(const int32_t *tokens, const void *emb, void *out, int rows, int d,
+                        int vocab, hipStream_t s) {
+  const int cpr = d * 2 / 16;
+  const int64_t total = static_cast<int64_t>(rows) * cpr;
+  if (total == 0) return TXL_OK;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(embed_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
+                     s, tokens, static_cast<const u32x4 *>(emb), static_cast<u32x4 *>(out), vocab,
+                     cpr, total);
+  return check_launch("embed_kernel");
+}
+
+}  // namespace txl

@@ -53,4 +53,32 @@ txl_status launch_mem_read_logical(const void *data, void *out, int B, int M,
 txl_status launch_rel_pos_table(txl_dtype dt, int M, int L, int d, int HD,
                                 const void *w_r, void *r, hipStream_t s);
 
+// ---- dense layers of the stack ---------------------------------------------
+enum { kEpiStoreBf16 = 0, kEpiGeluBf16 = 1, kEpiResidualF32 = 2 };
+// C[m, n] = sum_k A[m, k] W[n, k]; N split at n_split between (w0, c0) and
+// (w1, c1); n_split and N are multiples of 128, K a multiple of 32.
+struct GemmParams {
+  int rows, N, K;
+  // A rows: dense (a + m*lda), or gathered over [ring memory; segment] of
+  // each batch row (rows = B*(memM+segL), both with row stride lda)
+  const __bf16 *a;
+  int64_t lda;
+  int gather;
+  const __bf16 *ring, *seg;
+  const int32_t *valid;
+  int64_t head;
+  int memM, segL;
+  const __bf16 *w0, *w1;
+  int n_split;
+  void *c0, *c1;
+  int64_t ldc;
+  const __bf16 *res;  // residual [rows, ldres] for kEpiResidualF32
+  int64_t ldres;
+};
+txl_status launch_gemm(const GemmParams &p, int epi, hipStream_t s);
+txl_status launch_layernorm(const float *x, const void *gamma, const void *beta, void *y,
+                            int rows, int d, float eps, hipStream_t s);
+txl_status launch_embed(const int32_t *tokens, const void *emb, void *out, int rows, int d,
+                        int vocab, hipStream_t s);
+
 }  // namespace txl
