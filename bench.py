@@ -33,6 +33,12 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 N_RING_SETS = 16
 
+# HBM bytes per attention launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# (scaled by the same counters' reading of a plain copy of known size),
+# valid only for the kernel source they were taken on.
+ATTN_TRAFFIC = {"source_sha1": "f17e03237fd062b94bc2c6e4c54400de6bb5b3d2",
+                "bytes": 53.62e6}
+
 
 def attn_flops(B, H, L, M_eff, d_h):
     pairs = B * (L * M_eff + L * (L + 1) // 2)
@@ -70,6 +76,72 @@ def cpu_baseline(x, cfg, seconds: float):
                       f"{el:.1f} s, 1 thread"}
 
 
+def stack_flops(c, m_eff):
+    """Algorithmic flops of one segment step with m_eff valid memory states:
+    the Q, K/V (over m_eff + L rows), W^O and feed-forward products, plus the
+    attention's three contractions over visible pairs. R is built once per
+    stack and is not counted."""
+    hd = c.H * c.d_h
+    rows = c.B * c.L
+    per_layer = (2 * rows * c.d * hd + 4 * c.B * (m_eff + c.L) * c.d * hd
+                 + 2 * rows * hd * c.d + 4 * rows * c.d * c.d_ff
+                 + attn_flops(c.B, c.H, c.L, m_eff, c.d_h))
+    return c.n_layer * per_layer
+
+
+def stack_bench(name: str, steps: int, warmup: int) -> dict:
+    """One segment step of the stack with a full memory (steady state),
+    captured once as a HIP graph and replayed `steps` times between events."""
+    import torch
+
+    import txl_synth
+    import transformer_xl_relative_txl_amd as txl
+
+    c = txl_synth.STACK_CONFIGS[name]
+    dev = torch.device("cuda:0")
+    w = txl_synth.stack_weights(c)
+    out_major = ("wq", "wk", "wv", "wo", "wr", "w1", "w2")
+    emb = w["emb"].to(dev).contiguous()
+    layers = [{k: (t.t() if k in out_major else t).contiguous().to(dev) for k, t in lw.items()}
+              for lw in w["layers"]]
+    st = txl.TxlStack(n_layer=c.n_layer, d=c.d, n_head=c.H, d_h=c.d_h, d_ff=c.d_ff,
+                      vocab=c.vocab, B=c.B, L=c.L, M=c.M, emb=emb, layers=layers)
+    tokens = txl_synth.stack_tokens(c).to(dev)
+    mems = [txl.TxlMem.empty(c.B, c.M, c.d, device=dev) for _ in range(c.n_layer + 1)]
+    h = torch.empty((c.B, c.L, c.d), dtype=torch.bfloat16, device=dev)
+    s = 0
+    while int(mems[0].valid.min().item()) < c.M or s < warmup:   # fill the memory
+        st.step(tokens[s % c.n_seg].contiguous(), mems, h)
+        s += 1
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.step(tokens[0].contiguous(), mems, h)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fl = stack_flops(c, c.M)
+    st.close()
+    tflops = fl / (ms * 1e-3) / 1e12
+    return {"metric": "segment step TFLOP/s (N-layer stack, steady-state memory), 1 GPU",
+            "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+            "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"{c.n_layer}-layer stack segment step, d={c.d} H={c.H} "
+                                   f"d_ff={c.d_ff} B={c.B} L={c.L} M={c.M} (memory full)",
+                       "tokens_per_s": round(c.B * c.L / (ms * 1e-3), 1)},
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None},
+            "gflop_per_step": round(fl / 1e9, 2)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -77,12 +149,19 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle CPU baseline (0 skips it)")
+    ap.add_argument("--stack", choices=["C4", "C5"], default=None,
+                    help="measure the N-layer segment step instead (16-layer d=512 "
+                         "workload or 18-layer d=1024 long-memory workload)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not run "
               "(the step shards over batch rows with no communication; see DESIGN.md)",
               file=sys.stderr)
         return 2
+
+    if args.stack:
+        print(json.dumps(stack_bench(args.stack, args.steps, args.warmup)), flush=True)
+        return 0
 
     import torch
 
@@ -177,6 +256,12 @@ def main() -> int:
     mem_ms = timed(g_mem)[0]
     multi_ms = timed(capture(mem_multi))[0]
 
+    import hashlib
+    src = os.path.join(ROOT, "transformer_xl_relative_txl_amd", "csrc", "rel_attn_mfma.hip")
+    with open(src, "rb") as fh:
+        same_kernel = hashlib.sha1(fh.read()).hexdigest() == ATTN_TRAFFIC["source_sha1"]
+    traffic = ATTN_TRAFFIC["bytes"] if same_kernel else None
+
     flops = attn_flops(B, H, L, M, dh)
     Lp = min(L, M)
     mem_bytes = 2.0 * B * Lp * d * 2
@@ -202,7 +287,7 @@ def main() -> int:
                    "seed": cfg.seed},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "mem_update": {"bound": "hbm", "achieved": round(mem_gbps, 1), "peak": PEAK_HBM_GBPS,
                        "unit": "GB/s", "frac": round(mem_gbps / PEAK_HBM_GBPS, 4),
                        "bytes_per_launch": mem_bytes, "ms": round(mem_ms, 5)},
