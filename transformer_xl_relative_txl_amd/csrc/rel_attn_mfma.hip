@@ -53,14 +53,14 @@ constexpr int BQ = QW * NW;    // queries per workgroup
 constexpr int BK = 64;         // keys per tile
 constexpr int KS = DH + 8;     // K tile row stride (bf16 elements)
 constexpr int VS = BK + 8;     // V^T tile row stride (bf16 elements)
-constexpr int NU = BK + QW;    // band rows per tile: u = c + 31 - r in [0, 95)
+constexpr int NU = 2 * QW;     // band rows held at once: one 32-key half needs u = c + 31 - r in [0, 63)
 constexpr int US = QW + 2;     // band row stride (floats); odd multiple of 2 -> conflict-free skew
 constexpr float kLazyMax = 8.0f;  // keep the running max until a tile beats it by 2^8
 
-constexpr size_t kLdsK = size_t(BK) * KS * 2;
-constexpr size_t kLdsV = size_t(DH) * VS * 2;
+constexpr size_t kLdsK = size_t(BK) * KS * 2;   // one K tile
+constexpr size_t kLdsV = size_t(DH) * VS * 2;   // one V^T tile
 constexpr size_t kLdsBand = size_t(NW) * NU * US * 4;
-constexpr size_t kLdsTotal = kLdsK + kLdsV + kLdsBand;
+constexpr size_t kLdsTotal = 2 * (kLdsK + kLdsV) + kLdsBand;  // K / V^T double-buffered
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -135,9 +135,8 @@ __device__ inline void store_kv(const KVRegs &x, __bf16 *sk, __bf16 *svt, int ti
 
 __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int n_qt) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __bf16 *sk = reinterpret_cast<__bf16 *>(smem);
-  __bf16 *svt = reinterpret_cast<__bf16 *>(smem + kLdsK);
-  float *sband = reinterpret_cast<float *>(smem + kLdsK + kLdsV);
+  // buffer p holds K at smem + p*(kLdsK + kLdsV), V^T right after it
+  float *sband = reinterpret_cast<float *>(smem + 2 * (kLdsK + kLdsV));
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -211,125 +210,150 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
   float *band_w = band + 4 * hh * US + r;
   const float *band_r = band + (31 - r + 4 * hh) * US + r;
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int j0 = j_lo + kt * BK;
-    const bool tile_active = wave_active && (j0 - M <= iw + QW - 1);
-
-    __syncthreads();  // the previous tile's K / V^T reads are done
-    store_kv(nxt, sk, svt, tid);
-    // R rows t = j0 + u + L - 32 - iw of the three band blocks (u = 32bb + r);
-    // issued unconditionally so every wait below has a static count
-    bf16x8 rr[3][4];
+  // R rows t = j0 + u + L - 32 - iw of the three band blocks (u = 32bb + r),
+  // loaded one tile ahead into the registers the band MFMAs have just freed;
+  // rows outside [0, M+L) read as zero
+  bf16x8 rr[3][4];
+  auto load_r = [&](int j0) {
 #pragma unroll
     for (int bb = 0; bb < 3; ++bb) {
-      const int t = j0 + 32 * bb + r + L - 32 - iw;  // may fall outside [0, M+L): zeros
-      const int off = t * r_row_bytes + 16 * hh;
+      const int off = (j0 + 32 * bb + r + L - 32 - iw) * r_row_bytes + 16 * hh;
 #pragma unroll
       for (int s = 0; s < 4; ++s) rr[bb][s] = __builtin_bit_cast(bf16x8, bload(rrs, off + 32 * s));
     }
-    // next tile (past the last one every row is out of range and reads zero)
-    load_kv(nxt, krs, vrs, kv_row_bytes, j0 + BK, tid);
-    __syncthreads();
-    if (!tile_active) continue;
+  };
+  load_r(j_lo);
 
-    // ---- content scores S^T[key][query] = K (Q')^T ----
-    f32x16 s_acc[2];
+  // tile 0 into buffer 0, tile 1 in flight
+  store_kv(nxt, reinterpret_cast<__bf16 *>(smem), reinterpret_cast<__bf16 *>(smem + kLdsK), tid);
+  load_kv(nxt, krs, vrs, kv_row_bytes, j_lo + BK, tid);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int j0 = j_lo + kt * BK;
+    // Every wave runs every tile of its workgroup (no branch, so the compiler
+    // can count outstanding loads): a tile past a wave's diagonal is fully
+    // masked and leaves (m, l, O) unchanged, and the wave would otherwise wait
+    // at the barrier.
+    unsigned char *buf = smem + (kt & 1) * (kLdsK + kLdsV);
+    const __bf16 *sk = reinterpret_cast<const __bf16 *>(buf);
+    const __bf16 *svt = reinterpret_cast<const __bf16 *>(buf + kLdsK);
+
+    {
+      // ---- content scores S^T[key][query] = K (Q')^T ----
+      f32x16 s_acc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int x = 0; x < 16; ++x) s_acc[kb][x] = 0.0f;
+        for (int x = 0; x < 16; ++x) s_acc[kb][x] = 0.0f;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 a = load8(sk + (kb * 32 + r) * KS + 16 * s + 8 * hh);
-        s_acc[kb] = mfma32(a, qa[s], s_acc[kb]);
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 a = load8(sk + (kb * 32 + r) * KS + 16 * s + 8 * hh);
+          s_acc[kb] = mfma32(a, qa[s], s_acc[kb]);
+        }
       }
-    }
 
-    // ---- position band P[u][query] = R[t(u)] (Q'')^T, 96 rows ----
+      // ---- position band P[u][query] = R[t(u)] (Q'')^T, three blocks of 32 rows ----
+      f32x16 b_acc[3];
 #pragma unroll
-    for (int bb = 0; bb < 3; ++bb) {
-      f32x16 b_acc;
+      for (int bb = 0; bb < 3; ++bb) {
 #pragma unroll
-      for (int x = 0; x < 16; ++x) b_acc[x] = 0.0f;
+        for (int x = 0; x < 16; ++x) b_acc[bb][x] = 0.0f;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) b_acc = mfma32(rr[bb][s], qb[s], b_acc);
-      // register 4a+c' holds band row u = 32bb + 8a + 4hh + c'
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-          band_w[(32 * bb + 8 * a4 + cc) * US] = b_acc[4 * a4 + cc];
-    }
-    wave_lds_sync();
-
-    // ---- logits: content + shifted position (log2 units) ----
-    float sv[2][16];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int c = kb * 32 + 8 * (x >> 2) + (x & 3);  // + 4hh folded into band_r
-        sv[kb][x] = s_acc[kb][x] + band_r[c * US];
+        for (int s = 0; s < 4; ++s) b_acc[bb] = mfma32(rr[bb][s], qb[s], b_acc[bb]);
       }
-    // ---- mask: only tiles that reach past the wave's first query ----
-    if (j0 + BK - 1 - M > iw) {
+      // next tile's R rows into the registers just consumed
+      load_r(j0 + BK);
+
+      // register 4a+c' of block bb holds band row u = 32bb + 8a + 4hh + c'. The
+      // 32-key half kb needs rows u = c + 31 - r in [32kb, 32kb + 63): blocks kb
+      // and kb+1, stored as rows 0..63 so both halves read the same addresses.
+      float sv[2][16];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+              band_w[(32 * half + 8 * a4 + cc) * US] = b_acc[kb + half][4 * a4 + cc];
+        wave_lds_sync();
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const int c = 8 * (x >> 2) + (x & 3);  // key within the half (+ 4hh folded into band_r)
+          sv[kb][x] = s_acc[kb][x] + band_r[c * US];
+        }
+        wave_lds_sync();  // reads done before the next half overwrites the rows
+      }
+
+      // ---- mask: only tiles that reach past the wave's first query ----
+      if (j0 + BK - 1 - M > iw) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const int jj = j0 + kb * 32 + 8 * (x >> 2) + 4 * hh + (x & 3);
+            if (jj - M > i) sv[kb][x] = -INFINITY;
+          }
+      }
+
+      // ---- online softmax (the running max moves only when beaten by 2^8) ----
+      float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const int jj = j0 + kb * 32 + 8 * (x >> 2) + 4 * hh + (x & 3);
-          if (jj - M > i) sv[kb][x] = -INFINITY;
-        }
-    }
+        for (int x = 0; x < 16; ++x) mt = fmaxf(mt, sv[kb][x]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      if (mt > m_run + kLazyMax) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
+        m_run = mt;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) o_acc[db][x] *= alpha;
+      }
+      float psum = 0.0f;
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(sv[kb][8 * s2 + e] - m_run);
+            psum += pv;
+            pb[kb][s2][e] = static_cast<__bf16>(pv);
+          }
+      l_run += psum;
 
-    // ---- online softmax (the running max moves only when beaten by 2^8) ----
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) mt = fmaxf(mt, sv[kb][x]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    if (mt > m_run + kLazyMax) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
-      m_run = mt;
-      l_run *= alpha;
+      // ---- O^T[d][query] += V^T P^T: k-step (kb, s2) covers keys kb*32 + 16 s2 + {4hh..4hh+3, 8+4hh..8+4hh+3} ----
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) o_acc[db][x] *= alpha;
-    }
-    float psum = 0.0f;
-    bf16x8 pb[2][2];
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const __bf16 *vrow = svt + (db * 32 + r) * VS + kb * 32 + 16 * s2 + 4 * hh;
+            const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vrow);
+            const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vrow + 8);
+            bf16x8 a;
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(sv[kb][8 * s2 + e] - m_run);
-          psum += pv;
-          pb[kb][s2][e] = static_cast<__bf16>(pv);
-        }
-    l_run += psum;
-
-    // ---- O^T[d][query] += V^T P^T: k-step (kb, s2) covers keys kb*32 + 16 s2 + {4hh..4hh+3, 8+4hh..8+4hh+3} ----
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const __bf16 *vrow = svt + (db * 32 + r) * VS + kb * 32 + 16 * s2 + 4 * hh;
-          const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vrow);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vrow + 8);
-          bf16x8 a;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a[e] = lo[e];
-            a[e + 4] = hi[e];
+            for (int e = 0; e < 4; ++e) {
+              a[e] = lo[e];
+              a[e + 4] = hi[e];
+            }
+            o_acc[db] = mfma32(a, pb[kb][s2], o_acc[db]);
           }
-          o_acc[db] = mfma32(a, pb[kb][s2], o_acc[db]);
-        }
+    }
+
+    // stage tile kt+1 into the other buffer (its last readers finished before
+    // the previous barrier) and start loading tile kt+2
+    unsigned char *nbuf = smem + ((kt + 1) & 1) * (kLdsK + kLdsV);
+    store_kv(nxt, reinterpret_cast<__bf16 *>(nbuf), reinterpret_cast<__bf16 *>(nbuf + kLdsK), tid);
+    load_kv(nxt, krs, vrs, kv_row_bytes, j0 + 2 * BK, tid);
+    __syncthreads();
   }
 
   if (!wave_active) return;
