@@ -9,12 +9,13 @@
 // [mem; H] in memory, and skips row tiles whose memory slots are all invalid.
 //
 // GEMM: C[m, n] = sum_k A[m, k] W[n, k] (W output-major, like a torch Linear
-// weight), 128 x 128 tile per workgroup of 4 waves (2 x 2, each 64 x 64 as
-// 2 x 2 blocks of v_mfma_f32_32x32x16_bf16), K in slabs of 32 staged in LDS,
-// the next slab prefetched into registers during the MFMAs. Tiles are handed
-// out so that the tiles of one XCD are contiguous in row-major order (the
-// hardware deals workgroups to the 8 XCDs round robin), which keeps a row
-// tile's A rows in one L2.
+// weight), tiles of 128 or 64 rows x 128 or 64 columns per workgroup of 4
+// waves (chosen per call so a launch has about two tiles per CU), blocks of
+// v_mfma_f32_32x32x16_bf16, K in slabs of 32 or 64 through two LDS buffers with one
+// barrier per slab, the next slab prefetched into registers during the MFMAs.
+// Tiles are handed out so that the tiles of one XCD are contiguous in
+// row-major order (the hardware deals workgroups to the 8 XCDs round robin),
+// which keeps a row tile's A rows in one L2.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -29,18 +30,24 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128, BKS = 32;  // tile rows, cols, K slab
-constexpr int AS = BKS + 8;                   // LDS row stride (bf16 elements)
 constexpr int kXcds = 8;
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int E>
+// Tile BM x BN (each 64 or 128) per workgroup of 4 waves arranged 2 x 2; a
+// wave computes (BM/2) x (BN/2) as blocks of 32 x 32. K runs in slabs of BKS
+// (32 or 64) through two LDS buffers: the next slab is loaded into registers while the
+// MFMAs run and stored into the other buffer, one barrier per slab.
+template <int E, int BM, int BN, int BKS>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 sa[BM * AS];
-  __shared__ __attribute__((aligned(16))) __bf16 sb[BN * AS];
+  constexpr int AS = BKS + 8;                    // LDS row stride (bf16 elements)
+  constexpr int WM = BM / 64, WN = BN / 64;      // 32x32 blocks per wave
+  constexpr int A_CH = BM * BKS / 8 / 256;       // 16-byte chunks per thread
+  constexpr int B_CH = BN * BKS / 8 / 256;
+  __shared__ __attribute__((aligned(16))) __bf16 sa[2][BM * AS];
+  __shared__ __attribute__((aligned(16))) __bf16 sb[2][BN * AS];
 
   // XCD-contiguous tile assignment (a bijection on [0, T))
   const int T = gridDim.x;
@@ -57,14 +64,16 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
   const int r = lane & 31, g = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // this thread's two A rows and two W rows (16-byte chunk kc of each 32-slab)
-  const int kc = tid & 3;
-  const __bf16 *arow[2];
-  const __bf16 *wrow[2];
+  // this thread's A rows and W rows (16-byte chunk kc of each 32-wide slab)
+  constexpr int CPR = BKS / 8;                   // 16-byte chunks per slab row
+  constexpr int RPP = 256 / CPR;                 // rows covered per pass of the block
+  const int kc = tid % CPR;
+  const __bf16 *arow[A_CH];
+  const __bf16 *wrow[B_CH];
   int any_valid = 0;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = (tid >> 2) + 64 * j;
+  for (int j = 0; j < A_CH; ++j) {
+    const int row = tid / CPR + RPP * j;
     const int m = m0 + row;
     const __bf16 *src = nullptr;
     if (m < p.rows) {
@@ -88,69 +97,82 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
     }
     arow[j] = src;
     any_valid |= (src != nullptr);
-    const int n = n0 + row;
+  }
+#pragma unroll
+  for (int j = 0; j < B_CH; ++j) {
+    const int n = n0 + tid / CPR + RPP * j;
     wrow[j] = n < p.n_split ? p.w0 + static_cast<int64_t>(n) * p.K
                             : p.w1 + static_cast<int64_t>(n - p.n_split) * p.K;
   }
   if (p.gather && !__syncthreads_or(any_valid)) return;  // all rows are empty memory slots
 
-  u32x4 av[2], wv[2];
+  u32x4 av[A_CH], wv[B_CH];
   auto load = [&](int k0) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < A_CH; ++j)
       av[j] = arow[j] ? *reinterpret_cast<const u32x4 *>(arow[j] + k0 + 8 * kc) : u32x4{0u, 0u, 0u, 0u};
-      wv[j] = *reinterpret_cast<const u32x4 *>(wrow[j] + k0 + 8 * kc);
-    }
+#pragma unroll
+    for (int j = 0; j < B_CH; ++j) wv[j] = *reinterpret_cast<const u32x4 *>(wrow[j] + k0 + 8 * kc);
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < A_CH; ++j)
+      *reinterpret_cast<u32x4 *>(&sa[buf][(tid / CPR + RPP * j) * AS + 8 * kc]) = av[j];
+#pragma unroll
+    for (int j = 0; j < B_CH; ++j)
+      *reinterpret_cast<u32x4 *>(&sb[buf][(tid / CPR + RPP * j) * AS + 8 * kc]) = wv[j];
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[WM][WN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int jn = 0; jn < 2; ++jn)
+    for (int jn = 0; jn < WN; ++jn)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][jn][e] = 0.0f;
 
+  const int n_slab = p.K / BKS;
   load(0);
-  for (int k0 = 0; k0 < p.K; k0 += BKS) {
-    __syncthreads();
+  store(0);
+  __syncthreads();
+  for (int ks = 0; ks < n_slab; ++ks) {
+    const int cur = ks & 1;
+    const bool more = ks + 1 < n_slab;
+    if (more) load((ks + 1) * BKS);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = (tid >> 2) + 64 * j;
-      *reinterpret_cast<u32x4 *>(sa + row * AS + 8 * kc) = av[j];
-      *reinterpret_cast<u32x4 *>(sb + row * AS + 8 * kc) = wv[j];
+    for (int s = 0; s < BKS / 16; ++s) {
+      bf16x8 af[WM], bfr[WN];
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8 *>(
+            &sa[cur][(wm * (BM / 2) + i * 32 + r) * AS + 16 * s + 8 * g]);
+#pragma unroll
+      for (int jn = 0; jn < WN; ++jn)
+        bfr[jn] = *reinterpret_cast<const bf16x8 *>(
+            &sb[cur][(wn * (BN / 2) + jn * 32 + r) * AS + 16 * s + 8 * g]);
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < WN; ++jn) acc[i][jn] = mfma32(af[i], bfr[jn], acc[i][jn]);
     }
+    if (more) store(cur ^ 1);  // its last readers finished before the previous barrier
     __syncthreads();
-    if (k0 + BKS < p.K) load(k0 + BKS);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 af[2], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const bf16x8 *>(sa + (wm * 64 + i * 32 + r) * AS + 16 * s + 8 * g);
-#pragma unroll
-      for (int jn = 0; jn < 2; ++jn)
-        bfr[jn] = *reinterpret_cast<const bf16x8 *>(sb + (wn * 64 + jn * 32 + r) * AS + 16 * s + 8 * g);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int jn = 0; jn < 2; ++jn) acc[i][jn] = mfma32(af[i], bfr[jn], acc[i][jn]);
-    }
   }
 
-  // epilogue: register 4a+c of block (i, jn) holds C[wm*64 + 32i + 8a + 4g + c][wn*64 + 32jn + r]
+  // epilogue: register 4a+c of block (i, jn) holds
+  // C[wm*BM/2 + 32i + 8a + 4g + c][wn*BN/2 + 32jn + r]
   const bool second = n0 >= p.n_split;
 #pragma unroll
-  for (int jn = 0; jn < 2; ++jn) {
-    const int n = n0 + wn * 64 + jn * 32 + r;
+  for (int jn = 0; jn < WN; ++jn) {
+    const int n = n0 + wn * (BN / 2) + jn * 32 + r;
     const int nc = second ? n - p.n_split : n;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < WM; ++i)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const int m = m0 + wm * 64 + i * 32 + 8 * a4 + 4 * g + c;
+          const int m = m0 + wm * (BM / 2) + i * 32 + 8 * a4 + 4 * g + c;
           if (m >= p.rows) continue;
           float v = acc[i][jn][4 * a4 + c];
           if (E == kEpiResidualF32) {
@@ -234,20 +256,49 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ 
   out[e] = v;
 }
 
+template <int E, int BM, int BN>
+void launch_shape(const GemmParams &p, hipStream_t s) {
+  const int64_t tiles = static_cast<int64_t>((p.rows + BM - 1) / BM) * (p.N / BN);
+  // long reductions take 64-wide slabs (each slab's MFMAs cover more of the
+  // next slab's load latency), short ones 32-wide (less LDS, more workgroups)
+  if (p.K >= 1024 && p.K % 64 == 0)
+    hipLaunchKernelGGL((gemm_kernel<E, BM, BN, 64>), dim3(static_cast<unsigned>(tiles)), dim3(256),
+                       0, s, p);
+  else
+    hipLaunchKernelGGL((gemm_kernel<E, BM, BN, 32>), dim3(static_cast<unsigned>(tiles)), dim3(256),
+                       0, s, p);
+}
+
+template <int E>
+void launch_epi(const GemmParams &p, hipStream_t s) {
+  // the largest tile that still gives about two tiles per CU
+  auto tiles = [&](int bm, int bn) {
+    return static_cast<int64_t>((p.rows + bm - 1) / bm) * (p.N / bn);
+  };
+  const int64_t want = 512;
+  if (p.N % 128 == 0 && tiles(128, 128) >= want)
+    launch_shape<E, 128, 128>(p, s);
+  else if (tiles(128, 64) >= want)
+    launch_shape<E, 128, 64>(p, s);
+  else
+    launch_shape<E, 64, 64>(p, s);
+}
+
 }  // namespace
 
 txl_status launch_gemm(const GemmParams &p, int epi, hipStream_t s) {
   if (p.rows <= 0) return TXL_OK;
-  const int64_t tiles = static_cast<int64_t>((p.rows + BM - 1) / BM) * (p.N / BN);
+  if (p.K % 32 || p.N % 64 || p.n_split % 128)
+    return fail(TXL_ERR_UNSUPPORTED, "gemm: K must be a multiple of 32, N of 64 and the split of 128");
+  const int64_t tiles = static_cast<int64_t>((p.rows + 63) / 64) * (p.N / 64);
   if (tiles > 0x7fffffffLL) return fail(TXL_ERR_UNSUPPORTED, "gemm: too many tiles");
   (void)hipGetLastError();
-  const dim3 grid(static_cast<unsigned>(tiles)), block(256);
   if (epi == kEpiStoreBf16)
-    hipLaunchKernelGGL(gemm_kernel<kEpiStoreBf16>, grid, block, 0, s, p);
+    launch_epi<kEpiStoreBf16>(p, s);
   else if (epi == kEpiGeluBf16)
-    hipLaunchKernelGGL(gemm_kernel<kEpiGeluBf16>, grid, block, 0, s, p);
+    launch_epi<kEpiGeluBf16>(p, s);
   else
-    hipLaunchKernelGGL(gemm_kernel<kEpiResidualF32>, grid, block, 0, s, p);
+    launch_epi<kEpiResidualF32>(p, s);
   return check_launch("gemm_kernel");
 }
 
