@@ -14,15 +14,19 @@
 //    registers) is exactly the B-operand layout that O^T = V^T P^T needs, so
 //    the probabilities never leave registers.
 //  * The position term uses the same trick with Q'' = (q+v)*scale*log2(e):
-//    band rows R[t] for the wave's distance window are multiplied once each
-//    (64 new rows per key tile, the window slides with the keys), and the
-//    per-query diagonal read (the relative shift, [P1] "Relative Shift
-//    Trick" replaced by index arithmetic) goes through a per-wave LDS ring.
-//    The ring stores band value (u, r) at column (u + r + 1) mod 128 of
-//    query r's row, which turns the skewed read of 4 consecutive keys into
-//    one aligned 16-byte load.
-//  * K and V^T tiles are staged in LDS by the whole workgroup; R rows go
-//    straight from global/L2 into the A operand.
+//    the band P[u][query] = R[t(u)] (Q'')^T covers the 95 distances one key
+//    tile of one wave can need, as three 32-row MFMA blocks. The window
+//    slides by 64 rows per key tile, so the last block of a tile is the first
+//    block of the next: it is kept in registers, and each tile multiplies two
+//    new blocks (two 32-row R loads, 8 MFMAs).
+//  * The per-query diagonal read of the band (the relative shift, [P1]
+//    "Relative Shift Trick" replaced by index arithmetic) goes through a
+//    per-wave LDS band stored [u][query] with a row stride of 34 floats, 64
+//    rows (one 32-key half of the tile at a time): lane r reads row
+//    c + 31 - r for key c, which is conflict-free.
+//  * K and V^T tiles are staged in LDS by the whole workgroup and
+//    double-buffered (one barrier per tile); R rows go straight from L2 into
+//    the A operand, one tile ahead.
 //  * Online softmax in base 2 (scale folded into Q' and Q''), row max over
 //    the lane's registers plus one exchange with lane^32, row sums kept per
 //    lane and combined once at the end.
@@ -210,18 +214,32 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
   float *band_w = band + 4 * hh * US + r;
   const float *band_r = band + (31 - r + 4 * hh) * US + r;
 
-  // R rows t = j0 + u + L - 32 - iw of the three band blocks (u = 32bb + r),
-  // loaded one tile ahead into the registers the band MFMAs have just freed;
-  // rows outside [0, M+L) read as zero
-  bf16x8 rr[3][4];
+  // Band row u of the tile starting at key j0 is R row t = j0 + u + L - 32 - iw.
+  // rr holds band blocks 1 and 2 (u = 32 + r, 64 + r) of the next tile, loaded
+  // one tile ahead into the registers the band MFMAs have just freed; rows
+  // outside [0, M+L) read as zero.
+  bf16x8 rr[2][4];
   auto load_r = [&](int j0) {
 #pragma unroll
-    for (int bb = 0; bb < 3; ++bb) {
-      const int off = (j0 + 32 * bb + r + L - 32 - iw) * r_row_bytes + 16 * hh;
+    for (int bb = 0; bb < 2; ++bb) {
+      const int off = (j0 + 32 * (bb + 1) + r + L - 32 - iw) * r_row_bytes + 16 * hh;
 #pragma unroll
       for (int s = 0; s < 4; ++s) rr[bb][s] = __builtin_bit_cast(bf16x8, bload(rrs, off + 32 * s));
     }
   };
+  // band block 0 of the first tile; every later tile inherits it from the
+  // previous tile's block 2 (the same R rows against the same queries)
+  f32x16 b_carry;
+  {
+    bf16x8 r0[4];
+    const int off = (j_lo + r + L - 32 - iw) * r_row_bytes + 16 * hh;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) r0[s] = __builtin_bit_cast(bf16x8, bload(rrs, off + 32 * s));
+#pragma unroll
+    for (int x = 0; x < 16; ++x) b_carry[x] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) b_carry = mfma32(r0[s], qb[s], b_carry);
+  }
   load_r(j_lo);
 
   // tile 0 into buffer 0, tile 1 in flight
@@ -255,13 +273,15 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
 
       // ---- position band P[u][query] = R[t(u)] (Q'')^T, three blocks of 32 rows ----
       f32x16 b_acc[3];
+      b_acc[0] = b_carry;
 #pragma unroll
-      for (int bb = 0; bb < 3; ++bb) {
+      for (int bb = 1; bb < 3; ++bb) {
 #pragma unroll
         for (int x = 0; x < 16; ++x) b_acc[bb][x] = 0.0f;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) b_acc[bb] = mfma32(rr[bb][s], qb[s], b_acc[bb]);
+        for (int s = 0; s < 4; ++s) b_acc[bb] = mfma32(rr[bb - 1][s], qb[s], b_acc[bb]);
       }
+      b_carry = b_acc[2];
       // next tile's R rows into the registers just consumed
       load_r(j0 + BK);
 
