@@ -76,22 +76,28 @@ def cpu_baseline(x, cfg, seconds: float):
                       f"{el:.1f} s, 1 thread"}
 
 
-def stack_flops(c, m_eff):
+def stack_flops(c, m_eff, kv=False):
     """Algorithmic flops of one segment step with m_eff valid memory states:
-    the Q, K/V (over m_eff + L rows), W^O and feed-forward products, plus the
-    attention's three contractions over visible pairs. R is built once per
-    stack and is not counted."""
+    the Q, K/V (over m_eff + L rows; over the L new rows only when memory is
+    kept projected), W^O and feed-forward products, plus the attention's
+    three contractions over visible pairs. R is built once per stack and is
+    not counted."""
     hd = c.H * c.d_h
     rows = c.B * c.L
-    per_layer = (2 * rows * c.d * hd + 4 * c.B * (m_eff + c.L) * c.d * hd
+    kv_rows = c.B * c.L if kv else c.B * (m_eff + c.L)
+    per_layer = (2 * rows * c.d * hd + 4 * kv_rows * c.d * hd
                  + 2 * rows * hd * c.d + 4 * rows * c.d * c.d_ff
                  + attn_flops(c.B, c.H, c.L, m_eff, c.d_h))
     return c.n_layer * per_layer
 
 
-def stack_bench(name: str, steps: int, warmup: int) -> dict:
+def stack_bench(name: str, steps: int, warmup: int, kv: bool = False) -> dict:
     """One segment step of the stack with a full memory (steady state),
-    captured once as a HIP graph and replayed `steps` times between events."""
+    captured once as a HIP graph and replayed `steps` times between events.
+    With kv, memory is kept as projected keys / values (txl_segment_step_kv,
+    capacity 2M + L): the graph holds one whole period of the window (the
+    steps from one compaction to the next, the compaction included) and the
+    time is per segment."""
     import torch
 
     import txl_synth
@@ -107,16 +113,36 @@ def stack_bench(name: str, steps: int, warmup: int) -> dict:
     st = txl.TxlStack(n_layer=c.n_layer, d=c.d, n_head=c.H, d_h=c.d_h, d_ff=c.d_ff,
                       vocab=c.vocab, B=c.B, L=c.L, M=c.M, emb=emb, layers=layers)
     tokens = txl_synth.stack_tokens(c).to(dev)
-    mems = [txl.TxlMem.empty(c.B, c.M, c.d, device=dev) for _ in range(c.n_layer + 1)]
     h = torch.empty((c.B, c.L, c.d), dtype=torch.bfloat16, device=dev)
+    if kv:
+        cap = st.kv_min_capacity()
+        state = [txl.TxlKVCache.empty(c.B, cap, c.H * c.d_h, device=dev)
+                 for _ in range(c.n_layer)]
+        period = (cap - c.M - c.L) // c.L + 1
+
+        def step(i):
+            st.step_kv(tokens[i % c.n_seg].contiguous(), state, h)
+    else:
+        period = 1
+        state = [txl.TxlMem.empty(c.B, c.M, c.d, device=dev) for _ in range(c.n_layer + 1)]
+
+        def step(i):
+            st.step(tokens[i % c.n_seg].contiguous(), state, h)
     s = 0
-    while int(mems[0].valid.min().item()) < c.M or s < warmup:   # fill the memory
-        st.step(tokens[s % c.n_seg].contiguous(), mems, h)
+    while int(state[0].valid.min().item()) < c.M or s < warmup:   # fill the memory
+        step(s)
         s += 1
+    if kv:
+        while state[0].start != 0:          # start the captured period at the buffer front
+            step(s)
+            s += 1
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        st.step(tokens[0].contiguous(), mems, h)
+        for i in range(period):
+            step(i)
+    if kv:
+        assert state[0].start == 0
     g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -125,16 +151,19 @@ def stack_bench(name: str, steps: int, warmup: int) -> dict:
         g.replay()
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    fl = stack_flops(c, c.M)
+    ms = e0.elapsed_time(e1) / (steps * period)
+    fl = stack_flops(c, c.M, kv)
     st.close()
     tflops = fl / (ms * 1e-3) / 1e12
+    form = ("memory kept as projected K/V, capacity 2M+L, compactions included"
+            if kv else "memory kept as hidden states, re-projected every segment")
     return {"metric": "segment step TFLOP/s (N-layer stack, steady-state memory), 1 GPU",
             "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
             "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": f"{c.n_layer}-layer stack segment step, d={c.d} H={c.H} "
-                                   f"d_ff={c.d_ff} B={c.B} L={c.L} M={c.M} (memory full)",
+                                   f"d_ff={c.d_ff} B={c.B} L={c.L} M={c.M} (memory full; "
+                                   f"{form})",
                        "tokens_per_s": round(c.B * c.L / (ms * 1e-3), 1)},
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -152,6 +181,8 @@ def main() -> int:
     ap.add_argument("--stack", choices=["C4", "C5"], default=None,
                     help="measure the N-layer segment step instead (16-layer d=512 "
                          "workload or 18-layer d=1024 long-memory workload)")
+    ap.add_argument("--kv", action="store_true",
+                    help="with --stack: keep memory as projected keys / values")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not run "
@@ -160,7 +191,7 @@ def main() -> int:
         return 2
 
     if args.stack:
-        print(json.dumps(stack_bench(args.stack, args.steps, args.warmup)), flush=True)
+        print(json.dumps(stack_bench(args.stack, args.steps, args.warmup, args.kv)), flush=True)
         return 0
 
     import torch

@@ -222,6 +222,54 @@ TXL_API txl_status txl_segment_step(txl_stack *st, const int32_t *tokens, txl_me
                                     hipStream_t stream);
 TXL_API void txl_stack_destroy(txl_stack *st);
 
+/* ------------------------------------------------------------------------
+ * Evaluation with projected memory ([P1] "Relation to KV Cache": the pages'
+ * memory holds hidden states and re-projects them through W^K, W^V every
+ * segment, where a decoder KV cache keeps the projected keys and values).
+ * With fixed weights the two give the same keys and values, so for
+ * evaluation each layer may keep K and V of its memory instead and project
+ * only the L new rows per segment, saving 4*B*M*d*H*d_h flops per layer.
+ *
+ * A cache is a sliding window over a buffer of `capacity` rows per batch row:
+ * rows [start, start + M) hold the layer's memory keys / values in logical
+ * order (oldest first; the first M - valid[b] of them are masked and never
+ * read), and the call writes the segment's projections to rows
+ * [start + M, start + M + L), so the window [start, start + M + L) is the
+ * layer's key sequence. Afterwards start <- start + L and
+ * valid[b] <- min(M, valid[b] + L) (the memory update of the pages, with no
+ * rows moved). If the advanced window would pass the end of the buffer
+ * (start + M + L > capacity), the call then moves rows [start, start + M) of
+ * every batch row to [0, M) and sets start = 0: once every
+ * floor((capacity - M - L) / L) + 1 segments, 2*B*M*H*d_h*sizeof(dtype) bytes
+ * read and written per cache.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  void *k, *v;       /* [B, capacity, H*d_h] device, the stack's dtype */
+  int32_t *valid;    /* [B] device: valid memory rows per batch row, 0..M */
+  int64_t start;     /* host: first row of the window; the call advances it */
+  int32_t B, capacity, hd;  /* hd = H*d_h */
+  txl_dtype dtype;
+} txl_kv_cache;
+
+/* Smallest capacity a cache of this stack accepts: 2*M + L. */
+TXL_API int32_t txl_kv_cache_min_capacity(const txl_stack_config *c);
+/* One segment with projected memory: tokens [B, L] int32 device; caches:
+ * n_layer caches (cache n-1 serves layer n), all with the stack's B, dtype,
+ * hd = H*d_h, one common capacity >= txl_kv_cache_min_capacity and one
+ * common start in [0, capacity - M - L]; h_out [B, L, d]. L must be a
+ * multiple of 32. Uses the workspace of txl_segment_step (same size). The
+ * results equal txl_segment_step's on the same stream of segments and resets
+ * (the projections of each row are computed once instead of every segment,
+ * in the same order). Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP; on
+ * an error nothing has been enqueued. */
+TXL_API txl_status txl_segment_step_kv(txl_stack *st, const int32_t *tokens,
+                                       txl_kv_cache *caches, void *h_out, void *workspace,
+                                       size_t ws_bytes, hipStream_t stream);
+/* Document boundary for caches (as txl_mem_reset_rows): valid[b] <- 0 in
+ * every cache for rows with reset[b] != 0 (NULL resets every row). */
+TXL_API txl_status txl_kv_cache_reset_rows(txl_kv_cache *caches, int32_t n_caches,
+                                           const uint8_t *reset, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 TXL_API const char *txl_status_str(txl_status s);
 TXL_API const char *txl_last_error(void);  /* thread-local; "" if none */

@@ -63,3 +63,22 @@ def test_null_and_bad_sizes_rejected_without_gpu(lib):
     assert lib.txl_mem_update(None, -1, None, 4, None) == 1
     assert lib.txl_mem_reset_rows(None, -1, None, None) == 1
     assert lib.txl_mem_read_logical(None, None, None) == 1
+
+
+def test_stack_and_kv_cache_host_checks_without_gpu(lib):
+    from transformer_xl_relative_txl_amd import _binding as bd
+    cfg = bd.StackConfig(2, 256, 4, 64, 256, 50, 2, 32, 64, 1e-5, bd.TXL_BF16)
+    assert lib.txl_kv_cache_min_capacity(ctypes.byref(cfg)) == 2 * 64 + 32
+    bad = bd.StackConfig(2, 256, 4, 32, 256, 50, 2, 32, 64, 1e-5, bd.TXL_BF16)  # d_h 32
+    assert lib.txl_kv_cache_min_capacity(ctypes.byref(bad)) == 0
+    assert lib.txl_segment_step_workspace_bytes(ctypes.byref(bad)) == 0
+    assert lib.txl_segment_step_kv(None, None, None, None, None, 0, None) == 1
+    assert lib.txl_segment_step(None, None, None, None, None, 0, None) == 1
+    assert lib.txl_kv_cache_reset_rows(None, -1, None, None) == 1
+    assert lib.txl_kv_cache_reset_rows(None, 0, None, None) == 0       # nothing to do
+    arr = (bd.TxlKVCacheStruct * 2)()
+    arr[0].B, arr[1].B = 2, 3
+    assert lib.txl_kv_cache_reset_rows(arr, 2, None, None) == 1        # B differs
+    assert b"differ in B" in lib.txl_last_error()
+    arr[1].B = 2
+    assert lib.txl_kv_cache_reset_rows(arr, 2, None, None) == 1        # null valid

@@ -8,9 +8,11 @@ from ._binding import (  # noqa: F401
     TXL_BF16,
     TXL_F32,
     TxlError,
+    TxlKVCache,
     TxlMem,
     TxlStack,
     lib,
+    txl_kv_cache_reset_rows,
     txl_mem_read_logical,
     txl_mem_reset_rows,
     txl_mem_update,

@@ -61,6 +61,16 @@ class TxlMemStruct(ctypes.Structure):
     ]
 
 
+class TxlKVCacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("valid", ctypes.c_void_p),
+        ("start", ctypes.c_int64),
+        ("B", ctypes.c_int32), ("capacity", ctypes.c_int32), ("hd", ctypes.c_int32),
+        ("dtype", ctypes.c_int),
+    ]
+
+
 class StackConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("n_layer", "d", "n_head", "d_h", "d_ff", "vocab", "B", "L", "M")] + [
@@ -115,6 +125,12 @@ def _load() -> ctypes.CDLL:
     lib.txl_segment_step.restype = st
     lib.txl_stack_destroy.argtypes = [vp]
     lib.txl_stack_destroy.restype = None
+    lib.txl_kv_cache_min_capacity.argtypes = [ctypes.POINTER(StackConfig)]
+    lib.txl_kv_cache_min_capacity.restype = i32
+    lib.txl_segment_step_kv.argtypes = [vp, vp, ctypes.POINTER(TxlKVCacheStruct), vp, vp, sz, vp]
+    lib.txl_segment_step_kv.restype = st
+    lib.txl_kv_cache_reset_rows.argtypes = [ctypes.POINTER(TxlKVCacheStruct), i32, vp, vp]
+    lib.txl_kv_cache_reset_rows.restype = st
     del i64
     return lib
 
@@ -278,6 +294,48 @@ def txl_mem_read_logical(mem: TxlMem, out: torch.Tensor, stream=None) -> torch.T
     return out
 
 
+class TxlKVCache:
+    """Projected keys / values of one layer's memory (the C struct
+    txl_kv_cache): device tensors k, v [B, capacity, H*d_h] and valid [B],
+    plus the host-side window start."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, valid: torch.Tensor, start: int = 0):
+        assert k.dim() == 3 and k.shape == v.shape and k.is_contiguous() and v.is_contiguous()
+        assert valid.dtype == torch.int32 and valid.shape == (k.shape[0],)
+        self.k, self.v, self.valid, self.start = k, v, valid, int(start)
+
+    @classmethod
+    def empty(cls, B: int, capacity: int, hd: int, dtype=torch.bfloat16, device="cuda"):
+        """A fresh stream: no valid rows, window at row 0 (rows left uninitialised)."""
+        return cls(torch.empty((B, capacity, hd), dtype=dtype, device=device),
+                   torch.empty((B, capacity, hd), dtype=dtype, device=device),
+                   torch.zeros((B,), dtype=torch.int32, device=device), 0)
+
+    def _struct(self) -> TxlKVCacheStruct:
+        s = TxlKVCacheStruct()
+        s.k, s.v, s.valid, s.start = _ptr(self.k), _ptr(self.v), _ptr(self.valid), self.start
+        s.B, s.capacity, s.hd = self.k.shape
+        s.dtype = _dtype(self.k)
+        return s
+
+
+def _kv_structs(caches: Sequence[TxlKVCache]):
+    arr = (TxlKVCacheStruct * max(1, len(caches)))()
+    for i, c in enumerate(caches):
+        arr[i] = c._struct()
+    return arr
+
+
+def txl_kv_cache_reset_rows(caches: Sequence[TxlKVCache], reset: Optional[torch.Tensor] = None,
+                            stream=None) -> None:
+    """valid[b] = 0 in every cache for rows with reset[b] != 0 (uint8 [B]; None = all)."""
+    if reset is not None:
+        assert reset.dtype == torch.uint8
+    arr = _kv_structs(caches)
+    _check("txl_kv_cache_reset_rows",
+           lib().txl_kv_cache_reset_rows(arr, len(caches), _ptr(reset), _stream(stream)))
+
+
 class TxlStack:
     """An N-layer stack (txl_stack_create): weights are torch tensors in the
     C layout (bf16, output-major, contiguous); the persistent R buffer and
@@ -331,6 +389,24 @@ class TxlStack:
             m.head = int(arr[i].head)
         return h_out
 
+    def kv_min_capacity(self) -> int:
+        """txl_kv_cache_min_capacity: 2*M + L."""
+        return int(lib().txl_kv_cache_min_capacity(ctypes.byref(self.cfg)))
+
+    def step_kv(self, tokens: torch.Tensor, caches: Sequence["TxlKVCache"], h_out: torch.Tensor,
+                stream=None) -> torch.Tensor:
+        """txl_segment_step_kv: tokens [B, L] int32, n_layer caches, h_out [B, L, d]."""
+        assert tokens.dtype == torch.int32 and tokens.is_contiguous()
+        assert len(caches) == self.cfg.n_layer and h_out.is_contiguous()
+        arr = _kv_structs(caches)
+        _check("txl_segment_step_kv",
+               lib().txl_segment_step_kv(self._h, tokens.data_ptr(), arr, h_out.data_ptr(),
+                                         self.workspace.data_ptr(), self.workspace.numel(),
+                                         _stream(stream)))
+        for i, c in enumerate(caches):
+            c.start = int(arr[i].start)
+        return h_out
+
     def close(self):
         if getattr(self, "_h", None):
             lib().txl_stack_destroy(self._h)
@@ -348,4 +424,5 @@ def exported_symbols() -> List[str]:
     return ["txl_rel_pos_table", "txl_rel_attn_fwd", "txl_mem_update",
             "txl_mem_reset_rows", "txl_mem_read_logical", "txl_stack_persistent_bytes",
             "txl_stack_create", "txl_segment_step_workspace_bytes", "txl_segment_step",
-            "txl_stack_destroy", "txl_status_str", "txl_last_error", "txl_version"]
+            "txl_stack_destroy", "txl_kv_cache_min_capacity", "txl_segment_step_kv",
+            "txl_kv_cache_reset_rows", "txl_status_str", "txl_last_error", "txl_version"]

@@ -167,23 +167,30 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
     const int n = n0 + wn * (BN / 2) + jn * 32 + r;
     const int nc = second ? n - p.n_split : n;
 #pragma unroll
-    for (int i = 0; i < WM; ++i)
+    for (int i = 0; i < WM; ++i) {
+      // a 32-row block never straddles an output segment (c_seg % 32 == 0)
+      const int mb = m0 + wm * (BM / 2) + i * 32;
+      const int64_t ob = p.c_seg > 0
+                             ? (mb / p.c_seg) * p.c_bstride + p.c_row0 + mb % p.c_seg
+                             : static_cast<int64_t>(mb);
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const int m = m0 + wm * (BM / 2) + i * 32 + 8 * a4 + 4 * g + c;
+          const int mi = 8 * a4 + 4 * g + c;
+          const int m = mb + mi;
           if (m >= p.rows) continue;
+          const int64_t mo = ob + mi;
           float v = acc[i][jn][4 * a4 + c];
           if (E == kEpiResidualF32) {
             v += static_cast<float>(p.res[static_cast<int64_t>(m) * p.ldres + nc]);
-            static_cast<float *>(second ? p.c1 : p.c0)[static_cast<int64_t>(m) * p.ldc + nc] = v;
+            static_cast<float *>(second ? p.c1 : p.c0)[mo * p.ldc + nc] = v;
           } else {
             if (E == kEpiGeluBf16) v = 0.5f * v * (1.0f + erff(v * 0.7071067811865476f));
-            static_cast<__bf16 *>(second ? p.c1 : p.c0)[static_cast<int64_t>(m) * p.ldc + nc] =
-                static_cast<__bf16>(v);
+            static_cast<__bf16 *>(second ? p.c1 : p.c0)[mo * p.ldc + nc] = static_cast<__bf16>(v);
           }
         }
+    }
   }
 }
 
@@ -290,6 +297,8 @@ txl_status launch_gemm(const GemmParams &p, int epi, hipStream_t s) {
   if (p.rows <= 0) return TXL_OK;
   if (p.K % 32 || p.N % 64 || p.n_split % 128)
     return fail(TXL_ERR_UNSUPPORTED, "gemm: K must be a multiple of 32, N of 64 and the split of 128");
+  if (p.c_seg < 0 || p.c_seg % 32)
+    return fail(TXL_ERR_UNSUPPORTED, "gemm: output segment length must be a multiple of 32");
   const int64_t tiles = static_cast<int64_t>((p.rows + 63) / 64) * (p.N / 64);
   if (tiles > 0x7fffffffLL) return fail(TXL_ERR_UNSUPPORTED, "gemm: too many tiles");
   (void)hipGetLastError();

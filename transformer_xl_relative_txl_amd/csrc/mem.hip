@@ -91,6 +91,43 @@ __global__ void mem_reset_kernel(ValidPtrs vp, int n, int B,
   if (reset == nullptr || reset[b] != 0) vp.p[ring][b] = 0;
 }
 
+// valid[b] <- min(M, valid[b] + L) for every row of n caches (the count part
+// of the ring update, for memories that hold projected keys and values)
+__global__ void valid_advance_kernel(ValidPtrs vp, int n, int B, int M, int L) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n * B) return;
+  const int ring = e / B, b = e - ring * B;
+  const int nv = vp.p[ring][b] + L;
+  vp.p[ring][b] = nv < M ? nv : M;
+}
+
+// Window compaction of projected-key/value caches: rows [start, start + M)
+// of every batch row move to rows [0, M) (the caller guarantees start >= M,
+// so source and destination never overlap). One 16-byte chunk per thread over
+// the flattened (buffer, b, row, chunk) space.
+struct KVCompactMeta {
+  int M;
+  int64_t cap, start;
+  uint32_t cpr;
+  FastDiv div_cpr, div_m, div_b;
+  int B;
+  uint32_t total;
+};
+__global__ __launch_bounds__(kThreads) void kv_compact_kernel(KVBuffers kb, KVCompactMeta mt) {
+  const uint32_t e = blockIdx.x * kThreads + threadIdx.x;
+  if (e >= mt.total) return;
+  const uint32_t row = fdiv(e, mt.div_cpr);  // (buffer, b, k) flattened
+  const uint32_t c = e - row * mt.cpr;
+  const uint32_t bk = fdiv(row, mt.div_m);
+  const uint32_t k = row - bk * mt.M;
+  const uint32_t buf = fdiv(bk, mt.div_b);
+  const uint32_t b = bk - buf * mt.B;
+  u32x4 *base = reinterpret_cast<u32x4 *>(kb.p[buf]);
+  const int64_t brow = static_cast<int64_t>(b) * mt.cap;
+  const u32x4 v = __builtin_nontemporal_load(base + (brow + mt.start + k) * mt.cpr + c);
+  __builtin_nontemporal_store(v, base + (brow + k) * mt.cpr + c);
+}
+
 __global__ __launch_bounds__(kThreads) void mem_read_logical_kernel(
     const u32x4 *data, u32x4 *out, int M, int64_t head, uint32_t cpr, FastDiv div_cpr,
     FastDiv div_m, uint32_t total) {
@@ -142,6 +179,39 @@ txl_status launch_mem_reset(int32_t *const *valid, int n, int B,
   hipLaunchKernelGGL(mem_reset_kernel, dim3((total + 255) / 256), dim3(256), 0, s, vp, n, B,
                      reset);
   return check_launch("mem_reset_kernel");
+}
+
+txl_status launch_valid_advance(int32_t *const *valid, int n, int B, int M, int L,
+                                hipStream_t s) {
+  ValidPtrs vp;
+  for (int i = 0; i < n; ++i) vp.p[i] = valid[i];
+  const int total = n * B;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(valid_advance_kernel, dim3((total + 255) / 256), dim3(256), 0, s, vp, n, B,
+                     M, L);
+  return check_launch("valid_advance_kernel");
+}
+
+txl_status launch_kv_compact(const KVBuffers &kb, int n, int B, int M, int64_t cap,
+                             int64_t start, int64_t row_bytes, hipStream_t s) {
+  KVCompactMeta mt;
+  mt.M = M;
+  mt.cap = cap;
+  mt.start = start;
+  mt.B = B;
+  const int64_t cpr = row_bytes / 16;
+  const int64_t total = static_cast<int64_t>(n) * B * M * cpr;
+  if (total == 0) return TXL_OK;
+  if (total >= (int64_t(1) << 31)) return fail(TXL_ERR_UNSUPPORTED, "kv_compact: more than 2^31 chunks");
+  mt.cpr = static_cast<uint32_t>(cpr);
+  mt.div_cpr = make_fastdiv(mt.cpr);
+  mt.div_m = make_fastdiv(static_cast<uint32_t>(M));
+  mt.div_b = make_fastdiv(static_cast<uint32_t>(B));
+  mt.total = static_cast<uint32_t>(total);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(kv_compact_kernel, dim3(static_cast<unsigned>((total + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, kb, mt);
+  return check_launch("kv_compact_kernel");
 }
 
 txl_status launch_mem_read_logical(const void *data, void *out, int B, int M,

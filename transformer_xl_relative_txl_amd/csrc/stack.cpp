@@ -99,6 +99,97 @@ GemmParams dense(const void *a, int64_t lda, int rows, int N, int K, const void 
   return p;
 }
 
+struct StepBufs {
+  __bf16 *hc, *hn, *q, *k, *v, *o, *h1, *f;
+  float *x;
+};
+
+StepBufs bufs(const WsLayout &ws, void *workspace) {
+  char *base = static_cast<char *>(workspace);
+  StepBufs b;
+  b.hc = reinterpret_cast<__bf16 *>(base + ws.hc);
+  b.hn = reinterpret_cast<__bf16 *>(base + ws.hn);
+  b.q = reinterpret_cast<__bf16 *>(base + ws.q);
+  b.k = reinterpret_cast<__bf16 *>(base + ws.k);
+  b.v = reinterpret_cast<__bf16 *>(base + ws.v);
+  b.o = reinterpret_cast<__bf16 *>(base + ws.o);
+  b.x = reinterpret_cast<float *>(base + ws.x);
+  b.h1 = reinterpret_cast<__bf16 *>(base + ws.h1);
+  b.f = reinterpret_cast<__bf16 *>(base + ws.f);
+  return b;
+}
+
+txl_status check_workspace(const WsLayout &ws, const void *workspace, size_t ws_bytes,
+                           const void *h_out, const char *who) {
+  if (ws_bytes < ws.total)
+    return fail(TXL_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, ws.total);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) || !aligned16(h_out))
+    return fail(TXL_ERR_UNSUPPORTED, "%s: workspace must be 256-byte and h_out 16-byte aligned", who);
+  return TXL_OK;
+}
+
+// The part of layer n that does not depend on how memory is kept: Q = H W^Q,
+// relative attention over keys / values k, v ([B, M+L, H*d_h] with batch
+// stride kv_sb elements, memory first) masked by `valid`, X = H + A W^O,
+// H1 = LN1(X), X = H1 + GELU(H1 W1) W2, dst = LN2(X).
+txl_status layer_body(const txl_stack *st, int n, const __bf16 *hc, void *dst, const void *k,
+                      const void *v, int64_t kv_sb, const int32_t *valid, const StepBufs &b,
+                      hipStream_t stream) {
+  const txl_stack_config &c = st->cfg;
+  const txl_layer_weights &lw = st->layers[n];
+  const int HD = c.n_head * c.d_h;
+  const int rows = c.B * c.L;
+  txl_status s = launch_gemm(dense(hc, c.d, rows, HD, c.d, lw.wq, b.q, HD), kEpiStoreBf16, stream);
+  if (s != TXL_OK) return s;
+  txl_rel_attn_args a = {};
+  a.dtype = TXL_BF16;
+  a.B = c.B;
+  a.H = c.n_head;
+  a.L = c.L;
+  a.M = c.M;
+  a.d_h = c.d_h;
+  a.q = b.q;
+  a.q_sb = static_cast<int64_t>(c.L) * HD;
+  a.q_sh = c.d_h;
+  a.q_sl = HD;
+  a.k = k;
+  a.v = v;
+  a.kv_sb = kv_sb;
+  a.kv_sh = c.d_h;
+  a.kv_sl = HD;
+  a.r = static_cast<const char *>(st->persistent) + n * st->r_bytes;
+  a.r_sh = c.d_h;
+  a.r_sl = HD;
+  a.u = lw.u;
+  a.vb = lw.vb;
+  a.mem_valid = valid;
+  a.scale = 0.0f;
+  a.out = b.o;
+  a.o_sb = static_cast<int64_t>(c.L) * HD;
+  a.o_sh = c.d_h;
+  a.o_sl = HD;
+  a.lse = nullptr;
+  s = txl_rel_attn_fwd(&a, stream);
+  if (s != TXL_OK) return s;
+  // X = H + A W^O; H1 = LN1(X)
+  GemmParams po = dense(b.o, HD, rows, c.d, HD, lw.wo, b.x, c.d);
+  po.res = hc;
+  po.ldres = c.d;
+  s = launch_gemm(po, kEpiResidualF32, stream);
+  if (s != TXL_OK) return s;
+  s = launch_layernorm(b.x, lw.ln1_g, lw.ln1_b, b.h1, rows, c.d, c.ln_eps, stream);
+  if (s != TXL_OK) return s;
+  // F = GELU(H1 W1); X = H1 + F W2; H^(n) = LN2(X)
+  s = launch_gemm(dense(b.h1, c.d, rows, c.d_ff, c.d, lw.w1, b.f, c.d_ff), kEpiGeluBf16, stream);
+  if (s != TXL_OK) return s;
+  GemmParams p2 = dense(b.f, c.d_ff, rows, c.d, c.d_ff, lw.w2, b.x, c.d);
+  p2.res = b.h1;
+  p2.ldres = c.d;
+  s = launch_gemm(p2, kEpiResidualF32, stream);
+  if (s != TXL_OK) return s;
+  return launch_layernorm(b.x, lw.ln2_g, lw.ln2_b, dst, rows, c.d, c.ln_eps, stream);
+}
+
 }  // namespace
 }  // namespace txl
 
@@ -167,10 +258,8 @@ TXL_API txl_status txl_segment_step(txl_stack *st, const int32_t *tokens, txl_me
     return fail(TXL_ERR_INVALID_ARG, "segment_step: null argument");
   const txl_stack_config &c = st->cfg;
   const WsLayout ws = layout(c);
-  if (ws_bytes < ws.total)
-    return fail(TXL_ERR_WORKSPACE, "segment_step: workspace %zu < %zu bytes", ws_bytes, ws.total);
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) || !aligned16(h_out))
-    return fail(TXL_ERR_UNSUPPORTED, "segment_step: workspace must be 256-byte and h_out 16-byte aligned");
+  txl_status s = check_workspace(ws, workspace, ws_bytes, h_out, "segment_step");
+  if (s != TXL_OK) return s;
   for (int n = 0; n <= c.n_layer; ++n) {
     const txl_mem &m = mems[n];
     if (m.B != c.B || m.M != c.M || m.d != c.d || m.dtype != c.dtype)
@@ -183,30 +272,18 @@ TXL_API txl_status txl_segment_step(txl_stack *st, const int32_t *tokens, txl_me
       return fail(TXL_ERR_UNSUPPORTED, "segment_step: ring %d misaligned", n);
   }
 
-  char *base = static_cast<char *>(workspace);
-  __bf16 *hc = reinterpret_cast<__bf16 *>(base + ws.hc);
-  __bf16 *hn = reinterpret_cast<__bf16 *>(base + ws.hn);
-  __bf16 *q = reinterpret_cast<__bf16 *>(base + ws.q);
-  __bf16 *k = reinterpret_cast<__bf16 *>(base + ws.k);
-  __bf16 *v = reinterpret_cast<__bf16 *>(base + ws.v);
-  __bf16 *o = reinterpret_cast<__bf16 *>(base + ws.o);
-  float *x = reinterpret_cast<float *>(base + ws.x);
-  __bf16 *h1 = reinterpret_cast<__bf16 *>(base + ws.h1);
-  __bf16 *f = reinterpret_cast<__bf16 *>(base + ws.f);
+  StepBufs b = bufs(ws, workspace);
   const int HD = c.n_head * c.d_h;
   const int rows = c.B * c.L;
   const int ML = c.M + c.L;
-
-  txl_status s = launch_embed(tokens, st->emb, hc, rows, c.d, c.vocab, stream);
+  __bf16 *hc = b.hc, *hn = b.hn;
+  s = launch_embed(tokens, st->emb, hc, rows, c.d, c.vocab, stream);
   if (s != TXL_OK) return s;
   for (int n = 0; n < c.n_layer; ++n) {
     const txl_layer_weights &lw = st->layers[n];
     txl_mem &ring = mems[n];
-    // Q = H W^Q
-    s = launch_gemm(dense(hc, c.d, rows, HD, c.d, lw.wq, q, HD), kEpiStoreBf16, stream);
-    if (s != TXL_OK) return s;
-    // [K | V] = [ring; H] [W^K | W^V]
-    GemmParams pkv = dense(nullptr, c.d, c.B * ML, 2 * HD, c.d, lw.wk, k, HD);
+    // [K | V] = [ring; H] [W^K | W^V], memory rows gathered in logical order
+    GemmParams pkv = dense(nullptr, c.d, c.B * ML, 2 * HD, c.d, lw.wk, b.k, HD);
     pkv.gather = 1;
     pkv.ring = static_cast<const __bf16 *>(ring.data);
     pkv.seg = hc;
@@ -216,69 +293,135 @@ TXL_API txl_status txl_segment_step(txl_stack *st, const int32_t *tokens, txl_me
     pkv.segL = c.L;
     pkv.w1 = static_cast<const __bf16 *>(lw.wv);
     pkv.n_split = HD;
-    pkv.c1 = v;
+    pkv.c1 = b.v;
     s = launch_gemm(pkv, kEpiStoreBf16, stream);
     if (s != TXL_OK) return s;
-    // relative attention over the layer's memory (valid counts before the update)
-    txl_rel_attn_args a = {};
-    a.dtype = TXL_BF16;
-    a.B = c.B;
-    a.H = c.n_head;
-    a.L = c.L;
-    a.M = c.M;
-    a.d_h = c.d_h;
-    a.q = q;
-    a.q_sb = static_cast<int64_t>(c.L) * HD;
-    a.q_sh = c.d_h;
-    a.q_sl = HD;
-    a.k = k;
-    a.v = v;
-    a.kv_sb = static_cast<int64_t>(ML) * HD;
-    a.kv_sh = c.d_h;
-    a.kv_sl = HD;
-    a.r = static_cast<char *>(st->persistent) + n * st->r_bytes;
-    a.r_sh = c.d_h;
-    a.r_sl = HD;
-    a.u = lw.u;
-    a.vb = lw.vb;
-    a.mem_valid = ring.valid;
-    a.scale = 0.0f;
-    a.out = o;
-    a.o_sb = static_cast<int64_t>(c.L) * HD;
-    a.o_sh = c.d_h;
-    a.o_sl = HD;
-    a.lse = nullptr;
-    s = txl_rel_attn_fwd(&a, stream);
+    void *dst = (n + 1 == c.n_layer) ? h_out : static_cast<void *>(hn);
+    s = layer_body(st, n, hc, dst, b.k, b.v, static_cast<int64_t>(ML) * HD, ring.valid, b, stream);
     if (s != TXL_OK) return s;
-    // the ring of layer n-1 takes H^(n-1) now that it has been read
+    // the ring of layer n-1 takes H^(n-1) now that the layer has read it
     const void *hptr = hc;
     s = txl_mem_update(&ring, 1, &hptr, c.L, stream);
     if (s != TXL_OK) return s;
-    // X = H + A W^O; H1 = LN1(X)
-    GemmParams po = dense(o, HD, rows, c.d, HD, lw.wo, x, c.d);
-    po.res = hc;
-    po.ldres = c.d;
-    s = launch_gemm(po, kEpiResidualF32, stream);
-    if (s != TXL_OK) return s;
-    s = launch_layernorm(x, lw.ln1_g, lw.ln1_b, h1, rows, c.d, c.ln_eps, stream);
-    if (s != TXL_OK) return s;
-    // F = GELU(H1 W1); X = H1 + F W2; H^(n) = LN2(X)
-    s = launch_gemm(dense(h1, c.d, rows, c.d_ff, c.d, lw.w1, f, c.d_ff), kEpiGeluBf16, stream);
-    if (s != TXL_OK) return s;
-    GemmParams p2 = dense(f, c.d_ff, rows, c.d, c.d_ff, lw.w2, x, c.d);
-    p2.res = h1;
-    p2.ldres = c.d;
-    s = launch_gemm(p2, kEpiResidualF32, stream);
-    if (s != TXL_OK) return s;
-    void *dst = (n + 1 == c.n_layer) ? h_out : static_cast<void *>(hn);
-    s = launch_layernorm(x, lw.ln2_g, lw.ln2_b, dst, rows, c.d, c.ln_eps, stream);
-    if (s != TXL_OK) return s;
     __bf16 *t = hc;
-    hc = (n + 1 == c.n_layer) ? static_cast<__bf16 *>(h_out) : hn;
+    hc = static_cast<__bf16 *>(dst);
     hn = t;
   }
   const void *top = h_out;
   return txl_mem_update(&mems[c.n_layer], 1, &top, c.L, stream);
+}
+
+TXL_API int32_t txl_kv_cache_min_capacity(const txl_stack_config *c) {
+  if (check_config(c) != TXL_OK) return 0;
+  const int64_t cap = 2 * static_cast<int64_t>(c->M) + c->L;
+  return cap > 0x7fffffffLL ? 0 : static_cast<int32_t>(cap);
+}
+
+TXL_API txl_status txl_segment_step_kv(txl_stack *st, const int32_t *tokens,
+                                       txl_kv_cache *caches, void *h_out, void *workspace,
+                                       size_t ws_bytes, hipStream_t stream) {
+  if (!st || !tokens || !caches || !h_out || !workspace)
+    return fail(TXL_ERR_INVALID_ARG, "segment_step_kv: null argument");
+  const txl_stack_config &c = st->cfg;
+  const WsLayout ws = layout(c);
+  txl_status s = check_workspace(ws, workspace, ws_bytes, h_out, "segment_step_kv");
+  if (s != TXL_OK) return s;
+  const int HD = c.n_head * c.d_h;
+  if (c.L % 32) return fail(TXL_ERR_UNSUPPORTED, "segment_step_kv: L must be a multiple of 32");
+  const int64_t cap = caches[0].capacity;
+  const int64_t start = caches[0].start;
+  if (cap < 2 * static_cast<int64_t>(c.M) + c.L)
+    return fail(TXL_ERR_INVALID_ARG, "segment_step_kv: capacity %lld < 2*M + L", static_cast<long long>(cap));
+  if (start < 0 || start + c.M + c.L > cap)
+    return fail(TXL_ERR_INVALID_ARG, "segment_step_kv: start %lld outside [0, capacity - M - L]",
+                static_cast<long long>(start));
+  if (static_cast<int64_t>(c.B) * cap * 2 * HD >= (int64_t(1) << 40))
+    return fail(TXL_ERR_UNSUPPORTED, "segment_step_kv: cache too large");
+  for (int n = 0; n < c.n_layer; ++n) {
+    const txl_kv_cache &kc = caches[n];
+    if (kc.B != c.B || kc.hd != HD || kc.dtype != c.dtype)
+      return fail(TXL_ERR_INVALID_ARG, "segment_step_kv: cache %d shape differs from the stack", n);
+    if (kc.capacity != cap || kc.start != start)
+      return fail(TXL_ERR_INVALID_ARG, "segment_step_kv: caches differ in capacity or start");
+    if (!kc.k || !kc.v || !kc.valid)
+      return fail(TXL_ERR_INVALID_ARG, "segment_step_kv: cache %d has a null pointer", n);
+    if (!aligned16(kc.k) || !aligned16(kc.v) || (reinterpret_cast<uintptr_t>(kc.valid) & 3u))
+      return fail(TXL_ERR_UNSUPPORTED, "segment_step_kv: cache %d misaligned", n);
+  }
+
+  StepBufs b = bufs(ws, workspace);
+  const int rows = c.B * c.L;
+  __bf16 *hc = b.hc, *hn = b.hn;
+  s = launch_embed(tokens, st->emb, hc, rows, c.d, c.vocab, stream);
+  if (s != TXL_OK) return s;
+  for (int n = 0; n < c.n_layer; ++n) {
+    const txl_layer_weights &lw = st->layers[n];
+    txl_kv_cache &kc = caches[n];
+    // [K | V] of the segment rows only, into window rows [start + M, start + M + L)
+    GemmParams pkv = dense(hc, c.d, rows, 2 * HD, c.d, lw.wk, kc.k, HD);
+    pkv.w1 = static_cast<const __bf16 *>(lw.wv);
+    pkv.n_split = HD;
+    pkv.c1 = kc.v;
+    pkv.c_seg = c.L;
+    pkv.c_bstride = cap;
+    pkv.c_row0 = start + c.M;
+    s = launch_gemm(pkv, kEpiStoreBf16, stream);
+    if (s != TXL_OK) return s;
+    void *dst = (n + 1 == c.n_layer) ? h_out : static_cast<void *>(hn);
+    const int64_t w0 = start * HD;
+    s = layer_body(st, n, hc, dst, static_cast<const __bf16 *>(kc.k) + w0,
+                   static_cast<const __bf16 *>(kc.v) + w0, cap * HD, kc.valid, b, stream);
+    if (s != TXL_OK) return s;
+    __bf16 *t = hc;
+    hc = static_cast<__bf16 *>(dst);
+    hn = t;
+  }
+  // memory update: the window slides by L, the valid counts grow
+  for (int base = 0; base < c.n_layer; base += kMaxRingsPerLaunch) {
+    const int n = (c.n_layer - base) < kMaxRingsPerLaunch ? (c.n_layer - base) : kMaxRingsPerLaunch;
+    int32_t *valid[kMaxRingsPerLaunch];
+    for (int i = 0; i < n; ++i) valid[i] = caches[base + i].valid;
+    s = launch_valid_advance(valid, n, c.B, c.M, c.L, stream);
+    if (s != TXL_OK) return s;
+  }
+  int64_t next = start + c.L;
+  if (next + c.M + c.L > cap) {
+    // move the memory rows back to the front of the buffer (next > M: no overlap)
+    for (int base = 0; base < 2 * c.n_layer; base += kMaxRingsPerLaunch) {
+      const int n = (2 * c.n_layer - base) < kMaxRingsPerLaunch ? (2 * c.n_layer - base) : kMaxRingsPerLaunch;
+      KVBuffers kb;
+      for (int i = 0; i < n; ++i) {
+        const txl_kv_cache &kc = caches[(base + i) / 2];
+        kb.p[i] = ((base + i) & 1) ? kc.v : kc.k;
+      }
+      s = launch_kv_compact(kb, n, c.B, c.M, cap, next, static_cast<int64_t>(HD) * 2, stream);
+      if (s != TXL_OK) return s;
+    }
+    next = 0;
+  }
+  for (int n = 0; n < c.n_layer; ++n) caches[n].start = next;
+  return TXL_OK;
+}
+
+TXL_API txl_status txl_kv_cache_reset_rows(txl_kv_cache *caches, int32_t n_caches,
+                                           const uint8_t *reset, hipStream_t stream) {
+  if (n_caches < 0 || (n_caches > 0 && !caches))
+    return fail(TXL_ERR_INVALID_ARG, "kv_cache_reset_rows: null caches");
+  if (n_caches == 0) return TXL_OK;
+  const int B = caches[0].B;
+  for (int n = 0; n < n_caches; ++n)
+    if (caches[n].B != B) return fail(TXL_ERR_INVALID_ARG, "kv_cache_reset_rows: caches differ in B");
+  for (int n = 0; n < n_caches; ++n)
+    if (B > 0 && !caches[n].valid) return fail(TXL_ERR_INVALID_ARG, "kv_cache_reset_rows: null valid");
+  if (B <= 0) return B == 0 ? TXL_OK : fail(TXL_ERR_INVALID_ARG, "kv_cache_reset_rows: B < 0");
+  for (int base = 0; base < n_caches; base += kMaxRingsPerLaunch) {
+    const int n = (n_caches - base) < kMaxRingsPerLaunch ? (n_caches - base) : kMaxRingsPerLaunch;
+    int32_t *valid[kMaxRingsPerLaunch];
+    for (int i = 0; i < n; ++i) valid[i] = caches[base + i].valid;
+    txl_status s = launch_mem_reset(valid, n, B, reset, stream);
+    if (s != TXL_OK) return s;
+  }
+  return TXL_OK;
 }
 
 }  // extern "C"

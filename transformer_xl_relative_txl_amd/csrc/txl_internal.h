@@ -45,6 +45,14 @@ txl_status launch_mem_update(const RingBatch &rb, int n, int B, int M, int L,
                              int64_t row_bytes, hipStream_t s);
 txl_status launch_mem_reset(int32_t *const *valid, int n, int B,
                             const uint8_t *reset, hipStream_t s);
+txl_status launch_valid_advance(int32_t *const *valid, int n, int B, int M, int L,
+                                hipStream_t s);
+// projected-key/value caches: up to kMaxRingsPerLaunch buffers [B, cap, row]
+struct KVBuffers {
+  void *p[kMaxRingsPerLaunch];
+};
+txl_status launch_kv_compact(const KVBuffers &kb, int n, int B, int M, int64_t cap,
+                             int64_t start, int64_t row_bytes, hipStream_t s);
 txl_status launch_mem_read_logical(const void *data, void *out, int B, int M,
                                    int64_t head, int64_t row_bytes,
                                    hipStream_t s);
@@ -72,6 +80,10 @@ struct GemmParams {
   int n_split;
   void *c0, *c1;
   int64_t ldc;
+  // output rows: C row m is row m of c0/c1, or, when c_seg > 0 (a multiple
+  // of 32), row (m / c_seg) * c_bstride + c_row0 + m % c_seg
+  int c_seg;
+  int64_t c_bstride, c_row0;
   const __bf16 *res;  // residual [rows, ldres] for kEpiResidualF32
   int64_t ldres;
 };
