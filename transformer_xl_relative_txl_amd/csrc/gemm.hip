@@ -49,12 +49,19 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 sa[2][BM * AS];
   __shared__ __attribute__((aligned(16))) __bf16 sb[2][BN * AS];
 
-  // XCD-contiguous tile assignment (a bijection on [0, T))
+  // XCD-contiguous tile assignment (a bijection on [0, T)); with split-K the
+  // first T / k_splits indices are split 0, and so on
   const int T = gridDim.x;
   const int bid = blockIdx.x;
   const int x = bid % kXcds, local = bid / kXcds;
   const int q = T / kXcds, rem = T % kXcds;
-  const int tile = x * q + (x < rem ? x : rem) + local;
+  int tile = x * q + (x < rem ? x : rem) + local;
+  int split = 0;
+  if (E == kEpiPartialF32) {
+    const int per = T / p.k_splits;
+    split = tile / per;
+    tile -= split * per;
+  }
   const int n_tn = p.N / BN;
   const int tm = tile / n_tn, tn = tile - tm * n_tn;
   const int m0 = tm * BM, n0 = tn * BN;
@@ -131,13 +138,15 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][jn][e] = 0.0f;
 
-  const int n_slab = p.K / BKS;
-  load(0);
+  const int n_slab_all = p.K / BKS;
+  const int ks0 = E == kEpiPartialF32 ? split * n_slab_all / p.k_splits : 0;
+  const int ks1 = E == kEpiPartialF32 ? (split + 1) * n_slab_all / p.k_splits : n_slab_all;
+  load(ks0 * BKS);
   store(0);
   __syncthreads();
-  for (int ks = 0; ks < n_slab; ++ks) {
-    const int cur = ks & 1;
-    const bool more = ks + 1 < n_slab;
+  for (int ks = ks0; ks < ks1; ++ks) {
+    const int cur = (ks - ks0) & 1;
+    const bool more = ks + 1 < ks1;
     if (more) load((ks + 1) * BKS);
 #pragma unroll
     for (int s = 0; s < BKS / 16; ++s) {
@@ -182,7 +191,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
           if (m >= p.rows) continue;
           const int64_t mo = ob + mi;
           float v = acc[i][jn][4 * a4 + c];
-          if (E == kEpiResidualF32) {
+          if (E == kEpiPartialF32) {
+            static_cast<float *>(p.c0)[split * p.c_split_stride + mo * p.ldc + nc] = v;
+          } else if (E == kEpiResidualF32) {
             v += static_cast<float>(p.res[static_cast<int64_t>(m) * p.ldres + nc]);
             static_cast<float *>(second ? p.c1 : p.c0)[mo * p.ldc + nc] = v;
           } else {
@@ -199,6 +210,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
 constexpr int kLnMaxChunks = 16;  // 4-float chunks per lane: d <= 4096
 
 __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict__ x,
+                                                        int n_parts, int64_t part_stride,
+                                                        const __bf16 *__restrict__ res,
                                                         const __bf16 *__restrict__ gamma,
                                                         const __bf16 *__restrict__ beta,
                                                         __bf16 *__restrict__ y, int rows, int d,
@@ -214,6 +227,14 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
   for (int c = 0; c < kLnMaxChunks; ++c) {
     if (c < nch) {
       v[c] = *reinterpret_cast<const f32x4 *>(xr + 256 * c + 4 * lane);
+      // split-K partials in order, then the residual
+      for (int part = 1; part < n_parts; ++part)
+        v[c] += *reinterpret_cast<const f32x4 *>(xr + part * part_stride + 256 * c + 4 * lane);
+      if (res) {
+        const __bf16 *rr = res + static_cast<int64_t>(row) * d + 256 * c + 4 * lane;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[c][e] += static_cast<float>(rr[e]);
+      }
       s += (v[c][0] + v[c][1]) + (v[c][2] + v[c][3]);
     }
   }
@@ -265,7 +286,8 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ 
 
 template <int E, int BM, int BN>
 void launch_shape(const GemmParams &p, hipStream_t s) {
-  const int64_t tiles = static_cast<int64_t>((p.rows + BM - 1) / BM) * (p.N / BN);
+  const int64_t tiles = static_cast<int64_t>((p.rows + BM - 1) / BM) * (p.N / BN) *
+                        (E == kEpiPartialF32 ? p.k_splits : 1);
   // long reductions take 64-wide slabs (each slab's MFMAs cover more of the
   // next slab's load latency), short ones 32-wide (less LDS, more workgroups)
   if (p.K >= 1024 && p.K % 64 == 0)
@@ -280,7 +302,8 @@ template <int E>
 void launch_epi(const GemmParams &p, hipStream_t s) {
   // the largest tile that still gives about two tiles per CU
   auto tiles = [&](int bm, int bn) {
-    return static_cast<int64_t>((p.rows + bm - 1) / bm) * (p.N / bn);
+    return static_cast<int64_t>((p.rows + bm - 1) / bm) * (p.N / bn) *
+           (E == kEpiPartialF32 ? p.k_splits : 1);
   };
   const int64_t want = 512;
   if (p.N % 128 == 0 && tiles(128, 128) >= want)
@@ -299,23 +322,31 @@ txl_status launch_gemm(const GemmParams &p, int epi, hipStream_t s) {
     return fail(TXL_ERR_UNSUPPORTED, "gemm: K must be a multiple of 32, N of 64 and the split of 128");
   if (p.c_seg < 0 || p.c_seg % 32)
     return fail(TXL_ERR_UNSUPPORTED, "gemm: output segment length must be a multiple of 32");
-  const int64_t tiles = static_cast<int64_t>((p.rows + 63) / 64) * (p.N / 64);
+  if (epi == kEpiPartialF32 &&
+      (p.k_splits < 1 || p.k_splits > p.K / 64 || p.n_split != p.N || p.gather))
+    return fail(TXL_ERR_UNSUPPORTED, "gemm: split-K needs 1 <= splits <= K/64, no N split, no gather");
+  const int64_t tiles = static_cast<int64_t>((p.rows + 63) / 64) * (p.N / 64) *
+                        (epi == kEpiPartialF32 ? p.k_splits : 1);
   if (tiles > 0x7fffffffLL) return fail(TXL_ERR_UNSUPPORTED, "gemm: too many tiles");
   (void)hipGetLastError();
   if (epi == kEpiStoreBf16)
     launch_epi<kEpiStoreBf16>(p, s);
   else if (epi == kEpiGeluBf16)
     launch_epi<kEpiGeluBf16>(p, s);
-  else
+  else if (epi == kEpiResidualF32)
     launch_epi<kEpiResidualF32>(p, s);
+  else
+    launch_epi<kEpiPartialF32>(p, s);
   return check_launch("gemm_kernel");
 }
 
-txl_status launch_layernorm(const float *x, const void *gamma, const void *beta, void *y,
-                            int rows, int d, float eps, hipStream_t s) {
+txl_status launch_layernorm(const float *x, int n_parts, int64_t part_stride, const void *res,
+                            const void *gamma, const void *beta, void *y, int rows, int d,
+                            float eps, hipStream_t s) {
   if (rows <= 0) return TXL_OK;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(layernorm_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, x,
+  hipLaunchKernelGGL(layernorm_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, x, n_parts,
+                     part_stride, static_cast<const __bf16 *>(res),
                      static_cast<const __bf16 *>(gamma), static_cast<const __bf16 *>(beta),
                      static_cast<__bf16 *>(y), rows, d, eps);
   return check_launch("layernorm_kernel");

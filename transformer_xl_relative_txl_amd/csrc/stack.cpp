@@ -9,6 +9,7 @@
 // layer n-1 produced for the previous segment).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <new>
@@ -54,6 +55,17 @@ txl_status check_config(const txl_stack_config *c) {
   return TXL_OK;
 }
 
+// K splits of a residual product (rows x N, reduction K): split only GEMMs
+// whose 64x64 tiles cannot fill the chip (fewer than 512), up to 4 splits,
+// each keeping a K range of at least 256.
+int residual_splits(int rows, int N, int K) {
+  const int64_t tiles = static_cast<int64_t>((rows + 63) / 64) * (N / 64);
+  if (tiles >= 512) return 1;
+  int s = 1;
+  while (s < 4 && tiles * s < 1024 && K / (2 * s) >= 256) s *= 2;
+  return s;
+}
+
 struct WsLayout {
   size_t hc, hn, q, k, v, o, x, h1, f, total;
 };
@@ -75,7 +87,10 @@ WsLayout layout(const txl_stack_config &c) {
   w.k = take(krows * hd * 2);
   w.v = take(krows * hd * 2);
   w.o = take(rows * hd * 2);
-  w.x = take(rows * c.d * 4);
+  const int HDi = c.n_head * c.d_h;
+  const int rws = c.B * c.L;
+  const int parts = std::max(residual_splits(rws, c.d, HDi), residual_splits(rws, c.d, c.d_ff));
+  w.x = take(static_cast<size_t>(parts) * rows * c.d * 4);
   w.h1 = take(rows * c.d * 2);
   w.f = take(rows * static_cast<size_t>(c.d_ff) * 2);
   w.total = off;
@@ -128,6 +143,30 @@ txl_status check_workspace(const WsLayout &ws, const void *workspace, size_t ws_
   return TXL_OK;
 }
 
+// y = LN(res + A W) for a product p (A, W, rows, N = d, K; output p.c0 is the
+// fp32 scratch x): one GEMM with the residual in its epilogue, or, when the
+// tiles cannot fill the chip, a split-K GEMM writing fp32 partials that the
+// LayerNorm adds up in split order before the residual.
+txl_status residual_ln(GemmParams p, const __bf16 *res, const void *gamma, const void *beta,
+                       void *y, float eps, hipStream_t stream) {
+  const int splits = residual_splits(p.rows, p.N, p.K);
+  txl_status s;
+  if (splits > 1) {
+    p.k_splits = splits;
+    p.c_split_stride = static_cast<int64_t>(p.rows) * p.ldc;
+    s = launch_gemm(p, kEpiPartialF32, stream);
+    if (s != TXL_OK) return s;
+    return launch_layernorm(static_cast<const float *>(p.c0), splits, p.c_split_stride, res, gamma,
+                            beta, y, p.rows, p.N, eps, stream);
+  }
+  p.res = res;
+  p.ldres = p.N;
+  s = launch_gemm(p, kEpiResidualF32, stream);
+  if (s != TXL_OK) return s;
+  return launch_layernorm(static_cast<const float *>(p.c0), 1, 0, nullptr, gamma, beta, y, p.rows,
+                          p.N, eps, stream);
+}
+
 // The part of layer n that does not depend on how memory is kept: Q = H W^Q,
 // relative attention over keys / values k, v ([B, M+L, H*d_h] with batch
 // stride kv_sb elements, memory first) masked by `valid`, X = H + A W^O,
@@ -172,22 +211,14 @@ txl_status layer_body(const txl_stack *st, int n, const __bf16 *hc, void *dst, c
   s = txl_rel_attn_fwd(&a, stream);
   if (s != TXL_OK) return s;
   // X = H + A W^O; H1 = LN1(X)
-  GemmParams po = dense(b.o, HD, rows, c.d, HD, lw.wo, b.x, c.d);
-  po.res = hc;
-  po.ldres = c.d;
-  s = launch_gemm(po, kEpiResidualF32, stream);
-  if (s != TXL_OK) return s;
-  s = launch_layernorm(b.x, lw.ln1_g, lw.ln1_b, b.h1, rows, c.d, c.ln_eps, stream);
+  s = residual_ln(dense(b.o, HD, rows, c.d, HD, lw.wo, b.x, c.d), hc, lw.ln1_g, lw.ln1_b, b.h1,
+                  c.ln_eps, stream);
   if (s != TXL_OK) return s;
   // F = GELU(H1 W1); X = H1 + F W2; H^(n) = LN2(X)
   s = launch_gemm(dense(b.h1, c.d, rows, c.d_ff, c.d, lw.w1, b.f, c.d_ff), kEpiGeluBf16, stream);
   if (s != TXL_OK) return s;
-  GemmParams p2 = dense(b.f, c.d_ff, rows, c.d, c.d_ff, lw.w2, b.x, c.d);
-  p2.res = b.h1;
-  p2.ldres = c.d;
-  s = launch_gemm(p2, kEpiResidualF32, stream);
-  if (s != TXL_OK) return s;
-  return launch_layernorm(b.x, lw.ln2_g, lw.ln2_b, dst, rows, c.d, c.ln_eps, stream);
+  return residual_ln(dense(b.f, c.d_ff, rows, c.d, c.d_ff, lw.w2, b.x, c.d), b.h1, lw.ln2_g,
+                     lw.ln2_b, dst, c.ln_eps, stream);
 }
 
 }  // namespace

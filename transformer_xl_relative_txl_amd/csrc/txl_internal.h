@@ -62,7 +62,8 @@ txl_status launch_rel_pos_table(txl_dtype dt, int M, int L, int d, int HD,
                                 const void *w_r, void *r, hipStream_t s);
 
 // ---- dense layers of the stack ---------------------------------------------
-enum { kEpiStoreBf16 = 0, kEpiGeluBf16 = 1, kEpiResidualF32 = 2 };
+// kEpiPartialF32: split-K, split s stores its fp32 partial at c0 + s*c_split_stride
+enum { kEpiStoreBf16 = 0, kEpiGeluBf16 = 1, kEpiResidualF32 = 2, kEpiPartialF32 = 3 };
 // C[m, n] = sum_k A[m, k] W[n, k]; N split at n_split between (w0, c0) and
 // (w1, c1); n_split and N are multiples of 128, K a multiple of 32.
 struct GemmParams {
@@ -86,10 +87,17 @@ struct GemmParams {
   int64_t c_bstride, c_row0;
   const __bf16 *res;  // residual [rows, ldres] for kEpiResidualF32
   int64_t ldres;
+  // split-K (kEpiPartialF32 only): k_splits workgroups per tile, each over a
+  // contiguous range of K slabs
+  int k_splits;
+  int64_t c_split_stride;
 };
 txl_status launch_gemm(const GemmParams &p, int epi, hipStream_t s);
-txl_status launch_layernorm(const float *x, const void *gamma, const void *beta, void *y,
-                            int rows, int d, float eps, hipStream_t s);
+// y = LN(x) over rows of d, x = sum of n_parts fp32 buffers (part_stride
+// elements apart, added in order) plus the bf16 residual res (may be null)
+txl_status launch_layernorm(const float *x, int n_parts, int64_t part_stride, const void *res,
+                            const void *gamma, const void *beta, void *y, int rows, int d,
+                            float eps, hipStream_t s);
 txl_status launch_embed(const int32_t *tokens, const void *emb, void *out, int rows, int d,
                         int vocab, hipStream_t s);
 
