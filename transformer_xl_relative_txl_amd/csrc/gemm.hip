@@ -209,8 +209,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
 // biased variance, one wave per row, result rounded to bf16.
 constexpr int kLnMaxChunks = 16;  // 4-float chunks per lane: d <= 4096
 
+template <int NP>
 __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict__ x,
-                                                        int n_parts, int64_t part_stride,
+                                                        int64_t part_stride,
                                                         const __bf16 *__restrict__ res,
                                                         const __bf16 *__restrict__ gamma,
                                                         const __bf16 *__restrict__ beta,
@@ -228,7 +229,8 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
     if (c < nch) {
       v[c] = *reinterpret_cast<const f32x4 *>(xr + 256 * c + 4 * lane);
       // split-K partials in order, then the residual
-      for (int part = 1; part < n_parts; ++part)
+#pragma unroll
+      for (int part = 1; part < NP; ++part)
         v[c] += *reinterpret_cast<const f32x4 *>(xr + part * part_stride + 256 * c + 4 * lane);
       if (res) {
         const __bf16 *rr = res + static_cast<int64_t>(row) * d + 256 * c + 4 * lane;
@@ -345,10 +347,19 @@ txl_status launch_layernorm(const float *x, int n_parts, int64_t part_stride, co
                             float eps, hipStream_t s) {
   if (rows <= 0) return TXL_OK;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(layernorm_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, x, n_parts,
-                     part_stride, static_cast<const __bf16 *>(res),
-                     static_cast<const __bf16 *>(gamma), static_cast<const __bf16 *>(beta),
-                     static_cast<__bf16 *>(y), rows, d, eps);
+  const dim3 grid((rows + 3) / 4);
+  const __bf16 *r = static_cast<const __bf16 *>(res);
+  const __bf16 *g = static_cast<const __bf16 *>(gamma);
+  const __bf16 *b = static_cast<const __bf16 *>(beta);
+  __bf16 *o = static_cast<__bf16 *>(y);
+  if (n_parts == 1)
+    hipLaunchKernelGGL(layernorm_kernel<1>, grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps);
+  else if (n_parts == 2)
+    hipLaunchKernelGGL(layernorm_kernel<2>, grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps);
+  else if (n_parts == 4)
+    hipLaunchKernelGGL(layernorm_kernel<4>, grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps);
+  else
+    return fail(TXL_ERR_UNSUPPORTED, "layernorm: %d partial sums (1, 2 or 4 are built)", n_parts);
   return check_launch("layernorm_kernel");
 }
 
