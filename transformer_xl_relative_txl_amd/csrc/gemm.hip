@@ -290,9 +290,10 @@ template <int E, int BM, int BN>
 void launch_shape(const GemmParams &p, hipStream_t s) {
   const int64_t tiles = static_cast<int64_t>((p.rows + BM - 1) / BM) * (p.N / BN) *
                         (E == kEpiPartialF32 ? p.k_splits : 1);
-  // long reductions take 64-wide slabs (each slab's MFMAs cover more of the
-  // next slab's load latency), short ones 32-wide (less LDS, more workgroups)
-  if (p.K >= 1024 && p.K % 64 == 0)
+  // slab width by measurement on the stack's shapes (K = 512..4096): 128x128
+  // tiles run best with 32-wide slabs (their 64-wide double buffer takes 74 KB
+  // of LDS), narrower tiles with 64-wide slabs
+  if (!(BM == 128 && BN == 128) && p.K % 64 == 0)
     hipLaunchKernelGGL((gemm_kernel<E, BM, BN, 64>), dim3(static_cast<unsigned>(tiles)), dim3(256),
                        0, s, p);
   else
