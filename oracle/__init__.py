@@ -14,7 +14,8 @@ Pages cited (by title and section):
   [P1] zty624.github.io notes, "Transformer-XL" (sections "Segment-Level
        Recurrence", "Batched Tensor Contract", "Causal Mask With Memory",
        "Relative Positional Encoding", "Dimension Walkthrough", "Relative
-       Shift Trick", "Relative Shift Golden Test", "Batched Streams", ...)
+       Shift Trick", "Relative Shift Golden Test", "Batched Streams", "Stream
+       Sampler Contract", "Training Loop Sketch", ...)
   [P2] wq-win.github.io, "019 Transformer-XL" (section 3 pseudo-code and the
        worked example of a 4x12 score)
   [P3] iopencloud.com, "Transformer-XL与长序列建模" (section 2.2, the
@@ -33,5 +34,9 @@ Parity status of each function (what pins it is listed in the tests):
       layer body (W^O, post-LayerNorm, GELU feed-forward) parity unpinned:
       the pages fix Q from H and K/V from [mem; H] but not the rest of the
       layer; the memory plumbing is pinned by the unrolled-recurrence test.
+  evaluation.row_streams                                   pinned (hand-worked
+      example from the stream-state contract, stream invariants)
+  evaluation.segment_nll                                   pinned (closed form,
+      torch fp64 cross entropy)
 """
-from . import attention, memory, stack  # noqa: F401
+from . import attention, evaluation, memory, stack  # noqa: F401
