@@ -171,6 +171,52 @@ def stack_bench(name: str, steps: int, warmup: int, kv: bool = False) -> dict:
             "gflop_per_step": round(fl / 1e9, 2)}
 
 
+def loss_bench(steps: int, warmup: int) -> dict:
+    """Segment loss of the 16-layer workload: 16 x 384 tokens, d = 512,
+    vocabulary 32768 (tied embedding), as a replayed graph of txl_lm_loss."""
+    import torch
+
+    import transformer_xl_relative_txl_amd as txl
+
+    dev = torch.device("cuda:0")
+    n_tok, d, vocab = 16 * 384, 512, 32768
+    g = torch.Generator().manual_seed(0)
+    h = torch.randn((n_tok, d), generator=g).to(torch.bfloat16).to(dev)
+    w = (torch.randn((vocab, d), generator=g) * 0.02).to(torch.bfloat16).to(dev)
+    tg = torch.randint(0, vocab, (n_tok,), generator=g, dtype=torch.int32).to(dev)
+    nll = torch.empty(n_tok, dtype=torch.float32, device=dev)
+    ws = torch.empty(txl.lib().txl_lm_loss_workspace_bytes(n_tok, vocab), dtype=torch.uint8,
+                     device=dev)
+    for _ in range(max(1, warmup)):
+        txl.txl_lm_loss(h, w, tg, nll, workspace=ws)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        txl.txl_lm_loss(h, w, tg, nll, workspace=ws)
+    gr.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fl = 2.0 * n_tok * vocab * d
+    tflops = fl / (ms * 1e-3) / 1e12
+    return {"metric": "segment loss TFLOP/s (logits + log-softmax + NLL, logits never stored), 1 GPU",
+            "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+            "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"segment loss, {n_tok} tokens (16 x 384), d={d}, "
+                                   f"vocab={vocab}",
+                       "tokens_per_s": round(n_tok / (ms * 1e-3), 1)},
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None},
+            "gflop_per_step": round(fl / 1e9, 2)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,6 +229,8 @@ def main() -> int:
                          "workload or 18-layer d=1024 long-memory workload)")
     ap.add_argument("--kv", action="store_true",
                     help="with --stack: keep memory as projected keys / values")
+    ap.add_argument("--loss", action="store_true",
+                    help="measure the segment loss (logits + cross entropy) instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not run "
@@ -190,6 +238,9 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
+    if args.loss:
+        print(json.dumps(loss_bench(args.steps, args.warmup)), flush=True)
+        return 0
     if args.stack:
         print(json.dumps(stack_bench(args.stack, args.steps, args.warmup, args.kv)), flush=True)
         return 0

@@ -270,6 +270,57 @@ TXL_API txl_status txl_segment_step_kv(txl_stack *st, const int32_t *tokens,
 TXL_API txl_status txl_kv_cache_reset_rows(txl_kv_cache *caches, int32_t n_caches,
                                            const uint8_t *reset, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Evaluation ([P1] "Stream Sampler Contract", "Batched Streams", "Training
+ * Loop Sketch").
+ *
+ * Stream sampler (host only, no device work): every batch row is a state
+ * machine (doc_id, offset, reset) over its own list of documents. A step
+ * hands out the next up to L tokens of the row's current document and the
+ * reset flag the row held before the step; a row that reaches the end of its
+ * document moves to its next document (cyclically) at offset 0 with the flag
+ * raised, so that the following segment starts without context. Readings of
+ * this library: a token's target is the next token of the same document (the
+ * last token of a document has none); a segment shorter than L is padded to
+ * L with pad_id and its padded positions have no target (-1).
+ *
+ * doc_tokens holds all documents back to back: document k is
+ * doc_tokens[doc_offsets[k] .. doc_offsets[k+1]) (n_docs + 1 non-decreasing
+ * offsets; every document non-empty). Row b streams documents
+ * row_docs[row_offsets[b] .. row_offsets[b+1]) in that order (at least one per
+ * row). The sampler copies what it needs; the caller's arrays may be freed
+ * after the call. Every row starts at its first document with reset raised.
+ * ------------------------------------------------------------------------ */
+typedef struct txl_stream_sampler txl_stream_sampler; /* opaque host object */
+
+TXL_API txl_status txl_sampler_create(int32_t B, int32_t L, const int32_t *doc_tokens,
+                                      const int64_t *doc_offsets, int32_t n_docs,
+                                      const int32_t *row_offsets, const int32_t *row_docs,
+                                      int32_t pad_id, txl_stream_sampler **out);
+/* The next segment of every row, into host arrays: tokens [B, L],
+ * targets [B, L] (-1 = no target), reset [B] (1 = clear the row's memory
+ * before this segment: txl_mem_reset_rows / txl_kv_cache_reset_rows), and
+ * lengths [B] (tokens before the padding). Any output pointer may be NULL. */
+TXL_API txl_status txl_sampler_next(txl_stream_sampler *s, int32_t *tokens, int32_t *targets,
+                                    uint8_t *reset, int32_t *lengths);
+TXL_API void txl_sampler_destroy(txl_stream_sampler *s);
+
+/* Segment loss: for token n with logits z = w_out h_n (one per vocabulary
+ * entry), nll[n] = log(sum_v exp(z_v)) - z_{targets[n]}, and 0 where
+ * targets[n] is outside [0, vocab). The logits are never stored: each
+ * vocabulary tile of the bf16 MFMA product keeps, per token, its maximum and
+ * its sum of exponentials, and a second kernel combines the tiles.
+ * h [n_tok, d] bf16 contiguous (e.g. the stack's h_out), w_out [vocab, d] bf16
+ * contiguous (e.g. the tied embedding), targets [n_tok] int32 device,
+ * nll [n_tok] fp32 device. Served: n_tok a multiple of 64, d a multiple of 32,
+ * 16-byte aligned pointers. workspace: txl_lm_loss_workspace_bytes(n_tok,
+ * vocab) device bytes, 256-byte aligned; calls sharing it must not overlap.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+TXL_API size_t txl_lm_loss_workspace_bytes(int32_t n_tok, int32_t vocab);
+TXL_API txl_status txl_lm_loss(const void *h, const void *w_out, const int32_t *targets,
+                               int32_t n_tok, int32_t d, int32_t vocab, float *nll,
+                               void *workspace, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 TXL_API const char *txl_status_str(txl_status s);
 TXL_API const char *txl_last_error(void);  /* thread-local; "" if none */

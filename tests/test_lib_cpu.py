@@ -82,3 +82,52 @@ def test_stack_and_kv_cache_host_checks_without_gpu(lib):
     assert b"differ in B" in lib.txl_last_error()
     arr[1].B = 2
     assert lib.txl_kv_cache_reset_rows(arr, 2, None, None) == 1        # null valid
+
+
+def test_stream_sampler_equals_oracle_bitwise(lib):
+    """The library's host sampler against the oracle's reading of the stream
+    contract, on random documents: tokens, targets, resets and lengths equal."""
+    import numpy as np
+    from oracle import evaluation as ev
+    from transformer_xl_relative_txl_amd import _binding as bd
+    rng = np.random.default_rng(5)
+    for B, L, n_docs, max_len in [(4, 8, 5, 40), (3, 64, 3, 200), (2, 1, 2, 3)]:
+        docs = [[rng.integers(1, 1000, size=int(rng.integers(1, max_len + 1))).tolist()
+                 for _ in range(n_docs)] for _ in range(B)]
+        n_seg = 50
+        t, g, r, n = ev.row_streams(docs, L, n_seg, pad_id=7)
+        s = bd.StreamSampler(docs, L, pad_id=7)
+        for k in range(n_seg):
+            tok, tgt, rst, ln = s.next()
+            assert (tok == t[k]).all() and (tgt == g[k]).all(), (B, L, k)
+            assert (rst == r[k]).all() and (ln == n[k]).all(), (B, L, k)
+        s.close()
+
+
+def test_stream_sampler_and_loss_reject_bad_arguments(lib):
+    import numpy as np
+    from transformer_xl_relative_txl_amd import _binding as bd
+    tok = np.arange(10, dtype=np.int32)
+    off = np.array([0, 4, 4, 10], dtype=np.int64)        # document 1 is empty
+    ro = np.array([0, 1], dtype=np.int32)
+    rd = np.array([0], dtype=np.int32)
+    h = ctypes.c_void_p()
+    assert lib.txl_sampler_create(1, 4, tok.ctypes.data, off.ctypes.data, 3, ro.ctypes.data,
+                                  rd.ctypes.data, 0, ctypes.byref(h)) == 1
+    assert b"empty" in lib.txl_last_error()
+    off = np.array([0, 4, 10], dtype=np.int64)
+    rd = np.array([5], dtype=np.int32)                     # no such document
+    assert lib.txl_sampler_create(1, 4, tok.ctypes.data, off.ctypes.data, 2, ro.ctypes.data,
+                                  rd.ctypes.data, 0, ctypes.byref(h)) == 1
+    ro = np.array([0, 0], dtype=np.int32)                  # row without documents
+    assert lib.txl_sampler_create(1, 4, tok.ctypes.data, off.ctypes.data, 2, ro.ctypes.data,
+                                  rd.ctypes.data, 0, ctypes.byref(h)) == 1
+    assert lib.txl_sampler_next(None, None, None, None, None) == 1
+    # loss: checks before any launch
+    assert lib.txl_lm_loss(None, None, None, 0, 64, 100, None, None, 0, None) == 0   # nothing to do
+    assert lib.txl_lm_loss(None, None, None, 64, 64, 100, None, None, 0, None) == 1  # null
+    fake = 1 << 20
+    assert lib.txl_lm_loss(fake, fake, fake, 65, 64, 100, fake, fake, 1 << 30, None) == 2
+    assert lib.txl_lm_loss(fake, fake, fake, 64, 48, 100, fake, fake, 1 << 30, None) == 2
+    assert lib.txl_lm_loss(fake, fake, fake, 64, 64, 100, fake, fake, 16, None) == 3  # workspace
+    assert lib.txl_lm_loss_workspace_bytes(64, 100) >= 2 * 64 * 4 + 64 * 4

@@ -5,6 +5,7 @@ holds every kernel; this package only marshals torch tensors into its C ABI.
 """
 from ._binding import (  # noqa: F401
     LIB_PATH,
+    StreamSampler,
     TXL_BF16,
     TXL_F32,
     TxlError,
@@ -13,6 +14,7 @@ from ._binding import (  # noqa: F401
     TxlStack,
     lib,
     txl_kv_cache_reset_rows,
+    txl_lm_loss,
     txl_mem_read_logical,
     txl_mem_reset_rows,
     txl_mem_update,

@@ -131,6 +131,16 @@ def _load() -> ctypes.CDLL:
     lib.txl_segment_step_kv.restype = st
     lib.txl_kv_cache_reset_rows.argtypes = [ctypes.POINTER(TxlKVCacheStruct), i32, vp, vp]
     lib.txl_kv_cache_reset_rows.restype = st
+    lib.txl_sampler_create.argtypes = [i32, i32, vp, vp, i32, vp, vp, i32, ctypes.POINTER(vp)]
+    lib.txl_sampler_create.restype = st
+    lib.txl_sampler_next.argtypes = [vp, vp, vp, vp, vp]
+    lib.txl_sampler_next.restype = st
+    lib.txl_sampler_destroy.argtypes = [vp]
+    lib.txl_sampler_destroy.restype = None
+    lib.txl_lm_loss_workspace_bytes.argtypes = [i32, i32]
+    lib.txl_lm_loss_workspace_bytes.restype = sz
+    lib.txl_lm_loss.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
+    lib.txl_lm_loss.restype = st
     del i64
     return lib
 
@@ -419,10 +429,80 @@ class TxlStack:
             pass
 
 
+class StreamSampler:
+    """The per-row stream sampler (txl_sampler_*; host only): docs_per_row[b]
+    is the list of documents (token id sequences) row b streams, in order."""
+
+    def __init__(self, docs_per_row: Sequence[Sequence[Sequence[int]]], L: int, pad_id: int = 0):
+        import numpy as np
+        flat, offs, row_offs, row_docs = [], [0], [0], []
+        for docs in docs_per_row:
+            for doc in docs:
+                flat.extend(int(t) for t in doc)
+                offs.append(len(flat))
+                row_docs.append(len(offs) - 2)
+            row_offs.append(len(row_docs))
+        self.B, self.L = len(docs_per_row), int(L)
+        tok = np.asarray(flat, dtype=np.int32)
+        off = np.asarray(offs, dtype=np.int64)
+        ro = np.asarray(row_offs, dtype=np.int32)
+        rd = np.asarray(row_docs, dtype=np.int32)
+        h = ctypes.c_void_p()
+        _check("txl_sampler_create",
+               lib().txl_sampler_create(self.B, self.L, tok.ctypes.data, off.ctypes.data,
+                                        len(offs) - 1, ro.ctypes.data, rd.ctypes.data,
+                                        int(pad_id), ctypes.byref(h)))
+        self._h = h
+
+    def next(self):
+        """(tokens [B, L] int32, targets [B, L] int32, reset [B] uint8,
+        lengths [B] int32) as host numpy arrays."""
+        import numpy as np
+        tok = np.empty((self.B, self.L), dtype=np.int32)
+        tgt = np.empty((self.B, self.L), dtype=np.int32)
+        rst = np.empty((self.B,), dtype=np.uint8)
+        ln = np.empty((self.B,), dtype=np.int32)
+        _check("txl_sampler_next",
+               lib().txl_sampler_next(self._h, tok.ctypes.data, tgt.ctypes.data, rst.ctypes.data,
+                                      ln.ctypes.data))
+        return tok, tgt, rst, ln
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().txl_sampler_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def txl_lm_loss(h: torch.Tensor, w_out: torch.Tensor, targets: torch.Tensor, nll: torch.Tensor,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """nll[n] = logsumexp(w_out h[n]) - (w_out h[n])[targets[n]] (0 where the
+    target is outside the vocabulary). h [n_tok, d] and w_out [vocab, d] bf16
+    contiguous; targets int32 [n_tok]; nll fp32 [n_tok]."""
+    assert h.is_contiguous() and w_out.is_contiguous() and targets.is_contiguous()
+    assert targets.dtype == torch.int32 and nll.dtype == torch.float32
+    n_tok, d = h.reshape(-1, h.shape[-1]).shape
+    vocab = w_out.shape[0]
+    need = lib().txl_lm_loss_workspace_bytes(n_tok, vocab)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
+    _check("txl_lm_loss",
+           lib().txl_lm_loss(_ptr(h), _ptr(w_out), _ptr(targets), n_tok, d, vocab, _ptr(nll),
+                             _ptr(workspace), workspace.numel(), _stream(stream)))
+    return nll
+
+
 def exported_symbols() -> List[str]:
     """Names of the C entry points this binding wraps."""
     return ["txl_rel_pos_table", "txl_rel_attn_fwd", "txl_mem_update",
             "txl_mem_reset_rows", "txl_mem_read_logical", "txl_stack_persistent_bytes",
             "txl_stack_create", "txl_segment_step_workspace_bytes", "txl_segment_step",
             "txl_stack_destroy", "txl_kv_cache_min_capacity", "txl_segment_step_kv",
-            "txl_kv_cache_reset_rows", "txl_status_str", "txl_last_error", "txl_version"]
+            "txl_kv_cache_reset_rows", "txl_sampler_create", "txl_sampler_next",
+            "txl_sampler_destroy", "txl_lm_loss_workspace_bytes", "txl_lm_loss",
+            "txl_status_str", "txl_last_error", "txl_version"]

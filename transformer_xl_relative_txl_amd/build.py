@@ -27,6 +27,8 @@ SOURCES = [
     "rel_attn_mfma.hip",
     "gemm.hip",
     "stack.cpp",
+    "sampler.cpp",
+    "loss.cpp",
 ]
 
 ARCH = "gfx950"

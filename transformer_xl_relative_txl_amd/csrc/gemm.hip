@@ -170,6 +170,59 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
 
   // epilogue: register 4a+c of block (i, jn) holds
   // C[wm*BM/2 + 32i + 8a + 4g + c][wn*BN/2 + 32jn + r]
+  if (E == kEpiLse) {
+    // per column: this wave's rows (the two lane halves hold different rows
+    // of the same column), then the two row halves of the tile through LDS
+    float *xch = reinterpret_cast<float *>(&sa[0][0]);  // [BN][2]
+    float wmx[WN], wsm[WN];
+#pragma unroll
+    for (int jn = 0; jn < WN; ++jn) {
+      const int cl = wn * (BN / 2) + jn * 32 + r;
+      const int n = n0 + cl;
+      const int t = p.targets[n];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const int m = m0 + wm * (BM / 2) + i * 32 + 8 * (x >> 2) + 4 * g + (x & 3);
+          if (m < p.rows) mx = fmaxf(mx, acc[i][jn][x]);
+          if (m == t) p.tgt[n] = acc[i][jn][x];  // the one lane holding (t, n)
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float sm = 0.0f;
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const int m = m0 + wm * (BM / 2) + i * 32 + 8 * (x >> 2) + 4 * g + (x & 3);
+          if (m < p.rows) sm += __builtin_amdgcn_exp2f((acc[i][jn][x] - mx) * 1.4426950408889634f);
+        }
+      sm += __shfl_xor(sm, 32);
+      wmx[jn] = mx;
+      wsm[jn] = sm;
+      if (wm == 1 && g == 0) {
+        xch[2 * cl] = mx;
+        xch[2 * cl + 1] = sm;
+      }
+    }
+    __syncthreads();
+    if (wm == 0 && g == 0) {
+#pragma unroll
+      for (int jn = 0; jn < WN; ++jn) {
+        const int cl = wn * (BN / 2) + jn * 32 + r;
+        const float m1 = xch[2 * cl], s1 = xch[2 * cl + 1];
+        const float mm = fmaxf(wmx[jn], m1);
+        // a row half with no vocabulary rows has (-inf, 0)
+        float ss = wsm[jn] * __builtin_amdgcn_exp2f((wmx[jn] - mm) * 1.4426950408889634f);
+        if (s1 > 0.0f) ss += s1 * __builtin_amdgcn_exp2f((m1 - mm) * 1.4426950408889634f);
+        const int64_t at = static_cast<int64_t>(tm) * p.N + n0 + cl;
+        p.part_m[at] = mm;
+        p.part_s[at] = ss;
+      }
+    }
+    return;
+  }
   const bool second = n0 >= p.n_split;
 #pragma unroll
   for (int jn = 0; jn < WN; ++jn) {
@@ -271,6 +324,48 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
   }
 }
 
+// Combine the per-tile (max, sum of exponentials) of each token: a block of
+// 256 threads covers 16 tokens, sixteen threads per token splitting the
+// tiles (consecutive threads on consecutive tokens), then one combine in LDS.
+constexpr int kFinTok = 16, kFinGrp = 16;
+__global__ __launch_bounds__(256) void lse_finish_kernel(const float *__restrict__ part_m,
+                                                         const float *__restrict__ part_s,
+                                                         const float *__restrict__ tgt,
+                                                         const int32_t *__restrict__ targets,
+                                                         int n_tiles, int N, int vocab,
+                                                         float *__restrict__ nll) {
+  __shared__ float sm_m[kFinGrp][kFinTok], sm_s[kFinGrp][kFinTok];
+  const int tl = threadIdx.x % kFinTok, grp = threadIdx.x / kFinTok;
+  const int n = blockIdx.x * kFinTok + tl;
+  float m = -INFINITY, s = 0.0f;
+  if (n < N) {
+    for (int t = grp; t < n_tiles; t += kFinGrp) {
+      const float mt = part_m[static_cast<int64_t>(t) * N + n];
+      const float st = part_s[static_cast<int64_t>(t) * N + n];
+      if (st <= 0.0f) continue;
+      if (mt > m) {
+        s = s * __expf(m - mt) + st;
+        m = mt;
+      } else {
+        s += st * __expf(mt - m);
+      }
+    }
+  }
+  sm_m[grp][tl] = m;
+  sm_s[grp][tl] = s;
+  __syncthreads();
+  if (grp != 0 || n >= N) return;
+  float mm = sm_m[0][tl];
+#pragma unroll
+  for (int k = 1; k < kFinGrp; ++k) mm = fmaxf(mm, sm_m[k][tl]);
+  float ss = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kFinGrp; ++k)
+    if (sm_s[k][tl] > 0.0f) ss += sm_s[k][tl] * __expf(sm_m[k][tl] - mm);
+  const int t = targets[n];
+  nll[n] = (t >= 0 && t < vocab) ? (mm + __logf(ss)) - tgt[n] : 0.0f;
+}
+
 // H0[b, l, :] = emb[tokens[b, l], :]; ids outside [0, vocab) give a zero row.
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ tokens,
                                                     const u32x4 *__restrict__ emb,
@@ -303,6 +398,13 @@ void launch_shape(const GemmParams &p, hipStream_t s) {
 
 template <int E>
 void launch_epi(const GemmParams &p, hipStream_t s) {
+  if (E == kEpiLse) {  // the row tile must match lse_row_tiles
+    if (p.N % 128 == 0)
+      launch_shape<E, 128, 128>(p, s);
+    else
+      launch_shape<E, 128, 64>(p, s);
+    return;
+  }
   // the largest tile that still gives about two tiles per CU
   auto tiles = [&](int bm, int bn) {
     return static_cast<int64_t>((p.rows + bm - 1) / bm) * (p.N / bn) *
@@ -321,7 +423,7 @@ void launch_epi(const GemmParams &p, hipStream_t s) {
 
 txl_status launch_gemm(const GemmParams &p, int epi, hipStream_t s) {
   if (p.rows <= 0) return TXL_OK;
-  if (p.K % 32 || p.N % 64 || p.n_split % 128)
+  if (p.K % 32 || p.N % 64 || (p.n_split < p.N && p.n_split % 128))
     return fail(TXL_ERR_UNSUPPORTED, "gemm: K must be a multiple of 32, N of 64 and the split of 128");
   if (p.c_seg < 0 || p.c_seg % 32)
     return fail(TXL_ERR_UNSUPPORTED, "gemm: output segment length must be a multiple of 32");
@@ -338,8 +440,10 @@ txl_status launch_gemm(const GemmParams &p, int epi, hipStream_t s) {
     launch_epi<kEpiGeluBf16>(p, s);
   else if (epi == kEpiResidualF32)
     launch_epi<kEpiResidualF32>(p, s);
-  else
+  else if (epi == kEpiPartialF32)
     launch_epi<kEpiPartialF32>(p, s);
+  else
+    launch_epi<kEpiLse>(p, s);
   return check_launch("gemm_kernel");
 }
 
@@ -362,6 +466,18 @@ txl_status launch_layernorm(const float *x, int n_parts, int64_t part_stride, co
   else
     return fail(TXL_ERR_UNSUPPORTED, "layernorm: %d partial sums (1, 2 or 4 are built)", n_parts);
   return check_launch("layernorm_kernel");
+}
+
+int lse_row_tiles(int rows, int /*N*/) { return (rows + 127) / 128; }
+
+txl_status launch_lse_finish(const float *part_m, const float *part_s, const float *tgt,
+                             const int32_t *targets, int n_tiles, int N, int vocab, float *nll,
+                             hipStream_t s) {
+  if (N <= 0) return TXL_OK;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(lse_finish_kernel, dim3((N + kFinTok - 1) / kFinTok), dim3(256), 0, s, part_m, part_s, tgt,
+                     targets, n_tiles, N, vocab, nll);
+  return check_launch("lse_finish_kernel");
 }
 
 txl_status launch_embed(const int32_t *tokens, const void *emb, void *out, int rows, int d,

@@ -63,7 +63,10 @@ txl_status launch_rel_pos_table(txl_dtype dt, int M, int L, int d, int HD,
 
 // ---- dense layers of the stack ---------------------------------------------
 // kEpiPartialF32: split-K, split s stores its fp32 partial at c0 + s*c_split_stride
-enum { kEpiStoreBf16 = 0, kEpiGeluBf16 = 1, kEpiResidualF32 = 2, kEpiPartialF32 = 3 };
+// kEpiLse: C is not stored; per row tile tm and column n the tile's maximum
+//          and sum of exponentials over its rows go to part_m/part_s[tm*N + n],
+//          and C[targets[n]][n] to tgt[n] (rows = vocabulary, columns = tokens)
+enum { kEpiStoreBf16 = 0, kEpiGeluBf16 = 1, kEpiResidualF32 = 2, kEpiPartialF32 = 3, kEpiLse = 4 };
 // C[m, n] = sum_k A[m, k] W[n, k]; N split at n_split between (w0, c0) and
 // (w1, c1); n_split and N are multiples of 128, K a multiple of 32.
 struct GemmParams {
@@ -91,6 +94,9 @@ struct GemmParams {
   // contiguous range of K slabs
   int k_splits;
   int64_t c_split_stride;
+  // kEpiLse only
+  const int32_t *targets;
+  float *part_m, *part_s, *tgt;
 };
 txl_status launch_gemm(const GemmParams &p, int epi, hipStream_t s);
 // y = LN(x) over rows of d, x = sum of n_parts fp32 buffers (part_stride
@@ -98,6 +104,13 @@ txl_status launch_gemm(const GemmParams &p, int epi, hipStream_t s);
 txl_status launch_layernorm(const float *x, int n_parts, int64_t part_stride, const void *res,
                             const void *gamma, const void *beta, void *y, int rows, int d,
                             float eps, hipStream_t s);
+// row tiles the kEpiLse GEMM uses for `rows` rows (its part_m/part_s height)
+int lse_row_tiles(int rows, int N);
+// nll[n] = log(sum_t part_s[t][n] exp(part_m[t][n] - m)) + m - tgt[n] for
+// targets[n] in [0, vocab), else 0
+txl_status launch_lse_finish(const float *part_m, const float *part_s, const float *tgt,
+                             const int32_t *targets, int n_tiles, int N, int vocab, float *nll,
+                             hipStream_t s);
 txl_status launch_embed(const int32_t *tokens, const void *emb, void *out, int rows, int d,
                         int vocab, hipStream_t s);
 
