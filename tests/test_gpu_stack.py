@@ -181,6 +181,29 @@ def test_rel_pos_table_fp32_entry_point():
     assert err <= 1e-5
 
 
+def test_rel_pos_table_full_size_both_dtypes():
+    """R of the 18-layer workload's layer shape (M=640, L=128, d=1024, 16
+    heads of 64) against the fp64 oracle: fp32 output within 1e-5 of the
+    largest entry (normwise), bf16 output within one bf16 ulp plus fp32 slack."""
+    M, L, H, dh, d = 640, 128, 16, 64, 1024
+    g = torch.Generator().manual_seed(9)
+    wr = torch.randn((H * dh, d), generator=g) / d ** 0.5      # output-major
+    ref = ost.rel_pos_table(wr.t().double().numpy(), M, L, H, dh)
+    ref = ref.transpose(1, 0, 2).reshape(M + L, H * dh)
+    r32 = torch.empty((M + L, H * dh), device=DEV)
+    txl.txl_rel_pos_table(wr.to(DEV), M, L, H, dh, r32)
+    err32 = np.abs(f64(r32) - ref).max() / np.abs(ref).max()
+    wb = wr.to(torch.bfloat16)
+    refb = ost.rel_pos_table(wb.t().double().numpy(), M, L, H, dh)
+    refb = refb.transpose(1, 0, 2).reshape(M + L, H * dh)
+    rb = torch.empty((M + L, H * dh), dtype=torch.bfloat16, device=DEV)
+    txl.txl_rel_pos_table(wb.to(DEV), M, L, H, dh, rb)
+    errb = np.abs(f64(rb) - refb)
+    say(f"R full size: fp32 max rel err {err32:.2e}, bf16 max abs err {errb.max():.2e}")
+    assert err32 <= 1e-5
+    assert (errb <= 2.0 ** -8 * np.abs(refb) + 1e-5).all()
+
+
 def test_reset_row_equals_fresh_stream_bitwise():
     """A row reset at segment 2 produces bit-identical outputs to the same
     row of a stream that starts fresh at segment 2."""
