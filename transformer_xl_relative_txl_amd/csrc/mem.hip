@@ -79,6 +79,35 @@ __global__ __launch_bounds__(kThreads) void mem_update_kernel(RingBatch rb, Ring
     if (dst[j]) __builtin_nontemporal_store(v[j], dst[j]);
 }
 
+// The same update when a row is a whole number of wavefronts (WPR waves of
+// 64 chunks): the row, and with it the ring, batch row and slot, is uniform
+// across a wavefront, so it is decoded once in scalar registers and each lane
+// only adds its chunk index.
+template <int WPR>
+__global__ __launch_bounds__(kThreads) void mem_update_rows_kernel(RingBatch rb, RingMeta mt,
+                                                                   uint32_t n_rows) {
+  const uint32_t wave = (blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t row = __builtin_amdgcn_readfirstlane(wave / WPR);  // (ring, b, k) flattened
+  if (row >= n_rows) return;
+  const uint32_t c = (wave % WPR) * 64 + lane;
+  const uint32_t rk = fdiv(row, mt.div_lp);
+  const uint32_t k = row - rk * mt.Lp;
+  const uint32_t ring = fdiv(rk, mt.div_b);
+  const uint32_t b = rk - ring * mt.B;
+  const int64_t src_row = static_cast<int64_t>(b) * mt.L + (mt.L - mt.Lp + k);
+  int64_t slot = rb.head[ring] + k;
+  if (slot >= mt.M) slot -= mt.M;
+  const int64_t dst_row = static_cast<int64_t>(b) * mt.M + slot;
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(rb.h[ring]) + src_row * mt.cpr + c;
+  u32x4 *dst = reinterpret_cast<u32x4 *>(rb.data[ring]) + dst_row * mt.cpr + c;
+  __builtin_nontemporal_store(__builtin_nontemporal_load(src), dst);
+  if (k == 0 && c == 0) {
+    const int nv = rb.valid[ring][b] + mt.L;
+    rb.valid[ring][b] = nv < mt.M ? nv : mt.M;
+  }
+}
+
 struct ValidPtrs {
   int32_t *p[kMaxRingsPerLaunch];
 };
@@ -165,8 +194,14 @@ txl_status launch_mem_update(const RingBatch &rb, int n, int B, int M, int L,
   mt.total = static_cast<uint32_t>(total);
   const int64_t per_block = kThreads * kChunks;
   const unsigned blocks = static_cast<unsigned>((total + per_block - 1) / per_block);
+  const uint32_t n_rows = static_cast<uint32_t>(total / cpr);
   (void)hipGetLastError();
-  hipLaunchKernelGGL(mem_update_kernel, dim3(blocks), dim3(kThreads), 0, s, rb, mt);
+  if (cpr == 64)
+    hipLaunchKernelGGL(mem_update_rows_kernel<1>, dim3(blocks), dim3(kThreads), 0, s, rb, mt, n_rows);
+  else if (cpr == 128)
+    hipLaunchKernelGGL(mem_update_rows_kernel<2>, dim3(blocks), dim3(kThreads), 0, s, rb, mt, n_rows);
+  else
+    hipLaunchKernelGGL(mem_update_kernel, dim3(blocks), dim3(kThreads), 0, s, rb, mt);
   return check_launch("mem_update_kernel");
 }
 
