@@ -11,8 +11,9 @@
 // GEMM: C[m, n] = sum_k A[m, k] W[n, k] (W output-major, like a torch Linear
 // weight), tiles of 128 or 64 rows x 128 or 64 columns per workgroup of 4
 // waves (chosen per call so a launch has about two tiles per CU), blocks of
-// v_mfma_f32_32x32x16_bf16, K in slabs of 32 or 64 through two LDS buffers with one
-// barrier per slab, the next slab prefetched into registers during the MFMAs.
+// v_mfma_f32_32x32x16_bf16, K in slabs of 64 (32 when K is not a multiple of
+// 64) through two LDS buffers with one barrier per slab; global loads run two
+// slabs ahead in two register sets.
 // Tiles are handed out so that the tiles of one XCD are contiguous in
 // row-major order (the hardware deals workgroups to the 8 XCDs round robin),
 // which keeps a row tile's A rows in one L2.
@@ -113,21 +114,24 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
   }
   if (p.gather && !__syncthreads_or(any_valid)) return;  // all rows are empty memory slots
 
-  u32x4 av[A_CH], wv[B_CH];
-  auto load = [&](int k0) {
+  // two register sets: slab ks+2 is loaded while slab ks is multiplied and
+  // slab ks+1 waits in the other set for its LDS buffer
+  u32x4 av[2][A_CH], wv[2][B_CH];
+  auto load = [&](int set, int k0) {
 #pragma unroll
     for (int j = 0; j < A_CH; ++j)
-      av[j] = arow[j] ? *reinterpret_cast<const u32x4 *>(arow[j] + k0 + 8 * kc) : u32x4{0u, 0u, 0u, 0u};
+      av[set][j] = arow[j] ? *reinterpret_cast<const u32x4 *>(arow[j] + k0 + 8 * kc)
+                           : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int j = 0; j < B_CH; ++j) wv[j] = *reinterpret_cast<const u32x4 *>(wrow[j] + k0 + 8 * kc);
+    for (int j = 0; j < B_CH; ++j) wv[set][j] = *reinterpret_cast<const u32x4 *>(wrow[j] + k0 + 8 * kc);
   };
-  auto store = [&](int buf) {
+  auto store = [&](int set, int buf) {
 #pragma unroll
     for (int j = 0; j < A_CH; ++j)
-      *reinterpret_cast<u32x4 *>(&sa[buf][(tid / CPR + RPP * j) * AS + 8 * kc]) = av[j];
+      *reinterpret_cast<u32x4 *>(&sa[buf][(tid / CPR + RPP * j) * AS + 8 * kc]) = av[set][j];
 #pragma unroll
     for (int j = 0; j < B_CH; ++j)
-      *reinterpret_cast<u32x4 *>(&sb[buf][(tid / CPR + RPP * j) * AS + 8 * kc]) = wv[j];
+      *reinterpret_cast<u32x4 *>(&sb[buf][(tid / CPR + RPP * j) * AS + 8 * kc]) = wv[set][j];
   };
 
   f32x16 acc[WM][WN];
@@ -141,13 +145,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
   const int n_slab_all = p.K / BKS;
   const int ks0 = E == kEpiPartialF32 ? split * n_slab_all / p.k_splits : 0;
   const int ks1 = E == kEpiPartialF32 ? (split + 1) * n_slab_all / p.k_splits : n_slab_all;
-  load(ks0 * BKS);
-  store(0);
-  __syncthreads();
-  for (int ks = ks0; ks < ks1; ++ks) {
-    const int cur = (ks - ks0) & 1;
-    const bool more = ks + 1 < ks1;
-    if (more) load((ks + 1) * BKS);
+  auto compute = [&](int cur) {
 #pragma unroll
     for (int s = 0; s < BKS / 16; ++s) {
       bf16x8 af[WM], bfr[WN];
@@ -164,7 +162,22 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int jn = 0; jn < WN; ++jn) acc[i][jn] = mfma32(af[i], bfr[jn], acc[i][jn]);
     }
-    if (more) store(cur ^ 1);  // its last readers finished before the previous barrier
+  };
+  // slab ks lives in LDS buffer (ks - ks0) & 1 and register set (ks - ks0) & 1;
+  // a buffer is refilled only after the barrier that ends its last readers
+  load(0, ks0 * BKS);
+  if (ks0 + 1 < ks1) load(1, (ks0 + 1) * BKS);
+  store(0, 0);
+  __syncthreads();
+  for (int ks = ks0; ks < ks1; ks += 2) {
+    if (ks + 2 < ks1) load(0, (ks + 2) * BKS);
+    compute(0);
+    if (ks + 1 < ks1) store(1, 1);
+    __syncthreads();
+    if (ks + 1 >= ks1) break;
+    if (ks + 3 < ks1) load(1, (ks + 3) * BKS);
+    compute(1);
+    if (ks + 2 < ks1) store(0, 0);
     __syncthreads();
   }
 
@@ -385,10 +398,9 @@ template <int E, int BM, int BN>
 void launch_shape(const GemmParams &p, hipStream_t s) {
   const int64_t tiles = static_cast<int64_t>((p.rows + BM - 1) / BM) * (p.N / BN) *
                         (E == kEpiPartialF32 ? p.k_splits : 1);
-  // slab width by measurement on the stack's shapes (K = 512..4096): 128x128
-  // tiles run best with 32-wide slabs (their 64-wide double buffer takes 74 KB
-  // of LDS), narrower tiles with 64-wide slabs
-  if (!(BM == 128 && BN == 128) && p.K % 64 == 0)
+  // slab width by measurement on the stack's shapes (K = 512..4096): with
+  // loads two slabs ahead, 64-wide slabs win for every tile shape
+  if (p.K % 64 == 0)
     hipLaunchKernelGGL((gemm_kernel<E, BM, BN, 64>), dim3(static_cast<unsigned>(tiles)), dim3(256),
                        0, s, p);
   else
@@ -405,15 +417,18 @@ void launch_epi(const GemmParams &p, hipStream_t s) {
       launch_shape<E, 128, 64>(p, s);
     return;
   }
-  // the largest tile that still gives about two tiles per CU
+  // by measurement on the stack's shapes: 128x128 tiles when they alone give
+  // about two tiles per CU, except under the GELU epilogue (its per-output
+  // cost favours more, smaller tiles); split-K products 128x64 when the splits
+  // fill the chip; otherwise 64x64
   auto tiles = [&](int bm, int bn) {
     return static_cast<int64_t>((p.rows + bm - 1) / bm) * (p.N / bn) *
            (E == kEpiPartialF32 ? p.k_splits : 1);
   };
   const int64_t want = 512;
-  if (p.N % 128 == 0 && tiles(128, 128) >= want)
+  if (E != kEpiGeluBf16 && E != kEpiPartialF32 && p.N % 128 == 0 && tiles(128, 128) >= want)
     launch_shape<E, 128, 128>(p, s);
-  else if (tiles(128, 64) >= want)
+  else if (E == kEpiPartialF32 && tiles(128, 64) >= want)
     launch_shape<E, 128, 64>(p, s);
   else
     launch_shape<E, 64, 64>(p, s);
