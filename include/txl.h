@@ -115,6 +115,23 @@ typedef struct {
 TXL_API txl_status txl_rel_attn_fwd(const txl_rel_attn_args *a,
                                     hipStream_t stream);
 
+/* The same attention with the visible keys of every query tile cut into
+ * kv_splits contiguous ranges, each handled by its own workgroup, for short
+ * segments whose query tiles alone cannot fill the GPU. Each range keeps its
+ * own running max and sum and writes unnormalised results to `workspace`
+ * (txl_rel_attn_split_workspace_bytes(B, H, L, kv_splits) device bytes,
+ * 256-byte aligned); a second kernel combines them ([P1] "Dimension
+ * Walkthrough": the softmax over all visible keys is the same after the
+ * combination; only the fp32 summation order differs from txl_rel_attn_fwd).
+ * kv_splits in [1, 64]; 1 is txl_rel_attn_fwd. Splits above 1 are built for
+ * bf16 only (else UNSUPPORTED). Calls sharing a workspace must not overlap.
+ * Errors: those of txl_rel_attn_fwd, WORKSPACE. */
+TXL_API size_t txl_rel_attn_split_workspace_bytes(int32_t B, int32_t H, int32_t L,
+                                                  int32_t kv_splits);
+TXL_API txl_status txl_rel_attn_fwd_split(const txl_rel_attn_args *a, int32_t kv_splits,
+                                          void *workspace, size_t ws_bytes,
+                                          hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Per-layer FIFO memory as a ring buffer.
  * [P1] "Segment-Level Recurrence" and "Batched Tensor Contract": after the

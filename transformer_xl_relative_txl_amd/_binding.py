@@ -96,6 +96,7 @@ def _load() -> ctypes.CDLL:
             "`python -m transformer_xl_relative_txl_amd.build` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int
+    sz = ctypes.c_size_t
     lib.txl_status_str.argtypes = [st]
     lib.txl_status_str.restype = ctypes.c_char_p
     lib.txl_last_error.argtypes = []
@@ -106,6 +107,10 @@ def _load() -> ctypes.CDLL:
     lib.txl_rel_pos_table.restype = st
     lib.txl_rel_attn_fwd.argtypes = [ctypes.POINTER(RelAttnArgs), vp]
     lib.txl_rel_attn_fwd.restype = st
+    lib.txl_rel_attn_split_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.txl_rel_attn_split_workspace_bytes.restype = sz
+    lib.txl_rel_attn_fwd_split.argtypes = [ctypes.POINTER(RelAttnArgs), i32, vp, sz, vp]
+    lib.txl_rel_attn_fwd_split.restype = st
     lib.txl_mem_update.argtypes = [ctypes.POINTER(TxlMemStruct), i32,
                                    ctypes.POINTER(vp), i32, vp]
     lib.txl_mem_update.restype = st
@@ -113,7 +118,6 @@ def _load() -> ctypes.CDLL:
     lib.txl_mem_reset_rows.restype = st
     lib.txl_mem_read_logical.argtypes = [ctypes.POINTER(TxlMemStruct), vp, vp]
     lib.txl_mem_read_logical.restype = st
-    sz = ctypes.c_size_t
     lib.txl_stack_persistent_bytes.argtypes = [ctypes.POINTER(StackConfig)]
     lib.txl_stack_persistent_bytes.restype = sz
     lib.txl_segment_step_workspace_bytes.argtypes = [ctypes.POINTER(StackConfig)]
@@ -200,11 +204,13 @@ def txl_rel_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      r: torch.Tensor, u: torch.Tensor, vb: torch.Tensor,
                      out: torch.Tensor, mem_valid: Optional[torch.Tensor] = None,
                      lse: Optional[torch.Tensor] = None, scale: float = 0.0,
-                     stream=None) -> torch.Tensor:
+                     stream=None, kv_splits: int = 1,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Relative attention. q [B,H,L,d_h]; k, v [B,H,M+L,d_h] (same strides);
     r [H,M+L,d_h]; u, vb [H,d_h] contiguous; out [B,H,L,d_h]; mem_valid [B]
     int32; lse [B,H,L] float32. Any element strides with a contiguous last
-    dimension."""
+    dimension. kv_splits > 1 calls txl_rel_attn_fwd_split (workspace
+    allocated here when not given)."""
     B, H, L, d_h = q.shape
     M = k.shape[2] - L
     if k.stride() != v.stride():
@@ -224,7 +230,15 @@ def txl_rel_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     a.out = _ptr(out)
     a.o_sb, a.o_sh, a.o_sl = out.stride(0), out.stride(1), out.stride(2)
     a.lse = _ptr(lse)
-    _check("txl_rel_attn_fwd", lib().txl_rel_attn_fwd(ctypes.byref(a), _stream(stream)))
+    if kv_splits == 1:
+        _check("txl_rel_attn_fwd", lib().txl_rel_attn_fwd(ctypes.byref(a), _stream(stream)))
+        return out
+    need = lib().txl_rel_attn_split_workspace_bytes(B, H, L, kv_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check("txl_rel_attn_fwd_split",
+           lib().txl_rel_attn_fwd_split(ctypes.byref(a), kv_splits, _ptr(workspace),
+                                        workspace.numel(), _stream(stream)))
     return out
 
 
@@ -499,7 +513,8 @@ def txl_lm_loss(h: torch.Tensor, w_out: torch.Tensor, targets: torch.Tensor, nll
 
 def exported_symbols() -> List[str]:
     """Names of the C entry points this binding wraps."""
-    return ["txl_rel_pos_table", "txl_rel_attn_fwd", "txl_mem_update",
+    return ["txl_rel_pos_table", "txl_rel_attn_fwd", "txl_rel_attn_split_workspace_bytes",
+            "txl_rel_attn_fwd_split", "txl_mem_update",
             "txl_mem_reset_rows", "txl_mem_read_logical", "txl_stack_persistent_bytes",
             "txl_stack_create", "txl_segment_step_workspace_bytes", "txl_segment_step",
             "txl_stack_destroy", "txl_kv_cache_min_capacity", "txl_segment_step_kv",

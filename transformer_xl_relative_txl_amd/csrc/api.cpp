@@ -78,9 +78,10 @@ TXL_API txl_status txl_rel_pos_table(txl_dtype dtype, int32_t M, int32_t L,
 }
 
 // ---------------------------------------------------------------------------
-TXL_API txl_status txl_rel_attn_fwd(const txl_rel_attn_args *a,
-                                    hipStream_t stream) {
-  clear_error();
+// Checks the arguments and fills p; *nothing is set to true when there is no
+// work (B == 0 or L == 0).
+static txl_status attn_params(const txl_rel_attn_args *a, AttnParams *out, bool *nothing) {
+  *nothing = false;
   if (!a) return fail(TXL_ERR_INVALID_ARG, "rel_attn: null args");
   if (!dtype_ok(a->dtype)) return fail(TXL_ERR_INVALID_ARG, "rel_attn: bad dtype");
   if (a->B < 0 || a->H < 1 || a->L < 0 || a->M < 0)
@@ -91,7 +92,10 @@ TXL_API txl_status txl_rel_attn_fwd(const txl_rel_attn_args *a,
     return fail(TXL_ERR_INVALID_ARG, "rel_attn: M + L too large");
   if (!(std::isfinite(a->scale)))
     return fail(TXL_ERR_INVALID_ARG, "rel_attn: scale is not finite");
-  if (a->B == 0 || a->L == 0) return TXL_OK;
+  if (a->B == 0 || a->L == 0) {
+    *nothing = true;
+    return TXL_OK;
+  }
   if (!a->q || !a->k || !a->v || !a->r || !a->u || !a->vb || !a->out)
     return fail(TXL_ERR_INVALID_ARG, "rel_attn: null tensor pointer");
   const size_t es = dtype_size(a->dtype);
@@ -110,7 +114,7 @@ TXL_API txl_status txl_rel_attn_fwd(const txl_rel_attn_args *a,
   if (a->mem_valid && (reinterpret_cast<uintptr_t>(a->mem_valid) & 3u))
     return fail(TXL_ERR_INVALID_ARG, "rel_attn: mem_valid not 4-byte aligned");
 
-  AttnParams p;
+  AttnParams p = {};
   p.q = a->q; p.k = a->k; p.v = a->v; p.r = a->r; p.u = a->u; p.vb = a->vb;
   p.out = a->out; p.lse = a->lse; p.valid = a->mem_valid;
   p.q_sb = a->q_sb; p.q_sh = a->q_sh; p.q_sl = a->q_sl;
@@ -119,8 +123,56 @@ TXL_API txl_status txl_rel_attn_fwd(const txl_rel_attn_args *a,
   p.o_sb = a->o_sb; p.o_sh = a->o_sh; p.o_sl = a->o_sl;
   p.B = a->B; p.H = a->H; p.L = a->L; p.M = a->M;
   p.scale = a->scale != 0.0f ? a->scale : 1.0f / std::sqrt(static_cast<float>(a->d_h));
+  *out = p;
+  return TXL_OK;
+}
+
+TXL_API txl_status txl_rel_attn_fwd(const txl_rel_attn_args *a,
+                                    hipStream_t stream) {
+  clear_error();
+  AttnParams p;
+  bool nothing;
+  txl_status st = attn_params(a, &p, &nothing);
+  if (st != TXL_OK || nothing) return st;
   if (a->dtype == TXL_BF16) return launch_rel_attn_mfma(p, stream);
   return launch_rel_attn_valu(p, a->dtype, stream);
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+TXL_API size_t txl_rel_attn_split_workspace_bytes(int32_t B, int32_t H, int32_t L,
+                                                  int32_t kv_splits) {
+  if (B < 0 || H < 1 || L < 0 || kv_splits < 1) return 0;
+  const size_t rows = static_cast<size_t>(kv_splits) * B * H * L;
+  return align256(rows * 64 * sizeof(float)) + 2 * align256(rows * sizeof(float));
+}
+
+TXL_API txl_status txl_rel_attn_fwd_split(const txl_rel_attn_args *a, int32_t kv_splits,
+                                          void *workspace, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  AttnParams p;
+  bool nothing;
+  txl_status st = attn_params(a, &p, &nothing);
+  if (st != TXL_OK || nothing) return st;
+  if (kv_splits < 1 || kv_splits > 64)
+    return fail(TXL_ERR_INVALID_ARG, "rel_attn_split: kv_splits must be in [1, 64]");
+  if (a->dtype != TXL_BF16 && kv_splits > 1)
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_split: key splits are built for bf16 only");
+  if (kv_splits == 1) return a->dtype == TXL_BF16 ? launch_rel_attn_mfma(p, stream)
+                                                 : launch_rel_attn_valu(p, a->dtype, stream);
+  const size_t need = txl_rel_attn_split_workspace_bytes(a->B, a->H, a->L, kv_splits);
+  if (!workspace || ws_bytes < need)
+    return fail(TXL_ERR_WORKSPACE, "rel_attn_split: workspace %zu < %zu bytes", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_split: workspace not 256-byte aligned");
+  const size_t rows = static_cast<size_t>(kv_splits) * a->B * a->H * a->L;
+  char *base = static_cast<char *>(workspace);
+  p.n_split = kv_splits;
+  p.part_o = reinterpret_cast<float *>(base);
+  p.part_m = reinterpret_cast<float *>(base + align256(rows * 64 * sizeof(float)));
+  p.part_l = reinterpret_cast<float *>(base + align256(rows * 64 * sizeof(float)) +
+                                       align256(rows * sizeof(float)));
+  return launch_rel_attn_mfma(p, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -148,9 +148,12 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
   const int r = lane & 31;   // query within the wave (MFMA column)
   const int hh = lane >> 5;  // which half of the wave
 
-  // heaviest query tiles first; (batch, head) fastest
+  // heaviest query tiles first, a tile's key splits together; (batch, head) fastest
   const int BH = p.B * p.H;
-  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x) / BH;
+  const int S = p.n_split > 1 ? p.n_split : 1;
+  const int unit = static_cast<int>(blockIdx.x) / BH;
+  const int qt = n_qt - 1 - unit / S;
+  const int split = unit - (unit / S) * S;
   const int bh = static_cast<int>(blockIdx.x) % BH;
   const int b = bh / p.H;
   const int h = bh - b * p.H;
@@ -161,10 +164,14 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
 
   int valid = p.valid ? p.valid[b] : M;
   valid = valid < 0 ? 0 : (valid > M ? M : valid);
-  const int j_lo = M - valid;                       // first visible key (logical)
+  const int j_vis = M - valid;                      // first visible key (logical)
   const int i_last = (i0 + BQ < L ? i0 + BQ : L) - 1;
-  const int j_end = M + i_last + 1;                 // keys [j_lo, j_end) are staged
-  const int n_tiles = (j_end - j_lo + BK - 1) / BK;
+  const int j_end = M + i_last + 1;                 // keys [j_vis, j_end) are staged
+  // this workgroup's key tiles: all of them, or its split's contiguous share
+  const int n_all = (j_end - j_vis + BK - 1) / BK;
+  const int kt_b = split * n_all / S, kt_e = (split + 1) * n_all / S;
+  const int j_lo = j_vis + kt_b * BK;               // first key of this workgroup
+  const int n_tiles = kt_e - kt_b;
   const int ML = M + L;
 
   const __bf16 *qp = static_cast<const __bf16 *>(p.q) + b * p.q_sb + h * p.q_sh;
@@ -379,6 +386,24 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
   if (!wave_active) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (i >= L) return;
+  if (S > 1) {  // partial result of this key range, merged by rel_attn_merge_kernel
+    const int64_t row = (static_cast<int64_t>(split) * BH + bh) * L + i;
+    float *po = p.part_o + row * DH;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        f32x4 o4;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) o4[cc] = o_acc[db][4 * a4 + cc];
+        *reinterpret_cast<f32x4 *>(po + db * 32 + 8 * a4 + 4 * hh) = o4;
+      }
+    if (hh == 0) {
+      p.part_m[row] = m_run;
+      p.part_l[row] = l_tot;
+    }
+    return;
+  }
   const float inv = 1.0f / l_tot;
   __bf16 *op = static_cast<__bf16 *>(p.out) + b * p.o_sb + h * p.o_sh + static_cast<int64_t>(i) * p.o_sl;
 #pragma unroll
@@ -392,6 +417,40 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
     }
   if (p.lse && hh == 0)
     p.lse[(static_cast<int64_t>(b) * p.H + h) * L + i] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
+}
+
+// Merge of the key-range splits: per query, m = max_s m_s and
+// O = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s (a split that saw no key
+// has m_s = -inf and adds nothing). One thread per query and 4 dimensions.
+__global__ __launch_bounds__(256) void rel_attn_merge_kernel(AttnParams p) {
+  const int64_t BHL = static_cast<int64_t>(p.B) * p.H * p.L;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= BHL * (DH / 4)) return;
+  const int64_t row = e / (DH / 4);
+  const int c = static_cast<int>(e - row * (DH / 4));
+  float m = -INFINITY;
+  for (int sp = 0; sp < p.n_split; ++sp) m = fmaxf(m, p.part_m[sp * BHL + row]);
+  float l = 0.0f;
+  f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int sp = 0; sp < p.n_split; ++sp) {
+    const float ms = p.part_m[sp * BHL + row];
+    if (!(ms > -INFINITY)) continue;
+    const float w = __builtin_amdgcn_exp2f(ms - m);
+    l += w * p.part_l[sp * BHL + row];
+    const f32x4 os = *reinterpret_cast<const f32x4 *>(p.part_o + (sp * BHL + row) * DH + 4 * c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] += w * os[q];
+  }
+  const int64_t bh = row / p.L;
+  const int i = static_cast<int>(row - bh * p.L);
+  const int b = static_cast<int>(bh / p.H), h = static_cast<int>(bh - static_cast<int64_t>(b) * p.H);
+  const float inv = 1.0f / l;
+  bf16x4 o4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o4[q] = static_cast<__bf16>(o[q] * inv);
+  __bf16 *op = static_cast<__bf16 *>(p.out) + b * p.o_sb + h * p.o_sh + static_cast<int64_t>(i) * p.o_sl;
+  *reinterpret_cast<bf16x4 *>(op + 4 * c) = o4;
+  if (p.lse && c == 0) p.lse[row] = (m + log2f(l)) * 0.6931471805599453f;
 }
 
 }  // namespace
@@ -413,12 +472,18 @@ txl_status launch_rel_attn_mfma(const AttnParams &p, hipStream_t s) {
   if ((ML + BK) * p.kv_sl * 2 >= (int64_t(1) << 31) || (ML + BK + QW) * p.r_sl * 2 >= (int64_t(1) << 31))
     return fail(TXL_ERR_UNSUPPORTED, "rel_attn: key / R rows span more than 2 GiB per head");
   const int n_qt = (p.L + BQ - 1) / BQ;
-  const int64_t blocks = static_cast<int64_t>(n_qt) * p.B * p.H;
+  const int S = p.n_split > 1 ? p.n_split : 1;
+  const int64_t blocks = static_cast<int64_t>(n_qt) * p.B * p.H * S;
   if (blocks > 0x7fffffffLL) return fail(TXL_ERR_UNSUPPORTED, "rel_attn: grid too large");
   (void)hipGetLastError();
   hipLaunchKernelGGL(rel_attn_mfma_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256),
                      kLdsTotal, s, p, n_qt);
-  return check_launch("rel_attn_mfma_kernel");
+  txl_status st = check_launch("rel_attn_mfma_kernel");
+  if (st != TXL_OK || S == 1) return st;
+  const int64_t threads = static_cast<int64_t>(p.B) * p.H * p.L * (DH / 4);
+  hipLaunchKernelGGL(rel_attn_merge_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)),
+                     dim3(256), 0, s, p);
+  return check_launch("rel_attn_merge_kernel");
 }
 
 }  // namespace txl

@@ -66,8 +66,19 @@ int residual_splits(int rows, int N, int K) {
   return s;
 }
 
+// Key splits of a layer's attention. Measured on the stack's shapes: with
+// fewer query-tile workgroups (128 queries each, per batch row and head) than
+// CUs, two splits help (B=8 H=16 L=128 M=640: 27.1 -> 24.3 us); beyond that
+// the fp32 partial results and the merge cost more than the extra workgroups
+// bring (B=16 H=8 L=384 M=384: 35.8 -> 47.7 us with two), so no split.
+int attn_splits(const txl_stack_config &c) {
+  const int64_t grid = static_cast<int64_t>((c.L + 127) / 128) * c.B * c.n_head;
+  const int tiles = (c.M + c.L + 63) / 64;
+  return (grid < 256 && tiles >= 4) ? 2 : 1;
+}
+
 struct WsLayout {
-  size_t hc, hn, q, k, v, o, x, h1, f, total;
+  size_t hc, hn, q, k, v, o, x, h1, f, attn, attn_bytes, total;
 };
 
 WsLayout layout(const txl_stack_config &c) {
@@ -93,6 +104,9 @@ WsLayout layout(const txl_stack_config &c) {
   w.x = take(static_cast<size_t>(parts) * rows * c.d * 4);
   w.h1 = take(rows * c.d * 2);
   w.f = take(rows * static_cast<size_t>(c.d_ff) * 2);
+  const int splits = attn_splits(c);
+  w.attn_bytes = splits > 1 ? txl_rel_attn_split_workspace_bytes(c.B, c.n_head, c.L, splits) : 0;
+  w.attn = take(w.attn_bytes);
   w.total = off;
   return w;
 }
@@ -117,6 +131,8 @@ GemmParams dense(const void *a, int64_t lda, int rows, int N, int K, const void 
 struct StepBufs {
   __bf16 *hc, *hn, *q, *k, *v, *o, *h1, *f;
   float *x;
+  void *attn;
+  size_t attn_bytes;
 };
 
 StepBufs bufs(const WsLayout &ws, void *workspace) {
@@ -131,6 +147,8 @@ StepBufs bufs(const WsLayout &ws, void *workspace) {
   b.x = reinterpret_cast<float *>(base + ws.x);
   b.h1 = reinterpret_cast<__bf16 *>(base + ws.h1);
   b.f = reinterpret_cast<__bf16 *>(base + ws.f);
+  b.attn = base + ws.attn;
+  b.attn_bytes = ws.attn_bytes;
   return b;
 }
 
@@ -208,7 +226,9 @@ txl_status layer_body(const txl_stack *st, int n, const __bf16 *hc, void *dst, c
   a.o_sh = c.d_h;
   a.o_sl = HD;
   a.lse = nullptr;
-  s = txl_rel_attn_fwd(&a, stream);
+  const int splits = attn_splits(c);
+  s = splits > 1 ? txl_rel_attn_fwd_split(&a, splits, b.attn, b.attn_bytes, stream)
+                 : txl_rel_attn_fwd(&a, stream);
   if (s != TXL_OK) return s;
   // X = H + A W^O; H1 = LN1(X)
   s = residual_ln(dense(b.o, HD, rows, c.d, HD, lw.wo, b.x, c.d), hc, lw.ln1_g, lw.ln1_b, b.h1,

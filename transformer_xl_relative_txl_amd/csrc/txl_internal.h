@@ -26,6 +26,12 @@ struct AttnParams {
   int64_t q_sb, q_sh, q_sl, kv_sb, kv_sh, kv_sl, r_sh, r_sl, o_sb, o_sh, o_sl;
   int32_t B, H, L, M;
   float scale;
+  // key-range split (bf16 only): n_split > 1 workgroups per query tile, each
+  // over a contiguous range of key tiles, write unnormalised O and their
+  // running max / sum (base 2) here ([n_split][B*H][L] rows), then a merge
+  // kernel forms out and lse
+  int32_t n_split;
+  float *part_o, *part_m, *part_l;
 };
 // fp32 / bf16 VALU kernel (one thread per query row).
 txl_status launch_rel_attn_valu(const AttnParams &p, txl_dtype dt,
