@@ -27,6 +27,7 @@ namespace txl {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -299,7 +300,8 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
       for (int part = 1; part < NP; ++part)
         v[c] += *reinterpret_cast<const f32x4 *>(xr + part * part_stride + 256 * c + 4 * lane);
       if (res) {
-        const __bf16 *rr = res + static_cast<int64_t>(row) * d + 256 * c + 4 * lane;
+        const bf16x4 rr = *reinterpret_cast<const bf16x4 *>(res + static_cast<int64_t>(row) * d +
+                                                            256 * c + 4 * lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[c][e] += static_cast<float>(rr[e]);
       }
@@ -327,12 +329,15 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
 #pragma unroll
   for (int c = 0; c < kLnMaxChunks; ++c) {
     if (c < nch) {
+      const int col = 256 * c + 4 * lane;
+      const bf16x4 gm = *reinterpret_cast<const bf16x4 *>(gamma + col);
+      const bf16x4 bt = *reinterpret_cast<const bf16x4 *>(beta + col);
+      bf16x4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int col = 256 * c + 4 * lane + e;
-        yr[col] = static_cast<__bf16>((v[c][e] - mean) * inv * static_cast<float>(gamma[col]) +
-                                      static_cast<float>(beta[col]));
-      }
+      for (int e = 0; e < 4; ++e)
+        o[e] = static_cast<__bf16>((v[c][e] - mean) * inv * static_cast<float>(gm[e]) +
+                                   static_cast<float>(bt[e]));
+      *reinterpret_cast<bf16x4 *>(yr + col) = o;
     }
   }
 }

@@ -2,11 +2,13 @@
 //
 // Order of one layer n ([P2] "019 Transformer-XL", section 3 pseudo-code):
 // Q from H^(n-1), K/V from [ring n-1 in logical order; H^(n-1)], relative
-// attention with ring n-1's valid counts, then ring n-1 takes H^(n-1). The
-// ring is updated only after the K/V projection has read it and after the
-// attention has read its valid counts: the slots being overwritten hold the
-// oldest keys of this very layer ([P2] section 2: layer n reads the states
-// layer n-1 produced for the previous segment).
+// attention with ring n-1's valid counts. Ring n-1 takes H^(n-1) only after
+// the K/V projection has read it and the attention has read its valid
+// counts: the slots being overwritten hold the oldest keys of this very layer
+// ([P2] section 2: layer n reads the states layer n-1 produced for the
+// previous segment). When the states are small enough, every H^(n) is kept in
+// the workspace and all N+1 rings are updated by one batched call at the end
+// of the step.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -77,8 +79,19 @@ int attn_splits(const txl_stack_config &c) {
   return (grid < 256 && tiles >= 4) ? 2 : 1;
 }
 
+// Whether the ring step keeps every H^(n) and updates all rings with one
+// batched call at the end (one launch instead of N+1), or updates ring n-1
+// right after layer n with two alternating buffers. Measured: batching pays
+// while the kept states stay small (18-layer d=1024 B*L=1024: 38 MB, step
+// 2.85 -> 2.81 ms) and costs more in cache misses than it saves in launches
+// when they are large (16-layer d=512 B*L=6144: 101 MB, 2.68 -> 2.75 ms).
+bool batch_rings(const txl_stack_config &c) {
+  const size_t bytes = static_cast<size_t>(c.n_layer) * c.B * c.L * c.d * 2;
+  return bytes <= (size_t(64) << 20);
+}
+
 struct WsLayout {
-  size_t hc, hn, q, k, v, o, x, h1, f, attn, attn_bytes, total;
+  size_t hs, q, k, v, o, x, h1, f, attn, attn_bytes, total;
 };
 
 WsLayout layout(const txl_stack_config &c) {
@@ -92,8 +105,9 @@ WsLayout layout(const txl_stack_config &c) {
     off += align256(bytes);
     return at;
   };
-  w.hc = take(rows * c.d * 2);
-  w.hn = take(rows * c.d * 2);
+  // H^(0) .. H^(N-1) kept until the rings take them at the end of the step,
+  // or two alternating slots
+  w.hs = take(static_cast<size_t>(batch_rings(c) ? std::max(c.n_layer, 2) : 2) * rows * c.d * 2);
   w.q = take(rows * hd * 2);
   w.k = take(krows * hd * 2);
   w.v = take(krows * hd * 2);
@@ -129,7 +143,7 @@ GemmParams dense(const void *a, int64_t lda, int rows, int N, int K, const void 
 }
 
 struct StepBufs {
-  __bf16 *hc, *hn, *q, *k, *v, *o, *h1, *f;
+  __bf16 *hs, *q, *k, *v, *o, *h1, *f;
   float *x;
   void *attn;
   size_t attn_bytes;
@@ -138,8 +152,7 @@ struct StepBufs {
 StepBufs bufs(const WsLayout &ws, void *workspace) {
   char *base = static_cast<char *>(workspace);
   StepBufs b;
-  b.hc = reinterpret_cast<__bf16 *>(base + ws.hc);
-  b.hn = reinterpret_cast<__bf16 *>(base + ws.hn);
+  b.hs = reinterpret_cast<__bf16 *>(base + ws.hs);
   b.q = reinterpret_cast<__bf16 *>(base + ws.q);
   b.k = reinterpret_cast<__bf16 *>(base + ws.k);
   b.v = reinterpret_cast<__bf16 *>(base + ws.v);
@@ -327,12 +340,18 @@ TXL_API txl_status txl_segment_step(txl_stack *st, const int32_t *tokens, txl_me
   const int HD = c.n_head * c.d_h;
   const int rows = c.B * c.L;
   const int ML = c.M + c.L;
-  __bf16 *hc = b.hc, *hn = b.hn;
-  s = launch_embed(tokens, st->emb, hc, rows, c.d, c.vocab, stream);
+  // H^(n), the input of layer n, lives in slot n until the end of the step
+  // (batched ring update) or in slot n mod 2 (ring updated after the layer)
+  const bool batched = batch_rings(c);
+  auto slot = [&](int n) {
+    return b.hs + static_cast<size_t>(batched ? n : (n & 1)) * rows * c.d;
+  };
+  s = launch_embed(tokens, st->emb, slot(0), rows, c.d, c.vocab, stream);
   if (s != TXL_OK) return s;
   for (int n = 0; n < c.n_layer; ++n) {
     const txl_layer_weights &lw = st->layers[n];
     txl_mem &ring = mems[n];
+    const __bf16 *hc = slot(n);
     // [K | V] = [ring; H] [W^K | W^V], memory rows gathered in logical order
     GemmParams pkv = dense(nullptr, c.d, c.B * ML, 2 * HD, c.d, lw.wk, b.k, HD);
     pkv.gather = 1;
@@ -347,19 +366,25 @@ TXL_API txl_status txl_segment_step(txl_stack *st, const int32_t *tokens, txl_me
     pkv.c1 = b.v;
     s = launch_gemm(pkv, kEpiStoreBf16, stream);
     if (s != TXL_OK) return s;
-    void *dst = (n + 1 == c.n_layer) ? h_out : static_cast<void *>(hn);
+    void *dst = (n + 1 == c.n_layer) ? h_out : static_cast<void *>(slot(n + 1));
     s = layer_body(st, n, hc, dst, b.k, b.v, static_cast<int64_t>(ML) * HD, ring.valid, b, stream);
     if (s != TXL_OK) return s;
-    // the ring of layer n-1 takes H^(n-1) now that the layer has read it
-    const void *hptr = hc;
-    s = txl_mem_update(&ring, 1, &hptr, c.L, stream);
-    if (s != TXL_OK) return s;
-    __bf16 *t = hc;
-    hc = static_cast<__bf16 *>(dst);
-    hn = t;
+    if (!batched) {  // ring n-1 takes H^(n-1) now that layer n has read it
+      const void *hptr = hc;
+      s = txl_mem_update(&ring, 1, &hptr, c.L, stream);
+      if (s != TXL_OK) return s;
+    }
   }
-  const void *top = h_out;
-  return txl_mem_update(&mems[c.n_layer], 1, &top, c.L, stream);
+  if (!batched) {
+    const void *top = h_out;
+    return txl_mem_update(&mems[c.n_layer], 1, &top, c.L, stream);
+  }
+  // every ring takes its H^(n) at once, now that every layer has read its
+  // memory and valid counts (ring n is read only by layer n+1)
+  std::vector<const void *> hp(c.n_layer + 1);
+  for (int n = 0; n < c.n_layer; ++n) hp[n] = slot(n);
+  hp[c.n_layer] = h_out;
+  return txl_mem_update(mems, c.n_layer + 1, hp.data(), c.L, stream);
 }
 
 TXL_API int32_t txl_kv_cache_min_capacity(const txl_stack_config *c) {
@@ -402,7 +427,7 @@ TXL_API txl_status txl_segment_step_kv(txl_stack *st, const int32_t *tokens,
 
   StepBufs b = bufs(ws, workspace);
   const int rows = c.B * c.L;
-  __bf16 *hc = b.hc, *hn = b.hn;
+  __bf16 *hc = b.hs, *hn = b.hs + static_cast<size_t>(rows) * c.d;
   s = launch_embed(tokens, st->emb, hc, rows, c.d, c.vocab, stream);
   if (s != TXL_OK) return s;
   for (int n = 0; n < c.n_layer; ++n) {
