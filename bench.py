@@ -36,8 +36,8 @@ N_RING_SETS = 16
 # HBM bytes per attention launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # (scaled by the same counters' reading of a plain copy of known size),
 # valid only for the kernel source they were taken on.
-ATTN_TRAFFIC = {"source_sha1": "1cbf89ac433cba41948a60b4a4c3610fe24fd3a1",
-                "bytes": 52.67e6}
+ATTN_TRAFFIC = {"source_sha1": "4b4e76ef1317cf08804e9ec415156e3a328d5e9c",
+                "bytes": 52.62e6}
 
 
 def attn_flops(B, H, L, M_eff, d_h):
