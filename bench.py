@@ -224,7 +224,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle CPU baseline (0 skips it)")
-    ap.add_argument("--stack", choices=["C4", "C5"], default=None,
+    ap.add_argument("--stack", choices=["16layer_d512", "18layer_d1024"], default=None,
                     help="measure the N-layer segment step instead (16-layer d=512 "
                          "workload or 18-layer d=1024 long-memory workload)")
     ap.add_argument("--kv", action="store_true",
@@ -233,9 +233,9 @@ def main() -> int:
                     help="measure the segment loss (logits + cross entropy) instead")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not run "
-              "(the step shards over batch rows with no communication; see DESIGN.md)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not run. The step shards "
+              "over batch rows with no communication: each GPU would run this benchmark on "
+              "its own rows, and the job's rate is the sum.", file=sys.stderr)
         return 2
 
     if args.loss:
@@ -250,7 +250,7 @@ def main() -> int:
     import txl_synth
     import transformer_xl_relative_txl_amd as txl
 
-    cfg = txl_synth.ATTN_CONFIGS["C3"]
+    cfg = txl_synth.ATTN_CONFIGS["B8_H16_L512_M512"]
     B, H, L, M, dh = cfg.B, cfg.H, cfg.L, cfg.M, cfg.d_h
     d = H * dh
     dev = torch.device("cuda:0")
@@ -300,7 +300,7 @@ def main() -> int:
 
     # all layers' rings of the 16-layer stack (d=512, B=16, L=M=384) in one
     # launch: 17 rings x 12.6 MB, two rotating sets (428 MB)
-    sc = txl_synth.STACK_CONFIGS["C4"]
+    sc = txl_synth.STACK_CONFIGS["16layer_d512"]
     n_rings = sc.n_layer + 1
     multi = []
     for _s in range(2):

@@ -62,32 +62,32 @@ def check(cfg, x, what, b_idx=None, h_idx=None, lse=True, layout="bhld"):
         assert d <= tol * max(1.0, float(np.abs(ref["lse"]).max()))
 
 
-def test_c1_fp32_single_head_4x12():
-    cfg = txl_synth.ATTN_CONFIGS["C1"]
-    check(cfg, attn_case(cfg), "C1")
+def test_fp32_single_head_4x12():
+    cfg = txl_synth.ATTN_CONFIGS["4x12_f32"]
+    check(cfg, attn_case(cfg), "4x12_f32")
 
 
 @pytest.mark.parametrize("valid_mode", ["full", "mixed", "empty"])
-def test_c1_fp32_valid_counts(valid_mode):
-    cfg = txl_synth.ATTN_CONFIGS["C1"]
-    check(cfg, attn_case(cfg, B=3, valid_mode=valid_mode), f"C1 valid={valid_mode}")
+def test_fp32_4x12_valid_counts(valid_mode):
+    cfg = txl_synth.ATTN_CONFIGS["4x12_f32"]
+    check(cfg, attn_case(cfg, B=3, valid_mode=valid_mode), f"4x12_f32 valid={valid_mode}")
 
 
-def test_c2_bf16_memory():
-    cfg = txl_synth.ATTN_CONFIGS["C2"]
-    check(cfg, attn_case(cfg), "C2")
+def test_bf16_layer_with_memory():
+    cfg = txl_synth.ATTN_CONFIGS["B4_H8_L128_M128"]
+    check(cfg, attn_case(cfg), "B4_H8_L128_M128")
 
 
-def test_c2_bf16_no_memory():
-    cfg = txl_synth.ATTN_CONFIGS["C2m0"]
-    check(cfg, attn_case(cfg), "C2 M=0")
+def test_bf16_layer_without_memory():
+    cfg = txl_synth.ATTN_CONFIGS["B4_H8_L128_M0"]
+    check(cfg, attn_case(cfg), "B4 H8 L128 M0")
 
 
-def test_c3_bf16_full_size_sampled():
+def test_bf16_large_layer_full_size_sampled():
     """The large layer at full size, launched whole; the oracle checks two
     batch rows x three heads (all 512 queries each)."""
-    cfg = txl_synth.ATTN_CONFIGS["C3"]
-    check(cfg, attn_case(cfg), "C3", b_idx=[0, 7], h_idx=[0, 5, 15])
+    cfg = txl_synth.ATTN_CONFIGS["B8_H16_L512_M512"]
+    check(cfg, attn_case(cfg), "B8_H16_L512_M512", b_idx=[0, 7], h_idx=[0, 5, 15])
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -100,21 +100,21 @@ def test_c3_bf16_full_size_sampled():
     (2, 2, 130, 640, "mixed"),  # long memory (M = 5L)
 ])
 def test_ragged_shapes(dtype, B, H, L, M, mode):
-    cfg = txl_synth.ATTN_CONFIGS["C1" if dtype == "f32" else "C2"]
+    cfg = txl_synth.ATTN_CONFIGS["4x12_f32" if dtype == "f32" else "B4_H8_L128_M128"]
     check(cfg, attn_case(cfg, B=B, H=H, L=L, M=M, seed=B * 1000 + L + M, valid_mode=mode),
           f"ragged {dtype} B{B} H{H} L{L} M{M} {mode}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_strided_blhd_layout(dtype):
-    cfg = txl_synth.ATTN_CONFIGS["C1" if dtype == "f32" else "C2"]
+    cfg = txl_synth.ATTN_CONFIGS["4x12_f32" if dtype == "f32" else "B4_H8_L128_M128"]
     x = attn_case(cfg, B=2, H=4, L=70, M=50, seed=5, valid_mode="mixed")
     check(cfg, x, f"strided {dtype}", layout="blhd")
 
 
 @pytest.mark.parametrize("B,L", [(0, 16), (2, 0)])
 def test_empty_is_noop(B, L):
-    cfg = txl_synth.ATTN_CONFIGS["C2"]
+    cfg = txl_synth.ATTN_CONFIGS["B4_H8_L128_M128"]
     M, H, dh = 8, 2, 64
     q = torch.zeros((B, H, L, dh), dtype=torch.bfloat16, device=DEV)
     k = torch.zeros((B, H, M + L, dh), dtype=torch.bfloat16, device=DEV)
@@ -215,7 +215,7 @@ def test_mask_probe(dtype):
 # invariants
 # ----------------------------------------------------------------------------
 def test_deterministic_bitwise():
-    cfg = txl_synth.ATTN_CONFIGS["C2"]
+    cfg = txl_synth.ATTN_CONFIGS["B4_H8_L128_M128"]
     x = attn_case(cfg, valid_mode="mixed")
     a, _ = run_gpu(x)
     b, _ = run_gpu(x)
@@ -223,7 +223,7 @@ def test_deterministic_bitwise():
 
 
 def test_row_and_head_permutation_bitwise():
-    cfg = txl_synth.ATTN_CONFIGS["C2"]
+    cfg = txl_synth.ATTN_CONFIGS["B4_H8_L128_M128"]
     x = attn_case(cfg, valid_mode="mixed")
     base, _ = run_gpu(x)
     pb = torch.tensor([2, 0, 3, 1])
@@ -243,7 +243,7 @@ def test_row_and_head_permutation_bitwise():
 
 
 def test_invalid_arguments_rejected_before_launch():
-    cfg = txl_synth.ATTN_CONFIGS["C2"]
+    cfg = txl_synth.ATTN_CONFIGS["B4_H8_L128_M128"]
     x = attn_case(cfg, B=1, H=1, L=8, M=8)
     q, k, v = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
     r, u, vb = x["r"].to(DEV), x["u"].to(DEV), x["vb"].to(DEV)

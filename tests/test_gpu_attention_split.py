@@ -46,10 +46,10 @@ def check(x, kv_splits, what, b_idx=None, h_idx=None):
 
 @pytest.mark.parametrize("kv_splits", [2, 3, 4, 8])
 @pytest.mark.parametrize("valid_mode", ["full", "random"])
-def test_c2_layer_split(kv_splits, valid_mode):
-    cfg = txl_synth.ATTN_CONFIGS["C2"]
+def test_layer_split(kv_splits, valid_mode):
+    cfg = txl_synth.ATTN_CONFIGS["B4_H8_L128_M128"]
     x = attn_case(cfg, valid_mode=valid_mode)
-    check(x, kv_splits, f"C2 valid={valid_mode}")
+    check(x, kv_splits, f"B4_H8_L128_M128 valid={valid_mode}")
 
 
 @pytest.mark.parametrize("B,H,L,M,kv_splits", [(2, 3, 100, 77, 3), (1, 2, 64, 0, 8),
@@ -57,7 +57,7 @@ def test_c2_layer_split(kv_splits, valid_mode):
 def test_ragged_and_more_splits_than_tiles(B, H, L, M, kv_splits):
     """Partial tiles, no memory, one query; 8 splits of a single key tile
     leave seven empty splits, which the merge must ignore."""
-    cfg = txl_synth.ATTN_CONFIGS["C2"]
+    cfg = txl_synth.ATTN_CONFIGS["B4_H8_L128_M128"]
     x = attn_case(cfg, B=B, H=H, L=L, M=M, seed=11, valid_mode="random")
     check(x, kv_splits, f"ragged {B}x{H} L={L} M={M}")
 
@@ -73,7 +73,7 @@ def test_long_memory_shape_sampled():
 
 
 def test_split_agrees_with_unsplit():
-    cfg = txl_synth.ATTN_CONFIGS["C2"]
+    cfg = txl_synth.ATTN_CONFIGS["B4_H8_L128_M128"]
     x = attn_case(cfg, valid_mode="random")
     o1, l1 = run(x, 1)
     o4, l4 = run(x, 4)
@@ -84,7 +84,7 @@ def test_split_agrees_with_unsplit():
 
 
 def test_split_rejects_bad_arguments():
-    cfg = txl_synth.ATTN_CONFIGS["C2"]
+    cfg = txl_synth.ATTN_CONFIGS["B4_H8_L128_M128"]
     x = attn_case(cfg, B=1, H=1, L=64, M=64)
     q, k, v = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
     r, u, vb = x["r"].to(DEV), x["u"].to(DEV), x["vb"].to(DEV)

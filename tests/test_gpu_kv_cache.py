@@ -124,14 +124,14 @@ def test_kv_one_layer_stream_against_oracle():
     del keep
 
 
-def test_kv_c5_full_size_equals_ring_bitwise():
+def test_kv_eighteen_layers_full_size_equals_ring_bitwise():
     """18 layers, d=1024, B=8, L=128, M=640, 16 segments with every row
     resetting at segments 0, 4, 8, 12; capacity 2M + L (compaction every six
     segments)."""
-    cfg = txl_synth.STACK_CONFIGS["C5"]
+    cfg = txl_synth.STACK_CONFIGS["18layer_d1024"]
     resets = txl_synth.reset_schedule(cfg)
     n, comp = both_streams(cfg, 2 * cfg.M + cfg.L, resets)
-    say(f"C5: {n} segments bit-identical, {comp} compactions")
+    say(f"18 layers: {n} segments bit-identical, {comp} compactions")
     assert comp >= 2
 
 

@@ -300,27 +300,27 @@ def test_stack_rejects_bad_arguments():
 # ----------------------------------------------------------------------------
 # the full-size workloads, sampled
 # ----------------------------------------------------------------------------
-def test_c4_sixteen_layers_full_size_sampled():
+def test_sixteen_layers_full_size_sampled():
     """16 layers, d=512, B=16, L=M=384, 8 segments streamed (full size on the
     GPU); memories checked for every row and ring at segments 0, 1, 7, layer
     outputs teacher-forced for rows 0 and 15 at layers 1, 2, 8, 16."""
-    cfg = txl_synth.STACK_CONFIGS["C4"]
+    cfg = txl_synth.STACK_CONFIGS["16layer_d512"]
     w = txl_synth.stack_weights(cfg)
     tokens = txl_synth.stack_tokens(cfg)
     resets = txl_synth.reset_schedule(cfg)
     worst = run_stream(cfg, w, tokens, resets, check={0, 1, 7}, n_layer=cfg.n_layer,
                        rows_to_check=[0, cfg.B - 1], layers_to_check=[1, 2, 8, 16])
-    say(f"C4 worst: {worst}")
+    say(f"16 layers worst: {worst}")
 
 
-def test_c5_eighteen_layers_long_memory_with_resets_sampled():
+def test_eighteen_layers_long_memory_with_resets_sampled():
     """18 layers, d=1024, B=8, L=128, M=640, 16 segments with every row
     resetting at segments 0, 4, 8, 12; checks at segments 1, 3, 4 and 15
     (memories of 128, 384, 0 and 384 states)."""
-    cfg = txl_synth.STACK_CONFIGS["C5"]
+    cfg = txl_synth.STACK_CONFIGS["18layer_d1024"]
     w = txl_synth.stack_weights(cfg)
     tokens = txl_synth.stack_tokens(cfg)
     resets = txl_synth.reset_schedule(cfg)
     worst = run_stream(cfg, w, tokens, resets, check={1, 3, 4, 15}, n_layer=cfg.n_layer,
                        rows_to_check=[0, cfg.B - 1], layers_to_check=[1, 9, 18])
-    say(f"C5 worst: {worst}")
+    say(f"18 layers worst: {worst}")

@@ -67,7 +67,7 @@ def read_golden_kv(path):
 
 
 def c1_inputs():
-    cfg = txl_synth.ATTN_CONFIGS["C1"]
+    cfg = txl_synth.ATTN_CONFIGS["4x12_f32"]
     x = txl_synth.attn_inputs(cfg)
     r = ost.rel_pos_table(_f64(x["w_r"]), cfg.M, cfg.L, cfg.H, cfg.d_h)
     return cfg, x, r
@@ -197,7 +197,7 @@ def _sdpa(q, k, v, mask, scale):
 def test_no_memory_is_causal_attention_with_relative_bias():
     """M = 0: causal softmax attention whose additive bias is
     u.k_j + (q_i+v).R_{i-j}, the bias aligned with the page's shift."""
-    cfg = txl_synth.ATTN_CONFIGS["C2m0"]
+    cfg = txl_synth.ATTN_CONFIGS["B4_H8_L128_M0"]
     x = txl_synth.attn_inputs(cfg, B=2, H=3, L=37)
     L, dh = 37, cfg.d_h
     r = ost.rel_pos_table(_f64(x["w_r"])[:, : 3 * dh], 0, L, 3, dh)
@@ -297,7 +297,7 @@ def test_softmax_rows_sum_to_one_and_masked_weights_are_zero():
 
 
 def test_rows_and_heads_are_independent():
-    cfg = txl_synth.ATTN_CONFIGS["C2"]
+    cfg = txl_synth.ATTN_CONFIGS["B4_H8_L128_M128"]
     x = txl_synth.attn_inputs(cfg, B=3, H=2, L=9, M=6)
     q, k, v = _f64(x["q"]), _f64(x["k"]), _f64(x["v"])
     u, vb = _f64(x["u"]), _f64(x["vb"])

@@ -70,21 +70,21 @@ class StackConfig:
 
 ATTN_CONFIGS: Dict[str, AttnConfig] = {
     # 4 queries, 8 memory slots, one head: the 4x12 score of the worked example
-    "C1": AttnConfig("C1", "f32", B=1, H=1, d_h=64, L=4, M=8, seed=0,
+    "4x12_f32": AttnConfig("4x12_f32", "f32", B=1, H=1, d_h=64, L=4, M=8, seed=0,
                      qkv_std=1.0 / 8, bias_std=1.0 / 8, wr_std=1.0 / 8),
-    "C2": AttnConfig("C2", "bf16", B=4, H=8, d_h=64, L=128, M=128, seed=0,
+    "B4_H8_L128_M128": AttnConfig("B4_H8_L128_M128", "bf16", B=4, H=8, d_h=64, L=128, M=128, seed=0,
                      qkv_std=1.0, bias_std=0.02, wr_std=512 ** -0.5),
-    "C2m0": AttnConfig("C2m0", "bf16", B=4, H=8, d_h=64, L=128, M=0, seed=0,
+    "B4_H8_L128_M0": AttnConfig("B4_H8_L128_M0", "bf16", B=4, H=8, d_h=64, L=128, M=0, seed=0,
                        qkv_std=1.0, bias_std=0.02, wr_std=512 ** -0.5),
-    "C3": AttnConfig("C3", "bf16", B=8, H=16, d_h=64, L=512, M=512, seed=1,
+    "B8_H16_L512_M512": AttnConfig("B8_H16_L512_M512", "bf16", B=8, H=16, d_h=64, L=512, M=512, seed=1,
                      qkv_std=1.0, bias_std=0.02, wr_std=1024 ** -0.5),
 }
 
 STACK_CONFIGS: Dict[str, StackConfig] = {
-    "C4": StackConfig("C4", "bf16", n_layer=16, d=512, H=8, d_h=64, d_ff=2048,
+    "16layer_d512": StackConfig("16layer_d512", "bf16", n_layer=16, d=512, H=8, d_h=64, d_ff=2048,
                       vocab=32768, B=16, L=384, M=384, n_seg=8, seed=0,
                       w_std=0.02, reset_every=0),
-    "C5": StackConfig("C5", "bf16", n_layer=18, d=1024, H=16, d_h=64,
+    "18layer_d1024": StackConfig("18layer_d1024", "bf16", n_layer=18, d=1024, H=16, d_h=64,
                       d_ff=4096, vocab=32768, B=8, L=128, M=640, n_seg=16,
                       seed=0, w_std=0.02, reset_every=4),
 }
