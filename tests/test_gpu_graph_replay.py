@@ -1,0 +1,75 @@
+"""Captured-graph replays of the stateless entry points equal their eager
+results bit for bit: the relative attention (whole and with key splits), the
+segment loss and the relative-position table. Each graph is replayed several
+times with eager work and synchronisations between the replays, and every
+replay is checked. (The entry points record kernel launches only.)"""
+import pytest
+import torch
+
+import txl_synth
+import transformer_xl_relative_txl_amd as txl
+from tests.gpu_helpers import attn_case
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def replay_and_check(fn, outs, eager, n=3):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    for k in range(n):
+        for o in outs:
+            o.fill_(float("nan") if o.is_floating_point() else 0)
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device=DEV) * 3.0   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), k
+        del junk
+
+
+@pytest.mark.parametrize("kv_splits", [1, 3])
+def test_attention_graph_replays(kv_splits):
+    cfg = txl_synth.ATTN_CONFIGS["B4_H8_L128_M128"]
+    x = attn_case(cfg, valid_mode="random")
+    t = {k: v.to(DEV) for k, v in x.items()}
+    out = torch.empty_like(t["q"])
+    lse = torch.empty(t["q"].shape[:3], dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(1, txl.lib().txl_rel_attn_split_workspace_bytes(*t["q"].shape[:3], kv_splits)),
+                     dtype=torch.uint8, device=DEV)
+
+    def fn():
+        txl.txl_rel_attn_fwd(t["q"], t["k"], t["v"], t["r"], t["u"], t["vb"], out,
+                             mem_valid=t["valid"], lse=lse, kv_splits=kv_splits, workspace=ws)
+    fn()
+    torch.cuda.synchronize()
+    eager = [out.clone(), lse.clone()]
+    replay_and_check(fn, [out, lse], eager)
+
+
+def test_loss_and_rel_pos_table_graph_replays():
+    g = torch.Generator().manual_seed(3)
+    h = torch.randn((256, 128), generator=g).to(torch.bfloat16).to(DEV)
+    w = (torch.randn((1000, 128), generator=g) * 0.3).to(torch.bfloat16).to(DEV)
+    tg = torch.randint(-1, 1000, (256,), generator=g, dtype=torch.int32).to(DEV)
+    nll = torch.empty(256, dtype=torch.float32, device=DEV)
+    ws = torch.empty(txl.lib().txl_lm_loss_workspace_bytes(256, 1000), dtype=torch.uint8, device=DEV)
+    wr = (torch.randn((4 * 64, 256), generator=g) / 16).to(torch.bfloat16).to(DEV)
+    r = torch.empty((96, 4 * 64), dtype=torch.bfloat16, device=DEV)
+
+    def fn():
+        txl.txl_lm_loss(h, w, tg, nll, workspace=ws)
+        txl.txl_rel_pos_table(wr, 64, 32, 4, 64, r)
+    fn()
+    torch.cuda.synchronize()
+    eager = [nll.clone(), r.clone()]
+    replay_and_check(fn, [nll, r], eager)
