@@ -25,6 +25,9 @@ Pages cited (by title and section):
 
 Parity status of each function (what pins it is listed in the tests):
   attention.allow, attention.rel_ids, attention.rel_attn   pinned
+  attention.rel_attn_bwd                                   pinned (finite
+      differences of rel_attn, torch fp64 autograd of a dense formulation,
+      softmax identities)
   memory.tail, memory.update_mems, memory.update_rows      pinned
   stack.layer_norm, stack.gelu                             pinned (torch fp64)
   stack.sinusoid                                           parity unpinned

@@ -153,3 +153,81 @@ def attn_flops(B: int, H: int, L: int, dh: int, valid) -> float:
         valid = np.full((B,), int(valid[0]))
     pairs = float(np.sum(L * valid + L * (L + 1) // 2))
     return 6.0 * dh * H * pairs
+
+
+def rel_attn_bwd(q, k, v, r, u, vb, dout, valid=None,
+                 scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """Exact gradients of ``rel_attn``'s output with respect to every input.
+
+    ``dout`` [B,H,L,dh] is the gradient arriving at ``out``; the result holds
+    dq [B,H,L,dh], dk and dv [B,H,M+L,dh], dr [H,M+L,dh], du and dvb [H,dh].
+
+    The forward is the one of ``rel_attn`` (four-term score of [P1]
+    "Relative Positional Encoding" regrouped as (q+u).k + (q+v).R_{i-j}
+    ([P3] section 2.2), softmax over the keys allowed by [P1] "Causal Mask
+    With Memory"); this is its derivative written out per query with the
+    chain rule, in float64:
+        dp_j  = dout_i . v_j
+        ds_j  = p_j (dp_j - sum_k p_k dp_k)        (softmax Jacobian)
+        g_j   = ds_j * scale                       (gradient of the raw score)
+        dq_i += sum_j g_j (k_j + R_{i-j})
+        dk_j += g_j (q_i + u),   dv_j += p_j dout_i
+        dR_{i-j} += g_j (q_i + v)                  (row looked up by distance)
+        du   += sum_j g_j k_j,   dvb += sum_j g_j R_{i-j}
+    Memory keys get dk / dv like any other key: the stop-gradient of [P1]
+    "Why Stop Gradient" and [P2] section "stop-gradient到底切断哪里" cuts the
+    path back into the earlier segment that produced the memory, not the
+    gradient of this segment's keys and values (which still reaches W_K and
+    W_V). Hidden keys get exactly zero.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    vb = np.asarray(vb, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, H, L, dh = q.shape
+    M = k.shape[2] - L
+    assert M >= 0 and k.shape == (B, H, M + L, dh) and v.shape == k.shape
+    assert r.shape == (H, M + L, dh) and dout.shape == q.shape
+    if valid is None:
+        valid = np.full((B,), M, dtype=np.int64)
+    valid = np.asarray(valid, dtype=np.int64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dh)
+
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dr = np.zeros_like(r)
+    du = np.zeros_like(u)
+    dvb = np.zeros_like(vb)
+    key_pos = np.arange(-M, L)
+    for b in range(B):
+        for h in range(H):
+            for i in range(L):
+                jp = np.nonzero(allow(i, key_pos, int(valid[b])))[0]
+                rows = (M + L - 1) - (i - (jp - M))      # R row of each key's distance
+                r_d = r[h, rows]
+                kj = k[b, h, jp]
+                s = (kj @ (q[b, h, i] + u[h]) + r_d @ (q[b, h, i] + vb[h])) * scale
+                e = np.exp(s - s.max())
+                p = e / e.sum()
+                dp = v[b, h, jp] @ dout[b, h, i]
+                ds = p * (dp - p @ dp)
+                g = ds * scale
+                dq[b, h, i] += g @ kj + g @ r_d
+                dk[b, h, jp] += np.outer(g, q[b, h, i] + u[h])
+                dv[b, h, jp] += np.outer(p, dout[b, h, i])
+                dr[h, rows] += np.outer(g, q[b, h, i] + vb[h])   # rows distinct per query
+                du[h] += g @ kj
+                dvb[h] += g @ r_d
+    return {"dq": dq, "dk": dk, "dv": dv, "dr": dr, "du": du, "dvb": dvb}
+
+
+def attn_bwd_flops(B: int, H: int, L: int, dh: int, valid) -> float:
+    """Algorithmic flops of the backward: the two score contractions
+    recomputed (q.k, q.R) and the six gradient contractions (dout.v, p.dout,
+    g.k, g.R, g.(q+u), g.(q+v)), 2*dh flops each per visible pair."""
+    return attn_flops(B, H, L, dh, valid) * 8.0 / 3.0
