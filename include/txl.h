@@ -133,6 +133,53 @@ TXL_API txl_status txl_rel_attn_fwd_split(const txl_rel_attn_args *a, int32_t kv
                                           hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Gradients of txl_rel_attn_fwd (training).
+ * The exact derivative of the attention above, by the chain rule through
+ * the softmax: with p_ij the probabilities, dp_ij = dout_i . v_j,
+ * D_i = dout_i . out_i and g_ij = scale * p_ij (dp_ij - D_i),
+ *   dv_j = sum_i p_ij dout_i        dk_j = sum_i g_ij (q_i + u_h)
+ *   dq_i = sum_j g_ij (k_j + R_{i-j})
+ *   dR_t = sum_{b, i, j: row of R_{i-j} = t} g_ij (q_i + v_h)
+ *   du_h = sum_{b,i,j} g_ij k_j     dvb_h = sum_{b,i,j} g_ij R_{i-j}
+ * Memory keys receive dk / dv like the current ones: the stop-gradient of
+ * [P1] "Why Stop Gradient" and [P2] "stop-gradient到底切断哪里" cuts the path
+ * into the earlier segment that produced the memory; this segment's key and
+ * value projections of the memory still receive gradient (the caller feeds
+ * those rows to its W_K / W_V gradients and sends nothing further back).
+ * Hidden keys (beyond a row's valid memory) get exactly zero.
+ *
+ * a      : the arguments of the forward call that produced out and lse
+ *          (bf16 only, else UNSUPPORTED); a->out and a->lse are read, both
+ *          required.
+ * grads  : dout [B, H, L, d_h] bf16 (strided, 16-byte rows), and the fp32
+ *          outputs, all contiguous: dq [B, H, L, d_h], dk and dv
+ *          [B, H, M+L, d_h] (logical key order), dr [H, M+L, d_h] (row t <->
+ *          distance M+L-1-t), du and dvb [H, d_h]. Every element of every
+ *          output is written (B == 0 or L == 0: nothing is written).
+ * workspace: txl_rel_attn_bwd_workspace_bytes(B, H, L, M) device bytes,
+ *          256-byte aligned; it holds p and g for every query row (bf16,
+ *          about 4 B per (query, key) pair). Calls sharing a workspace must
+ *          not overlap.
+ * Errors: those of txl_rel_attn_fwd, INVALID_ARG (null lse / gradient
+ * pointers, misaligned outputs), WORKSPACE, UNSUPPORTED (fp32, B*H > 65535).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  const void *dout;              /* [B, H, L, d_h] bf16: gradient at out    */
+  int64_t do_sb, do_sh, do_sl;
+  float *dq;                     /* [B, H, L, d_h]                          */
+  float *dk, *dv;                /* [B, H, M+L, d_h]                        */
+  float *dr;                     /* [H, M+L, d_h]                           */
+  float *du, *dvb;               /* [H, d_h]                                */
+} txl_rel_attn_grads;
+
+TXL_API size_t txl_rel_attn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t L,
+                                                int32_t M);
+TXL_API txl_status txl_rel_attn_bwd(const txl_rel_attn_args *a,
+                                    const txl_rel_attn_grads *grads,
+                                    void *workspace, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Per-layer FIFO memory as a ring buffer.
  * [P1] "Segment-Level Recurrence" and "Batched Tensor Contract": after the
  * step every layer's memory becomes Tail_M([mem; H]) (the last M states;

@@ -131,3 +131,39 @@ def test_stream_sampler_and_loss_reject_bad_arguments(lib):
     assert lib.txl_lm_loss(fake, fake, fake, 64, 48, 100, fake, fake, 1 << 30, None) == 2
     assert lib.txl_lm_loss(fake, fake, fake, 64, 64, 100, fake, fake, 16, None) == 3  # workspace
     assert lib.txl_lm_loss_workspace_bytes(64, 100) >= 2 * 64 * 4 + 64 * 4
+
+
+def test_attention_backward_checks_without_gpu(lib):
+    """The gradient entry point validates before launching: fake but aligned
+    device addresses are never dereferenced on these error paths."""
+    from transformer_xl_relative_txl_amd import _binding as bd
+    a = bd.RelAttnArgs()
+    a.dtype, a.B, a.H, a.L, a.M, a.d_h = 1, 2, 3, 64, 32, 64
+    fake = 1 << 20
+    a.q = a.k = a.v = a.r = a.u = a.vb = a.out = fake
+    a.q_sb, a.q_sh, a.q_sl = 3 * 64 * 64, 64 * 64, 64
+    a.kv_sb, a.kv_sh, a.kv_sl = 3 * 96 * 64, 96 * 64, 64
+    a.r_sh, a.r_sl = 96 * 64, 64
+    a.o_sb, a.o_sh, a.o_sl = a.q_sb, a.q_sh, a.q_sl
+    g = bd.RelAttnGrads()
+    assert lib.txl_rel_attn_bwd(ctypes.byref(a), None, None, 0, None) == 1       # null grads
+    a.lse = None
+    assert lib.txl_rel_attn_bwd(ctypes.byref(a), ctypes.byref(g), None, 0, None) == 1  # no lse
+    a.lse = fake
+    assert lib.txl_rel_attn_bwd(ctypes.byref(a), ctypes.byref(g), None, 0, None) == 1  # null outputs
+    g.dout = g.dq = g.dk = g.dv = g.dr = g.du = g.dvb = fake
+    g.do_sb, g.do_sh, g.do_sl = a.q_sb, a.q_sh, a.q_sl
+    assert lib.txl_rel_attn_bwd(ctypes.byref(a), ctypes.byref(g), None, 0, None) == 3  # workspace
+    need = lib.txl_rel_attn_bwd_workspace_bytes(2, 3, 64, 32)
+    assert lib.txl_rel_attn_bwd(ctypes.byref(a), ctypes.byref(g), fake, need - 1, None) == 3
+    assert lib.txl_rel_attn_bwd(ctypes.byref(a), ctypes.byref(g), fake + 16, need, None) == 2
+    g.do_sl = 65                                                                 # odd stride
+    assert lib.txl_rel_attn_bwd(ctypes.byref(a), ctypes.byref(g), fake, need, None) == 2
+    g.do_sl = 64
+    a.dtype = 0                                                                  # fp32 inputs
+    assert lib.txl_rel_attn_bwd(ctypes.byref(a), ctypes.byref(g), fake, need, None) == 2
+    assert b"bf16" in lib.txl_last_error()
+    # p and g rows of (M + L) rounded up to 8 elements dominate the workspace
+    ldp = (32 + 64 + 7) // 8 * 8
+    assert need >= 2 * 2 * 3 * 64 * ldp * 2
+    assert lib.txl_rel_attn_bwd_workspace_bytes(-1, 3, 64, 32) == 0

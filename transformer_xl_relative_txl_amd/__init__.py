@@ -18,6 +18,8 @@ from ._binding import (  # noqa: F401
     txl_mem_read_logical,
     txl_mem_reset_rows,
     txl_mem_update,
+    txl_rel_attn_bwd,
+    txl_rel_attn_bwd_workspace_bytes,
     txl_rel_attn_fwd,
     txl_rel_pos_table,
     txl_version,

@@ -51,6 +51,15 @@ class RelAttnArgs(ctypes.Structure):
     ]
 
 
+class RelAttnGrads(ctypes.Structure):
+    _fields_ = [
+        ("dout", ctypes.c_void_p),
+        ("do_sb", ctypes.c_int64), ("do_sh", ctypes.c_int64), ("do_sl", ctypes.c_int64),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("dr", ctypes.c_void_p), ("du", ctypes.c_void_p), ("dvb", ctypes.c_void_p),
+    ]
+
+
 class TxlMemStruct(ctypes.Structure):
     _fields_ = [
         ("data", ctypes.c_void_p),
@@ -111,6 +120,11 @@ def _load() -> ctypes.CDLL:
     lib.txl_rel_attn_split_workspace_bytes.restype = sz
     lib.txl_rel_attn_fwd_split.argtypes = [ctypes.POINTER(RelAttnArgs), i32, vp, sz, vp]
     lib.txl_rel_attn_fwd_split.restype = st
+    lib.txl_rel_attn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.txl_rel_attn_bwd_workspace_bytes.restype = sz
+    lib.txl_rel_attn_bwd.argtypes = [ctypes.POINTER(RelAttnArgs), ctypes.POINTER(RelAttnGrads),
+                                     vp, sz, vp]
+    lib.txl_rel_attn_bwd.restype = st
     lib.txl_mem_update.argtypes = [ctypes.POINTER(TxlMemStruct), i32,
                                    ctypes.POINTER(vp), i32, vp]
     lib.txl_mem_update.restype = st
@@ -212,6 +226,21 @@ def txl_rel_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     dimension. kv_splits > 1 calls txl_rel_attn_fwd_split (workspace
     allocated here when not given)."""
     B, H, L, d_h = q.shape
+    a = _attn_args(q, k, v, r, u, vb, out, mem_valid, lse, scale)
+    if kv_splits == 1:
+        _check("txl_rel_attn_fwd", lib().txl_rel_attn_fwd(ctypes.byref(a), _stream(stream)))
+        return out
+    need = lib().txl_rel_attn_split_workspace_bytes(B, H, L, kv_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check("txl_rel_attn_fwd_split",
+           lib().txl_rel_attn_fwd_split(ctypes.byref(a), kv_splits, _ptr(workspace),
+                                        workspace.numel(), _stream(stream)))
+    return out
+
+
+def _attn_args(q, k, v, r, u, vb, out, mem_valid, lse, scale) -> RelAttnArgs:
+    B, H, L, d_h = q.shape
     M = k.shape[2] - L
     if k.stride() != v.stride():
         raise ValueError("k and v must share strides")
@@ -230,16 +259,47 @@ def txl_rel_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     a.out = _ptr(out)
     a.o_sb, a.o_sh, a.o_sl = out.stride(0), out.stride(1), out.stride(2)
     a.lse = _ptr(lse)
-    if kv_splits == 1:
-        _check("txl_rel_attn_fwd", lib().txl_rel_attn_fwd(ctypes.byref(a), _stream(stream)))
-        return out
-    need = lib().txl_rel_attn_split_workspace_bytes(B, H, L, kv_splits)
+    return a
+
+
+def txl_rel_attn_bwd_workspace_bytes(B: int, H: int, L: int, M: int) -> int:
+    return int(lib().txl_rel_attn_bwd_workspace_bytes(B, H, L, M))
+
+
+def txl_rel_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     r: torch.Tensor, u: torch.Tensor, vb: torch.Tensor,
+                     out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                     grads: dict, mem_valid: Optional[torch.Tensor] = None,
+                     scale: float = 0.0, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> dict:
+    """Gradients of txl_rel_attn_fwd (bf16). q..lse are the forward call's
+    tensors (out and lse as it wrote them); dout [B,H,L,d_h] bf16; grads
+    holds contiguous float32 outputs dq [B,H,L,d_h], dk, dv [B,H,M+L,d_h],
+    dr [H,M+L,d_h], du, dvb [H,d_h] (allocated here when missing); the
+    workspace is allocated here when not given."""
+    B, H, L, d_h = q.shape
+    M = k.shape[2] - L
+    a = _attn_args(q, k, v, r, u, vb, out, mem_valid, lse, scale)
+    shapes = {"dq": (B, H, L, d_h), "dk": (B, H, M + L, d_h), "dv": (B, H, M + L, d_h),
+              "dr": (H, M + L, d_h), "du": (H, d_h), "dvb": (H, d_h)}
+    for name, shp in shapes.items():
+        if name not in grads:
+            grads[name] = torch.empty(shp, dtype=torch.float32, device=q.device)
+        t = grads[name]
+        if t.shape != shp or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shp}")
+    g = RelAttnGrads()
+    g.dout = _ptr(dout)
+    g.do_sb, g.do_sh, g.do_sl = dout.stride(0), dout.stride(1), dout.stride(2)
+    for name in shapes:
+        setattr(g, name, _ptr(grads[name]))
     if workspace is None:
+        need = txl_rel_attn_bwd_workspace_bytes(B, H, L, M)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    _check("txl_rel_attn_fwd_split",
-           lib().txl_rel_attn_fwd_split(ctypes.byref(a), kv_splits, _ptr(workspace),
-                                        workspace.numel(), _stream(stream)))
-    return out
+    _check("txl_rel_attn_bwd",
+           lib().txl_rel_attn_bwd(ctypes.byref(a), ctypes.byref(g), _ptr(workspace),
+                                  workspace.numel(), _stream(stream)))
+    return grads
 
 
 class TxlMem:
@@ -514,7 +574,8 @@ def txl_lm_loss(h: torch.Tensor, w_out: torch.Tensor, targets: torch.Tensor, nll
 def exported_symbols() -> List[str]:
     """Names of the C entry points this binding wraps."""
     return ["txl_rel_pos_table", "txl_rel_attn_fwd", "txl_rel_attn_split_workspace_bytes",
-            "txl_rel_attn_fwd_split", "txl_mem_update",
+            "txl_rel_attn_fwd_split", "txl_rel_attn_bwd_workspace_bytes", "txl_rel_attn_bwd",
+            "txl_mem_update",
             "txl_mem_reset_rows", "txl_mem_read_logical", "txl_stack_persistent_bytes",
             "txl_stack_create", "txl_segment_step_workspace_bytes", "txl_segment_step",
             "txl_stack_destroy", "txl_kv_cache_min_capacity", "txl_segment_step_kv",

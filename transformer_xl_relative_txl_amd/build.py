@@ -25,6 +25,7 @@ SOURCES = [
     "mem.hip",
     "rel_attn_valu.hip",
     "rel_attn_mfma.hip",
+    "rel_attn_bwd.hip",
     "gemm.hip",
     "stack.cpp",
     "sampler.cpp",

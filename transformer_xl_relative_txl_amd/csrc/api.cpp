@@ -176,6 +176,83 @@ TXL_API txl_status txl_rel_attn_fwd_split(const txl_rel_attn_args *a, int32_t kv
 }
 
 // ---------------------------------------------------------------------------
+// Workspace of txl_rel_attn_bwd: byte offsets of its pieces, each 256-byte aligned.
+struct BwdLayout {
+  size_t qu, qv, dd, pm, gm, pu, pv, total;
+  int64_t ldp;
+};
+static BwdLayout bwd_layout(int32_t B, int32_t H, int32_t L, int32_t M) {
+  BwdLayout w{};
+  const size_t bhl = static_cast<size_t>(B) * H * L;
+  w.ldp = static_cast<int64_t>(rel_attn_bwd_ldp(M, L));
+  const size_t n_mt = (static_cast<size_t>(L) + 63) / 64;
+  size_t off = 0;
+  w.qu = off; off += align256(bhl * 64 * 2);
+  w.qv = off; off += align256(bhl * 64 * 2);
+  w.dd = off; off += align256(bhl * 4);
+  w.pm = off; off += align256(bhl * static_cast<size_t>(w.ldp) * 2);
+  w.gm = off; off += align256(bhl * static_cast<size_t>(w.ldp) * 2);
+  w.pu = off; off += align256(static_cast<size_t>(B) * H * n_mt * 64 * 4);
+  w.pv = off; off += align256(static_cast<size_t>(B) * H * n_mt * 64 * 4);
+  w.total = off;
+  return w;
+}
+
+TXL_API size_t txl_rel_attn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t M) {
+  if (B < 0 || H < 1 || L < 0 || M < 0) return 0;
+  return bwd_layout(B, H, L, M).total;
+}
+
+TXL_API txl_status txl_rel_attn_bwd(const txl_rel_attn_args *a, const txl_rel_attn_grads *gr,
+                                    void *workspace, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  AttnParams p;
+  bool nothing;
+  txl_status st = attn_params(a, &p, &nothing);
+  if (st != TXL_OK) return st;
+  if (!gr) return fail(TXL_ERR_INVALID_ARG, "rel_attn_bwd: null gradient arguments");
+  if (a->dtype != TXL_BF16)
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: gradients are built for bf16 inputs only");
+  if (nothing) return TXL_OK;
+  if (!a->lse) return fail(TXL_ERR_INVALID_ARG, "rel_attn_bwd: the forward's lse is required");
+  if (!gr->dout || !gr->dq || !gr->dk || !gr->dv || !gr->dr || !gr->du || !gr->dvb)
+    return fail(TXL_ERR_INVALID_ARG, "rel_attn_bwd: null gradient pointer");
+  if (!aligned16(gr->dout))
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: dout not 16-byte aligned");
+  const int64_t dstr[] = {gr->do_sb, gr->do_sh, gr->do_sl};
+  for (int64_t s : dstr)
+    if (!stride_ok(s, 2))
+      return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: dout stride %lld is negative or not a multiple of 16 bytes",
+                  static_cast<long long>(s));
+  const float *outs[] = {gr->dq, gr->dk, gr->dv, gr->dr, gr->du, gr->dvb};
+  for (const float *o : outs)
+    if (reinterpret_cast<uintptr_t>(o) & 3u)
+      return fail(TXL_ERR_INVALID_ARG, "rel_attn_bwd: gradient output not 4-byte aligned");
+  if (static_cast<int64_t>(a->B) * a->H > 65535)
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: B * H above 65535");
+  const BwdLayout w = bwd_layout(a->B, a->H, a->L, a->M);
+  if (!workspace || ws_bytes < w.total)
+    return fail(TXL_ERR_WORKSPACE, "rel_attn_bwd: workspace %zu < %zu bytes", ws_bytes, w.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: workspace not 256-byte aligned");
+  char *base = static_cast<char *>(workspace);
+  BwdParams g = {};
+  g.dout = static_cast<const __bf16 *>(gr->dout);
+  g.do_sb = gr->do_sb; g.do_sh = gr->do_sh; g.do_sl = gr->do_sl;
+  g.lse = a->lse;
+  g.dq = gr->dq; g.dk = gr->dk; g.dv = gr->dv; g.dr = gr->dr; g.du = gr->du; g.dvb = gr->dvb;
+  g.qu = reinterpret_cast<__bf16 *>(base + w.qu);
+  g.qv = reinterpret_cast<__bf16 *>(base + w.qv);
+  g.dd = reinterpret_cast<float *>(base + w.dd);
+  g.pm = reinterpret_cast<__bf16 *>(base + w.pm);
+  g.gm = reinterpret_cast<__bf16 *>(base + w.gm);
+  g.ldp = w.ldp;
+  g.part_u = reinterpret_cast<float *>(base + w.pu);
+  g.part_v = reinterpret_cast<float *>(base + w.pv);
+  return launch_rel_attn_bwd(p, g, stream);
+}
+
+// ---------------------------------------------------------------------------
 static txl_status check_rings(const txl_mem *mems, int32_t n_mems, const char *who) {
   if (n_mems < 0) return fail(TXL_ERR_INVALID_ARG, "%s: n_mems < 0", who);
   if (n_mems > 0 && !mems) return fail(TXL_ERR_INVALID_ARG, "%s: null mems", who);

@@ -39,6 +39,24 @@ txl_status launch_rel_attn_valu(const AttnParams &p, txl_dtype dt,
 // bf16 MFMA kernel.
 txl_status launch_rel_attn_mfma(const AttnParams &p, hipStream_t s);
 
+// gradients (bf16 inputs): p holds the forward's arguments (out = the
+// forward's output); g the incoming gradient, the forward's lse, the fp32
+// gradient outputs (contiguous) and the workspace pieces
+struct BwdParams {
+  const __bf16 *dout;
+  int64_t do_sb, do_sh, do_sl;
+  const float *lse;
+  float *dq, *dk, *dv, *dr, *du, *dvb;
+  __bf16 *qu, *qv;        // [B*H*L, 64]: q + u, q + v
+  float *dd;              // [B*H*L]: dout . out
+  __bf16 *pm, *gm;        // [B*H*L, ldp]: probabilities and score gradients
+  int64_t ldp;
+  float *part_u, *part_v; // [B*H][ceil(L/64)][64] column sums of dq's two parts
+};
+// row length of pm / gm for M memory slots and L queries
+size_t rel_attn_bwd_ldp(int M, int L);
+txl_status launch_rel_attn_bwd(const AttnParams &p, const BwdParams &g, hipStream_t s);
+
 // ---- memory ring ---------------------------------------------------------
 constexpr int kMaxRingsPerLaunch = 32;
 struct RingBatch {
