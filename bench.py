@@ -217,6 +217,71 @@ def loss_bench(steps: int, warmup: int) -> dict:
             "gflop_per_step": round(fl / 1e9, 2)}
 
 
+def bwd_bench(steps: int, warmup: int) -> dict:
+    """Gradients of the relative attention at the attention workload's shape
+    (B=8, H=16, d_h=64, L=512, M=512 fully valid): one txl_rel_attn_bwd call
+    per step (score recompute, p/g, five contractions, bias sums), replayed
+    as a captured graph; forward outputs and the incoming gradient are
+    resident before timing."""
+    import torch
+
+    import txl_synth
+    import transformer_xl_relative_txl_amd as txl
+
+    cfg = txl_synth.ATTN_CONFIGS["B8_H16_L512_M512"]
+    B, H, L, M, dh = cfg.B, cfg.H, cfg.L, cfg.M, cfg.d_h
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = txl_synth.attn_inputs(cfg)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    u, vb = x["u"].to(dev), x["vb"].to(dev)
+    valid = torch.full((B,), M, dtype=torch.int32, device=dev)
+    w_r = x["w_r"].t().contiguous().to(dev)
+    r_flat = torch.empty((M + L, H * dh), dtype=torch.bfloat16, device=dev)
+    txl.txl_rel_pos_table(w_r, M, L, H, dh, r_flat)
+    r = r_flat.view(M + L, H, dh).permute(1, 0, 2)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+    txl.txl_rel_attn_fwd(q, k, v, r, u, vb, out, mem_valid=valid, lse=lse)
+    g = torch.Generator("cpu").manual_seed(cfg.seed + 200)
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16).to(dev)
+    grads: dict = {}
+    ws = torch.empty(txl.txl_rel_attn_bwd_workspace_bytes(B, H, L, M), dtype=torch.uint8, device=dev)
+
+    def bwd():
+        txl.txl_rel_attn_bwd(q, k, v, r, u, vb, out, lse, dout, grads, mem_valid=valid, workspace=ws)
+
+    for _ in range(max(1, warmup)):
+        bwd()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for _ in range(steps):
+            bwd()
+    gr.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fl = attn_flops(B, H, L, M, dh) * 8.0 / 3.0
+    tflops = fl / (ms * 1e-3) / 1e12
+    return {"metric": "relative attention backward TFLOP/s (dq, dk, dv, dR, du, dv-bias), 1 GPU",
+            "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+            "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"relative attention gradients, B={B} H={H} d_h={dh} L={L} M={M}",
+                       "flops_counted": "16*d_h per visible pair: 2 score contractions "
+                                        "recomputed + 6 gradient contractions",
+                       "workspace_MB": round(ws.numel() / 1e6, 1)},
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None, "scope": "whole backward call"},
+            "gflop_per_step": round(fl / 1e9, 2)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,6 +296,8 @@ def main() -> int:
                     help="with --stack: keep memory as projected keys / values")
     ap.add_argument("--loss", action="store_true",
                     help="measure the segment loss (logits + cross entropy) instead")
+    ap.add_argument("--bwd", action="store_true",
+                    help="measure the attention gradients (txl_rel_attn_bwd) instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not run. The step shards "
@@ -240,6 +307,9 @@ def main() -> int:
 
     if args.loss:
         print(json.dumps(loss_bench(args.steps, args.warmup)), flush=True)
+        return 0
+    if args.bwd:
+        print(json.dumps(bwd_bench(args.steps, args.warmup)), flush=True)
         return 0
     if args.stack:
         print(json.dumps(stack_bench(args.stack, args.steps, args.warmup, args.kv)), flush=True)

@@ -178,7 +178,7 @@ TXL_API txl_status txl_rel_attn_fwd_split(const txl_rel_attn_args *a, int32_t kv
 // ---------------------------------------------------------------------------
 // Workspace of txl_rel_attn_bwd: byte offsets of its pieces, each 256-byte aligned.
 struct BwdLayout {
-  size_t qu, qv, dd, pm, gm, pu, pv, total;
+  size_t qu, qv, dd, pm, gm, pu, pv, pr, total;
   int64_t ldp;
 };
 static BwdLayout bwd_layout(int32_t B, int32_t H, int32_t L, int32_t M) {
@@ -194,6 +194,7 @@ static BwdLayout bwd_layout(int32_t B, int32_t H, int32_t L, int32_t M) {
   w.gm = off; off += align256(bhl * static_cast<size_t>(w.ldp) * 2);
   w.pu = off; off += align256(static_cast<size_t>(B) * H * n_mt * 64 * 4);
   w.pv = off; off += align256(static_cast<size_t>(B) * H * n_mt * 64 * 4);
+  w.pr = off; off += align256(static_cast<size_t>(B) * H * (static_cast<size_t>(M) + L) * 64 * 4);
   w.total = off;
   return w;
 }
@@ -249,6 +250,7 @@ TXL_API txl_status txl_rel_attn_bwd(const txl_rel_attn_args *a, const txl_rel_at
   g.ldp = w.ldp;
   g.part_u = reinterpret_cast<float *>(base + w.pu);
   g.part_v = reinterpret_cast<float *>(base + w.pv);
+  g.part_r = reinterpret_cast<float *>(base + w.pr);
   return launch_rel_attn_bwd(p, g, stream);
 }
 

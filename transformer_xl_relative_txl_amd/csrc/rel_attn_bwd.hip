@@ -29,8 +29,8 @@
 //    for query i is g[i][t + i - (L-1)], a matrix whose row stride is one
 //    more than g's, so dq's position part and dR are ordinary products over
 //    that skewed view.
-//  * bwd_bias_reduce: du and dv_bias from per-tile column sums of dq's two
-//    parts.
+//  * bwd_reduce: dR summed over batch rows (its product runs per row, for
+//    parallelism), du and dv_bias from per-tile column sums of dq's two parts.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -326,15 +326,30 @@ __global__ __launch_bounds__(256, 2) void bwd_pg_kernel(AttnParams p, BwdParams 
         *reinterpret_cast<bf16x4 *>(stg + (QW + r) * PS + key) = g4;
       }
     wave_lds_sync();
-    {
+    if ((j_lo & 3) == 0) {
+      // tiles start 4-aligned: 4 keys per lane, 16 lanes per row, 4 rows per store
+      const int kk = (lane & 15) * 4, jj = j0 + kk;
+      if (jj < ML) {
+#pragma unroll
+        for (int it = 0; it < QW / 4; ++it) {
+          const int qq = (lane >> 4) + 4 * it, row = iw + qq;
+          if (row < L) {
+            *reinterpret_cast<bf16x4 *>(pm + static_cast<int64_t>(row) * g.ldp + jj) =
+                *reinterpret_cast<const bf16x4 *>(stg + qq * PS + kk);
+            *reinterpret_cast<bf16x4 *>(gm + static_cast<int64_t>(row) * g.ldp + jj) =
+                *reinterpret_cast<const bf16x4 *>(stg + (QW + qq) * PS + kk);
+          }
+        }
+      }
+    } else {
       const int jj = j0 + lane;
       if (jj < ML) {
 #pragma unroll 4
-        for (int q = 0; q < QW; ++q) {
-          const int row = iw + q;
+        for (int qq = 0; qq < QW; ++qq) {
+          const int row = iw + qq;
           if (row < L) {
-            pm[static_cast<int64_t>(row) * g.ldp + jj] = stg[q * PS + lane];
-            gm[static_cast<int64_t>(row) * g.ldp + jj] = stg[(QW + q) * PS + lane];
+            pm[static_cast<int64_t>(row) * g.ldp + jj] = stg[qq * PS + lane];
+            gm[static_cast<int64_t>(row) * g.ldp + jj] = stg[(QW + qq) * PS + lane];
           }
         }
       }
@@ -357,7 +372,7 @@ __global__ __launch_bounds__(256, 2) void bwd_pg_kernel(AttnParams p, BwdParams 
 //   3  A(m = row t, k = query i)   at a + k*lda + c, c = m + k - (L-1), batch row = outer k
 // (kinds 2 and 3 are the diagonal view: key c of query i has distance row t).
 constexpr int GT = 64;    // output rows per workgroup
-constexpr int GK = 32;    // k per slab
+constexpr int GK = 64;    // k per slab
 constexpr int GS = GK + 8;
 
 struct BgParams {
@@ -375,6 +390,26 @@ struct BgParams {
   int M, L;
 };
 
+// 16 consecutive bf16 of a buffer starting at any element offset off0 (zero
+// outside the buffer): three aligned 16-byte loads and a byte-align shift.
+__device__ inline void load16_unaligned(rsrc_t rs, int off0, bf16x8 &x0, bf16x8 &x1) {
+  const int o = off0 & 7, base8 = off0 - o;
+  const u32x4 w0 = bload(rs, 2 * base8), w1 = bload(rs, 2 * base8 + 16), w2 = bload(rs, 2 * base8 + 32);
+  const uint32_t win[12] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3],
+                            w2[0], w2[1], w2[2], w2[3]};
+  const int wsh = o >> 1, sub = (o & 1) * 2;
+  u32x4 pk0, pk1;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t lo = wsh == 0 ? win[j] : wsh == 1 ? win[j + 1] : wsh == 2 ? win[j + 2] : win[j + 3];
+    const uint32_t hi = wsh == 0 ? win[j + 1] : wsh == 1 ? win[j + 2] : wsh == 2 ? win[j + 3] : win[j + 4];
+    const uint32_t w = __builtin_amdgcn_alignbyte(hi, lo, sub);
+    if (j < 4) pk0[j] = w; else pk1[j - 4] = w;
+  }
+  x0 = __builtin_bit_cast(bf16x8, pk0);
+  x1 = __builtin_bit_cast(bf16x8, pk1);
+}
+
 __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
   __shared__ __attribute__((aligned(16))) __bf16 sa[GT * GS];
   __shared__ __attribute__((aligned(16))) __bf16 sb[DH * GS];
@@ -382,8 +417,23 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const int wm = wave & 1, wn = wave >> 1;
-  const int m0 = static_cast<int>(blockIdx.x) * GT;
-  const int z = static_cast<int>(blockIdx.y);
+  // Workgroups are dealt to the 8 XCDs in turn. When the batch count allows,
+  // all row tiles of one z go to the same XCD so that its B operand (the
+  // keys, dout, q+u or q+v of that batch row and head) is fetched into one L2
+  // instead of eight.
+  const int n_mt = (q.rows + GT - 1) / GT;
+  const int n_z = static_cast<int>(gridDim.x) / n_mt;
+  const int l = static_cast<int>(blockIdx.x);
+  int z, mt;
+  if ((n_z & 7) == 0) {
+    const int w = l >> 3;
+    z = (l & 7) + 8 * (w / n_mt);
+    mt = w - (w / n_mt) * n_mt;
+  } else {
+    z = l / n_mt;
+    mt = l - z * n_mt;
+  }
+  const int m0 = mt * GT;
   const int z1 = z / q.Z2, z2 = z - z1 * q.Z2;
   const int M = q.M, L = q.L, ML = M + L;
   const bool trans = q.kind == 0 || q.kind == 3;
@@ -393,19 +443,23 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
 #pragma unroll
   for (int x = 0; x < 16; ++x) acc[x] = 0.0f;
 
-  // per-thread load coordinates
-  const int a_mm = trans ? (tid & 7) * 8 : tid >> 2;   // m offset in the tile
-  const int a_kk = trans ? tid >> 3 : (tid & 3) * 8;   // k offset in the slab
-  const int b_kk = tid >> 3, b_nc = (tid & 7) * 8;
-  bf16x8 ra, rb;
+  // Each thread moves 16 consecutive elements of A and of B per slab. Where
+  // the tile is transposed on its way to LDS (A stored k-major, and every B)
+  // the 64 lanes of a wave take 64 consecutive k, so each 2-byte LDS store of
+  // the wave touches every bank once or twice.
+  const int a_mm = trans ? (tid >> 6) * 16 : tid >> 2;  // m offset in the tile
+  const int a_kk = trans ? tid & 63 : (tid & 3) * 16;   // k offset in the slab
+  const int b_kk = tid & 63, b_nc = (tid >> 6) * 16;
+  bf16x8 ra[2], rb[2];
 
   for (int ko = 0; ko < q.K_out; ++ko) {
-    const int bb = q.kind == 3 ? ko : z1;      // batch row of the A elements
+    const int bb = q.K_out > 1 ? ko : z1;      // batch row of the A elements
     int valid = q.valid ? q.valid[bb] : M;
     valid = valid < 0 ? 0 : (valid > M ? M : valid);
     const int jv = M - valid;
-    const __bf16 *abase = q.a + (q.kind == 3 ? ko * q.a_so : z1 * q.a_s1) + z2 * q.a_s2;
+    const __bf16 *abase = q.a + (q.K_out > 1 ? ko * q.a_so : z1 * q.a_s1) + z2 * q.a_s2;
     const __bf16 *bbase = q.b + z1 * q.b_s1 + z2 * q.b_s2 + ko * q.b_so;
+    const rsrc_t ars = make_rsrc(abase, static_cast<uint32_t>(L * q.lda * 2));
     const int m_last = (m0 + GT < q.rows ? m0 + GT : q.rows) - 1;
     int k_lo = 0, k_hi = q.K;
     if (q.kind == 0) {
@@ -420,43 +474,48 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
     k_lo = k_lo < 0 ? 0 : (k_lo & ~(GK - 1));
 
     auto load = [&](int k0) {
-      // A: 8 consecutive elements along the contiguous dimension
       const int m = m0 + a_mm, k = k0 + a_kk;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ra[e] = static_cast<__bf16>(0.0f);
+      // row (query) of the stored matrix and first key / distance of the run
+      const int qi = trans ? k : m, t0 = trans ? m : k;
+      bf16x8 x[2];
       if (!skew) {
-        // row (query) index of the stored matrix, and first key of the chunk
-        const int qi = trans ? k : m, key0 = trans ? m : k;
-        if (qi < L && key0 < ML) {
-          const bf16x8 x = load8(abase + static_cast<int64_t>(qi) * q.lda + key0);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int key = key0 + e;
-            if (key >= jv && key <= M + qi) ra[e] = x[e];
-          }
+        x[0] = x[1] = zero8();
+        if (qi < L) {
+          const __bf16 *src = abase + static_cast<int64_t>(qi) * q.lda + t0;
+          if (t0 < ML) x[0] = load8(src);
+          if (t0 + 8 < ML) x[1] = load8(src + 8);
         }
       } else {
+        load16_unaligned(ars, qi * static_cast<int>(q.lda) + t0 + qi - (L - 1), x[0], x[1]);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int mm = trans ? m + e : m, kk = trans ? k : k + e;
-          const int qi = trans ? kk : mm, t = trans ? mm : kk;
-          const int key = t + qi - (L - 1);
-          if (qi < L && t < ML && key >= jv && key <= M + qi)
-            ra[e] = abase[static_cast<int64_t>(qi) * q.lda + key];
+          const int idx = t0 + 8 * c + e;                 // key (plain) or distance row (skew)
+          const int key = skew ? idx + qi - (L - 1) : idx;
+          const bool ok = qi < L && idx < ML && key >= jv && key <= M + qi;
+          ra[c][e] = ok ? x[c][e] : static_cast<__bf16>(0.0f);
         }
-      }
       const int kb = k0 + b_kk;
-      rb = kb < q.K ? load8(bbase + static_cast<int64_t>(kb) * q.ldb + b_nc) : zero8();
+      const __bf16 *bsrc = bbase + static_cast<int64_t>(kb) * q.ldb + b_nc;
+      rb[0] = kb < q.K ? load8(bsrc) : zero8();
+      rb[1] = kb < q.K ? load8(bsrc + 8) : zero8();
     };
     auto store = [&]() {
       if (trans) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sa[(a_mm + e) * GS + a_kk] = ra[e];
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sa[(a_mm + 8 * c + e) * GS + a_kk] = ra[c][e];
       } else {
-        *reinterpret_cast<bf16x8 *>(sa + a_mm * GS + a_kk) = ra;
+        *reinterpret_cast<bf16x8 *>(sa + a_mm * GS + a_kk) = ra[0];
+        *reinterpret_cast<bf16x8 *>(sa + a_mm * GS + a_kk + 8) = ra[1];
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sb[(b_nc + e) * GS + b_kk] = rb[e];
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sb[(b_nc + 8 * c + e) * GS + b_kk] = rb[c][e];
     };
 
     if (k_lo < k_hi) load(k_lo);
@@ -466,7 +525,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
       __syncthreads();
       if (k0 + GK < k_hi) load(k0 + GK);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < GK / 16; ++s) {
         const bf16x8 av = load8(sa + (wm * 32 + r) * GS + 16 * s + 8 * hh);
         const bf16x8 bv = load8(sb + (wn * 32 + r) * GS + 16 * s + 8 * hh);
         acc = mfma32(av, bv, acc);
@@ -491,26 +550,51 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
     s += __shfl_xor(s, 32);
     if (hh == 0) scol[wm][n] = s;
     __syncthreads();
-    if (tid < DH) {
-      const int n_mt = static_cast<int>(gridDim.x);
-      q.colsum[(static_cast<int64_t>(z) * n_mt + blockIdx.x) * DH + tid] = scol[0][tid] + scol[1][tid];
-    }
+    if (tid < DH) q.colsum[(static_cast<int64_t>(z) * n_mt + mt) * DH + tid] = scol[0][tid] + scol[1][tid];
   }
 }
 
-// du[h][n] = sum over (b, row tile) of part_u, the same for dv_bias.
-__global__ __launch_bounds__(256) void bwd_bias_reduce_kernel(const float *part_u, const float *part_v,
-                                                              float *du, float *dvb, int B, int H,
-                                                              int n_mt) {
-  const int e = static_cast<int>(blockIdx.x) * 256 + threadIdx.x;
-  if (e >= 2 * H * DH) return;
-  const int which = e / (H * DH), hn = e - which * H * DH;
-  const int h = hn / DH, n = hn - h * DH;
-  const float *src = which ? part_v : part_u;
+// dR = sum over batch rows of the per-row products (one thread per element,
+// the first 2H workgroups excepted); du[h][n] (dv_bias) = sum over (b, row
+// tile) of the column sums of dq's content (position) part, one workgroup
+// per (part, head): 4 groups of 64 lanes split the items, then combine.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *part_r, float *dr, int64_t n_r,
+                                                         const float *part_u, const float *part_v,
+                                                         float *du, float *dvb, int B, int H, int n_mt) {
+  __shared__ float red[4][DH];
+  const int tid = threadIdx.x;
+  if (static_cast<int>(blockIdx.x) < 2 * H) {
+    const int which = static_cast<int>(blockIdx.x) / H, h = static_cast<int>(blockIdx.x) - which * H;
+    const float *src = which ? part_v : part_u;
+    const int n = tid & 63, grp = tid >> 6, items = B * n_mt;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int it0 = grp; it0 < items; it0 += 16) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int it = it0 + 4 * x;
+        if (it < items) {
+          const int b = it / n_mt, t = it - b * n_mt;
+          acc[x] += src[((static_cast<int64_t>(b) * H + h) * n_mt + t) * DH + n];
+        }
+      }
+    }
+    red[grp][n] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    __syncthreads();
+    if (tid < DH) (which ? dvb : du)[h * DH + tid] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+    return;
+  }
+  const int64_t e = (static_cast<int64_t>(blockIdx.x) - 2 * H) * 256 + tid;
+  if (e >= n_r) return;
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  for (int b0 = 0; b0 < B; b0 += 8) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+      if (b0 + x < B) acc[x] += part_r[(b0 + x) * n_r + e];
+  }
   float s = 0.0f;
-  for (int b = 0; b < B; ++b)
-    for (int t = 0; t < n_mt; ++t) s += src[((static_cast<int64_t>(b) * H + h) * n_mt + t) * DH + n];
-  (which ? dvb : du)[hn] = s;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) s += acc[x];
+  dr[e] = s;
 }
 
 }  // namespace
@@ -531,6 +615,8 @@ txl_status launch_rel_attn_bwd(const AttnParams &p, const BwdParams &g, hipStrea
   const int64_t ML = static_cast<int64_t>(p.M) + p.L;
   if ((ML + BK) * p.kv_sl * 2 >= (int64_t(1) << 31) || (ML + BK + QW) * p.r_sl * 2 >= (int64_t(1) << 31))
     return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: key / R rows span more than 2 GiB per head");
+  if ((static_cast<int64_t>(p.L) * g.ldp + 16) * 2 >= (int64_t(1) << 31))
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: p / g rows span more than 2 GiB per head");
   const int B = p.B, H = p.H, L = p.L;
   const int64_t BHL = static_cast<int64_t>(B) * H * L;
   const int n_qt = (L + BQ - 1) / BQ;
@@ -550,8 +636,8 @@ txl_status launch_rel_attn_bwd(const AttnParams &p, const BwdParams &g, hipStrea
     q.valid = p.valid;
     q.M = p.M;
     q.L = L;
-    const dim3 grid(static_cast<unsigned>((q.rows + GT - 1) / GT), static_cast<unsigned>(z_count));
-    hipLaunchKernelGGL(bgemm_kernel, grid, dim3(256), 0, s, q);
+    const int64_t wgs = static_cast<int64_t>((q.rows + GT - 1) / GT) * z_count;
+    hipLaunchKernelGGL(bgemm_kernel, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, s, q);
     return check_launch("bgemm_kernel");
   };
   const int64_t pz = static_cast<int64_t>(L) * g.ldp;      // p / g per (b, h)
@@ -583,17 +669,19 @@ txl_status launch_rel_attn_bwd(const AttnParams &p, const BwdParams &g, hipStrea
   q.b = static_cast<const __bf16 *>(p.r); q.ldb = p.r_sl; q.b_s1 = 0; q.b_s2 = p.r_sh;
   q.accumulate = 1; q.colsum = g.part_v;
   if ((st = run(q, B * H)) != TXL_OK) return st;
-  // dR = sum over batch rows and queries of g (q + v), diagonal view
+  // dR per batch row = sum over queries of g (q + v), diagonal view; summed
+  // over batch rows by the reduction below
   q = BgParams{};
-  q.rows = ml; q.K = L; q.K_out = B; q.kind = 3;
-  q.a = g.gm; q.lda = g.ldp; q.a_so = H * pz; q.a_s2 = pz;
-  q.b = g.qv; q.ldb = DH; q.b_so = static_cast<int64_t>(H) * L * DH; q.b_s2 = static_cast<int64_t>(L) * DH;
-  q.c = g.dr; q.ldc = DH; q.c_s2 = static_cast<int64_t>(ml) * DH;
+  q.rows = ml; q.K = L; q.K_out = 1; q.kind = 3;
+  q.a = g.gm; q.lda = g.ldp; q.a_s1 = H * pz; q.a_s2 = pz;
+  q.b = g.qv; q.ldb = DH; q.b_s1 = static_cast<int64_t>(H) * L * DH; q.b_s2 = static_cast<int64_t>(L) * DH;
+  q.c = g.part_r; q.ldc = DH; q.c_s1 = static_cast<int64_t>(H) * ml * DH; q.c_s2 = static_cast<int64_t>(ml) * DH;
   q.Z2 = H;
-  if ((st = run(q, H)) != TXL_OK) return st;
-  hipLaunchKernelGGL(bwd_bias_reduce_kernel, dim3(static_cast<unsigned>((2 * H * DH + 255) / 256)), dim3(256),
-                     0, s, g.part_u, g.part_v, g.du, g.dvb, B, H, n_mt_q);
-  return check_launch("bwd_bias_reduce_kernel");
+  if ((st = run(q, B * H)) != TXL_OK) return st;
+  const int64_t n_r = static_cast<int64_t>(H) * ml * DH;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>(2 * H + (n_r + 255) / 256)), dim3(256), 0, s,
+                     g.part_r, g.dr, n_r, g.part_u, g.part_v, g.du, g.dvb, B, H, n_mt_q);
+  return check_launch("bwd_reduce_kernel");
 }
 
 }  // namespace txl

@@ -52,6 +52,7 @@ struct BwdParams {
   __bf16 *pm, *gm;        // [B*H*L, ldp]: probabilities and score gradients
   int64_t ldp;
   float *part_u, *part_v; // [B*H][ceil(L/64)][64] column sums of dq's two parts
+  float *part_r;          // [B][H][M+L][64] dR of each batch row
 };
 // row length of pm / gm for M memory slots and L queries
 size_t rel_attn_bwd_ldp(int M, int L);
