@@ -450,7 +450,9 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
   const int a_mm = trans ? (tid >> 6) * 16 : tid >> 2;  // m offset in the tile
   const int a_kk = trans ? tid & 63 : (tid & 3) * 16;   // k offset in the slab
   const int b_kk = tid & 63, b_nc = (tid >> 6) * 16;
-  bf16x8 ra[2], rb[2];
+  // two register sets: the slab being stored to LDS and the next one, so two
+  // slabs' loads are in flight while a slab is multiplied
+  bf16x8 ra[2][2], rb[2][2];
 
   for (int ko = 0; ko < q.K_out; ++ko) {
     const int bb = q.K_out > 1 ? ko : z1;      // batch row of the A elements
@@ -472,11 +474,13 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
       k_lo = jv + L - 1 - m_last;
     }
     k_lo = k_lo < 0 ? 0 : (k_lo & ~(GK - 1));
+    const int n_slabs = k_hi > k_lo ? (k_hi - k_lo + GK - 1) / GK : 0;
 
-    auto load = [&](int k0) {
+    auto load = [&](int set, int k0) {
       const int m = m0 + a_mm, k = k0 + a_kk;
       // row (query) of the stored matrix and first key / distance of the run
       const int qi = trans ? k : m, t0 = trans ? m : k;
+      const int sh = skew ? qi - (L - 1) : 0;         // key = index + sh
       bf16x8 x[2];
       if (!skew) {
         x[0] = x[1] = zero8();
@@ -486,50 +490,61 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
           if (t0 + 8 < ML) x[1] = load8(src + 8);
         }
       } else {
-        load16_unaligned(ars, qi * static_cast<int>(q.lda) + t0 + qi - (L - 1), x[0], x[1]);
+        load16_unaligned(ars, qi * static_cast<int>(q.lda) + t0 + sh, x[0], x[1]);
       }
+      // visible keys of this query: [jv, M + qi]; indices stay below M + L
+      const int k_first = t0 + sh, k_last = t0 + 15 + sh;
+      if (qi < L && k_first >= jv && k_last <= M + qi && t0 + 15 < ML) {
+        ra[set][0] = x[0];
+        ra[set][1] = x[1];
+      } else {
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int idx = t0 + 8 * c + e;                 // key (plain) or distance row (skew)
-          const int key = skew ? idx + qi - (L - 1) : idx;
-          const bool ok = qi < L && idx < ML && key >= jv && key <= M + qi;
-          ra[c][e] = ok ? x[c][e] : static_cast<__bf16>(0.0f);
-        }
+          for (int e = 0; e < 8; ++e) {
+            const int idx = t0 + 8 * c + e, key = idx + sh;
+            const bool ok = qi < L && idx < ML && key >= jv && key <= M + qi;
+            ra[set][c][e] = ok ? x[c][e] : static_cast<__bf16>(0.0f);
+          }
+      }
       const int kb = k0 + b_kk;
       const __bf16 *bsrc = bbase + static_cast<int64_t>(kb) * q.ldb + b_nc;
-      rb[0] = kb < q.K ? load8(bsrc) : zero8();
-      rb[1] = kb < q.K ? load8(bsrc + 8) : zero8();
+      rb[set][0] = kb < q.K ? load8(bsrc) : zero8();
+      rb[set][1] = kb < q.K ? load8(bsrc + 8) : zero8();
     };
-    auto store = [&]() {
+    auto store = [&](int set) {
       if (trans) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sa[(a_mm + 8 * c + e) * GS + a_kk] = ra[c][e];
+          for (int e = 0; e < 8; ++e) sa[(a_mm + 8 * c + e) * GS + a_kk] = ra[set][c][e];
       } else {
-        *reinterpret_cast<bf16x8 *>(sa + a_mm * GS + a_kk) = ra[0];
-        *reinterpret_cast<bf16x8 *>(sa + a_mm * GS + a_kk + 8) = ra[1];
+        *reinterpret_cast<bf16x8 *>(sa + a_mm * GS + a_kk) = ra[set][0];
+        *reinterpret_cast<bf16x8 *>(sa + a_mm * GS + a_kk + 8) = ra[set][1];
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sb[(b_nc + 8 * c + e) * GS + b_kk] = rb[c][e];
+        for (int e = 0; e < 8; ++e) sb[(b_nc + 8 * c + e) * GS + b_kk] = rb[set][c][e];
     };
-
-    if (k_lo < k_hi) load(k_lo);
-    for (int k0 = k_lo; k0 < k_hi; k0 += GK) {
+    auto step = [&](int set, int s) {
       __syncthreads();
-      store();
+      store(set);
       __syncthreads();
-      if (k0 + GK < k_hi) load(k0 + GK);
+      if (s + 2 < n_slabs) load(set, k_lo + (s + 2) * GK);
 #pragma unroll
-      for (int s = 0; s < GK / 16; ++s) {
-        const bf16x8 av = load8(sa + (wm * 32 + r) * GS + 16 * s + 8 * hh);
-        const bf16x8 bv = load8(sb + (wn * 32 + r) * GS + 16 * s + 8 * hh);
+      for (int kk = 0; kk < GK / 16; ++kk) {
+        const bf16x8 av = load8(sa + (wm * 32 + r) * GS + 16 * kk + 8 * hh);
+        const bf16x8 bv = load8(sb + (wn * 32 + r) * GS + 16 * kk + 8 * hh);
         acc = mfma32(av, bv, acc);
       }
+    };
+
+    if (n_slabs > 0) load(0, k_lo);
+    if (n_slabs > 1) load(1, k_lo + GK);
+    for (int s = 0; s < n_slabs; s += 2) {
+      step(0, s);
+      if (s + 1 < n_slabs) step(1, s + 1);
     }
   }
 
