@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "txl_internal.h"
 
@@ -238,6 +239,66 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
     return;
   }
   const bool second = n0 >= p.n_split;
+  // Staged epilogue: the tile goes to LDS (free after the last barrier of the
+  // loop) and leaves as 16-byte row chunks, the output row of each 32-row
+  // block remapped once, instead of one 2-byte or 4-byte store per element.
+  constexpr bool kStaged = BKS == 64 && (E == kEpiStoreBf16 || E == kEpiGeluBf16 ||
+                                         ((E == kEpiResidualF32 || E == kEpiPartialF32) && BN == 64));
+  if constexpr (kStaged) {
+    typedef typename std::conditional<(E == kEpiStoreBf16 || E == kEpiGeluBf16), __bf16, float>::type OT;
+    constexpr int VE = 16 / static_cast<int>(sizeof(OT));       // elements per 16-byte chunk
+    constexpr int OS = BN + VE;                                  // LDS row stride (elements)
+    constexpr int CPRo = BN / VE, RP = 256 / CPRo, IT = BM / RP;
+    static_assert(size_t(BM) * OS * sizeof(OT) <= sizeof(sa), "staged tile must fit the A buffers");
+    static_assert(32 % RP == 0 || RP % 32 == 0, "row passes must tile 32-row blocks");
+    const uintptr_t al = reinterpret_cast<uintptr_t>(p.c0) | reinterpret_cast<uintptr_t>(p.c1);
+    bool vec_ok = (al & 15) == 0 && p.ldc % VE == 0;
+    if (E == kEpiResidualF32) vec_ok = vec_ok && p.ldres % 4 == 0 && (reinterpret_cast<uintptr_t>(p.res) & 7) == 0;
+    if (E == kEpiPartialF32) vec_ok = vec_ok && p.c_split_stride % 4 == 0;
+    if (vec_ok) {
+      OT *ct = reinterpret_cast<OT *>(&sa[0][0]);
+#pragma unroll
+      for (int jn = 0; jn < WN; ++jn)
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const int row = wm * (BM / 2) + i * 32 + 8 * a4 + 4 * g + c;
+              const int col = wn * (BN / 2) + jn * 32 + r;
+              float v = acc[i][jn][4 * a4 + c];
+              if (E == kEpiGeluBf16) v = 0.5f * v * (1.0f + erff(v * 0.7071067811865476f));
+              ct[row * OS + col] = static_cast<OT>(v);
+            }
+      __syncthreads();
+      const int cc = tid % CPRo, rr0 = tid / CPRo;
+      const int nc0 = (second ? n0 - p.n_split : n0) + cc * VE;
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int row = rr0 + RP * it;
+        const int m = m0 + row;
+        if (m >= p.rows) continue;
+        // a 32-row block never straddles an output segment (c_seg % 32 == 0)
+        const int mb = m0 + (RP * it / 32) * 32;
+        const int64_t mo = (p.c_seg > 0 ? (mb / p.c_seg) * p.c_bstride + p.c_row0 + mb % p.c_seg
+                                        : static_cast<int64_t>(mb)) + (row & 31);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(ct + row * OS + cc * VE);
+        if (E == kEpiPartialF32) {
+          *reinterpret_cast<u32x4 *>(static_cast<float *>(p.c0) + split * p.c_split_stride + mo * p.ldc + nc0) = v;
+        } else if (E == kEpiResidualF32) {
+          const bf16x4 rv = *reinterpret_cast<const bf16x4 *>(p.res + static_cast<int64_t>(m) * p.ldres + nc0);
+          f32x4 o = __builtin_bit_cast(f32x4, v);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] += static_cast<float>(rv[e]);
+          *reinterpret_cast<f32x4 *>(static_cast<float *>(second ? p.c1 : p.c0) + mo * p.ldc + nc0) = o;
+        } else {
+          *reinterpret_cast<u32x4 *>(static_cast<__bf16 *>(second ? p.c1 : p.c0) + mo * p.ldc + nc0) = v;
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int jn = 0; jn < WN; ++jn) {
     const int n = n0 + wn * (BN / 2) + jn * 32 + r;
