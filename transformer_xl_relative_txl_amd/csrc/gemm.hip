@@ -39,6 +39,21 @@ __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// GELU with the exact erf form, erf by Abramowitz & Stegun formula 7.1.26
+// (|error| <= 1.5e-7; about 5e-7 in fp32 arithmetic, far below the bf16
+// rounding of the output): erf(|x|) = 1 - t (a1 + t (a2 + ... a5)) e^{-x^2},
+// t = 1 / (1 + p |x|), odd in x. One reciprocal and one exp2 per element.
+__device__ inline float gelu_erf(float v) {
+  const float x = v * 0.7071067811865476f;
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
+  const float poly =
+      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
+  const float erf_x = copysignf(1.0f - poly * e, x);
+  return 0.5f * v * (1.0f + erf_x);
+}
+
 // Tile BM x BN (each 64 or 128) per workgroup of 4 waves arranged 2 x 2; a
 // wave computes (BM/2) x (BN/2) as blocks of 32 x 32. K runs in slabs of BKS
 // (32 or 64) through two LDS buffers: the next slab is loaded into registers while the
@@ -268,7 +283,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
               const int row = wm * (BM / 2) + i * 32 + 8 * a4 + 4 * g + c;
               const int col = wn * (BN / 2) + jn * 32 + r;
               float v = acc[i][jn][4 * a4 + c];
-              if (E == kEpiGeluBf16) v = 0.5f * v * (1.0f + erff(v * 0.7071067811865476f));
+              if (E == kEpiGeluBf16) v = gelu_erf(v);
               ct[row * OS + col] = static_cast<OT>(v);
             }
       __syncthreads();
@@ -325,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
             v += static_cast<float>(p.res[static_cast<int64_t>(m) * p.ldres + nc]);
             static_cast<float *>(second ? p.c1 : p.c0)[mo * p.ldc + nc] = v;
           } else {
-            if (E == kEpiGeluBf16) v = 0.5f * v * (1.0f + erff(v * 0.7071067811865476f));
+            if (E == kEpiGeluBf16) v = gelu_erf(v);
             static_cast<__bf16 *>(second ? p.c1 : p.c0)[mo * p.ldc + nc] = static_cast<__bf16>(v);
           }
         }
