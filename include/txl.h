@@ -45,7 +45,7 @@ typedef enum { TXL_F32 = 0, TXL_BF16 = 1 } txl_dtype;
 typedef enum {
   TXL_OK = 0,
   TXL_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent shapes */
-  TXL_ERR_UNSUPPORTED = 2, /* valid request this build does not serve (d_h, alignment) */
+  TXL_ERR_UNSUPPORTED = 2, /* valid request the library does not serve (d_h, alignment) */
   TXL_ERR_WORKSPACE = 3,   /* caller buffer too small */
   TXL_ERR_HIP = 4          /* a HIP launch failed; see txl_last_error() */
 } txl_status;
