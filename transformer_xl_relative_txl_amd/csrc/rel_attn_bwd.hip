@@ -15,20 +15,22 @@
 // the earlier segment that produced the memory, while this segment's
 // projections of it still receive gradient.
 //
-// Design (first version, built for clarity of the data flow):
+// Design:
 //  * bwd_prep: D_i, and (q+u), (q+v) rounded to bf16 once.
-//  * bwd_pg: one pass per query tile that recomputes the scores exactly as
-//    the forward does (same MFMA layouts, band reuse and LDS diagonal read),
-//    forms p from the forward's log-sum-exp, dp = dout V^T with MFMA, and
-//    g; p and g go to a workspace as bf16 rows [b, h, i, j'] (staged through
-//    LDS so each row segment is written by consecutive lanes).
-//  * bgemm: one small MFMA kernel for the five contractions over p and g,
-//    reading the visible part of each row only (hidden entries are masked on
-//    load, so nothing outside the visited tiles needs clearing). The
-//    position terms read g along diagonals: the element of distance row t
-//    for query i is g[i][t + i - (L-1)], a matrix whose row stride is one
-//    more than g's, so dq's position part and dR are ordinary products over
-//    that skewed view.
+//  * bwd_kv: key-major. A workgroup holds 128 keys of one (batch, head); each
+//    wave keeps its 32 K and V rows and its dK, dV accumulators in registers
+//    while query tiles of 32 stream through LDS. Per tile it recomputes the
+//    scores as the forward does (content MFMA, the position band and its
+//    diagonal read through LDS), forms p = 2^(s - lse) from the forward's
+//    log-sum-exp, dp = dout V^T and g = scale p (dp - D), and accumulates
+//    dV += p^T dout and dK += g^T (q+u) on the chip. g leaves twice, as bf16
+//    rows by key, g[i][j'], and by distance, g[i][t] with t = j' + L - 1 - i
+//    (consecutive lanes write consecutive keys of a row in both).
+//  * bgemm: one small MFMA kernel for the remaining contractions, reading the
+//    visible part of each row only (hidden entries are masked on load, so
+//    nothing outside the visited pairs needs clearing): dq = g K over keys,
+//    dq += g R over distances, dR = sum over queries of g (q + v) per batch
+//    row.
 //  * bwd_reduce: dR summed over batch rows (its product runs per row, for
 //    parallelism), du and dv_bias from per-tile column sums of dq's two parts.
 #include <hip/hip_runtime.h>
@@ -43,22 +45,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int DH = 64;
-constexpr int QW = 32;         // queries per wave
 constexpr int NW = 4;          // waves per workgroup
-constexpr int BQ = QW * NW;
-constexpr int BK = 64;         // keys per tile
-constexpr int KS = DH + 8;     // K / V tile row stride (bf16)
-constexpr int NU = 2 * QW;
-constexpr int US = QW + 2;     // band row stride (floats)
-constexpr int PS = BK + 4;     // p / g staging row stride (bf16): 8-byte aligned rows
-
-constexpr size_t kLdsT = size_t(BK) * KS * 2;   // one K or V tile
-constexpr size_t kLdsBand = size_t(NW) * NU * US * 4;
-constexpr size_t kLdsTotal = 4 * kLdsT + kLdsBand;  // K and V, double-buffered
-static_assert(size_t(2) * QW * PS * 2 <= size_t(NU) * US * 4, "p/g staging must fit a wave's band");
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -122,55 +113,50 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnParams p, BwdParams g
 }
 
 // ---------------------------------------------------------------------------
-// p and g for every visited (query, key) pair of a query tile.
-struct KVRegs {
-  u32x4 k[2], v[2];
-};
-__device__ inline void load_kv(KVRegs &x, rsrc_t krs, rsrc_t vrs, int row_bytes, int j0, int tid) {
-#pragma unroll
-  for (int rep = 0; rep < 2; ++rep) {
-    const int cidx = tid + rep * 256;
-    const int off = (j0 + (cidx >> 3)) * row_bytes + (cidx & 7) * 16;
-    x.k[rep] = bload(krs, off);
-    x.v[rep] = bload(vrs, off);
-  }
-}
-__device__ inline void store_kv(const KVRegs &x, __bf16 *sk, __bf16 *sv, int tid) {
-#pragma unroll
-  for (int rep = 0; rep < 2; ++rep) {
-    const int cidx = tid + rep * 256;
-    const int o = (cidx >> 3) * KS + (cidx & 7) * 8;
-    *reinterpret_cast<u32x4 *>(sk + o) = x.k[rep];
-    *reinterpret_cast<u32x4 *>(sv + o) = x.v[rep];
-  }
-}
+// Key-major pass: one workgroup = 4 waves x 32 keys of one (batch, head); each
+// wave keeps its K and V rows (MFMA B operands) and its dK^T, dV^T
+// accumulators in registers while query tiles of 32 stream through LDS.
+// Per query tile, in the [query][key] accumulator layout (lane = key):
+//   S = Q' K^T (+ the position band Q'' R^T read along its diagonal through
+//   LDS), p = 2^(S - lse2), dp = dout V^T, g = scale p (dp - D),
+//   dV^T += dout^T p, dK^T += (q+u)^T g  (k-order of the query index matching
+//   the accumulator rows, as the forward's PV product),
+// and g goes out twice: by key, g[i][j'], and by distance, g[i][t] with
+// t = j' + L - 1 - i (both rows written by consecutive lanes).
+constexpr int KW = 32;            // keys per wave
+constexpr int KB2 = KW * NW;      // keys per workgroup
+constexpr int QT = 32;            // queries per tile
+constexpr int TS = DH + 8;        // Q' / Q'' / dout tile row stride (bf16)
+constexpr int TT = QT + 8;        // transposed tile row stride (bf16)
+constexpr int BS = 2 * QT + 4;    // band row stride (floats): [query][u], u < 64
+constexpr size_t kKvLdsTile = size_t(QT) * TS * 2;          // one [32][72] bf16 tile
+constexpr size_t kKvLdsTr = size_t(DH) * TT * 2;            // one [64][40] bf16 tile
+constexpr size_t kKvLdsBand = size_t(NW) * QT * BS * 4;
+constexpr size_t kKvLdsTotal = 3 * kKvLdsTile + 2 * kKvLdsTr + 2 * QT * 4 + kKvLdsBand;
+static_assert(size_t(KW) * (DH + 4) * 4 <= size_t(QT) * BS * 4, "dK / dV staging must fit a wave's band");
 
-__global__ __launch_bounds__(256, 2) void bwd_pg_kernel(AttnParams p, BwdParams g, int n_qt) {
+__global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams g, int n_kb) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  float *sband = reinterpret_cast<float *>(smem + 4 * kLdsT);
+  __bf16 *sQa = reinterpret_cast<__bf16 *>(smem);
+  __bf16 *sQb = sQa + QT * TS;
+  __bf16 *sDo = sQb + QT * TS;
+  __bf16 *sQuT = sDo + QT * TS;            // [64 dims][32 queries]
+  __bf16 *sDoT = sQuT + DH * TT;
+  float *sLse = reinterpret_cast<float *>(sDoT + DH * TT);
+  float *sD = sLse + QT;
+  float *sband = sD + QT;
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int r = lane & 31;
-  const int hh = lane >> 5;
-
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const int BH = p.B * p.H;
-  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x) / BH;
+  const int kb = static_cast<int>(blockIdx.x) / BH;       // key blocks in order: most queries first
   const int bh = static_cast<int>(blockIdx.x) % BH;
-  const int b = bh / p.H;
-  const int h = bh - b * p.H;
+  const int b = bh / p.H, h = bh - b * p.H;
   const int L = p.L, M = p.M, ML = M + L;
-  const int i0 = qt * BQ;
-  const int iw = i0 + wave * QW;
-  const int i = iw + r;
+  const int jb = kb * KB2, jw = jb + wave * KW, j = jw + r;   // this lane's key
 
   int valid = p.valid ? p.valid[b] : M;
   valid = valid < 0 ? 0 : (valid > M ? M : valid);
-  const int j_lo = M - valid;
-  const int i_last = (i0 + BQ < L ? i0 + BQ : L) - 1;
-  const int j_end = M + i_last + 1;
-  const int n_tiles = (j_end - j_lo + BK - 1) / BK;
+  const int jv = M - valid;
 
   const __bf16 *qp = static_cast<const __bf16 *>(p.q) + b * p.q_sb + h * p.q_sh;
   const __bf16 *kp = static_cast<const __bf16 *>(p.k) + b * p.kv_sb + h * p.kv_sh;
@@ -179,187 +165,224 @@ __global__ __launch_bounds__(256, 2) void bwd_pg_kernel(AttnParams p, BwdParams 
   const __bf16 *up = static_cast<const __bf16 *>(p.u) + h * DH;
   const __bf16 *vbp = static_cast<const __bf16 *>(p.vb) + h * DH;
   const __bf16 *dop = g.dout + b * g.do_sb + h * g.do_sh;
+  const int64_t row_bh = static_cast<int64_t>(bh) * L;
+  float *dkp = g.dk + static_cast<int64_t>(bh) * ML * DH;
+  float *dvp = g.dv + static_cast<int64_t>(bh) * ML * DH;
+  float *band = sband + wave * (QT * BS);
 
-  const int kv_row_bytes = static_cast<int>(p.kv_sl) * 2;
-  const int r_row_bytes = static_cast<int>(p.r_sl) * 2;
-  const rsrc_t krs = make_rsrc(kp, static_cast<uint32_t>((j_end - 1) * kv_row_bytes + 2 * DH));
-  const rsrc_t vrs = make_rsrc(vp, static_cast<uint32_t>((j_end - 1) * kv_row_bytes + 2 * DH));
-  const rsrc_t rrs = make_rsrc(rp, static_cast<uint32_t>((ML - 1) * r_row_bytes + 2 * DH));
+  // keys below the first valid one, or past the last, take no gradient; a
+  // block of only such keys writes zeros and stops
+  const int q_first = jb + KB2 - 1 < M ? 0 : ((jb - M > 0 ? jb - M : 0) & ~(QT - 1));
+  if (jb + KB2 - 1 < jv || q_first >= L) {
+    for (int e = tid; e < KB2 * DH / 4; e += 256) {
+      const int kk = e / (DH / 4), c4 = e - kk * (DH / 4);
+      if (jb + kk < ML) {
+        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+        *reinterpret_cast<f32x4 *>(dkp + static_cast<int64_t>(jb + kk) * DH + 4 * c4) = z;
+        *reinterpret_cast<f32x4 *>(dvp + static_cast<int64_t>(jb + kk) * DH + 4 * c4) = z;
+      }
+    }
+    return;
+  }
 
-  KVRegs nxt;
-  load_kv(nxt, krs, vrs, kv_row_bytes, j_lo, tid);
-
-  // the forward's scaled operands, and dout as the B operand of dp^T = V dout^T
-  const float c2 = p.scale * 1.4426950408889634f;
-  bf16x8 qa[4], qb[4], dob[4];
+  // K and V rows of this lane's key as B operands (zero past the end)
+  bf16x8 kreg[4], vreg[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int d0 = 16 * s + 8 * hh;
-    const bf16x8 qv = i < L ? load8(qp + static_cast<int64_t>(i) * p.q_sl + d0) : zero8();
-    dob[s] = i < L ? load8(dop + static_cast<int64_t>(i) * g.do_sl + d0) : zero8();
-    const bf16x8 uv = load8(up + d0);
-    const bf16x8 vv = load8(vbp + d0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = static_cast<float>(qv[e]);
-      qa[s][e] = static_cast<__bf16>((x + static_cast<float>(uv[e])) * c2);
-      qb[s][e] = static_cast<__bf16>((x + static_cast<float>(vv[e])) * c2);
-    }
+    kreg[s] = j < ML ? load8(kp + static_cast<int64_t>(j) * p.kv_sl + d0) : zero8();
+    vreg[s] = j < ML ? load8(vp + static_cast<int64_t>(j) * p.kv_sl + d0) : zero8();
   }
-  const int64_t row_bh = static_cast<int64_t>(bh) * L;
-  const float lse2 = i < L ? g.lse[row_bh + i] * 1.4426950408889634f : 0.0f;
-  const float dd = i < L ? g.dd[row_bh + i] : 0.0f;
+  const int r_row_bytes = static_cast<int>(p.r_sl) * 2;
+  const rsrc_t rrs = make_rsrc(rp, static_cast<uint32_t>((ML - 1) * r_row_bytes + 2 * DH));
 
-  float *band = sband + wave * (NU * US);
-  float *band_w = band + 4 * hh * US + r;
-  const float *band_r = band + (31 - r + 4 * hh) * US + r;
-  __bf16 *stg = reinterpret_cast<__bf16 *>(band);   // p rows [32][PS], then g rows
-
-  bf16x8 rr[2][4];
-  auto load_r = [&](int j0) {
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      const int off = (j0 + 32 * (bb + 1) + r + L - 32 - iw) * r_row_bytes + 16 * hh;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) rr[bb][s] = __builtin_bit_cast(bf16x8, bload(rrs, off + 32 * s));
+  // query-tile staging: thread -> (query row, 8-dim chunk)
+  const int st_row = tid >> 3, st_c = (tid & 7) * 8;
+  const float c2 = p.scale * 1.4426950408889634f;
+  bf16x8 nq, ndo;
+  float nlse = 0.0f, nd = 0.0f;
+  auto fetch = [&](int i0) {
+    const int i = i0 + st_row;
+    nq = i < L ? load8(qp + static_cast<int64_t>(i) * p.q_sl + st_c) : zero8();
+    ndo = i < L ? load8(dop + static_cast<int64_t>(i) * g.do_sl + st_c) : zero8();
+    if (tid < QT) {
+      const int ii = i0 + tid;
+      nlse = ii < L ? g.lse[row_bh + ii] * 1.4426950408889634f : 0.0f;
+      nd = ii < L ? g.dd[row_bh + ii] : 0.0f;
     }
   };
-  f32x16 b_carry;
-  {
-    bf16x8 r0[4];
-    const int off = (j_lo + r + L - 32 - iw) * r_row_bytes + 16 * hh;
+  auto stage = [&]() {
+    const bf16x8 u8 = load8(up + st_c), v8 = load8(vbp + st_c);
+    bf16x8 a, bq, qu;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) r0[s] = __builtin_bit_cast(bf16x8, bload(rrs, off + 32 * s));
+    for (int e = 0; e < 8; ++e) {
+      const float x = static_cast<float>(nq[e]);
+      const float xu = x + static_cast<float>(u8[e]);
+      a[e] = static_cast<__bf16>(xu * c2);
+      bq[e] = static_cast<__bf16>((x + static_cast<float>(v8[e])) * c2);
+      qu[e] = static_cast<__bf16>(xu);
+    }
+    *reinterpret_cast<bf16x8 *>(sQa + st_row * TS + st_c) = a;
+    *reinterpret_cast<bf16x8 *>(sQb + st_row * TS + st_c) = bq;
+    *reinterpret_cast<bf16x8 *>(sDo + st_row * TS + st_c) = ndo;
 #pragma unroll
-    for (int x = 0; x < 16; ++x) b_carry[x] = 0.0f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) b_carry = mfma32(r0[s], qb[s], b_carry);
-  }
-  load_r(j_lo);
+    for (int e = 0; e < 8; ++e) {
+      sQuT[(st_c + e) * TT + st_row] = qu[e];
+      sDoT[(st_c + e) * TT + st_row] = ndo[e];
+    }
+    if (tid < QT) {
+      sLse[tid] = nlse;
+      sD[tid] = nd;
+    }
+  };
 
-  store_kv(nxt, reinterpret_cast<__bf16 *>(smem), reinterpret_cast<__bf16 *>(smem + kLdsT), tid);
-  load_kv(nxt, krs, vrs, kv_row_bytes, j_lo + BK, tid);
+  f32x16 dv_acc[2], dk_acc[2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) dv_acc[db][x] = dk_acc[db][x] = 0.0f;
+
+  // R rows of the band: for query tile i0 the band columns are t0 + 0..63,
+  // t0 = jw + L - 1 - i0 - 31; column block c holds R rows t0 + 32c + r
+  auto load_rblk = [&](bf16x8 (&dst)[4], int t_first) {
+    const int off = (t_first + r) * r_row_bytes + 16 * hh;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dst[s] = __builtin_bit_cast(bf16x8, bload(rrs, off + 32 * s));
+  };
+  bf16x8 rb0[4], rb1[4];
+  load_rblk(rb0, jw + L - 1 - q_first - 31);
+  load_rblk(rb1, jw + L - 1 - q_first - 31 + 32);
+
+  fetch(q_first);
   __syncthreads();
+  stage();
+  __syncthreads();
+  const float scale = p.scale;
+  for (int i0 = q_first; i0 < L; i0 += QT) {
+    if (i0 + QT < L) fetch(i0 + QT);
 
-  __bf16 *pm = g.pm + row_bh * g.ldp;
-  __bf16 *gm = g.gm + row_bh * g.ldp;
-
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int j0 = j_lo + kt * BK;
-    unsigned char *buf = smem + (kt & 1) * (2 * kLdsT);
-    const __bf16 *sk = reinterpret_cast<const __bf16 *>(buf);
-    const __bf16 *svr = reinterpret_cast<const __bf16 *>(buf + kLdsT);
-
-    // ---- scores, exactly as the forward computes them ----
-    f32x16 s_acc[2];
+    // ---- the band Q'' R^T, one 32-column block at a time, to LDS as
+    // band[q][u] (u = t - t0); the next tile's band starts 32 rows lower, so
+    // its block 1 is this block 0 ----
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int c = 0; c < 2; ++c) {
+      f32x16 bacc;
 #pragma unroll
-      for (int x = 0; x < 16; ++x) s_acc[kb][x] = 0.0f;
+      for (int x = 0; x < 16; ++x) bacc[x] = 0.0f;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        s_acc[kb] = mfma32(load8(sk + (kb * 32 + r) * KS + 16 * s + 8 * hh), qa[s], s_acc[kb]);
+        bacc = mfma32(load8(sQb + r * TS + 16 * s + 8 * hh), c == 0 ? rb0[s] : rb1[s], bacc);
+#pragma unroll
+      for (int x = 0; x < 16; ++x) band[(8 * (x >> 2) + 4 * hh + (x & 3)) * BS + 32 * c + r] = bacc[x];
     }
-    f32x16 b_acc[3];
-    b_acc[0] = b_carry;
 #pragma unroll
-    for (int bb = 1; bb < 3; ++bb) {
+    for (int s = 0; s < 4; ++s) rb1[s] = rb0[s];
+    if (i0 + QT < L) load_rblk(rb0, jw + L - 1 - (i0 + QT) - 31);
+    // ---- S[q][key] = Q' K^T, plus S_pos[q][key] = band[q][key - q + 31] ----
+    f32x16 sacc;
 #pragma unroll
-      for (int x = 0; x < 16; ++x) b_acc[bb][x] = 0.0f;
+    for (int x = 0; x < 16; ++x) sacc[x] = 0.0f;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) b_acc[bb] = mfma32(rr[bb - 1][s], qb[s], b_acc[bb]);
-    }
-    b_carry = b_acc[2];
-    load_r(j0 + BK);
-
-    float sv[2][16];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc)
-            band_w[(32 * half + 8 * a4 + cc) * US] = b_acc[kb + half][4 * a4 + cc];
-      wave_lds_sync();
-#pragma unroll
-      for (int x = 0; x < 16; ++x) sv[kb][x] = s_acc[kb][x] + band_r[(8 * (x >> 2) + (x & 3)) * US];
-      wave_lds_sync();
-    }
-    if (j0 + BK - 1 - M > iw) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const int jj = j0 + kb * 32 + 8 * (x >> 2) + 4 * hh + (x & 3);
-          if (jj - M > i) sv[kb][x] = -INFINITY;
-        }
-    }
-
-    // ---- dp^T[key][query] = V dout^T ----
-    f32x16 dp_acc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int x = 0; x < 16; ++x) dp_acc[kb][x] = 0.0f;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        dp_acc[kb] = mfma32(load8(svr + (kb * 32 + r) * KS + 16 * s + 8 * hh), dob[s], dp_acc[kb]);
-    }
-
-    // ---- p = 2^(s - lse2), g = scale p (dp - D); staged as rows [query][key] ----
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        bf16x4 p4, g4;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const int x = 4 * a4 + cc;
-          const float pv = __builtin_amdgcn_exp2f(sv[kb][x] - lse2);
-          p4[cc] = static_cast<__bf16>(pv);
-          g4[cc] = static_cast<__bf16>(p.scale * pv * (dp_acc[kb][x] - dd));
-        }
-        const int key = kb * 32 + 8 * a4 + 4 * hh;
-        *reinterpret_cast<bf16x4 *>(stg + r * PS + key) = p4;
-        *reinterpret_cast<bf16x4 *>(stg + (QW + r) * PS + key) = g4;
-      }
+    for (int s = 0; s < 4; ++s) sacc = mfma32(load8(sQa + r * TS + 16 * s + 8 * hh), kreg[s], sacc);
     wave_lds_sync();
-    if ((j_lo & 3) == 0) {
-      // tiles start 4-aligned: 4 keys per lane, 16 lanes per row, 4 rows per store
-      const int kk = (lane & 15) * 4, jj = j0 + kk;
-      if (jj < ML) {
+    float sv[16];
 #pragma unroll
-        for (int it = 0; it < QW / 4; ++it) {
-          const int qq = (lane >> 4) + 4 * it, row = iw + qq;
-          if (row < L) {
-            *reinterpret_cast<bf16x4 *>(pm + static_cast<int64_t>(row) * g.ldp + jj) =
-                *reinterpret_cast<const bf16x4 *>(stg + qq * PS + kk);
-            *reinterpret_cast<bf16x4 *>(gm + static_cast<int64_t>(row) * g.ldp + jj) =
-                *reinterpret_cast<const bf16x4 *>(stg + (QW + qq) * PS + kk);
-          }
-        }
+    for (int x = 0; x < 16; ++x) {
+      const int qq = 8 * (x >> 2) + 4 * hh + (x & 3);
+      sv[x] = sacc[x] + band[qq * BS + r + 31 - qq];
+    }
+    wave_lds_sync();
+
+    // ---- dp[q][key] = dout V^T ----
+    f32x16 dpa;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) dpa[x] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dpa = mfma32(load8(sDo + r * TS + 16 * s + 8 * hh), vreg[s], dpa);
+
+    // ---- p and g; masked pairs (hidden key, future key, query past the end) get 0 ----
+    bf16x8 pb[2], gb[2];
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sLse + 8 * a4 + 4 * hh);
+      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sD + 8 * a4 + 4 * hh);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int x = 4 * a4 + c;
+        const int i = i0 + 8 * a4 + 4 * hh + c;
+        const bool vis = i < L && j >= jv && j < ML && j - M <= i;
+        const float pv = vis ? __builtin_amdgcn_exp2f(sv[x] - l4[c]) : 0.0f;
+        const float gg = scale * pv * (dpa[x] - d4[c]);
+        pb[x >> 3][x & 7] = static_cast<__bf16>(pv);
+        gb[x >> 3][x & 7] = static_cast<__bf16>(gg);
       }
-    } else {
-      const int jj = j0 + lane;
-      if (jj < ML) {
-#pragma unroll 4
-        for (int qq = 0; qq < QW; ++qq) {
-          const int row = iw + qq;
-          if (row < L) {
-            pm[static_cast<int64_t>(row) * g.ldp + jj] = stg[qq * PS + lane];
-            gm[static_cast<int64_t>(row) * g.ldp + jj] = stg[(QW + qq) * PS + lane];
-          }
+    }
+
+    // ---- dV^T += dout^T p, dK^T += (q+u)^T g: k-step s2 covers queries
+    // 16 s2 + {4hh..4hh+3, 8+4hh..8+4hh+3} ----
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int o = (db * 32 + r) * TT + 16 * s2 + 4 * hh;
+        const bf16x4 dlo = *reinterpret_cast<const bf16x4 *>(sDoT + o);
+        const bf16x4 dhi = *reinterpret_cast<const bf16x4 *>(sDoT + o + 8);
+        const bf16x4 ulo = *reinterpret_cast<const bf16x4 *>(sQuT + o);
+        const bf16x4 uhi = *reinterpret_cast<const bf16x4 *>(sQuT + o + 8);
+        bf16x8 ad, au;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ad[e] = dlo[e];
+          ad[e + 4] = dhi[e];
+          au[e] = ulo[e];
+          au[e + 4] = uhi[e];
+        }
+        dv_acc[db] = mfma32(ad, pb[s2], dv_acc[db]);
+        dk_acc[db] = mfma32(au, gb[s2], dk_acc[db]);
+      }
+
+    // ---- g by key and by distance (rows of consecutive keys) ----
+    if (j < ML) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int i = i0 + 8 * (x >> 2) + 4 * hh + (x & 3);
+        if (i < L) {
+          const __bf16 gbv = gb[x >> 3][x & 7];
+          g.gm[(row_bh + i) * g.ldp + j] = gbv;
+          if (j >= jv && j - M <= i) g.pm[(row_bh + i) * g.ldp + (j + L - 1 - i)] = gbv;
         }
       }
     }
 
-    unsigned char *nbuf = smem + ((kt + 1) & 1) * (2 * kLdsT);
-    store_kv(nxt, reinterpret_cast<__bf16 *>(nbuf), reinterpret_cast<__bf16 *>(nbuf + kLdsT), tid);
-    load_kv(nxt, krs, vrs, kv_row_bytes, j0 + 2 * BK, tid);
+    __syncthreads();   // every wave is done with this tile's LDS
+    if (i0 + QT < L) stage();
     __syncthreads();
   }
+
+  // ---- dK, dV rows through LDS (this wave's band area), 16-byte stores ----
+  float *st = band;   // [32 keys][64 + 4 dims]
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int dh = db * 32 + 8 * (x >> 2) + 4 * hh + (x & 3);
+        st[r * (DH + 4) + dh] = pass == 0 ? dk_acc[db][x] : dv_acc[db][x];
+      }
+    wave_lds_sync();
+    float *dst = pass == 0 ? dkp : dvp;
+#pragma unroll
+    for (int it = 0; it < KW * DH / 4 / 64; ++it) {
+      const int e = lane + 64 * it;
+      const int kk = e / (DH / 4), c4 = e - kk * (DH / 4);
+      if (jw + kk < ML)
+        *reinterpret_cast<f32x4 *>(dst + static_cast<int64_t>(jw + kk) * DH + 4 * c4) =
+            *reinterpret_cast<const f32x4 *>(st + kk * (DH + 4) + 4 * c4);
+    }
+    wave_lds_sync();
+  }
+  (void)n_kb;
 }
 
 // ---------------------------------------------------------------------------
@@ -388,6 +411,7 @@ struct BgParams {
   int Z2;
   const int32_t *valid;
   int M, L;
+  int gs;         // kinds 2, 3: A stored by distance, element (i, t) at a + i*lda + t
 };
 
 // 16 consecutive bf16 of a buffer starting at any element offset off0 (zero
@@ -437,7 +461,8 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
   const int z1 = z / q.Z2, z2 = z - z1 * q.Z2;
   const int M = q.M, L = q.L, ML = M + L;
   const bool trans = q.kind == 0 || q.kind == 3;
-  const bool skew = q.kind >= 2;
+  const bool skew = q.kind >= 2;              // indexed by distance: key = t + i - (L-1)
+  const bool unaligned = skew && !q.gs;       // read along g's diagonals
 
   f32x16 acc;
 #pragma unroll
@@ -482,7 +507,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
       const int qi = trans ? k : m, t0 = trans ? m : k;
       const int sh = skew ? qi - (L - 1) : 0;         // key = index + sh
       bf16x8 x[2];
-      if (!skew) {
+      if (!unaligned) {
         x[0] = x[1] = zero8();
         if (qi < L) {
           const __bf16 *src = abase + static_cast<int64_t>(qi) * q.lda + t0;
@@ -619,23 +644,22 @@ size_t rel_attn_bwd_ldp(int M, int L) { return (static_cast<size_t>(M) + L + 7) 
 txl_status launch_rel_attn_bwd(const AttnParams &p, const BwdParams &g, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_pg_kernel),
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_kv_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(kLdsTotal)) != hipSuccess)
-      return fail(TXL_ERR_HIP, "rel_attn_bwd: cannot raise the LDS limit to %zu bytes", kLdsTotal);
+                            static_cast<int>(kKvLdsTotal)) != hipSuccess)
+      return fail(TXL_ERR_HIP, "rel_attn_bwd: cannot raise the LDS limit to %zu bytes", kKvLdsTotal);
     attr_set = true;
   }
   if (p.kv_sl < DH || p.r_sl < DH || p.q_sl < DH || p.o_sl < DH || g.do_sl < DH)
     return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: bf16 row strides must be >= d_h");
   const int64_t ML = static_cast<int64_t>(p.M) + p.L;
-  if ((ML + BK) * p.kv_sl * 2 >= (int64_t(1) << 31) || (ML + BK + QW) * p.r_sl * 2 >= (int64_t(1) << 31))
+  if ((ML + KB2) * p.kv_sl * 2 >= (int64_t(1) << 31) || (ML + 2 * QT) * p.r_sl * 2 >= (int64_t(1) << 31))
     return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: key / R rows span more than 2 GiB per head");
   if ((static_cast<int64_t>(p.L) * g.ldp + 16) * 2 >= (int64_t(1) << 31))
     return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: p / g rows span more than 2 GiB per head");
   const int B = p.B, H = p.H, L = p.L;
   const int64_t BHL = static_cast<int64_t>(B) * H * L;
-  const int n_qt = (L + BQ - 1) / BQ;
-  const int64_t blocks = static_cast<int64_t>(n_qt) * B * H;
+  const int64_t blocks = (ML + KB2 - 1) / KB2 * B * H;
   if (blocks > 0x7fffffffLL || BHL * 8 / 256 + 1 > 0x7fffffffLL)
     return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: grid too large");
   (void)hipGetLastError();
@@ -643,8 +667,10 @@ txl_status launch_rel_attn_bwd(const AttnParams &p, const BwdParams &g, hipStrea
                      p, g);
   txl_status st = check_launch("bwd_prep_kernel");
   if (st != TXL_OK) return st;
-  hipLaunchKernelGGL(bwd_pg_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), kLdsTotal, s, p, g, n_qt);
-  if ((st = check_launch("bwd_pg_kernel")) != TXL_OK) return st;
+  const int n_kb = (static_cast<int>(ML) + KB2 - 1) / KB2;
+  hipLaunchKernelGGL(bwd_kv_kernel, dim3(static_cast<unsigned>(static_cast<int64_t>(n_kb) * B * H)), dim3(256),
+                     kKvLdsTotal, s, p, g, n_kb);
+  if ((st = check_launch("bwd_kv_kernel")) != TXL_OK) return st;
 
   const int ml = static_cast<int>(ML);
   auto run = [&](BgParams q, int z_count) -> txl_status {
@@ -655,22 +681,10 @@ txl_status launch_rel_attn_bwd(const AttnParams &p, const BwdParams &g, hipStrea
     hipLaunchKernelGGL(bgemm_kernel, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, s, q);
     return check_launch("bgemm_kernel");
   };
-  const int64_t pz = static_cast<int64_t>(L) * g.ldp;      // p / g per (b, h)
+  const int64_t pz = static_cast<int64_t>(L) * g.ldp;      // g by key / by distance per (b, h)
   const int n_mt_q = (L + GT - 1) / GT;
 
   BgParams q = {};
-  // dv = p^T dout
-  q.rows = ml; q.K = L; q.K_out = 1; q.kind = 0;
-  q.a = g.pm; q.lda = g.ldp; q.a_s1 = H * pz; q.a_s2 = pz;
-  q.b = g.dout; q.ldb = g.do_sl; q.b_s1 = g.do_sb; q.b_s2 = g.do_sh;
-  q.c = g.dv; q.ldc = DH; q.c_s1 = static_cast<int64_t>(H) * ml * DH; q.c_s2 = static_cast<int64_t>(ml) * DH;
-  q.Z2 = H;
-  if ((st = run(q, B * H)) != TXL_OK) return st;
-  // dk = g^T (q + u)
-  q.a = g.gm;
-  q.b = g.qu; q.ldb = DH; q.b_s1 = static_cast<int64_t>(H) * L * DH; q.b_s2 = static_cast<int64_t>(L) * DH;
-  q.c = g.dk;
-  if ((st = run(q, B * H)) != TXL_OK) return st;
   // dq = g k (content part) ...
   q = BgParams{};
   q.rows = L; q.K = ml; q.K_out = 1; q.kind = 1;
@@ -679,8 +693,9 @@ txl_status launch_rel_attn_bwd(const AttnParams &p, const BwdParams &g, hipStrea
   q.c = g.dq; q.ldc = DH; q.c_s1 = static_cast<int64_t>(H) * L * DH; q.c_s2 = static_cast<int64_t>(L) * DH;
   q.colsum = g.part_u; q.Z2 = H;
   if ((st = run(q, B * H)) != TXL_OK) return st;
-  // ... + g R over the diagonal view (position part)
+  // ... + g R by distance (position part)
   q.kind = 2;
+  q.a = g.pm; q.gs = 1;
   q.b = static_cast<const __bf16 *>(p.r); q.ldb = p.r_sl; q.b_s1 = 0; q.b_s2 = p.r_sh;
   q.accumulate = 1; q.colsum = g.part_v;
   if ((st = run(q, B * H)) != TXL_OK) return st;
@@ -688,7 +703,7 @@ txl_status launch_rel_attn_bwd(const AttnParams &p, const BwdParams &g, hipStrea
   // over batch rows by the reduction below
   q = BgParams{};
   q.rows = ml; q.K = L; q.K_out = 1; q.kind = 3;
-  q.a = g.gm; q.lda = g.ldp; q.a_s1 = H * pz; q.a_s2 = pz;
+  q.a = g.pm; q.gs = 1; q.lda = g.ldp; q.a_s1 = H * pz; q.a_s2 = pz;
   q.b = g.qv; q.ldb = DH; q.b_s1 = static_cast<int64_t>(H) * L * DH; q.b_s2 = static_cast<int64_t>(L) * DH;
   q.c = g.part_r; q.ldc = DH; q.c_s1 = static_cast<int64_t>(H) * ml * DH; q.c_s2 = static_cast<int64_t>(ml) * DH;
   q.Z2 = H;

@@ -49,7 +49,7 @@ struct BwdParams {
   float *dq, *dk, *dv, *dr, *du, *dvb;
   __bf16 *qu, *qv;        // [B*H*L, 64]: q + u, q + v
   float *dd;              // [B*H*L]: dout . out
-  __bf16 *pm, *gm;        // [B*H*L, ldp]: probabilities and score gradients
+  __bf16 *pm, *gm;        // [B*H*L, ldp]: score gradients by distance and by key
   int64_t ldp;
   float *part_u, *part_v; // [B*H][ceil(L/64)][64] column sums of dq's two parts
   float *part_r;          // [B][H][M+L][64] dR of each batch row
