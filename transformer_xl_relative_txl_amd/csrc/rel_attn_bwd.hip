@@ -75,6 +75,11 @@ __device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 __device__ inline u32x4 bload(rsrc_t rs, int byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0));
 }
+// 2-byte store; offsets past the buffer's end are dropped by the range check
+__device__ inline void bstore16(__bf16 v, rsrc_t rs, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), rs, voff, soff, 0);
+}
+constexpr int kDropOffset = 0x40000000;   // past any p / g slice (slices stay below 1 GiB)
 
 // ---------------------------------------------------------------------------
 // D_i = dout_i . out_i (fp32), qu = bf16(q + u), qv = bf16(q + v); one thread
@@ -127,7 +132,7 @@ constexpr int KW = 32;            // keys per wave
 constexpr int KB2 = KW * NW;      // keys per workgroup
 constexpr int QT = 32;            // queries per tile
 constexpr int TS = DH + 8;        // Q' / Q'' / dout tile row stride (bf16)
-constexpr int TT = QT + 8;        // transposed tile row stride (bf16)
+constexpr int TT = QT + 4;        // transposed tile row stride (bf16): 8-byte rows, 4-way at most
 constexpr int BS = 2 * QT + 4;    // band row stride (floats): [query][u], u < 64
 constexpr size_t kKvLdsTile = size_t(QT) * TS * 2;          // one [32][72] bf16 tile
 constexpr size_t kKvLdsTr = size_t(DH) * TT * 2;            // one [64][40] bf16 tile
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams 
     if (tid < QT) {
       const int ii = i0 + tid;
       nlse = ii < L ? g.lse[row_bh + ii] * 1.4426950408889634f : 0.0f;
-      nd = ii < L ? g.dd[row_bh + ii] : 0.0f;
+      nd = ii < L ? g.dd[row_bh + ii] * p.scale : 0.0f;   // scale * D
     }
   };
   auto stage = [&]() {
@@ -235,6 +240,17 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams 
       sD[tid] = nd;
     }
   };
+
+  // g by key: element (i, j) at byte (i*ldp + j)*2 of the (b, h) slice; by
+  // distance: (i, j + L-1-i) at byte (i*(ldp-1) + j + L-1)*2. The lane part of
+  // the offset is in voff, the register's row part (a multiple of the row
+  // stride) in soff; hidden keys and lanes past the end use kDropOffset.
+  const uint32_t slice_bytes = static_cast<uint32_t>(static_cast<int64_t>(L) * g.ldp * 2);
+  const rsrc_t grs = make_rsrc(g.gm + row_bh * g.ldp, slice_bytes);
+  const rsrc_t srs = make_rsrc(g.pm + row_bh * g.ldp, slice_bytes);
+  const int ldp = static_cast<int>(g.ldp);
+  const bool j_ok = j >= jv && j < ML;
+  const bool tile_keys_visible = jw >= jv && jw + KW - 1 < ML;
 
   f32x16 dv_acc[2], dk_acc[2];
 #pragma unroll
@@ -300,8 +316,10 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams 
 #pragma unroll
     for (int s = 0; s < 4; ++s) dpa = mfma32(load8(sDo + r * TS + 16 * s + 8 * hh), vreg[s], dpa);
 
-    // ---- p and g; masked pairs (hidden key, future key, query past the end) get 0 ----
+    // ---- p and g; masked pairs (hidden key, future key, query past the end)
+    // get 0; a tile whose pairs are all visible skips the test ----
     bf16x8 pb[2], gb[2];
+    const bool all_vis = tile_keys_visible && i0 + QT <= L && jw + KW - 1 - M <= i0;
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
       const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sLse + 8 * a4 + 4 * hh);
@@ -310,9 +328,9 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams 
       for (int c = 0; c < 4; ++c) {
         const int x = 4 * a4 + c;
         const int i = i0 + 8 * a4 + 4 * hh + c;
-        const bool vis = i < L && j >= jv && j < ML && j - M <= i;
+        const bool vis = all_vis || (i < L && j_ok && j - M <= i);
         const float pv = vis ? __builtin_amdgcn_exp2f(sv[x] - l4[c]) : 0.0f;
-        const float gg = scale * pv * (dpa[x] - d4[c]);
+        const float gg = pv * (dpa[x] * scale - d4[c]);
         pb[x >> 3][x & 7] = static_cast<__bf16>(pv);
         gb[x >> 3][x & 7] = static_cast<__bf16>(gg);
       }
@@ -341,16 +359,20 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams 
         dk_acc[db] = mfma32(au, gb[s2], dk_acc[db]);
       }
 
-    // ---- g by key and by distance (rows of consecutive keys) ----
-    if (j < ML) {
+    // ---- g by key and by distance (rows of consecutive keys); rows past L
+    // fall outside the slice and are dropped ----
+    {
+      const int ih = i0 + 4 * hh;   // this lane half's first row (+ 8 a4 + c)
+      const int vg = j < ML ? (ih * ldp + j) * 2 : kDropOffset;
+      const int vs = (ih * (ldp - 1) + j + L - 1) * 2;
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        const int i = i0 + 8 * (x >> 2) + 4 * hh + (x & 3);
-        if (i < L) {
-          const __bf16 gbv = gb[x >> 3][x & 7];
-          g.gm[(row_bh + i) * g.ldp + j] = gbv;
-          if (j >= jv && j - M <= i) g.pm[(row_bh + i) * g.ldp + (j + L - 1 - i)] = gbv;
-        }
+        const int rr = 8 * (x >> 2) + (x & 3);   // row offset common to the wave
+        const __bf16 gbv = gb[x >> 3][x & 7];
+        bstore16(gbv, grs, vg, rr * ldp * 2);
+        // (by distance, a row past L can map back into the slice: test it)
+        const bool vis = all_vis || (j_ok && j - M <= ih + rr && ih + rr < L);
+        bstore16(gbv, srs, vis ? vs : kDropOffset, rr * (ldp - 1) * 2);
       }
     }
 
@@ -655,8 +677,8 @@ txl_status launch_rel_attn_bwd(const AttnParams &p, const BwdParams &g, hipStrea
   const int64_t ML = static_cast<int64_t>(p.M) + p.L;
   if ((ML + KB2) * p.kv_sl * 2 >= (int64_t(1) << 31) || (ML + 2 * QT) * p.r_sl * 2 >= (int64_t(1) << 31))
     return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: key / R rows span more than 2 GiB per head");
-  if ((static_cast<int64_t>(p.L) * g.ldp + 16) * 2 >= (int64_t(1) << 31))
-    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: p / g rows span more than 2 GiB per head");
+  if ((static_cast<int64_t>(p.L) * g.ldp + 16) * 2 >= (int64_t(1) << 30))
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: g rows span more than 1 GiB per (batch row, head)");
   const int B = p.B, H = p.H, L = p.L;
   const int64_t BHL = static_cast<int64_t>(B) * H * L;
   const int64_t blocks = (ML + KB2 - 1) / KB2 * B * H;
