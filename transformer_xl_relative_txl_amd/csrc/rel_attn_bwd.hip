@@ -329,7 +329,8 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams 
         const int x = 4 * a4 + c;
         const int i = i0 + 8 * a4 + 4 * hh + c;
         const bool vis = all_vis || (i < L && j_ok && j - M <= i);
-        const float pv = vis ? __builtin_amdgcn_exp2f(sv[x] - l4[c]) : 0.0f;
+        // a select on the argument (2^-inf = 0), not a branch around the exp
+        const float pv = __builtin_amdgcn_exp2f(vis ? sv[x] - l4[c] : -INFINITY);
         const float gg = pv * (dpa[x] * scale - d4[c]);
         pb[x >> 3][x & 7] = static_cast<__bf16>(pv);
         gb[x >> 3][x & 7] = static_cast<__bf16>(gg);
@@ -420,20 +421,25 @@ constexpr int GT = 64;    // output rows per workgroup
 constexpr int GK = 64;    // k per slab
 constexpr int GS = GK + 8;
 
-struct BgParams {
-  int rows, K, K_out, kind;
+// One operand set of a product: C += A B over K, A addressed by kind.
+struct BgPhase {
+  int kind, K;
+  int gs;         // kinds 2, 3: A stored by distance, element (i, t) at a + i*lda + t
   const __bf16 *a;
-  int64_t lda, a_s1, a_s2, a_so;
+  int64_t lda, a_s1, a_s2;
   const __bf16 *b;
-  int64_t ldb, b_s1, b_s2, b_so;
+  int64_t ldb, b_s1, b_s2;
+  float *colsum;  // optional [z][m tile][64]: column sums of this phase's share of C
+};
+// C = sum over phases (one or two, sharing the output rows) of A B.
+struct BgParams {
+  int rows, n_phase;
+  BgPhase ph[2];
   float *c;
   int64_t ldc, c_s1, c_s2;
-  int accumulate;
-  float *colsum;  // optional [z][m tile][64]
   int Z2;
   const int32_t *valid;
   int M, L;
-  int gs;         // kinds 2, 3: A stored by distance, element (i, t) at a + i*lda + t
 };
 
 // 16 consecutive bf16 of a buffer starting at any element offset off0 (zero
@@ -465,7 +471,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
   const int wm = wave & 1, wn = wave >> 1;
   // Workgroups are dealt to the 8 XCDs in turn. When the batch count allows,
   // all row tiles of one z go to the same XCD so that its B operand (the
-  // keys, dout, q+u or q+v of that batch row and head) is fetched into one L2
+  // keys, R or q+v of that batch row and head) is fetched into one L2
   // instead of eight.
   const int n_mt = (q.rows + GT - 1) / GT;
   const int n_z = static_cast<int>(gridDim.x) / n_mt;
@@ -482,41 +488,43 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
   const int m0 = mt * GT;
   const int z1 = z / q.Z2, z2 = z - z1 * q.Z2;
   const int M = q.M, L = q.L, ML = M + L;
-  const bool trans = q.kind == 0 || q.kind == 3;
-  const bool skew = q.kind >= 2;              // indexed by distance: key = t + i - (L-1)
-  const bool unaligned = skew && !q.gs;       // read along g's diagonals
+  int valid = q.valid ? q.valid[z1] : M;
+  valid = valid < 0 ? 0 : (valid > M ? M : valid);
+  const int jv = M - valid;
+  const int m_last = (m0 + GT < q.rows ? m0 + GT : q.rows) - 1;
+  const int n = wn * 32 + r;
 
   f32x16 acc;
 #pragma unroll
   for (int x = 0; x < 16; ++x) acc[x] = 0.0f;
+  float col_before = 0.0f;   // this lane's column sum before the phase
 
-  // Each thread moves 16 consecutive elements of A and of B per slab. Where
-  // the tile is transposed on its way to LDS (A stored k-major, and every B)
-  // the 64 lanes of a wave take 64 consecutive k, so each 2-byte LDS store of
-  // the wave touches every bank once or twice.
-  const int a_mm = trans ? (tid >> 6) * 16 : tid >> 2;  // m offset in the tile
-  const int a_kk = trans ? tid & 63 : (tid & 3) * 16;   // k offset in the slab
-  const int b_kk = tid & 63, b_nc = (tid >> 6) * 16;
   // two register sets: the slab being stored to LDS and the next one, so two
   // slabs' loads are in flight while a slab is multiplied
   bf16x8 ra[2][2], rb[2][2];
 
-  for (int ko = 0; ko < q.K_out; ++ko) {
-    const int bb = q.K_out > 1 ? ko : z1;      // batch row of the A elements
-    int valid = q.valid ? q.valid[bb] : M;
-    valid = valid < 0 ? 0 : (valid > M ? M : valid);
-    const int jv = M - valid;
-    const __bf16 *abase = q.a + (q.K_out > 1 ? ko * q.a_so : z1 * q.a_s1) + z2 * q.a_s2;
-    const __bf16 *bbase = q.b + z1 * q.b_s1 + z2 * q.b_s2 + ko * q.b_so;
-    const rsrc_t ars = make_rsrc(abase, static_cast<uint32_t>(L * q.lda * 2));
-    const int m_last = (m0 + GT < q.rows ? m0 + GT : q.rows) - 1;
-    int k_lo = 0, k_hi = q.K;
-    if (q.kind == 0) {
+  for (int ph = 0; ph < q.n_phase; ++ph) {
+    const BgPhase &P = q.ph[ph];
+    const bool trans = P.kind == 0 || P.kind == 3;
+    const bool skew = P.kind >= 2;              // indexed by distance: key = t + i - (L-1)
+    const bool unaligned = skew && !P.gs;       // read along g's diagonals
+    // Each thread moves 16 consecutive elements of A and of B per slab. Where
+    // the tile is transposed on its way to LDS (A stored k-major, and every B)
+    // the 64 lanes of a wave take 64 consecutive k, so each 2-byte LDS store of
+    // the wave touches every bank once or twice.
+    const int a_mm = trans ? (tid >> 6) * 16 : tid >> 2;  // m offset in the tile
+    const int a_kk = trans ? tid & 63 : (tid & 3) * 16;   // k offset in the slab
+    const int b_kk = tid & 63, b_nc = (tid >> 6) * 16;
+    const __bf16 *abase = P.a + z1 * P.a_s1 + z2 * P.a_s2;
+    const __bf16 *bbase = P.b + z1 * P.b_s1 + z2 * P.b_s2;
+    const rsrc_t ars = make_rsrc(abase, static_cast<uint32_t>(L * P.lda * 2));
+    int k_lo = 0, k_hi = P.K;
+    if (P.kind == 0) {
       k_lo = m0 - M;
       if (m_last < jv) k_hi = 0;
-    } else if (q.kind == 1) {
+    } else if (P.kind == 1) {
       k_lo = jv;
-      k_hi = M + m_last + 1 < q.K ? M + m_last + 1 : q.K;
+      k_hi = M + m_last + 1 < P.K ? M + m_last + 1 : P.K;
     } else {
       k_lo = jv + L - 1 - m_last;
     }
@@ -532,12 +540,12 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
       if (!unaligned) {
         x[0] = x[1] = zero8();
         if (qi < L) {
-          const __bf16 *src = abase + static_cast<int64_t>(qi) * q.lda + t0;
+          const __bf16 *src = abase + static_cast<int64_t>(qi) * P.lda + t0;
           if (t0 < ML) x[0] = load8(src);
           if (t0 + 8 < ML) x[1] = load8(src + 8);
         }
       } else {
-        load16_unaligned(ars, qi * static_cast<int>(q.lda) + t0 + sh, x[0], x[1]);
+        load16_unaligned(ars, qi * static_cast<int>(P.lda) + t0 + sh, x[0], x[1]);
       }
       // visible keys of this query: [jv, M + qi]; indices stay below M + L
       const int k_first = t0 + sh, k_last = t0 + 15 + sh;
@@ -555,9 +563,9 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
           }
       }
       const int kb = k0 + b_kk;
-      const __bf16 *bsrc = bbase + static_cast<int64_t>(kb) * q.ldb + b_nc;
-      rb[set][0] = kb < q.K ? load8(bsrc) : zero8();
-      rb[set][1] = kb < q.K ? load8(bsrc + 8) : zero8();
+      const __bf16 *bsrc = bbase + static_cast<int64_t>(kb) * P.ldb + b_nc;
+      rb[set][0] = kb < P.K ? load8(bsrc) : zero8();
+      rb[set][1] = kb < P.K ? load8(bsrc + 8) : zero8();
     };
     auto store = [&](int set) {
       if (trans) {
@@ -589,30 +597,30 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
 
     if (n_slabs > 0) load(0, k_lo);
     if (n_slabs > 1) load(1, k_lo + GK);
-    for (int s = 0; s < n_slabs; s += 2) {
-      step(0, s);
-      if (s + 1 < n_slabs) step(1, s + 1);
+    for (int s2 = 0; s2 < n_slabs; s2 += 2) {
+      step(0, s2);
+      if (s2 + 1 < n_slabs) step(1, s2 + 1);
+    }
+
+    if (P.colsum) {   // (uniform) this phase's share of the column sums
+      float sum = 0.0f;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) sum += acc[x];  // rows past the end hold zero
+      sum += __shfl_xor(sum, 32);
+      const float share = sum - col_before;
+      col_before = sum;
+      __syncthreads();   // scol of an earlier phase has been read
+      if (hh == 0) scol[wm][n] = share;
+      __syncthreads();
+      if (tid < DH) P.colsum[(static_cast<int64_t>(z) * n_mt + mt) * DH + tid] = scol[0][tid] + scol[1][tid];
     }
   }
 
   float *cp = q.c + z1 * q.c_s1 + z2 * q.c_s2;
-  const int n = wn * 32 + r;
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
     const int m = m0 + wm * 32 + 8 * (x >> 2) + 4 * hh + (x & 3);
-    if (m < q.rows) {
-      float *dst = cp + static_cast<int64_t>(m) * q.ldc + n;
-      *dst = q.accumulate ? *dst + acc[x] : acc[x];
-    }
-  }
-  if (q.colsum) {
-    float s = 0.0f;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) s += acc[x];  // rows past the end hold zero
-    s += __shfl_xor(s, 32);
-    if (hh == 0) scol[wm][n] = s;
-    __syncthreads();
-    if (tid < DH) q.colsum[(static_cast<int64_t>(z) * n_mt + mt) * DH + tid] = scol[0][tid] + scol[1][tid];
+    if (m < q.rows) cp[static_cast<int64_t>(m) * q.ldc + n] = acc[x];
   }
 }
 
@@ -706,27 +714,29 @@ txl_status launch_rel_attn_bwd(const AttnParams &p, const BwdParams &g, hipStrea
   const int64_t pz = static_cast<int64_t>(L) * g.ldp;      // g by key / by distance per (b, h)
   const int n_mt_q = (L + GT - 1) / GT;
 
+  // dq = g K over keys, then + g R over distances, in one accumulator; the
+  // column sums of the two shares give du and dv_bias
   BgParams q = {};
-  // dq = g k (content part) ...
-  q = BgParams{};
-  q.rows = L; q.K = ml; q.K_out = 1; q.kind = 1;
-  q.a = g.gm; q.lda = g.ldp; q.a_s1 = H * pz; q.a_s2 = pz;
-  q.b = static_cast<const __bf16 *>(p.k); q.ldb = p.kv_sl; q.b_s1 = p.kv_sb; q.b_s2 = p.kv_sh;
+  q.rows = L; q.n_phase = 2;
+  q.ph[0].kind = 1; q.ph[0].K = ml;
+  q.ph[0].a = g.gm; q.ph[0].lda = g.ldp; q.ph[0].a_s1 = H * pz; q.ph[0].a_s2 = pz;
+  q.ph[0].b = static_cast<const __bf16 *>(p.k); q.ph[0].ldb = p.kv_sl; q.ph[0].b_s1 = p.kv_sb;
+  q.ph[0].b_s2 = p.kv_sh; q.ph[0].colsum = g.part_u;
+  q.ph[1].kind = 2; q.ph[1].K = ml; q.ph[1].gs = 1;
+  q.ph[1].a = g.pm; q.ph[1].lda = g.ldp; q.ph[1].a_s1 = H * pz; q.ph[1].a_s2 = pz;
+  q.ph[1].b = static_cast<const __bf16 *>(p.r); q.ph[1].ldb = p.r_sl; q.ph[1].b_s1 = 0;
+  q.ph[1].b_s2 = p.r_sh; q.ph[1].colsum = g.part_v;
   q.c = g.dq; q.ldc = DH; q.c_s1 = static_cast<int64_t>(H) * L * DH; q.c_s2 = static_cast<int64_t>(L) * DH;
-  q.colsum = g.part_u; q.Z2 = H;
+  q.Z2 = H;
   if ((st = run(q, B * H)) != TXL_OK) return st;
-  // ... + g R by distance (position part)
-  q.kind = 2;
-  q.a = g.pm; q.gs = 1;
-  q.b = static_cast<const __bf16 *>(p.r); q.ldb = p.r_sl; q.b_s1 = 0; q.b_s2 = p.r_sh;
-  q.accumulate = 1; q.colsum = g.part_v;
-  if ((st = run(q, B * H)) != TXL_OK) return st;
-  // dR per batch row = sum over queries of g (q + v), diagonal view; summed
-  // over batch rows by the reduction below
+  // dR per batch row = sum over queries of g (q + v), by distance; summed over
+  // batch rows by the reduction below
   q = BgParams{};
-  q.rows = ml; q.K = L; q.K_out = 1; q.kind = 3;
-  q.a = g.pm; q.gs = 1; q.lda = g.ldp; q.a_s1 = H * pz; q.a_s2 = pz;
-  q.b = g.qv; q.ldb = DH; q.b_s1 = static_cast<int64_t>(H) * L * DH; q.b_s2 = static_cast<int64_t>(L) * DH;
+  q.rows = ml; q.n_phase = 1;
+  q.ph[0].kind = 3; q.ph[0].K = L; q.ph[0].gs = 1;
+  q.ph[0].a = g.pm; q.ph[0].lda = g.ldp; q.ph[0].a_s1 = H * pz; q.ph[0].a_s2 = pz;
+  q.ph[0].b = g.qv; q.ph[0].ldb = DH; q.ph[0].b_s1 = static_cast<int64_t>(H) * L * DH;
+  q.ph[0].b_s2 = static_cast<int64_t>(L) * DH;
   q.c = g.part_r; q.ldc = DH; q.c_s1 = static_cast<int64_t>(H) * ml * DH; q.c_s2 = static_cast<int64_t>(ml) * DH;
   q.Z2 = H;
   if ((st = run(q, B * H)) != TXL_OK) return st;
