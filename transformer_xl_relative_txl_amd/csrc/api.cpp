@@ -178,7 +178,7 @@ TXL_API txl_status txl_rel_attn_fwd_split(const txl_rel_attn_args *a, int32_t kv
 // ---------------------------------------------------------------------------
 // Workspace of txl_rel_attn_bwd: byte offsets of its pieces, each 256-byte aligned.
 struct BwdLayout {
-  size_t qu, qv, dd, pm, gm, pu, pv, pr, total;
+  size_t qv, dd, pm, gm, pu, pv, pr, total;
   int64_t ldp;
 };
 static BwdLayout bwd_layout(int32_t B, int32_t H, int32_t L, int32_t M) {
@@ -187,7 +187,6 @@ static BwdLayout bwd_layout(int32_t B, int32_t H, int32_t L, int32_t M) {
   w.ldp = static_cast<int64_t>(rel_attn_bwd_ldp(M, L));
   const size_t n_mt = (static_cast<size_t>(L) + 63) / 64;
   size_t off = 0;
-  w.qu = off; off += align256(bhl * 64 * 2);
   w.qv = off; off += align256(bhl * 64 * 2);
   w.dd = off; off += align256(bhl * 4);
   w.pm = off; off += align256(bhl * static_cast<size_t>(w.ldp) * 2);
@@ -242,7 +241,6 @@ TXL_API txl_status txl_rel_attn_bwd(const txl_rel_attn_args *a, const txl_rel_at
   g.do_sb = gr->do_sb; g.do_sh = gr->do_sh; g.do_sl = gr->do_sl;
   g.lse = a->lse;
   g.dq = gr->dq; g.dk = gr->dk; g.dv = gr->dv; g.dr = gr->dr; g.du = gr->du; g.dvb = gr->dvb;
-  g.qu = reinterpret_cast<__bf16 *>(base + w.qu);
   g.qv = reinterpret_cast<__bf16 *>(base + w.qv);
   g.dd = reinterpret_cast<float *>(base + w.dd);
   g.pm = reinterpret_cast<__bf16 *>(base + w.pm);

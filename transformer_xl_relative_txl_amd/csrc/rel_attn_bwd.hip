@@ -16,7 +16,7 @@
 // projections of it still receive gradient.
 //
 // Design:
-//  * bwd_prep: D_i, and (q+u), (q+v) rounded to bf16 once.
+//  * bwd_prep: D_i, and (q+v) rounded to bf16 for the dR product.
 //  * bwd_kv: key-major. A workgroup holds 128 keys of one (batch, head); each
 //    wave keeps its 32 K and V rows and its dK, dV accumulators in registers
 //    while query tiles of 32 stream through LDS. Per tile it recomputes the
@@ -82,8 +82,8 @@ __device__ inline void bstore16(__bf16 v, rsrc_t rs, int voff, int soff) {
 constexpr int kDropOffset = 0x40000000;   // past any p / g slice (slices stay below 1 GiB)
 
 // ---------------------------------------------------------------------------
-// D_i = dout_i . out_i (fp32), qu = bf16(q + u), qv = bf16(q + v); one thread
-// per query row and 8 dimensions.
+// D_i = dout_i . out_i (fp32) and qv = bf16(q + v) (the dR product's operand);
+// one thread per query row and 8 dimensions.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnParams p, BwdParams g) {
   const int64_t BHL = static_cast<int64_t>(p.B) * p.H * p.L;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -98,17 +98,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnParams p, BwdParams g
     const __bf16 *op = static_cast<const __bf16 *>(p.out) + b * p.o_sb + h * p.o_sh + i * p.o_sl + 8 * c;
     const __bf16 *dp = g.dout + b * g.do_sb + h * g.do_sh + i * g.do_sl + 8 * c;
     const bf16x8 qv = load8(qp), ov = load8(op), dv = load8(dp);
-    const bf16x8 uv = load8(static_cast<const __bf16 *>(p.u) + h * DH + 8 * c);
     const bf16x8 vv = load8(static_cast<const __bf16 *>(p.vb) + h * DH + 8 * c);
-    bf16x8 a, bq;
+    bf16x8 bq;
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      const float qf = static_cast<float>(qv[x]);
-      a[x] = static_cast<__bf16>(qf + static_cast<float>(uv[x]));
-      bq[x] = static_cast<__bf16>(qf + static_cast<float>(vv[x]));
+      bq[x] = static_cast<__bf16>(static_cast<float>(qv[x]) + static_cast<float>(vv[x]));
       acc += static_cast<float>(dv[x]) * static_cast<float>(ov[x]);
     }
-    *reinterpret_cast<bf16x8 *>(g.qu + row * DH + 8 * c) = a;
     *reinterpret_cast<bf16x8 *>(g.qv + row * DH + 8 * c) = bq;
   }
   acc += __shfl_xor(acc, 1);

@@ -47,7 +47,7 @@ struct BwdParams {
   int64_t do_sb, do_sh, do_sl;
   const float *lse;
   float *dq, *dk, *dv, *dr, *du, *dvb;
-  __bf16 *qu, *qv;        // [B*H*L, 64]: q + u, q + v
+  __bf16 *qv;             // [B*H*L, 64]: q + v
   float *dd;              // [B*H*L]: dout . out
   __bf16 *pm, *gm;        // [B*H*L, ldp]: score gradients by distance and by key
   int64_t ldp;
