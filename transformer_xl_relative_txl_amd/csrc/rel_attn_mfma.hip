@@ -27,14 +27,25 @@
 //  * K and V^T tiles are staged in LDS by the whole workgroup and
 //    double-buffered (one barrier per tile); R rows go straight from L2 into
 //    the A operand, one tile ahead.
-//  * Online softmax in base 2 (scale folded into Q' and Q''), row max over
-//    the lane's registers plus one exchange with lane^32, row sums kept per
-//    lane and combined once at the end.
+//  * The shifted position term is read from LDS straight into the score
+//    accumulator, and the content MFMA K (Q')^T accumulates onto it, so the
+//    two terms are summed by the matrix unit, not by VALU adds.
+//  * Masking: band row u of a half is one distance for every query of the
+//    wave, and the rows of negative distance (key after query) are exactly
+//    the rows past a wave-uniform limit; on tiles that cross the diagonal
+//    those rows are overwritten with -inf in LDS before the diagonal read,
+//    so masked scores are -inf with no per-element compare.
+//  * Online softmax in base 2 (scale folded into Q' and Q''). The running
+//    max m is kept as long as every p = 2^(s - m) of a tile stays <= 2^8,
+//    which is checked once per tile through each lane's sum of p (the sum
+//    exceeds 2^8 whenever one p does); only then, and on the first tile, is
+//    the row max taken (lane registers plus one exchange with lane^32) and
+//    O, l rescaled. The row sum adds the fp32 p (the log-sum-exp handed to
+//    the gradients keeps fp32 accuracy); PV uses p rounded to bf16.
 //  * Key tiles run from the row's first valid memory slot to the diagonal;
-//    fully masked tiles are never visited, and only tiles that cross the
-//    diagonal evaluate the mask. Query tiles are scheduled heaviest first
-//    and the (batch, head) index varies fastest, so the tiles of one head
-//    land on the same XCD and share its L2.
+//    fully masked tiles are never visited. Query tiles are scheduled
+//    heaviest first and the (batch, head) index varies fastest, so the
+//    tiles of one head land on the same XCD and share its L2.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -59,7 +70,7 @@ constexpr int KS = DH + 8;     // K tile row stride (bf16 elements)
 constexpr int VS = BK + 8;     // V^T tile row stride (bf16 elements)
 constexpr int NU = 2 * QW;     // band rows held at once: one 32-key half needs u = c + 31 - r in [0, 63)
 constexpr int US = QW + 2;     // band row stride (floats); odd multiple of 2 -> conflict-free skew
-constexpr float kLazyMax = 8.0f;  // keep the running max until a tile beats it by 2^8
+constexpr float kPsumLimit = 256.0f;  // a tile keeps the running max while each lane's sum of p stays <= 2^8
 
 constexpr size_t kLdsK = size_t(BK) * KS * 2;   // one K tile
 constexpr size_t kLdsV = size_t(DH) * VS * 2;   // one V^T tile
@@ -265,19 +276,6 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
     const __bf16 *svt = reinterpret_cast<const __bf16 *>(buf + kLdsK);
 
     {
-      // ---- content scores S^T[key][query] = K (Q')^T ----
-      f32x16 s_acc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int x = 0; x < 16; ++x) s_acc[kb][x] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 a = load8(sk + (kb * 32 + r) * KS + 16 * s + 8 * hh);
-          s_acc[kb] = mfma32(a, qa[s], s_acc[kb]);
-        }
-      }
-
       // ---- position band P[u][query] = R[t(u)] (Q'')^T, three blocks of 32 rows ----
       f32x16 b_acc[3];
       b_acc[0] = b_carry;
@@ -292,10 +290,17 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
       // next tile's R rows into the registers just consumed
       load_r(j0 + BK);
 
+      // Band row u of half kb is distance M - j0 - 32kb - u + 31 + iw, so the
+      // rows past the diagonal (negative distance, key after query) are the
+      // rows u > ul, the same for every query of the wave.
+      const int ul0 = M - j0 + 31 + iw;
+
+      // ---- scores S^T[key][query]: the accumulator starts from the shifted
+      // position term and the content MFMA K (Q')^T adds onto it ----
       // register 4a+c' of block bb holds band row u = 32bb + 8a + 4hh + c'. The
       // 32-key half kb needs rows u = c + 31 - r in [32kb, 32kb + 63): blocks kb
       // and kb+1, stored as rows 0..63 so both halves read the same addresses.
-      float sv[2][16];
+      f32x16 s_acc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -305,54 +310,73 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc)
               band_w[(32 * half + 8 * a4 + cc) * US] = b_acc[kb + half][4 * a4 + cc];
+        const int ul = ul0 - 32 * kb;
+        if (ul < NU - 1) {
+          // rows ul+1 .. 63 become -inf (masked keys get weight exactly 0);
+          // rounding the start down to 4 floats only touches the padding
+          // columns of row ul (US = 34 is 2 mod 4)
+          const int start = ((ul + 1 > 0 ? ul + 1 : 0) * US) & ~3;
+          const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+          for (int f = start + 4 * lane; f < NU * US; f += 256)
+            *reinterpret_cast<f32x4 *>(band + f) = ninf;
+        }
         wave_lds_sync();
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int c = 8 * (x >> 2) + (x & 3);  // key within the half (+ 4hh folded into band_r)
-          sv[kb][x] = s_acc[kb][x] + band_r[c * US];
+          s_acc[kb][x] = band_r[c * US];
         }
         wave_lds_sync();  // reads done before the next half overwrites the rows
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 a = load8(sk + (kb * 32 + r) * KS + 16 * s + 8 * hh);
+          s_acc[kb] = mfma32(a, qa[s], s_acc[kb]);
+        }
       }
 
-      // ---- mask: only tiles that reach past the wave's first query ----
-      if (j0 + BK - 1 - M > iw) {
+      // ---- online softmax in base 2 ----
+      // p = 2^(s - m) with the running max m kept while every p of the tile
+      // stays at most 2^8 (checked through the lane's sum of p, which exceeds
+      // 2^8 whenever one p does); otherwise, and on the first tile, m moves to
+      // the row's maximum so far and O, l are rescaled.
+      bf16x8 pb[2][2];
+      float psum;
+      auto exp_tile = [&]() {
+        psum = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int x = 0; x < 16; ++x) {
-            const int jj = j0 + kb * 32 + 8 * (x >> 2) + 4 * hh + (x & 3);
-            if (jj - M > i) sv[kb][x] = -INFINITY;
-          }
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float pv = __builtin_amdgcn_exp2f(s_acc[kb][8 * s2 + e] - m_run);
+              psum += pv;
+              pb[kb][s2][e] = static_cast<__bf16>(pv);
+            }
+      };
+      bool rescale = kt == 0;
+      if (!rescale) {
+        exp_tile();
+        rescale = __builtin_amdgcn_ballot_w64(psum > kPsumLimit) != 0;
       }
-
-      // ---- online softmax (the running max moves only when beaten by 2^8) ----
-      float mt = -INFINITY;
+      if (rescale) {
+        float mt = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) mt = fmaxf(mt, sv[kb][x]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      if (mt > m_run + kLazyMax) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
-        m_run = mt;
-        l_run *= alpha;
+          for (int x = 0; x < 16; ++x) mt = fmaxf(mt, s_acc[kb][x]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        if (mt > m_run) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
+          m_run = mt;
+          l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+          for (int db = 0; db < 2; ++db)
 #pragma unroll
-          for (int x = 0; x < 16; ++x) o_acc[db][x] *= alpha;
+            for (int x = 0; x < 16; ++x) o_acc[db][x] *= alpha;
+        }
+        exp_tile();
       }
-      float psum = 0.0f;
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pv = __builtin_amdgcn_exp2f(sv[kb][8 * s2 + e] - m_run);
-            psum += pv;
-            pb[kb][s2][e] = static_cast<__bf16>(pv);
-          }
       l_run += psum;
 
       // ---- O^T[d][query] += V^T P^T: k-step (kb, s2) covers keys kb*32 + 16 s2 + {4hh..4hh+3, 8+4hh..8+4hh+3} ----
@@ -374,7 +398,6 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
             o_acc[db] = mfma32(a, pb[kb][s2], o_acc[db]);
           }
     }
-
     // stage tile kt+1 into the other buffer (its last readers finished before
     // the previous barrier) and start loading tile kt+2
     unsigned char *nbuf = smem + ((kt + 1) & 1) * (kLdsK + kLdsV);
