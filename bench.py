@@ -36,8 +36,8 @@ N_RING_SETS = 16
 # HBM bytes per attention launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # (scaled by the same counters' reading of a plain copy of known size),
 # valid only for the kernel source they were taken on.
-ATTN_TRAFFIC = {"source_sha1": "4b4e76ef1317cf08804e9ec415156e3a328d5e9c",
-                "bytes": 52.62e6}
+ATTN_TRAFFIC = {"source_sha1": "dad0cbaa8ccded431b220dddbc343dbcbc9ebbf1",
+                "bytes": 52.44e6}
 
 
 def attn_flops(B, H, L, M_eff, d_h):
@@ -285,8 +285,8 @@ def bwd_bench(steps: int, warmup: int) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle CPU baseline (0 skips it)")
     ap.add_argument("--stack", choices=["16layer_d512", "18layer_d1024"], default=None,
@@ -351,7 +351,7 @@ def main() -> int:
     def mem(i):
         txl.txl_mem_update([rings[i % N_RING_SETS]], [segs[i % N_RING_SETS]])
 
-    for i in range(args.warmup):
+    for i in range(2):  # first touch of every buffer
         attn()
         mem(i)
     torch.cuda.synchronize()
@@ -388,6 +388,17 @@ def main() -> int:
 
     for i in range(2):
         mem_multi(i)
+    # W untimed warmup steps, replayed from a graph so the GPU runs them
+    # back to back (its clocks settle before the timed region)
+    if args.warmup > 0:
+        g_warm = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_warm):
+            for i in range(args.warmup):
+                attn()
+                mem(i)
+        g_warm.replay()
+        torch.cuda.synchronize()
+        del g_warm
     g_step = capture(lambda i: (attn(), mem(i)))
     g_attn = capture(lambda i: attn())
     g_mem = capture(lambda i: mem(i))
