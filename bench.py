@@ -36,8 +36,8 @@ N_RING_SETS = 16
 # HBM bytes per attention launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # (scaled by the same counters' reading of a plain copy of known size),
 # valid only for the kernel source they were taken on.
-ATTN_TRAFFIC = {"source_sha1": "dad0cbaa8ccded431b220dddbc343dbcbc9ebbf1",
-                "bytes": 52.44e6}
+ATTN_TRAFFIC = {"source_sha1": "805f111906c066d6db017843a46e0827310f9248",
+                "bytes": 52.43e6}
 
 
 def attn_flops(B, H, L, M_eff, d_h):
@@ -286,7 +286,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle CPU baseline (0 skips it)")
     ap.add_argument("--stack", choices=["16layer_d512", "18layer_d1024"], default=None,

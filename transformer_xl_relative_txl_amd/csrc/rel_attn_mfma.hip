@@ -21,12 +21,15 @@
 //    new blocks (two 32-row R loads, 8 MFMAs).
 //  * The per-query diagonal read of the band (the relative shift, [P1]
 //    "Relative Shift Trick" replaced by index arithmetic) goes through a
-//    per-wave LDS band stored [u][query] with a row stride of 34 floats, 64
-//    rows (one 32-key half of the tile at a time): lane r reads row
-//    c + 31 - r for key c, which is conflict-free.
-//  * K and V^T tiles are staged in LDS by the whole workgroup and
-//    double-buffered (one barrier per tile); R rows go straight from L2 into
-//    the A operand, one tile ahead.
+//    per-wave LDS band stored [u][query] with a row stride of 34 floats and
+//    all 96 rows of the tile's three blocks (written once per tile, read by
+//    both 32-key halves): lane r reads row c + 31 - r (+32 for the second
+//    half) for key c, which is conflict-free.
+//  * K and V^T tiles are staged in LDS by the whole workgroup in a single
+//    buffer (a barrier before and after each refill; the next tile's K / V
+//    sit in registers meanwhile), which leaves room for the 96-row bands at
+//    two workgroups per CU; R rows go straight from L2 into the A operand,
+//    one tile ahead.
 //  * The shifted position term is read from LDS straight into the score
 //    accumulator, and the content MFMA K (Q')^T accumulates onto it, so the
 //    two terms are summed by the matrix unit, not by VALU adds.
@@ -68,14 +71,14 @@ constexpr int BQ = QW * NW;    // queries per workgroup
 constexpr int BK = 64;         // keys per tile
 constexpr int KS = DH + 8;     // K tile row stride (bf16 elements)
 constexpr int VS = BK + 8;     // V^T tile row stride (bf16 elements)
-constexpr int NU = 2 * QW;     // band rows held at once: one 32-key half needs u = c + 31 - r in [0, 63)
+constexpr int NU = 3 * QW;     // band rows of a tile: key c of half kb reads u = c + 31 - r + 32kb < 95
 constexpr int US = QW + 2;     // band row stride (floats); odd multiple of 2 -> conflict-free skew
 constexpr float kPsumLimit = 256.0f;  // a tile keeps the running max while each lane's sum of p stays <= 2^8
 
 constexpr size_t kLdsK = size_t(BK) * KS * 2;   // one K tile
 constexpr size_t kLdsV = size_t(DH) * VS * 2;   // one V^T tile
 constexpr size_t kLdsBand = size_t(NW) * NU * US * 4;
-constexpr size_t kLdsTotal = 2 * (kLdsK + kLdsV) + kLdsBand;  // K / V^T double-buffered
+constexpr size_t kLdsTotal = (kLdsK + kLdsV) + kLdsBand;  // 70656 bytes: two workgroups per CU
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -151,7 +154,7 @@ __device__ inline void store_kv(const KVRegs &x, __bf16 *sk, __bf16 *svt, int ti
 __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int n_qt) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // buffer p holds K at smem + p*(kLdsK + kLdsV), V^T right after it
-  float *sband = reinterpret_cast<float *>(smem + 2 * (kLdsK + kLdsV));
+  float *sband = reinterpret_cast<float *>(smem + (kLdsK + kLdsV));
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -271,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
     // can count outstanding loads): a tile past a wave's diagonal is fully
     // masked and leaves (m, l, O) unchanged, and the wave would otherwise wait
     // at the barrier.
-    unsigned char *buf = smem + (kt & 1) * (kLdsK + kLdsV);
+    unsigned char *buf = smem;
     const __bf16 *sk = reinterpret_cast<const __bf16 *>(buf);
     const __bf16 *svt = reinterpret_cast<const __bf16 *>(buf + kLdsK);
 
@@ -297,42 +300,40 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
 
       // ---- scores S^T[key][query]: the accumulator starts from the shifted
       // position term and the content MFMA K (Q')^T adds onto it ----
-      // register 4a+c' of block bb holds band row u = 32bb + 8a + 4hh + c'. The
-      // 32-key half kb needs rows u = c + 31 - r in [32kb, 32kb + 63): blocks kb
-      // and kb+1, stored as rows 0..63 so both halves read the same addresses.
+      // register 4a+c' of block bb holds band row u = 32bb + 8a + 4hh + c'; the
+      // three blocks go to rows 0..95 once, and the 32-key half kb reads rows
+      // u = c + 31 - r + 32kb. Rows past the diagonal become -inf (masked keys
+      // get weight exactly 0); rounding the fill's start down to 4 floats only
+      // touches the padding columns of row ul0 (US = 34 is 2 mod 4).
       f32x16 s_acc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int bb = 0; bb < 3; ++bb)
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
+        for (int a4 = 0; a4 < 4; ++a4)
 #pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4)
+          for (int cc = 0; cc < 4; ++cc)
+            band_w[(32 * bb + 8 * a4 + cc) * US] = b_acc[bb][4 * a4 + cc];
+      if (ul0 < NU - 1) {
+        const int start = ((ul0 + 1 > 0 ? ul0 + 1 : 0) * US) & ~3;
+        const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        for (int f = start + 4 * lane; f < NU * US; f += 256)
+          *reinterpret_cast<f32x4 *>(band + f) = ninf;
+      }
+      wave_lds_sync();
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc)
-              band_w[(32 * half + 8 * a4 + cc) * US] = b_acc[kb + half][4 * a4 + cc];
-        const int ul = ul0 - 32 * kb;
-        if (ul < NU - 1) {
-          // rows ul+1 .. 63 become -inf (masked keys get weight exactly 0);
-          // rounding the start down to 4 floats only touches the padding
-          // columns of row ul (US = 34 is 2 mod 4)
-          const int start = ((ul + 1 > 0 ? ul + 1 : 0) * US) & ~3;
-          const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-          for (int f = start + 4 * lane; f < NU * US; f += 256)
-            *reinterpret_cast<f32x4 *>(band + f) = ninf;
-        }
-        wave_lds_sync();
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-          const int c = 8 * (x >> 2) + (x & 3);  // key within the half (+ 4hh folded into band_r)
-          s_acc[kb][x] = band_r[c * US];
+          const int c = 8 * (x >> 2) + (x & 3);
+          s_acc[kb][x] = band_r[(c + 32 * kb) * US];
         }
-        wave_lds_sync();  // reads done before the next half overwrites the rows
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const bf16x8 a = load8(sk + (kb * 32 + r) * KS + 16 * s + 8 * hh);
           s_acc[kb] = mfma32(a, qa[s], s_acc[kb]);
         }
-      }
 
       // ---- online softmax in base 2 ----
       // p = 2^(s - m) with the running max m kept while every p of the tile
@@ -398,10 +399,10 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
             o_acc[db] = mfma32(a, pb[kb][s2], o_acc[db]);
           }
     }
-    // stage tile kt+1 into the other buffer (its last readers finished before
-    // the previous barrier) and start loading tile kt+2
-    unsigned char *nbuf = smem + ((kt + 1) & 1) * (kLdsK + kLdsV);
-    store_kv(nxt, reinterpret_cast<__bf16 *>(nbuf), reinterpret_cast<__bf16 *>(nbuf + kLdsK), tid);
+    // refill the K / V^T buffer with tile kt+1 once every wave has finished
+    // reading tile kt, and start loading tile kt+2
+    __syncthreads();
+    store_kv(nxt, reinterpret_cast<__bf16 *>(smem), reinterpret_cast<__bf16 *>(smem + kLdsK), tid);
     load_kv(nxt, krs, vrs, kv_row_bytes, j0 + 2 * BK, tid);
     __syncthreads();
   }
