@@ -98,6 +98,8 @@ def test_bf16_large_layer_full_size_sampled():
     (2, 1, 257, 300, "mixed"),  # M > L, several tiles, partial last
     (1, 2, 65, 1, "full"),
     (2, 2, 130, 640, "mixed"),  # long memory (M = 5L)
+    (2, 2, 600, 50, "mixed"),   # five query tiles (odd count, ragged last)
+    (1, 1, 1000, 24, "full"),   # eight query tiles
 ])
 def test_ragged_shapes(dtype, B, H, L, M, mode):
     cfg = txl_synth.ATTN_CONFIGS["4x12_f32" if dtype == "f32" else "B4_H8_L128_M128"]
