@@ -108,6 +108,31 @@ __global__ __launch_bounds__(kThreads) void mem_update_rows_kernel(RingBatch rb,
   }
 }
 
+// The same update for a single ring with its pointers passed directly: the
+// pointer tables of the batched launch are a 1 KiB kernel argument, which a
+// lone ring of a few MB pays for measurably.
+__global__ __launch_bounds__(kThreads) void mem_update_one_kernel(u32x4 *__restrict__ data,
+                                                                  const u32x4 *__restrict__ h,
+                                                                  int32_t *__restrict__ valid,
+                                                                  int64_t head, RingMeta mt) {
+  const uint32_t e = blockIdx.x * kThreads + threadIdx.x;
+  if (e >= mt.total) return;
+  const uint32_t row = fdiv(e, mt.div_cpr);  // (b, k) flattened
+  const uint32_t c = e - row * mt.cpr;
+  const uint32_t b = fdiv(row, mt.div_lp);
+  const uint32_t k = row - b * mt.Lp;
+  const int64_t src_row = static_cast<int64_t>(b) * mt.L + (mt.L - mt.Lp + k);
+  int64_t slot = head + k;
+  if (slot >= mt.M) slot -= mt.M;
+  const int64_t dst_row = static_cast<int64_t>(b) * mt.M + slot;
+  __builtin_nontemporal_store(__builtin_nontemporal_load(h + src_row * mt.cpr + c),
+                              data + dst_row * mt.cpr + c);
+  if (k == 0 && c == 0) {
+    const int nv = valid[b] + mt.L;
+    valid[b] = nv < mt.M ? nv : mt.M;
+  }
+}
+
 struct ValidPtrs {
   int32_t *p[kMaxRingsPerLaunch];
 };
@@ -196,7 +221,11 @@ txl_status launch_mem_update(const RingBatch &rb, int n, int B, int M, int L,
   const unsigned blocks = static_cast<unsigned>((total + per_block - 1) / per_block);
   const uint32_t n_rows = static_cast<uint32_t>(total / cpr);
   (void)hipGetLastError();
-  if (cpr == 64)
+  if (n == 1)
+    hipLaunchKernelGGL(mem_update_one_kernel, dim3(blocks), dim3(kThreads), 0, s,
+                       static_cast<u32x4 *>(rb.data[0]), static_cast<const u32x4 *>(rb.h[0]),
+                       rb.valid[0], rb.head[0], mt);
+  else if (cpr == 64)
     hipLaunchKernelGGL(mem_update_rows_kernel<1>, dim3(blocks), dim3(kThreads), 0, s, rb, mt, n_rows);
   else if (cpr == 128)
     hipLaunchKernelGGL(mem_update_rows_kernel<2>, dim3(blocks), dim3(kThreads), 0, s, rb, mt, n_rows);
