@@ -36,8 +36,8 @@ N_RING_SETS = 16
 # HBM bytes per attention launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # (scaled by the same counters' reading of a plain copy of known size),
 # valid only for the kernel source they were taken on.
-ATTN_TRAFFIC = {"source_sha1": "e465d941d70d063676ec82c1b39576dd5f0243b9",
-                "bytes": 52.42e6}
+ATTN_TRAFFIC = {"source_sha1": "15d0b996c33a468aaf3d1257f86fde780f9bc68f",
+                "bytes": 52.43e6}
 
 
 def attn_flops(B, H, L, M_eff, d_h):

@@ -33,7 +33,7 @@
 //  * The shifted position term is read from LDS straight into the score
 //    accumulator, and the content MFMA K (Q')^T accumulates onto it, so the
 //    two terms are summed by the matrix unit, not by VALU adds.
-//  * Masking: band row u of a half is one distance for every query of the
+//  * Masking: band row u of a tile is one distance for every query of the
 //    wave, and the rows of negative distance (key after query) are exactly
 //    the rows past a wave-uniform limit; on tiles that cross the diagonal
 //    those rows are overwritten with -inf in LDS before the diagonal read,
@@ -45,10 +45,12 @@
 //    the row max taken (lane registers plus one exchange with lane^32) and
 //    O, l rescaled. The row sum adds the fp32 p (the log-sum-exp handed to
 //    the gradients keeps fp32 accuracy); PV uses p rounded to bf16.
-//  * Key tiles run from the row's first valid memory slot to the diagonal;
-//    fully masked tiles are never visited. Query tiles are scheduled
-//    heaviest first and the (batch, head) index varies fastest, so the
-//    tiles of one head land on the same XCD and share its L2.
+//  * Key tiles run from the row's first valid memory slot to the
+//    workgroup's diagonal. Query tiles are dealt heavier half first
+//    (heaviest first), then the lighter half lightest first, so that a CU's
+//    two resident workgroups pair a heavy tile with a light one; the
+//    (batch, head) index varies fastest, so the tiles of one head land on
+//    the same XCD and share its L2.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -153,7 +155,7 @@ __device__ inline void store_kv(const KVRegs &x, __bf16 *sk, __bf16 *svt, int ti
 
 __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int n_qt) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  // buffer p holds K at smem + p*(kLdsK + kLdsV), V^T right after it
+  // the K tile at smem, the V^T tile right after it, then the waves' bands
   float *sband = reinterpret_cast<float *>(smem + (kLdsK + kLdsV));
 
   const int tid = threadIdx.x;
