@@ -33,13 +33,13 @@ def _check_rows(mem, ref_rows):
         assert np.array_equal(got, ref), b
 
 
+@pytest.mark.parametrize("n_rings", [1, 3])   # one ring takes its own kernel
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("B,M,L,d", [(1, 8, 4, 64), (3, 5, 2, 16), (2, 6, 6, 32),
                                       (2, 4, 7, 64), (8, 512, 512, 1024), (4, 640, 128, 64)])
-def test_ring_matches_tail(dtype, B, M, L, d):
-    say(f"ring B{B} M{M} L{L} d{d} {dtype}")
+def test_ring_matches_tail(dtype, B, M, L, d, n_rings):
+    say(f"ring B{B} M{M} L{L} d{d} {dtype} rings {n_rings}")
     g = torch.Generator().manual_seed(B * 100 + M + L)
-    n_rings = 3
     mems = [txl.TxlMem.empty(B, M, d, dtype=dtype) for _ in range(n_rings)]
     ref = [[np.zeros((0, d)) for _ in range(B)] for _ in range(n_rings)]
     for s in range(5):
