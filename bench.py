@@ -6,9 +6,12 @@ layer's FIFO memory update, bf16, B=8, H=16, d_h=64 (d=1024), segment L=512,
 memory M=512 fully valid. Inputs are seeded synthetic tensors of that shape,
 resident in HBM before timing starts; the relative-position table R (a
 function of the weights and of M, L only) is built once by the library
-before timing. Each timed step is txl_rel_attn_fwd followed by
-txl_mem_update; the update rotates over 16 ring/segment buffer pairs
-(268 MB) so that it is not served from the 256 MB last-level cache.
+before timing. Each timed step is txl_rel_attn_fwd_mem_update: the
+attention, masked by the ring's valid counts, and the append of the segment
+to that ring, in one launch; the step rotates over 16 ring/segment buffer
+pairs (268 MB) so that the append is not served from the 256 MB last-level
+cache. The same step as two launches (txl_rel_attn_fwd, then txl_mem_update)
+and each of those alone are timed as well.
 
 Prints one JSON line. `value` is attention TFLOP/s over the whole step
 (algorithmic flops: 6*d_h per visible (query, key) pair, masked pairs not
@@ -33,16 +36,22 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 N_RING_SETS = 16
 
-# HBM bytes per attention launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
-# (scaled by the same counters' reading of a plain copy of known size),
-# valid only for the kernel source they were taken on.
-ATTN_TRAFFIC = {"source_sha1": "15d0b996c33a468aaf3d1257f86fde780f9bc68f",
-                "bytes": 52.43e6}
+# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by the
+# same counters' reading of a plain copy of known size), valid only for the
+# kernel source they were taken on.
+ATTN_TRAFFIC = {"source_sha1": "6e7571f10367a97fcf4d14ad4659e856e3e127db",
+                "rel_attn_mfma_append_kernel": 69.24e6, "rel_attn_mfma_kernel": 52.43e6}
 
 
 def attn_flops(B, H, L, M_eff, d_h):
     pairs = B * (L * M_eff + L * (L + 1) // 2)
     return 6.0 * d_h * H * pairs
+
+
+def attn_hbm_bytes(B, H, L, M, d_h):
+    """Algorithmic bf16 bytes of one attention launch with every memory slot
+    valid: q, k, v and R read once, out written once."""
+    return 2.0 * d_h * (2 * B * H * L + 2 * B * H * (M + L) + H * (M + L))
 
 
 def cpu_baseline(x, cfg, seconds: float):
@@ -345,13 +354,21 @@ def main() -> int:
         hs = x["h"] if s == 0 else torch.randn((B, L, d), generator=g).to(torch.bfloat16)
         segs.append(hs.to(dev).contiguous())
 
+    ws = torch.zeros(1, dtype=torch.int32, device=dev)  # the fused call's counter
+
+    def step(i):
+        ring = rings[i % N_RING_SETS]
+        txl.txl_rel_attn_fwd_mem_update(q, k, v, r, u, vb, out, ring, segs[i % N_RING_SETS], ws,
+                                        mem_valid=ring.valid)
+
     def attn():
         txl.txl_rel_attn_fwd(q, k, v, r, u, vb, out, mem_valid=valid)
 
     def mem(i):
         txl.txl_mem_update([rings[i % N_RING_SETS]], [segs[i % N_RING_SETS]])
 
-    for i in range(2):  # first touch of every buffer
+    for i in range(2 * N_RING_SETS):  # first touch of every buffer
+        step(i)
         attn()
         mem(i)
     torch.cuda.synchronize()
@@ -388,23 +405,27 @@ def main() -> int:
 
     for i in range(2):
         mem_multi(i)
+    # Every graph is captured first: capturing leaves the GPU idle long
+    # enough for its clocks to drop, which a timed replay right after would
+    # pay for.
+    g_step = capture(step)
+    g_sep = capture(lambda i: (attn(), mem(i)))
+    g_attn = capture(lambda i: attn())
+    g_mem = capture(lambda i: mem(i))
+    g_multi = capture(mem_multi)
     # W untimed warmup steps, replayed from a graph so the GPU runs them
     # back to back (its clocks settle before the timed region)
     if args.warmup > 0:
         g_warm = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_warm):
             for i in range(args.warmup):
-                attn()
-                mem(i)
+                step(i)
         g_warm.replay()
         torch.cuda.synchronize()
-        del g_warm
-    g_step = capture(lambda i: (attn(), mem(i)))
-    g_attn = capture(lambda i: attn())
-    g_mem = capture(lambda i: mem(i))
 
     def timed(g):
-        g.replay()  # untimed replay: first-touch and cache state
+        for _ in range(3):  # untimed replays: cache state, and >= 25 ms of back-to-back work
+            g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t = time.perf_counter()
@@ -415,17 +436,20 @@ def main() -> int:
         return e0.elapsed_time(e1) / K, time.perf_counter() - t
 
     step_ms, wall = timed(g_step)
+    sep_ms = timed(g_sep)[0]
     attn_ms = timed(g_attn)[0]
     mem_ms = timed(g_mem)[0]
-    multi_ms = timed(capture(mem_multi))[0]
+    multi_ms = timed(g_multi)[0]
 
     import hashlib
     src = os.path.join(ROOT, "transformer_xl_relative_txl_amd", "csrc", "rel_attn_mfma.hip")
     with open(src, "rb") as fh:
         same_kernel = hashlib.sha1(fh.read()).hexdigest() == ATTN_TRAFFIC["source_sha1"]
-    traffic = ATTN_TRAFFIC["bytes"] if same_kernel else None
+    traffic = ATTN_TRAFFIC["rel_attn_mfma_append_kernel"] if same_kernel else None
+    attn_traffic = ATTN_TRAFFIC["rel_attn_mfma_kernel"] if same_kernel else None
 
     flops = attn_flops(B, H, L, M, dh)
+    attn_bytes = attn_hbm_bytes(B, H, L, M, dh)
     Lp = min(L, M)
     mem_bytes = 2.0 * B * Lp * d * 2
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
@@ -448,9 +472,16 @@ def main() -> int:
         "config": {"workload": "one layer rel-attn + mem update, B=8 H=16 d_h=64 L=512 M=512",
                    "B": B, "H": H, "d_h": dh, "L": L, "M": M, "valid": M,
                    "seed": cfg.seed},
-        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        # the step's one launch: the attention with the ring append in its shadow
+        "roofline": {"kernel": "rel_attn_mfma_append_kernel", "bound": "mfma",
+                     "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "algorithmic_bytes": round(attn_bytes + mem_bytes)},
+        "step_two_launches_ms": round(sep_ms, 5),
+        "attention_alone": {"kernel": "rel_attn_mfma_kernel", "ms": round(attn_ms, 5),
+                            "achieved": round(attn_tflops, 2), "unit": "TFLOP/s",
+                            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                            "traffic": attn_traffic, "algorithmic_bytes": round(attn_bytes)},
         "mem_update": {"bound": "hbm", "achieved": round(mem_gbps, 1), "peak": PEAK_HBM_GBPS,
                        "unit": "GB/s", "frac": round(mem_gbps / PEAK_HBM_GBPS, 4),
                        "bytes_per_launch": mem_bytes, "ms": round(mem_ms, 5)},

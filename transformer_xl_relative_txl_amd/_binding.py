@@ -128,6 +128,9 @@ def _load() -> ctypes.CDLL:
     lib.txl_mem_update.argtypes = [ctypes.POINTER(TxlMemStruct), i32,
                                    ctypes.POINTER(vp), i32, vp]
     lib.txl_mem_update.restype = st
+    lib.txl_rel_attn_fwd_mem_update.argtypes = [ctypes.POINTER(RelAttnArgs),
+                                                ctypes.POINTER(TxlMemStruct), vp, vp, sz, vp]
+    lib.txl_rel_attn_fwd_mem_update.restype = st
     lib.txl_mem_reset_rows.argtypes = [ctypes.POINTER(TxlMemStruct), i32, vp, vp]
     lib.txl_mem_reset_rows.restype = st
     lib.txl_mem_read_logical.argtypes = [ctypes.POINTER(TxlMemStruct), vp, vp]
@@ -359,6 +362,27 @@ def txl_mem_update(mems: Sequence[TxlMem], hs: Sequence[torch.Tensor],
         m.head = int(arr[i].head)
 
 
+def txl_rel_attn_fwd_mem_update(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                r: torch.Tensor, u: torch.Tensor, vb: torch.Tensor,
+                                out: torch.Tensor, mem: TxlMem, h: torch.Tensor,
+                                workspace: torch.Tensor, mem_valid: Optional[torch.Tensor] = None,
+                                lse: Optional[torch.Tensor] = None, scale: float = 0.0,
+                                stream=None) -> torch.Tensor:
+    """txl_rel_attn_fwd followed by txl_mem_update([mem], [h]), as one launch.
+    h [B,L,d] contiguous in the ring's dtype; workspace: at least 4 device
+    bytes that are zero before the first call (each call leaves them zero)."""
+    assert h.is_contiguous()
+    a = _attn_args(q, k, v, r, u, vb, out, mem_valid, lse, scale)
+    s = mem._struct()
+    _check("txl_rel_attn_fwd_mem_update",
+           lib().txl_rel_attn_fwd_mem_update(ctypes.byref(a), ctypes.byref(s), _ptr(h),
+                                             _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(),
+                                             _stream(stream)))
+    mem.head = int(s.head)
+    return out
+
+
 def txl_mem_reset_rows(mems: Sequence[TxlMem], reset: Optional[torch.Tensor] = None,
                        stream=None) -> None:
     """valid[b] = 0 in every ring for rows with reset[b] != 0 (uint8 [B]; None = all)."""
@@ -575,7 +599,7 @@ def exported_symbols() -> List[str]:
     """Names of the C entry points this binding wraps."""
     return ["txl_rel_pos_table", "txl_rel_attn_fwd", "txl_rel_attn_split_workspace_bytes",
             "txl_rel_attn_fwd_split", "txl_rel_attn_bwd_workspace_bytes", "txl_rel_attn_bwd",
-            "txl_mem_update",
+            "txl_mem_update", "txl_rel_attn_fwd_mem_update",
             "txl_mem_reset_rows", "txl_mem_read_logical", "txl_stack_persistent_bytes",
             "txl_stack_create", "txl_segment_step_workspace_bytes", "txl_segment_step",
             "txl_stack_destroy", "txl_kv_cache_min_capacity", "txl_segment_step_kv",

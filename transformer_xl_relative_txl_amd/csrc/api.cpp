@@ -175,6 +175,76 @@ TXL_API txl_status txl_rel_attn_fwd_split(const txl_rel_attn_args *a, int32_t kv
   return launch_rel_attn_mfma(p, stream);
 }
 
+static txl_status check_rings(const txl_mem *mems, int32_t n_mems, const char *who);
+
+TXL_API txl_status txl_rel_attn_fwd_mem_update(const txl_rel_attn_args *a, txl_mem *mem,
+                                               const void *h, void *workspace, size_t ws_bytes,
+                                               hipStream_t stream) {
+  clear_error();
+  AttnParams p;
+  bool nothing;
+  txl_status st = attn_params(a, &p, &nothing);
+  if (st != TXL_OK) return st;
+  if (!mem) return fail(TXL_ERR_INVALID_ARG, "rel_attn_mem_update: null ring");
+  st = check_rings(mem, 1, "rel_attn_mem_update");
+  if (st != TXL_OK) return st;
+  if (mem->B != a->B || mem->M != a->M)
+    return fail(TXL_ERR_INVALID_ARG, "rel_attn_mem_update: ring B, M (%d, %d) differ from the "
+                "attention's (%d, %d)", mem->B, mem->M, a->B, a->M);
+  if (nothing) return TXL_OK;  // B == 0 or L == 0: no attention and no append
+  if (mem->M == 0)             // nothing to append
+    return a->dtype == TXL_BF16 ? launch_rel_attn_mfma(p, stream)
+                                : launch_rel_attn_valu(p, a->dtype, stream);
+  if (!h) return fail(TXL_ERR_INVALID_ARG, "rel_attn_mem_update: null h");
+  const int64_t row_bytes = static_cast<int64_t>(mem->d) * dtype_size(mem->dtype);
+  if (row_bytes % 16)
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_mem_update: d * sizeof(dtype) must be a multiple of 16");
+  if (!aligned16(h) || !aligned16(mem->data))
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_mem_update: ring or h not 16-byte aligned");
+  if (!workspace || ws_bytes < 4)
+    return fail(TXL_ERR_WORKSPACE, "rel_attn_mem_update: workspace %zu < 4 bytes", ws_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 3u)
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_mem_update: workspace not 4-byte aligned");
+  const int B = mem->B, M = mem->M, L = a->L;
+  const int Lp = L < M ? L : M;
+  const int64_t h_bytes = static_cast<int64_t>(B) * L * row_bytes;
+  const int64_t data_bytes = static_cast<int64_t>(B) * M * row_bytes;
+  const int64_t limit = (int64_t(1) << 31) - 16;
+  if (a->dtype != TXL_BF16 || h_bytes >= limit || data_bytes >= limit) {
+    // the two as separate launches (same results)
+    st = a->dtype == TXL_BF16 ? launch_rel_attn_mfma(p, stream)
+                              : launch_rel_attn_valu(p, a->dtype, stream);
+    if (st != TXL_OK) return st;
+    RingBatch rb;
+    rb.data[0] = mem->data;
+    rb.valid[0] = mem->valid;
+    rb.h[0] = h;
+    rb.head[0] = mem->head;
+    st = launch_mem_update(rb, 1, B, M, L, row_bytes, stream);
+  } else {
+    RingAppend ra = {};
+    ra.h = h;
+    ra.data = mem->data;
+    ra.valid = mem->valid;
+    ra.done = static_cast<uint32_t *>(workspace);
+    ra.head = mem->head;
+    ra.B = B;
+    ra.M = M;
+    ra.L = L;
+    ra.Lp = Lp;
+    ra.cpr = static_cast<uint32_t>(row_bytes / 16);
+    ra.div_cpr = make_fastdiv(ra.cpr);
+    ra.div_lp = make_fastdiv(static_cast<uint32_t>(Lp));
+    ra.total = static_cast<uint32_t>(static_cast<int64_t>(B) * Lp * ra.cpr);
+    ra.h_bytes = static_cast<uint32_t>(h_bytes);
+    ra.data_bytes = static_cast<uint32_t>(data_bytes);
+    st = launch_rel_attn_mfma_append(p, ra, stream);
+  }
+  if (st != TXL_OK) return st;
+  mem->head = (mem->head + Lp) % M;
+  return TXL_OK;
+}
+
 // ---------------------------------------------------------------------------
 // Workspace of txl_rel_attn_bwd: byte offsets of its pieces, each 256-byte aligned.
 struct BwdLayout {

@@ -25,20 +25,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kChunks = 1;  // 16-byte chunks per thread (more per thread measured slower)
 
-// floor(n / d) = (umulhi(n, m) + n) >> s for 0 <= n < 2^31, d >= 1
-struct FastDiv {
-  uint32_t d, m, s;
-};
-FastDiv make_fastdiv(uint32_t d) {
-  uint32_t s = 0;
-  while ((uint64_t(1) << s) < d) ++s;
-  const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1;
-  return FastDiv{d, static_cast<uint32_t>(m), s};
-}
-__device__ inline uint32_t fdiv(uint32_t n, FastDiv f) {
-  return (__umulhi(n, f.m) + n) >> f.s;
-}
-
 struct RingMeta {
   int B, M, L, Lp;
   uint32_t cpr;         // 16-byte chunks per row

@@ -114,6 +114,26 @@ __device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 __device__ inline u32x4 bload(rsrc_t rs, int byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0));
 }
+// Non-temporal 16-byte copy through buffer loads / stores: an offset past the
+// buffer's range loads zeros and stores nothing.
+constexpr int kNonTemporal = 2;
+constexpr int kOutOfRange = 0x7ffffff0;
+constexpr int kAppendBatch = 8;  // ring-append chunks in flight per thread
+
+// Counts a workgroup in *done and returns the count before it; the count wraps
+// to zero after the grid's last workgroup, so the counter is zero again
+// between launches. (The wrapping increment also keeps the compiler from
+// turning the one-lane atomic into a wave reduction followed by a wait for
+// every outstanding load.)
+__device__ inline uint32_t count_done(uint32_t *done) {
+  return __builtin_amdgcn_atomic_inc32(done, gridDim.x - 1u, __ATOMIC_RELAXED, "agent");
+}
+__device__ inline u32x4 bload_nt(rsrc_t rs, int byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, kNonTemporal));
+}
+__device__ inline void bstore_nt(rsrc_t rs, int byte_off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, byte_off, 0, kNonTemporal);
+}
 
 // One tile of K (two 16-byte chunks per thread) and V (two keys x 8 dims
 // per thread), held in registers between the global load and the LDS store.
@@ -153,8 +173,17 @@ __device__ inline void store_kv(const KVRegs &x, __bf16 *sk, __bf16 *svt, int ti
   }
 }
 
-__global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int n_qt) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+// The attention of one query tile; with kAppend the workgroups of the lighter
+// half of the query tiles also move the ring append's chunks once their key
+// tiles are done. Each CU holds a light and a heavy workgroup side by side,
+// and the light one's copy runs while the heavy one is still computing.
+// (Copying inside the tile loop instead put the stores' completion on the
+// chain: a wave's wait for its next R rows also waits for every older store.
+// Counting the heavy workgroups in at their start instead of their end put
+// the contended atomic's return on their first tile's wait.)
+template <bool kAppend>
+__device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, const RingAppend &ra,
+                                              unsigned char *smem) {
   // the K tile at smem, the V^T tile right after it, then the waves' bands
   float *sband = reinterpret_cast<float *>(smem + (kLdsK + kLdsV));
 
@@ -212,6 +241,7 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
 
   KVRegs nxt;
   load_kv(nxt, krs, vrs, kv_row_bytes, j_lo, tid);
+
 
   // Q' = (q+u) c and Q'' = (q+v) c as B operands: k-step s holds dims 16s+8hh..+7
   const float c2 = p.scale * 1.4426950408889634f;
@@ -275,6 +305,7 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
   store_kv(nxt, reinterpret_cast<__bf16 *>(smem), reinterpret_cast<__bf16 *>(smem + kLdsK), tid);
   load_kv(nxt, krs, vrs, kv_row_bytes, j_lo + BK, tid);
   __syncthreads();
+
 
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int j0 = j_lo + kt * BK;
@@ -415,6 +446,61 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
     __syncthreads();
   }
 
+  if constexpr (kAppend) {
+    // Copy workers: the workgroups at dealing positions [copy_pos0,
+    // copy_pos0 + copy_npos), the lighter query tiles. Worker thread g moves
+    // chunks e = g + n * (worker threads), kAppendBatch rounds in flight at a
+    // time; chunk e is byte 16c of new row k of batch row b
+    // (e = (b L' + k) cpr + c), read from h row b L + L - L' + k and written
+    // to ring slot (head + k) mod M.
+    if (pos >= ra.copy_pos0 && pos < ra.copy_pos0 + ra.copy_npos) {
+      const rsrc_t src_rs = make_rsrc(ra.h, ra.h_bytes);
+      const rsrc_t dst_rs = make_rsrc(ra.data, ra.data_bytes);
+      const uint32_t gid =
+          static_cast<uint32_t>((pos - ra.copy_pos0) * BH + bh) * 256u + static_cast<uint32_t>(tid);
+      const uint32_t step = ra.worker_threads;
+      for (uint32_t n0 = 0; n0 < ra.rounds; n0 += kAppendBatch) {
+        u32x4 val[kAppendBatch];
+        int dst[kAppendBatch];
+#pragma unroll
+        for (int t = 0; t < kAppendBatch; ++t) {
+          const uint32_t n = n0 + t;
+          const uint32_t e = gid + n * step;
+          const bool ok = n < ra.rounds && e < ra.total;
+          const uint32_t ee = ok ? e : 0u;
+          const uint32_t row = fdiv(ee, ra.div_cpr);
+          const uint32_t c = ee - row * ra.cpr;
+          const uint32_t bb = fdiv(row, ra.div_lp);
+          const uint32_t k = row - bb * static_cast<uint32_t>(ra.Lp);
+          const uint32_t src_row =
+              bb * static_cast<uint32_t>(ra.L) + static_cast<uint32_t>(ra.L - ra.Lp) + k;
+          uint32_t slot = static_cast<uint32_t>(ra.head) + k;
+          if (slot >= static_cast<uint32_t>(ra.M)) slot -= static_cast<uint32_t>(ra.M);
+          const uint32_t dst_row = bb * static_cast<uint32_t>(ra.M) + slot;
+          val[t] = bload_nt(src_rs, ok ? static_cast<int>((src_row * ra.cpr + c) * 16u) : kOutOfRange);
+          dst[t] = ok ? static_cast<int>((dst_row * ra.cpr + c) * 16u) : kOutOfRange;
+        }
+#pragma unroll
+        for (int t = 0; t < kAppendBatch; ++t) bstore_nt(dst_rs, dst[t], val[t]);
+      }
+    }
+    // Each workgroup counts itself in *done at its end; every thread of it
+    // read the valid counts, and used them for its key range, before the tile
+    // loop's barriers. The workgroup that counts last therefore runs after
+    // every read of them in the grid: it advances them. (The reads have
+    // returned before the increment is issued, so it needs no release
+    // ordering, which would write back the L2.)
+    int *last = reinterpret_cast<int *>(smem);
+    if (tid == 0) *last = count_done(ra.done) == gridDim.x - 1u;
+    __syncthreads();
+    if (*last) {
+      for (int bb = tid; bb < ra.B; bb += 256) {
+        const int nv = ra.valid[bb] + ra.L;
+        ra.valid[bb] = nv < ra.M ? nv : ra.M;
+      }
+    }
+  }
+
   if (!wave_active) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (i >= L) return;
@@ -449,6 +535,17 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int
     }
   if (p.lse && hh == 0)
     p.lse[(static_cast<int64_t>(b) * p.H + h) * L + i] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
+}
+
+__global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int n_qt) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  rel_attn_tile<false>(p, n_qt, RingAppend{}, smem);
+}
+
+__global__ __launch_bounds__(256, 2) void rel_attn_mfma_append_kernel(AttnParams p, int n_qt,
+                                                                      RingAppend ra) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  rel_attn_tile<true>(p, n_qt, ra, smem);
 }
 
 // Merge of the key-range splits: per query, m = max_s m_s and
@@ -487,14 +584,15 @@ __global__ __launch_bounds__(256) void rel_attn_merge_kernel(AttnParams p) {
 
 }  // namespace
 
-txl_status launch_rel_attn_mfma(const AttnParams &p, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(rel_attn_mfma_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
+// Raises the kernel's LDS limit once; checks the shapes the buffer loads
+// rely on and returns the grid (query tiles x splits x batch rows x heads).
+static txl_status prepare_launch(const void *kernel, bool *attr_set, const AttnParams &p,
+                                 int *n_qt, int64_t *blocks) {
+  if (!*attr_set) {
+    if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(kLdsTotal)) != hipSuccess)
       return fail(TXL_ERR_HIP, "rel_attn: cannot raise the LDS limit to %zu bytes", kLdsTotal);
-    attr_set = true;
+    *attr_set = true;
   }
   // buffer loads address rows by 32-bit byte offsets from the (batch, head)
   // base and rely on rows not overlapping for the out-of-range zero fill
@@ -503,10 +601,60 @@ txl_status launch_rel_attn_mfma(const AttnParams &p, hipStream_t s) {
   const int64_t ML = static_cast<int64_t>(p.M) + p.L;
   if ((ML + BK) * p.kv_sl * 2 >= (int64_t(1) << 31) || (ML + BK + QW) * p.r_sl * 2 >= (int64_t(1) << 31))
     return fail(TXL_ERR_UNSUPPORTED, "rel_attn: key / R rows span more than 2 GiB per head");
-  const int n_qt = (p.L + BQ - 1) / BQ;
+  *n_qt = (p.L + BQ - 1) / BQ;
   const int S = p.n_split > 1 ? p.n_split : 1;
-  const int64_t blocks = static_cast<int64_t>(n_qt) * p.B * p.H * S;
-  if (blocks > 0x7fffffffLL) return fail(TXL_ERR_UNSUPPORTED, "rel_attn: grid too large");
+  *blocks = static_cast<int64_t>(*n_qt) * p.B * p.H * S;
+  if (*blocks > 0x7fffffffLL) return fail(TXL_ERR_UNSUPPORTED, "rel_attn: grid too large");
+  return TXL_OK;
+}
+
+txl_status launch_rel_attn_mfma_append(const AttnParams &p, const RingAppend &ra, hipStream_t s) {
+  static bool attr_set = false;
+  if (p.n_split > 1) return fail(TXL_ERR_UNSUPPORTED, "rel_attn_append: key splits are not served");
+  int n_qt;
+  int64_t blocks;
+  txl_status st = prepare_launch(reinterpret_cast<const void *>(rel_attn_mfma_append_kernel),
+                                 &attr_set, p, &n_qt, &blocks);
+  if (st != TXL_OK) return st;
+  // Copy workers: the lighter half of the query tiles (dealt after the
+  // heavier half), or every tile when there is one. (Measured at B8 H16
+  // L512 M512: the lightest quarter alone, or every workgroup, copied
+  // slower; so did 2, 4 or 16 chunks in flight per thread instead of 8.)
+  // Chunk indices g + n * threads stay below 2^32 while the grid's thread
+  // count and the chunk count are both below 2^31.
+  const int64_t threads = blocks * 256;
+  const int copy_pos0 = n_qt > 1 ? (n_qt + 1) / 2 : 0;
+  const int copy_npos = n_qt > 1 ? n_qt - copy_pos0 : 1;
+  const int64_t workers = static_cast<int64_t>(copy_npos) * p.B * p.H * 256;
+  if (threads >= (int64_t(1) << 31)) {  // the two as separate launches
+    st = launch_rel_attn_mfma(p, s);
+    if (st != TXL_OK) return st;
+    RingBatch rb;
+    rb.data[0] = ra.data;
+    rb.valid[0] = ra.valid;
+    rb.h[0] = ra.h;
+    rb.head[0] = ra.head;
+    return launch_mem_update(rb, 1, ra.B, ra.M, ra.L, static_cast<int64_t>(ra.cpr) * 16, s);
+  }
+  RingAppend a = ra;
+  a.copy_pos0 = copy_pos0;
+  a.copy_npos = copy_npos;
+  a.worker_threads = static_cast<uint32_t>(workers);
+  a.rounds = static_cast<uint32_t>((static_cast<int64_t>(a.total) + workers - 1) / workers);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(rel_attn_mfma_append_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256),
+                     kLdsTotal, s, p, n_qt, a);
+  return check_launch("rel_attn_mfma_append_kernel");
+}
+
+txl_status launch_rel_attn_mfma(const AttnParams &p, hipStream_t s) {
+  static bool attr_set = false;
+  int n_qt;
+  int64_t blocks;
+  txl_status st0 = prepare_launch(reinterpret_cast<const void *>(rel_attn_mfma_kernel), &attr_set,
+                                  p, &n_qt, &blocks);
+  if (st0 != TXL_OK) return st0;
+  const int S = p.n_split > 1 ? p.n_split : 1;
   (void)hipGetLastError();
   hipLaunchKernelGGL(rel_attn_mfma_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256),
                      kLdsTotal, s, p, n_qt);

@@ -39,6 +39,44 @@ txl_status launch_rel_attn_valu(const AttnParams &p, txl_dtype dt,
 // bf16 MFMA kernel.
 txl_status launch_rel_attn_mfma(const AttnParams &p, hipStream_t s);
 
+// floor(n / d) = (umulhi(n, m) + n) >> s for 0 <= n < 2^31, d >= 1
+struct FastDiv {
+  uint32_t d, m, s;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((uint64_t(1) << s) < d) ++s;
+  const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1;
+  return FastDiv{d, static_cast<uint32_t>(m), s};
+}
+__device__ inline uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
+
+// One ring's append (txl_mem_update of a single ring) carried out by the bf16
+// attention kernel in the same launch: the 16-byte chunks of the L' = min(L, M)
+// new rows are spread over the threads of the workgroups with the lighter
+// query tiles, which copy after their key tiles; the workgroup that finishes
+// last (counted in *done, which wraps back to zero) advances valid after
+// every workgroup has read it.
+struct RingAppend {
+  const void *h;        // [B, L, d] contiguous
+  void *data;           // [B, M, d]
+  int32_t *valid;       // [B]
+  uint32_t *done;       // one counter, zero between calls
+  int64_t head;
+  int32_t B, M, L, Lp;
+  uint32_t cpr;         // 16-byte chunks per row
+  FastDiv div_cpr, div_lp;
+  uint32_t total;       // chunks to move
+  int32_t copy_pos0, copy_npos;  // dealing positions of the copying workgroups
+  uint32_t worker_threads;  // their threads
+  uint32_t rounds;      // ceil(total / worker_threads)
+  uint32_t h_bytes, data_bytes;
+};
+// The attention of p (n_split must be 1) and the append of ra in one launch.
+txl_status launch_rel_attn_mfma_append(const AttnParams &p, const RingAppend &ra, hipStream_t s);
+
 // gradients (bf16 inputs): p holds the forward's arguments (out = the
 // forward's output); g the incoming gradient, the forward's lse, the fp32
 // gradient outputs (contiguous) and the workspace pieces
