@@ -39,8 +39,8 @@ N_RING_SETS = 16
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by the
 # same counters' reading of a plain copy of known size), valid only for the
 # kernel source they were taken on.
-ATTN_TRAFFIC = {"source_sha1": "6e7571f10367a97fcf4d14ad4659e856e3e127db",
-                "rel_attn_mfma_append_kernel": 69.24e6, "rel_attn_mfma_kernel": 52.43e6}
+ATTN_TRAFFIC = {"source_sha1": "f9bd12747e674ab4bf92b2ccb2ae0115423501a8",
+                "rel_attn_mfma_append_kernel": 69.22e6, "rel_attn_mfma_kernel": 52.42e6}
 
 
 def attn_flops(B, H, L, M_eff, d_h):
@@ -354,7 +354,7 @@ def main() -> int:
         hs = x["h"] if s == 0 else torch.randn((B, L, d), generator=g).to(torch.bfloat16)
         segs.append(hs.to(dev).contiguous())
 
-    ws = torch.zeros(1, dtype=torch.int32, device=dev)  # the fused call's counter
+    ws = txl.txl_rel_attn_mem_update_workspace(B, device=dev)  # the fused call's counters
 
     def step(i):
         ring = rings[i % N_RING_SETS]

@@ -231,15 +231,18 @@ TXL_API txl_status txl_mem_read_logical(const txl_mem *m, void *out,
  * of txl_rel_attn_fwd(a) followed by txl_mem_update(mem, 1, &h, a->L): out
  * and lse bit for bit, the ring's slots, valid counts and head likewise, also
  * when a->mem_valid is mem->valid (the valid counts advance only after every
- * workgroup of the attention has read them). The attention is latency-bound
- * and leaves HBM mostly idle; the append's copy runs in its shadow.
+ * workgroup of the attention has read them; each batch row's workgroups
+ * count themselves in that row's counter in `workspace`, and the last one
+ * advances the row). The attention is latency-bound and leaves HBM mostly
+ * idle; the append's copy runs in its shadow.
  *
  * a         : as for txl_rel_attn_fwd.
  * mem       : one ring with mem->B == a->B and mem->M == a->M; its head is
  *             advanced on success.
  * h         : [B, L, d] contiguous device array, the ring's dtype (L = a->L).
  *             The ring's slots must not overlap the attention's inputs.
- * workspace : at least 4 device bytes, 4-byte aligned, zero before the first
+ * workspace : txl_rel_attn_mem_update_workspace_bytes(B) device bytes
+ *             (256 per batch row), 256-byte aligned, zero before the first
  *             call; every call leaves them zero. Calls sharing a workspace
  *             must not overlap.
  * fp32 attention, and rings or segments of 2 GiB or more, run as the two
@@ -247,6 +250,7 @@ TXL_API txl_status txl_mem_read_logical(const txl_mem *m, void *out,
  * alone.
  * Errors: those of txl_rel_attn_fwd and txl_mem_update, INVALID_ARG (ring
  * shape differs from the attention's), WORKSPACE. */
+TXL_API size_t txl_rel_attn_mem_update_workspace_bytes(int32_t B);
 TXL_API txl_status txl_rel_attn_fwd_mem_update(const txl_rel_attn_args *a, txl_mem *mem,
                                                const void *h, void *workspace,
                                                size_t ws_bytes, hipStream_t stream);

@@ -1,6 +1,7 @@
 """Captured-graph replays of the stateless entry points equal their eager
 results bit for bit: the relative attention (whole and with key splits), the
-segment loss and the relative-position table. Each graph is replayed several
+segment loss and the relative-position table; and the attention with the ring
+append replayed from the same ring state. Each graph is replayed several
 times with eager work and synchronisations between the replays, and every
 replay is checked. (The entry points record kernel launches only.)"""
 import pytest
@@ -73,3 +74,59 @@ def test_loss_and_rel_pos_table_graph_replays():
     torch.cuda.synchronize()
     eager = [nll.clone(), r.clone()]
     replay_and_check(fn, [nll, r], eager)
+
+
+def test_fused_attention_ring_append_graph_replays():
+    """The attention with the ring append in one launch, captured once and
+    replayed from the same ring state each time: out, lse, the ring's slots
+    and valid counts equal the eager call's, and the counter is back at zero."""
+    cfg = txl_synth.ATTN_CONFIGS["B4_H8_L128_M128"]
+    x = attn_case(cfg, valid_mode="mixed")
+    t = {k: v.to(DEV) for k, v in x.items()}
+    B, H, L, dh = t["q"].shape
+    gen = torch.Generator().manual_seed(7)
+    data0 = torch.randn((B, cfg.M, H * dh), generator=gen).to(torch.bfloat16).to(DEV)
+    h = torch.randn((B, L, H * dh), generator=gen).to(torch.bfloat16).to(DEV)
+    valid0 = t["valid"].clone()
+    ring = txl.TxlMem(data0.clone(), valid0.clone(), 5)
+    counter = txl.txl_rel_attn_mem_update_workspace(B)
+    out = torch.empty_like(t["q"])
+    lse = torch.empty(t["q"].shape[:3], dtype=torch.float32, device=DEV)
+
+    def fn():
+        ring.head = 5
+        txl.txl_rel_attn_fwd_mem_update(t["q"], t["k"], t["v"], t["r"], t["u"], t["vb"], out,
+                                        ring, h, counter, mem_valid=ring.valid, lse=lse)
+
+    def restore():
+        ring.data.copy_(data0)
+        ring.valid.copy_(valid0)
+
+    restore()
+    fn()
+    torch.cuda.synchronize()
+    eager = [out.clone(), lse.clone(), ring.data.clone(), ring.valid.clone()]
+    assert ring.head == (5 + min(L, cfg.M)) % cfg.M
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        restore()
+        fn()                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for k in range(3):
+        restore()
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device=DEV) * 3.0   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip([out, lse, ring.data, ring.valid], eager):
+            assert torch.equal(o, e), k
+        assert (counter.cpu() == 0).all(), k
+        del junk

@@ -131,6 +131,8 @@ def _load() -> ctypes.CDLL:
     lib.txl_rel_attn_fwd_mem_update.argtypes = [ctypes.POINTER(RelAttnArgs),
                                                 ctypes.POINTER(TxlMemStruct), vp, vp, sz, vp]
     lib.txl_rel_attn_fwd_mem_update.restype = st
+    lib.txl_rel_attn_mem_update_workspace_bytes.argtypes = [i32]
+    lib.txl_rel_attn_mem_update_workspace_bytes.restype = sz
     lib.txl_mem_reset_rows.argtypes = [ctypes.POINTER(TxlMemStruct), i32, vp, vp]
     lib.txl_mem_reset_rows.restype = st
     lib.txl_mem_read_logical.argtypes = [ctypes.POINTER(TxlMemStruct), vp, vp]
@@ -365,13 +367,17 @@ def txl_mem_update(mems: Sequence[TxlMem], hs: Sequence[torch.Tensor],
 def txl_rel_attn_fwd_mem_update(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                 r: torch.Tensor, u: torch.Tensor, vb: torch.Tensor,
                                 out: torch.Tensor, mem: TxlMem, h: torch.Tensor,
-                                workspace: torch.Tensor, mem_valid: Optional[torch.Tensor] = None,
+                                workspace: Optional[torch.Tensor] = None,
+                                mem_valid: Optional[torch.Tensor] = None,
                                 lse: Optional[torch.Tensor] = None, scale: float = 0.0,
                                 stream=None) -> torch.Tensor:
     """txl_rel_attn_fwd followed by txl_mem_update([mem], [h]), as one launch.
-    h [B,L,d] contiguous in the ring's dtype; workspace: at least 4 device
-    bytes that are zero before the first call (each call leaves them zero)."""
+    h [B,L,d] contiguous in the ring's dtype; workspace: the per-batch-row
+    counters (txl_rel_attn_mem_update_workspace(B)), zero before the first
+    call and left zero by each; allocated here when not given."""
     assert h.is_contiguous()
+    if workspace is None:
+        workspace = txl_rel_attn_mem_update_workspace(mem.B, device=h.device)
     a = _attn_args(q, k, v, r, u, vb, out, mem_valid, lse, scale)
     s = mem._struct()
     _check("txl_rel_attn_fwd_mem_update",
@@ -381,6 +387,12 @@ def txl_rel_attn_fwd_mem_update(q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
                                              _stream(stream)))
     mem.head = int(s.head)
     return out
+
+
+def txl_rel_attn_mem_update_workspace(B: int, device="cuda") -> torch.Tensor:
+    """Zeroed counters for txl_rel_attn_fwd_mem_update (keep and reuse them)."""
+    n = int(lib().txl_rel_attn_mem_update_workspace_bytes(B))
+    return torch.zeros(max(n, 4) // 4, dtype=torch.int32, device=device)
 
 
 def txl_mem_reset_rows(mems: Sequence[TxlMem], reset: Optional[torch.Tensor] = None,
@@ -600,6 +612,7 @@ def exported_symbols() -> List[str]:
     return ["txl_rel_pos_table", "txl_rel_attn_fwd", "txl_rel_attn_split_workspace_bytes",
             "txl_rel_attn_fwd_split", "txl_rel_attn_bwd_workspace_bytes", "txl_rel_attn_bwd",
             "txl_mem_update", "txl_rel_attn_fwd_mem_update",
+            "txl_rel_attn_mem_update_workspace_bytes",
             "txl_mem_reset_rows", "txl_mem_read_logical", "txl_stack_persistent_bytes",
             "txl_stack_create", "txl_segment_step_workspace_bytes", "txl_segment_step",
             "txl_stack_destroy", "txl_kv_cache_min_capacity", "txl_segment_step_kv",

@@ -177,6 +177,10 @@ TXL_API txl_status txl_rel_attn_fwd_split(const txl_rel_attn_args *a, int32_t kv
 
 static txl_status check_rings(const txl_mem *mems, int32_t n_mems, const char *who);
 
+TXL_API size_t txl_rel_attn_mem_update_workspace_bytes(int32_t B) {
+  return B > 0 ? static_cast<size_t>(B) * 256 : 0;
+}
+
 TXL_API txl_status txl_rel_attn_fwd_mem_update(const txl_rel_attn_args *a, txl_mem *mem,
                                                const void *h, void *workspace, size_t ws_bytes,
                                                hipStream_t stream) {
@@ -201,11 +205,12 @@ TXL_API txl_status txl_rel_attn_fwd_mem_update(const txl_rel_attn_args *a, txl_m
     return fail(TXL_ERR_UNSUPPORTED, "rel_attn_mem_update: d * sizeof(dtype) must be a multiple of 16");
   if (!aligned16(h) || !aligned16(mem->data))
     return fail(TXL_ERR_UNSUPPORTED, "rel_attn_mem_update: ring or h not 16-byte aligned");
-  if (!workspace || ws_bytes < 4)
-    return fail(TXL_ERR_WORKSPACE, "rel_attn_mem_update: workspace %zu < 4 bytes", ws_bytes);
-  if (reinterpret_cast<uintptr_t>(workspace) & 3u)
-    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_mem_update: workspace not 4-byte aligned");
   const int B = mem->B, M = mem->M, L = a->L;
+  const size_t need = txl_rel_attn_mem_update_workspace_bytes(B);
+  if (!workspace || ws_bytes < need)
+    return fail(TXL_ERR_WORKSPACE, "rel_attn_mem_update: workspace %zu < %zu bytes", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_mem_update: workspace not 256-byte aligned");
   const int Lp = L < M ? L : M;
   const int64_t h_bytes = static_cast<int64_t>(B) * L * row_bytes;
   const int64_t data_bytes = static_cast<int64_t>(B) * M * row_bytes;

@@ -56,14 +56,14 @@ __device__ inline uint32_t fdiv(uint32_t n, FastDiv f) {
 // One ring's append (txl_mem_update of a single ring) carried out by the bf16
 // attention kernel in the same launch: the 16-byte chunks of the L' = min(L, M)
 // new rows are spread over the threads of the workgroups with the lighter
-// query tiles, which copy after their key tiles; the workgroup that finishes
-// last (counted in *done, which wraps back to zero) advances valid after
-// every workgroup has read it.
+// query tiles, which copy after their key tiles; in each batch row the
+// workgroup that finishes last (counted in the row's counter, which wraps back
+// to zero) advances valid[b] after every workgroup of the row has read it.
 struct RingAppend {
   const void *h;        // [B, L, d] contiguous
   void *data;           // [B, M, d]
   int32_t *valid;       // [B]
-  uint32_t *done;       // one counter, zero between calls
+  uint32_t *done;       // per batch row a counter 256 bytes apart, zero between calls
   int64_t head;
   int32_t B, M, L, Lp;
   uint32_t cpr;         // 16-byte chunks per row
