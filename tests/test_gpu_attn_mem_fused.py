@@ -108,6 +108,12 @@ def test_fused_segment_longer_than_memory():
     _run_case(CFG, B=2, L=200, M=64, H=2, valid_mode="mixed", head=10)
 
 
+@pytest.mark.parametrize("L,M", [(300, 100), (600, 40)])
+def test_fused_odd_query_tile_counts(L, M):
+    # 3 and 5 query tiles of 128: the copy goes to the lighter 1 and 2 of them
+    _run_case(CFG, B=2, L=L, M=M, H=2, valid_mode="mixed", head=M - 1, steps=2)
+
+
 def test_fused_fp32_wide_ring_many_rounds():
     # ring width and dtype independent of the attention: 16 KiB rows, two
     # workgroups, so nearly all rounds run after the key tiles
@@ -148,6 +154,22 @@ def test_fused_zero_memory_is_attention_only():
     torch.cuda.synchronize()
     assert torch.equal(out_f.cpu(), out_s.cpu())
     assert mem.head == 0 and (mem.valid.cpu() == 0).all()
+
+
+def test_fused_empty_segment_is_noop():
+    x = attn_case(CFG, B=2, L=8, M=16, H=2, seed=6)
+    mem = txl.TxlMem(torch.ones((2, 16, 128), dtype=torch.bfloat16, device=DEV),
+                     torch.full((2,), 5, dtype=torch.int32, device=DEV), 3)
+    q = torch.empty((2, 2, 0, 64), dtype=torch.bfloat16, device=DEV)
+    k = x["k"][:, :, :16].to(DEV)
+    r = x["r"][:, :16].to(DEV)
+    out = torch.empty_like(q)
+    h = torch.empty((2, 0, 128), dtype=torch.bfloat16, device=DEV)
+    ws = txl.txl_rel_attn_mem_update_workspace(2)
+    txl.txl_rel_attn_fwd_mem_update(q, k, k, r, x["u"].to(DEV), x["vb"].to(DEV), out, mem, h, ws,
+                                    mem_valid=mem.valid)
+    torch.cuda.synchronize()
+    assert mem.head == 3 and (mem.valid.cpu() == 5).all() and (mem.data.cpu() == 1).all()
 
 
 def test_fused_rejects_bad_arguments():
