@@ -179,10 +179,11 @@ __device__ inline void store_kv(const KVRegs &x, __bf16 *sk, __bf16 *svt, int ti
 // half of the query tiles also move the ring append's chunks once their key
 // tiles are done. Each CU holds a light and a heavy workgroup side by side,
 // and the light one's copy runs while the heavy one is still computing.
-// (Copying inside the tile loop instead put the stores' completion on the
-// chain: a wave's wait for its next R rows also waits for every older store.
-// Counting the heavy workgroups in at their start instead of their end put
-// the contended atomic's return on their first tile's wait.)
+// (Copying inside the tile loop, one chunk per thread and tile, was slower:
+// the tile loads, latency-critical here, then share the memory system with
+// the copy, and a wave's wait for loads issued after a store also waits for
+// that store. Counting the heavy workgroups in at their start instead of
+// their end put the contended atomic's return on their first tile's wait.)
 template <bool kAppend>
 __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, const RingAppend &ra,
                                               unsigned char *smem) {
