@@ -167,3 +167,39 @@ def test_attention_backward_checks_without_gpu(lib):
     ldp = (32 + 64 + 7) // 8 * 8
     assert need >= 2 * 2 * 3 * 64 * ldp * 2
     assert lib.txl_rel_attn_bwd_workspace_bytes(-1, 3, 64, 32) == 0
+
+
+def test_attention_with_ring_append_checks_without_gpu(lib):
+    """The fused attention + ring append validates before launching: fake
+    but aligned device addresses are never dereferenced on these error paths,
+    and the ring's host head is left alone when a call is rejected."""
+    from transformer_xl_relative_txl_amd import _binding as bd
+    a = bd.RelAttnArgs()
+    a.dtype, a.B, a.H, a.L, a.M, a.d_h = 1, 2, 3, 64, 32, 64
+    fake = 1 << 20
+    a.q = a.k = a.v = a.r = a.u = a.vb = a.out = fake
+    a.q_sb, a.q_sh, a.q_sl = 3 * 64 * 64, 64 * 64, 64
+    a.kv_sb, a.kv_sh, a.kv_sl = 3 * 96 * 64, 96 * 64, 64
+    a.r_sh, a.r_sl = 96 * 64, 64
+    a.o_sb, a.o_sh, a.o_sl = a.q_sb, a.q_sh, a.q_sl
+    m = bd.TxlMemStruct()
+    m.data, m.valid, m.head, m.B, m.M, m.d, m.dtype = fake, fake, 7, 2, 32, 192, 1
+    need = lib.txl_rel_attn_mem_update_workspace_bytes(2)
+    assert need == 2 * 256 and lib.txl_rel_attn_mem_update_workspace_bytes(0) == 0
+    call = lambda ring, h, ws, n: lib.txl_rel_attn_fwd_mem_update(
+        ctypes.byref(a), ring, h, ws, n, None)
+    assert call(None, fake, fake, need) == 1                          # no ring
+    assert call(ctypes.byref(m), None, fake, need) == 1               # no h
+    assert call(ctypes.byref(m), fake, None, need) == 3               # no workspace
+    assert call(ctypes.byref(m), fake, fake, need - 1) == 3           # workspace too small
+    assert call(ctypes.byref(m), fake, fake + 16, need) == 2          # workspace not 256-aligned
+    assert call(ctypes.byref(m), fake + 8, fake, need) == 2           # h not 16-byte aligned
+    m.d = 100                                                         # row of 200 bytes
+    assert call(ctypes.byref(m), fake, fake, need) == 2
+    m.d, m.M = 192, 33                                                # capacity != attention's M
+    assert call(ctypes.byref(m), fake, fake, need) == 1
+    m.M, m.B = 32, 3                                                  # rows != attention's B
+    assert call(ctypes.byref(m), fake, fake, need) == 1
+    assert m.head == 7                                                # untouched by rejections
+    m.B, m.head = 2, 32                                               # head outside [0, M)
+    assert call(ctypes.byref(m), fake, fake, need) == 1
