@@ -245,7 +245,6 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
   KVRegs nxt;
   load_kv(nxt, krs, vrs, kv_row_bytes, j_lo, tid);
 
-
   // Q' = (q+u) c and Q'' = (q+v) c as B operands: k-step s holds dims 16s+8hh..+7
   const float c2 = p.scale * 1.4426950408889634f;
   bf16x8 qa[4], qb[4];
@@ -308,7 +307,6 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
   store_kv(nxt, reinterpret_cast<__bf16 *>(smem), reinterpret_cast<__bf16 *>(smem + kLdsK), tid);
   load_kv(nxt, krs, vrs, kv_row_bytes, j_lo + BK, tid);
   __syncthreads();
-
 
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int j0 = j_lo + kt * BK;
