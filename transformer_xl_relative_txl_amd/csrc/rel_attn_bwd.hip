@@ -477,6 +477,13 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
     const int w = l >> 3;
     z = (l & 7) + 8 * (w / n_mt);
     mt = w - (w / n_mt) * n_mt;
+    // Rows see triangular key ranges (the last row tile about twice the keys
+    // of the first), and an XCD deals its workgroups to its 32 CUs in turn,
+    // so CU c would receive row tile c mod n_mt in every round. Every other
+    // round of 32 takes the row tiles in reverse, so a CU holds tiles mt and
+    // n_mt - 1 - mt alike. (Only where n_mt divides 32, so that one batch
+    // row's tiles stay within one round and the mapping stays one-to-one.)
+    if ((32 % n_mt) == 0 && ((w >> 5) & 1)) mt = n_mt - 1 - mt;
   } else {
     z = l / n_mt;
     mt = l - z * n_mt;
