@@ -296,11 +296,13 @@ typedef struct {
 
 typedef struct txl_stack txl_stack; /* opaque host object */
 
-/* Bytes of the caller-owned persistent device buffer that holds R per layer. */
+/* Bytes of the caller-owned persistent device buffer that holds R per layer
+ * and the counters of the layers' attention + ring append launches. */
 TXL_API size_t txl_stack_persistent_bytes(const txl_stack_config *c);
 /* Checks the configuration, copies the weight pointer table (the weights
  * themselves must outlive the stack), builds every layer's R into
- * `persistent` on `stream`, and returns a host object in *out (free it with
+ * `persistent` on `stream` and zeroes the counters after them (steps on
+ * other streams must wait for this work), and returns a host object in *out (free it with
  * txl_stack_destroy). Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE
  * (persistent_bytes too small), HIP. */
 TXL_API txl_status txl_stack_create(const txl_stack_config *c, const txl_stack_weights *w,

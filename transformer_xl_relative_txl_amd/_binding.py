@@ -491,7 +491,7 @@ class TxlStack:
         """Layer `layer`'s R as built by the library: [M+L, H*d_h] bf16 view."""
         c = self.cfg
         hd = c.n_head * c.d_h
-        per = self.persistent.numel() // c.n_layer
+        per = ((c.M + c.L) * hd * 2 + 255) // 256 * 256   # 256-byte aligned tables
         raw = self.persistent[layer * per: layer * per + (c.M + c.L) * hd * 2]
         return raw.view(torch.bfloat16).view(c.M + c.L, hd)
 

@@ -26,6 +26,8 @@ struct txl_stack {
   std::vector<txl_layer_weights> layers;
   void *persistent;
   size_t r_bytes;  // one layer's R table
+  void *counters;  // after the R tables: the attention + ring append's per-row counters
+  size_t counter_bytes;
 };
 
 namespace txl {
@@ -202,9 +204,12 @@ txl_status residual_ln(GemmParams p, const __bf16 *res, const void *gamma, const
 // relative attention over keys / values k, v ([B, M+L, H*d_h] with batch
 // stride kv_sb elements, memory first) masked by `valid`, X = H + A W^O,
 // H1 = LN1(X), X = H1 + GELU(H1 W1) W2, dst = LN2(X).
+// With `append` set, the attention also appends hc to that ring in the same
+// launch (txl_rel_attn_fwd_mem_update: the ring masked by `valid` takes the
+// layer's input once the attention has read its valid counts).
 txl_status layer_body(const txl_stack *st, int n, const __bf16 *hc, void *dst, const void *k,
                       const void *v, int64_t kv_sb, const int32_t *valid, const StepBufs &b,
-                      hipStream_t stream) {
+                      hipStream_t stream, txl_mem *append = nullptr) {
   const txl_stack_config &c = st->cfg;
   const txl_layer_weights &lw = st->layers[n];
   const int HD = c.n_head * c.d_h;
@@ -240,8 +245,11 @@ txl_status layer_body(const txl_stack *st, int n, const __bf16 *hc, void *dst, c
   a.o_sl = HD;
   a.lse = nullptr;
   const int splits = attn_splits(c);
-  s = splits > 1 ? txl_rel_attn_fwd_split(&a, splits, b.attn, b.attn_bytes, stream)
-                 : txl_rel_attn_fwd(&a, stream);
+  if (append)
+    s = txl_rel_attn_fwd_mem_update(&a, append, hc, st->counters, st->counter_bytes, stream);
+  else
+    s = splits > 1 ? txl_rel_attn_fwd_split(&a, splits, b.attn, b.attn_bytes, stream)
+                   : txl_rel_attn_fwd(&a, stream);
   if (s != TXL_OK) return s;
   // X = H + A W^O; H1 = LN1(X)
   s = residual_ln(dense(b.o, HD, rows, c.d, HD, lw.wo, b.x, c.d), hc, lw.ln1_g, lw.ln1_b, b.h1,
@@ -261,10 +269,15 @@ using namespace txl;
 
 extern "C" {
 
+static size_t r_table_bytes(const txl_stack_config *c) {
+  const size_t hd = static_cast<size_t>(c->n_head) * c->d_h;
+  return align256(static_cast<size_t>(c->M + c->L) * hd * 2);
+}
+
 TXL_API size_t txl_stack_persistent_bytes(const txl_stack_config *c) {
   if (check_config(c) != TXL_OK) return 0;
-  const size_t hd = static_cast<size_t>(c->n_head) * c->d_h;
-  return static_cast<size_t>(c->n_layer) * align256(static_cast<size_t>(c->M + c->L) * hd * 2);
+  return static_cast<size_t>(c->n_layer) * r_table_bytes(c) +
+         align256(txl_rel_attn_mem_update_workspace_bytes(c->B));
 }
 
 TXL_API size_t txl_segment_step_workspace_bytes(const txl_stack_config *c) {
@@ -300,7 +313,17 @@ TXL_API txl_status txl_stack_create(const txl_stack_config *c, const txl_stack_w
   s->emb = w->emb;
   s->layers.assign(w->layers, w->layers + c->n_layer);
   s->persistent = persistent;
-  s->r_bytes = need / c->n_layer;
+  s->r_bytes = r_table_bytes(c);
+  s->counters = static_cast<char *>(persistent) + static_cast<size_t>(c->n_layer) * s->r_bytes;
+  s->counter_bytes = txl_rel_attn_mem_update_workspace_bytes(c->B);
+  if (s->counter_bytes > 0) {  // zero by a kernel (no memset: a caller may capture this)
+    int32_t *cnt = static_cast<int32_t *>(s->counters);
+    st = launch_mem_reset(&cnt, 1, static_cast<int>(s->counter_bytes / 4), nullptr, stream);
+    if (st != TXL_OK) {
+      delete s;
+      return st;
+    }
+  }
   for (int n = 0; n < c->n_layer; ++n) {
     st = txl_rel_pos_table(TXL_BF16, c->M, c->L, c->d, c->n_head, c->d_h, s->layers[n].wr,
                            static_cast<char *>(persistent) + n * s->r_bytes, stream);
@@ -367,9 +390,14 @@ TXL_API txl_status txl_segment_step(txl_stack *st, const int32_t *tokens, txl_me
     s = launch_gemm(pkv, kEpiStoreBf16, stream);
     if (s != TXL_OK) return s;
     void *dst = (n + 1 == c.n_layer) ? h_out : static_cast<void *>(slot(n + 1));
-    s = layer_body(st, n, hc, dst, b.k, b.v, static_cast<int64_t>(ML) * HD, ring.valid, b, stream);
+    // Without the batched update, ring n-1 takes H^(n-1) now that layer n has
+    // read it: inside the attention's launch when it runs unsplit (the copy
+    // then runs in the shadow of the latency-bound attention), else after it.
+    const bool fused = !batched && attn_splits(c) == 1;
+    s = layer_body(st, n, hc, dst, b.k, b.v, static_cast<int64_t>(ML) * HD, ring.valid, b, stream,
+                   fused ? &ring : nullptr);
     if (s != TXL_OK) return s;
-    if (!batched) {  // ring n-1 takes H^(n-1) now that layer n has read it
+    if (!batched && !fused) {
       const void *hptr = hc;
       s = txl_mem_update(&ring, 1, &hptr, c.L, stream);
       if (s != TXL_OK) return s;
