@@ -39,8 +39,8 @@ N_RING_SETS = 16
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by the
 # same counters' reading of a plain copy of known size), valid only for the
 # kernel source they were taken on.
-ATTN_TRAFFIC = {"source_sha1": "22e3b613c610427ad79591b9f735966f75701ceb",
-                "rel_attn_mfma_append_kernel": 69.24e6, "rel_attn_mfma_kernel": 52.43e6}
+ATTN_TRAFFIC = {"source_sha1": "68bf396aa18ddc953739b97cc49ff93dcbfb5f44",
+                "rel_attn_mfma_append_kernel": 69.25e6, "rel_attn_mfma_kernel": 52.44e6}
 
 
 def attn_flops(B, H, L, M_eff, d_h):
