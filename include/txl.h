@@ -312,8 +312,10 @@ TXL_API txl_status txl_stack_create(const txl_stack_config *c, const txl_stack_w
 TXL_API size_t txl_segment_step_workspace_bytes(const txl_stack_config *c);
 /* One segment: tokens [B, L] int32 device; mems: n_layer + 1 rings (each
  * [B, M, d] of the stack's dtype; heads are advanced); h_out [B, L, d].
- * Calls with the same workspace must not overlap. Errors: INVALID_ARG,
- * UNSUPPORTED, WORKSPACE, HIP; on an error nothing has been enqueued. */
+ * Calls with the same workspace, or on the same stack (its layers' attention
+ * + ring append launches share counters in the persistent buffer), must not
+ * overlap. Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP; on an error
+ * nothing has been enqueued. */
 TXL_API txl_status txl_segment_step(txl_stack *st, const int32_t *tokens, txl_mem *mems,
                                     void *h_out, void *workspace, size_t ws_bytes,
                                     hipStream_t stream);
