@@ -28,15 +28,22 @@ Parity status of each function (what pins it is listed in the tests):
   attention.rel_attn_bwd                                   pinned (finite
       differences of rel_attn, torch fp64 autograd of a dense formulation,
       softmax identities)
-  memory.tail, memory.update_mems, memory.update_rows      pinned
+  memory.tail_rows, tail, update_mems, update_rows        pinned
   stack.layer_norm, stack.gelu                             pinned (torch fp64)
   stack.sinusoid                                           parity unpinned
       (the pages only say "sinusoidal"; the formula is a stated reading,
        checked for internal properties only)
-  stack.layer_forward, stack.segment_step_row, stack.stream
-      layer body (W^O, post-LayerNorm, GELU feed-forward) parity unpinned:
-      the pages fix Q from H and K/V from [mem; H] but not the rest of the
-      layer; the memory plumbing is pinned by the unrolled-recurrence test.
+  stack.layer_forward (and its steps split_heads, merge_heads, context,
+      r_for_memory, add_norm)                              pinned (closed
+      forms: two torch fp64 LayerNorms with the sublayers off, torch fp64
+      SDPA for the attention sublayer with u = v = W_R = 0, the pinned
+      relative attention on raw states, the capacity-m table equal to the
+      last m + L rows of the capacity-M one, head-permutation invariance;
+      each pin fails on a planted mistake). The layer body itself (W^O,
+      post-LayerNorm, GELU feed-forward) is a reading of this build: the
+      pins fix how it is composed, not that the pages prescribe it.
+  stack.segment_step_row, stack.stream                    pinned (the
+      hand-unrolled recurrence; reset equals a fresh stream)
   evaluation.row_streams                                   pinned (hand-worked
       example from the stream-state contract, stream invariants)
   evaluation.segment_nll                                   pinned (closed form,

@@ -48,12 +48,17 @@ def visible_mask(L: int, M: int, valid: Optional[int] = None) -> np.ndarray:
 def rel_ids(L: int, M: int) -> np.ndarray:
     """Relative distance i - j for every (query i, key position j).
 
-    [P1] section "Relative Shift Golden Test": key positions -M..L-1, query
-    positions 0..L-1, target distance i - j.
+    [P1] section "Relative Shift Golden Test": queries sit at positions
+    0..L-1 and keys at -M..L-1, and the target of entry (i, j) is the
+    distance i - j. Written out per entry: logical key index j' holds key
+    position j = j' - M.
     """
-    key_pos = np.arange(-M, L)
-    query_pos = np.arange(L)
-    return query_pos[:, None] - key_pos[None, :]
+    ids = np.zeros((L, M + L), dtype=np.int64)
+    for i in range(L):
+        for jp in range(M + L):
+            j = jp - M
+            ids[i, jp] = i - j
+    return ids
 
 
 def rel_attn(q, k, v, r, u, vb, valid=None, scale: Optional[float] = None,

@@ -32,7 +32,7 @@ import numpy as np
 from scipy.special import erf
 
 from .attention import rel_attn
-from .memory import tail
+from .memory import tail_rows
 
 LN_EPS = 1e-5
 
@@ -84,6 +84,47 @@ def _f64(w: Dict[str, object]) -> Dict[str, np.ndarray]:
     return {k: np.asarray(v, dtype=np.float64) for k, v in w.items()}
 
 
+def split_heads(x: np.ndarray, H: int, dh: int) -> np.ndarray:
+    """[n, H*dh] -> [H, n, dh]: head h owns columns h*dh .. (h+1)*dh - 1
+    ([P1] "Dimension Walkthrough": the projections are cut into H heads of
+    d_h)."""
+    n = x.shape[0]
+    out = np.empty((H, n, dh))
+    for h in range(H):
+        out[h] = x[:, h * dh:(h + 1) * dh]
+    return out
+
+
+def merge_heads(x: np.ndarray) -> np.ndarray:
+    """[H, n, dh] -> [n, H*dh], the inverse of split_heads."""
+    H, n, dh = x.shape
+    out = np.empty((n, H * dh))
+    for h in range(H):
+        out[:, h * dh:(h + 1) * dh] = x[h]
+    return out
+
+
+def r_for_memory(r_table: np.ndarray, M: int, m: int) -> np.ndarray:
+    """The rows of a capacity-M table ([H, M+L, dh], row t = distance
+    M+L-1-t) that a memory of m <= M stored states needs: distances m+L-1 ..
+    0, i.e. rows M-m .. M+L-1 ([P1] "Dimension Walkthrough": R covers the
+    distances from the farthest key present to the current position)."""
+    r_table = np.asarray(r_table, dtype=np.float64)
+    return r_table[:, M - m:, :]
+
+
+def context(mem: np.ndarray, h: np.ndarray) -> np.ndarray:
+    """The extended context [SG(mem); h] the keys and values are projected
+    from: the stored memory first (oldest first), then the current segment
+    ([P1] "Segment-Level Recurrence", "Batched Tensor Contract")."""
+    return np.concatenate([mem, h], axis=0)
+
+
+def add_norm(x: np.ndarray, f: np.ndarray, g: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Residual then LayerNorm (post-LN): LN(x + f)."""
+    return layer_norm(x + f, g, b)
+
+
 def layer_forward(h: np.ndarray, mem: np.ndarray, lw: Dict[str, np.ndarray],
                   r_table: np.ndarray, M: int, H: int, dh: int) -> np.ndarray:
     """One layer for one batch row.
@@ -93,22 +134,24 @@ def layer_forward(h: np.ndarray, mem: np.ndarray, lw: Dict[str, np.ndarray],
     of capacity M ([H, M+L, dh]); with m < M stored states only its last m+L
     rows (distances m+L-1 .. 0) are used.
     Weights in math orientation: y = x W with W [in, out].
+    Steps: Q from h, K and V from [SG(mem); h] ([P1] "Segment-Level
+    Recurrence"; [P2] section 3), the relative attention of each head, then
+    (reading) X = LN1(h + A W^O), out = LN2(X + GELU(X W1) W2).
     """
     lw = _f64(lw)
     h = np.asarray(h, dtype=np.float64)
     mem = np.asarray(mem, dtype=np.float64)
-    L, d = h.shape
     m = mem.shape[0]
-    ext = np.concatenate([mem, h], axis=0)           # [SG(mem); H]
-    q = (h @ lw["wq"]).reshape(L, H, dh).transpose(1, 0, 2)[None]
-    k = (ext @ lw["wk"]).reshape(m + L, H, dh).transpose(1, 0, 2)[None]
-    v = (ext @ lw["wv"]).reshape(m + L, H, dh).transpose(1, 0, 2)[None]
-    r = np.asarray(r_table, dtype=np.float64)[:, M - m:, :]
+    ext = context(mem, h)                            # [SG(mem); H]
+    q = split_heads(h @ lw["wq"], H, dh)[None]
+    k = split_heads(ext @ lw["wk"], H, dh)[None]
+    v = split_heads(ext @ lw["wv"], H, dh)[None]
+    r = r_for_memory(r_table, M, m)
     att = rel_attn(q, k, v, r, lw["u"], lw["vb"], valid=[m])["out"][0]
-    a = att.transpose(1, 0, 2).reshape(L, H * dh) @ lw["wo"]
-    h1 = layer_norm(h + a, lw["ln1_g"], lw["ln1_b"])
+    a = merge_heads(att) @ lw["wo"]
+    h1 = add_norm(h, a, lw["ln1_g"], lw["ln1_b"])
     f = gelu(h1 @ lw["w1"]) @ lw["w2"]
-    return layer_norm(h1 + f, lw["ln2_g"], lw["ln2_b"])
+    return add_norm(h1, f, lw["ln2_g"], lw["ln2_b"])
 
 
 def segment_step_row(tokens: np.ndarray, mems: Sequence[np.ndarray],
@@ -126,9 +169,7 @@ def segment_step_row(tokens: np.ndarray, mems: Sequence[np.ndarray],
     for n, lw in enumerate(layers):
         h = layer_forward(h, mems[n], lw, r_tables[n], M, H, dh)
         hs.append(h)
-    new_mems = [tail(np.concatenate([np.asarray(mems[n], dtype=np.float64),
-                                     hs[n]], axis=0), M).copy()
-                for n in range(len(layers) + 1)]
+    new_mems = [tail_rows(mems[n], hs[n], M) for n in range(len(layers) + 1)]
     return hs, new_mems
 
 

@@ -23,24 +23,39 @@ def _f64(t):
 
 
 def shift_by_reshape(x: np.ndarray) -> np.ndarray:
-    """The pad -> reshape -> slice alignment described in zty624.github.io
-    "Transformer-XL" notes, section "Relative Shift Trick", written here
-    from its description: prepend one zero column, reread the buffer as
-    [k_len + 1, q_len], drop the first row, reread as [q_len, k_len]."""
+    """The alignment of zty624.github.io "Transformer-XL" notes, section
+    "Relative Shift Trick", stated by where each output entry comes from.
+
+    The page pads one zero column in front of the [q_len, k_len] logits,
+    rereads that buffer as k_len + 1 rows of q_len, drops the first row and
+    rereads the rest as [q_len, k_len]. In flat (row-major) indices: output
+    entry (i, c) is entry f = q_len + i*k_len + c of the padded buffer, whose
+    rows are k_len + 1 long; padded entry f sits in column f mod (k_len + 1)
+    of row f div (k_len + 1), and column 0 is the zero pad while column
+    b > 0 holds logit (row, b - 1)."""
     q_len, k_len = x.shape[-2:]
-    pad = np.zeros(x.shape[:-1] + (1,))
-    padded = np.concatenate([pad, x], axis=-1)
-    reread = padded.reshape(x.shape[:-2] + (k_len + 1, q_len))
-    return reread[..., 1:, :].reshape(x.shape)
+    out = np.zeros(x.shape)
+    for i in range(q_len):
+        for c in range(k_len):
+            f = q_len + i * k_len + c
+            row, col = divmod(f, k_len + 1)
+            if col > 0:
+                out[..., i, c] = x[..., row, col - 1]
+    return out
 
 
 def make_txl_mask(q_len: int, mem_len: int) -> np.ndarray:
-    """The visible-mask construction of the same page, section "Causal Mask
-    With Memory": an all-visible memory block beside a lower-triangular
-    current block (True = visible)."""
-    mem = np.ones((q_len, mem_len), dtype=bool)
-    cur = np.tril(np.ones((q_len, q_len), dtype=bool))
-    return np.concatenate([mem, cur], axis=1)
+    """The visible mask as the same page's section "Causal Mask With Memory"
+    builds it, block by block: an all-visible [q_len, mem_len] memory block
+    beside a lower-triangular [q_len, q_len] block for the current segment
+    (True = visible)."""
+    mask = np.zeros((q_len, mem_len + q_len), dtype=bool)
+    for i in range(q_len):
+        for c in range(mem_len):
+            mask[i, c] = True
+        for c in range(q_len):
+            mask[i, mem_len + c] = c <= i
+    return mask
 
 
 def read_golden_mask(path):
