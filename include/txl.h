@@ -204,12 +204,17 @@ typedef struct {
 /* Append the segment to every ring: with L' = min(L, M), rows
  * h[n][b, L-L'+k, :] go to slot (head + k) mod M of ring n, then
  * head <- (head + L') mod M and valid[b] <- min(M, valid[b] + L).
- * h: host array of n_mems device pointers, each [B, L, d] contiguous.
- * All rings in one call must share B, M, d and dtype; one launch covers all.
- * M == 0 or L == 0: nothing to do. Moves 2*B*L'*d*sizeof(dtype) bytes per ring. */
+ * h: host array of n_mems device pointers, each a [B, L, d] segment whose
+ * row (b, l) starts at element (b*L + l) * h_row_stride (h_row_stride = 0
+ * means d, i.e. contiguous; otherwise >= d, e.g. a view of a wider buffer),
+ * 16-byte aligned rows. All rings in one call must share B, M, d and dtype;
+ * one launch covers all. M == 0 or L == 0: nothing to do. Moves
+ * 2*B*L'*d*sizeof(dtype) bytes per ring.
+ * Errors: INVALID_ARG (ring fields, null h, h_row_stride < d), UNSUPPORTED
+ * (misaligned rows or row strides), HIP. */
 TXL_API txl_status txl_mem_update(txl_mem *mems, int32_t n_mems,
-                                  const void *const *h, int32_t L,
-                                  hipStream_t stream);
+                                  const void *const *h, int64_t h_row_stride,
+                                  int32_t L, hipStream_t stream);
 
 /* Document boundary ([P1] "Batched Streams": the reset flag is per row):
  * valid[b] <- 0 in every ring for rows with reset[b] != 0 (reset: [B] uint8
@@ -219,8 +224,13 @@ TXL_API txl_status txl_mem_reset_rows(txl_mem *mems, int32_t n_mems,
                                       const uint8_t *reset, hipStream_t stream);
 
 /* Copy a ring out in logical order: out[b, j', :] = data[b, (head+j') mod M, :]
- * (out: [B, M, d] contiguous device). Used to checkpoint a stream or to
- * compare memories; rows' invalid prefixes are copied as they are. */
+ * (out: [B, M, d] contiguous device). [P1] "Segment-Level Recurrence": the
+ * memories are the whole recurrent state carried from one segment to the
+ * next, so a stream is checkpointed (or two memories compared) by reading
+ * them out oldest first together with the valid counts; a ring restored
+ * from such a copy with head = 0 continues the stream exactly. Rows'
+ * invalid prefixes are copied as they are.
+ * Errors: INVALID_ARG, UNSUPPORTED (misaligned), HIP. */
 TXL_API txl_status txl_mem_read_logical(const txl_mem *m, void *out,
                                         hipStream_t stream);
 
@@ -314,8 +324,13 @@ TXL_API size_t txl_segment_step_workspace_bytes(const txl_stack_config *c);
  * [B, M, d] of the stack's dtype; heads are advanced); h_out [B, L, d].
  * Calls with the same workspace, or on the same stack (its layers' attention
  * + ring append launches share counters in the persistent buffer), must not
- * overlap. Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP; on an error
- * nothing has been enqueued. */
+ * overlap. Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. Every argument
+ * and shape is checked before the first launch: on INVALID_ARG, UNSUPPORTED
+ * or WORKSPACE nothing has been enqueued and no head has moved. TXL_ERR_HIP
+ * means a kernel launch itself failed part way: the launches before it are
+ * enqueued, the rings whose update was enqueued have advanced their heads,
+ * and the stream of segments cannot continue from that state (restore the
+ * rings from a checkpoint, see txl_mem_read_logical). */
 TXL_API txl_status txl_segment_step(txl_stack *st, const int32_t *tokens, txl_mem *mems,
                                     void *h_out, void *workspace, size_t ws_bytes,
                                     hipStream_t stream);
@@ -359,8 +374,10 @@ TXL_API int32_t txl_kv_cache_min_capacity(const txl_stack_config *c);
  * multiple of 32. Uses the workspace of txl_segment_step (same size). The
  * results equal txl_segment_step's on the same stream of segments and resets
  * (the projections of each row are computed once instead of every segment,
- * in the same order). Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP; on
- * an error nothing has been enqueued. */
+ * in the same order). Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP; as
+ * for txl_segment_step, only TXL_ERR_HIP (a failed launch) can come after
+ * work was enqueued; the caches' starts have then not moved, and the stream
+ * cannot continue from that state. */
 TXL_API txl_status txl_segment_step_kv(txl_stack *st, const int32_t *tokens,
                                        txl_kv_cache *caches, void *h_out, void *workspace,
                                        size_t ws_bytes, hipStream_t stream);

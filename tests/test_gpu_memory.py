@@ -104,3 +104,36 @@ def test_rejects_mismatched_rings():
         txl.txl_mem_update([a, b], [h, torch.zeros((3, 2, 8), device=DEV)])
     assert e.value.status_name == "TXL_ERR_INVALID_ARG"
     assert a.head == 0 and b.head == 0
+
+
+@pytest.mark.parametrize("n_rings", [1, 3])
+@pytest.mark.parametrize("B,M,L,d,extra", [(2, 6, 4, 16, 8), (3, 5, 7, 64, 64),
+                                            (2, 384, 384, 512, 512), (1, 8, 3, 1024, 24)])
+def test_strided_segment_view(B, M, L, d, extra, n_rings):
+    """h_row_stride: each segment is the first d columns of a wider
+    [B, L, d + extra] buffer (row stride d + extra); the ring must equal
+    Tail_M of those d columns, and nothing of the extra columns may enter."""
+    say(f"strided ring B{B} M{M} L{L} d{d} stride {d + extra} rings {n_rings}")
+    g = torch.Generator().manual_seed(B * 7 + M + L + d)
+    mems = [txl.TxlMem.empty(B, M, d, dtype=torch.bfloat16) for _ in range(n_rings)]
+    ref = [[np.zeros((0, d)) for _ in range(B)] for _ in range(n_rings)]
+    for s in range(4):
+        wide = [torch.randn((B, L, d + extra), generator=g).to(torch.bfloat16)
+                for _ in range(n_rings)]
+        views = [w.to(DEV)[:, :, :d] for w in wide]
+        assert views[0].stride(1) == d + extra
+        txl.txl_mem_update(mems, views)
+        for n in range(n_rings):
+            ref[n] = om.update_rows(ref[n], wide[n][:, :, :d].double().numpy(), M)
+            _check_rows(mems[n], ref[n])
+
+
+def test_row_stride_below_width_is_rejected():
+    a = txl.TxlMem.empty(2, 4, 16, dtype=torch.float32)
+    import ctypes
+    from transformer_xl_relative_txl_amd import _binding as bd
+    h = torch.zeros((2, 3, 16), device=DEV)
+    arr = bd._structs([a])
+    ptrs = (ctypes.c_void_p * 1)(h.data_ptr())
+    st = bd.lib().txl_mem_update(arr, 1, ptrs, 8, 3, None)
+    assert st == 1 and a.head == 0

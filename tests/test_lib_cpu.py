@@ -60,7 +60,7 @@ def test_null_and_bad_sizes_rejected_without_gpu(lib):
     a.dtype = 7
     assert lib.txl_rel_attn_fwd(ctypes.byref(a), None) == 1      # bad dtype
     assert lib.txl_rel_pos_table(1, 8, 4, 63, 1, 64, None, None, None) == 1  # odd d
-    assert lib.txl_mem_update(None, -1, None, 4, None) == 1
+    assert lib.txl_mem_update(None, -1, None, 0, 4, None) == 1
     assert lib.txl_mem_reset_rows(None, -1, None, None) == 1
     assert lib.txl_mem_read_logical(None, None, None) == 1
 
@@ -203,3 +203,18 @@ def test_attention_with_ring_append_checks_without_gpu(lib):
     assert m.head == 7                                                # untouched by rejections
     m.B, m.head = 2, 32                                               # head outside [0, M)
     assert call(ctypes.byref(m), fake, fake, need) == 1
+
+
+def test_mem_update_row_stride_checks_without_gpu(lib):
+    """h_row_stride is checked on the host before anything is launched (the
+    device pointers below are never dereferenced)."""
+    from transformer_xl_relative_txl_amd import _binding as bd
+    ring = bd.TxlMemStruct()
+    ring.data, ring.valid, ring.head = 4096, 4096, 0
+    ring.B, ring.M, ring.d, ring.dtype = 2, 4, 16, bd.TXL_F32
+    h = (ctypes.c_void_p * 1)(8192)
+    assert lib.txl_mem_update(ctypes.byref(ring), 1, h, 8, 3, None) == 1      # stride < d
+    assert b"h_row_stride" in lib.txl_last_error()
+    assert lib.txl_mem_update(ctypes.byref(ring), 1, h, 18, 3, None) == 2     # 72-byte rows
+    assert lib.txl_mem_update(ctypes.byref(ring), 1, h, -1, 3, None) == 1
+    assert ring.head == 0

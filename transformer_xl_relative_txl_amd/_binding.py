@@ -126,7 +126,7 @@ def _load() -> ctypes.CDLL:
                                      vp, sz, vp]
     lib.txl_rel_attn_bwd.restype = st
     lib.txl_mem_update.argtypes = [ctypes.POINTER(TxlMemStruct), i32,
-                                   ctypes.POINTER(vp), i32, vp]
+                                   ctypes.POINTER(vp), i64, i32, vp]
     lib.txl_mem_update.restype = st
     lib.txl_rel_attn_fwd_mem_update.argtypes = [ctypes.POINTER(RelAttnArgs),
                                                 ctypes.POINTER(TxlMemStruct), vp, vp, sz, vp]
@@ -164,7 +164,6 @@ def _load() -> ctypes.CDLL:
     lib.txl_lm_loss_workspace_bytes.restype = sz
     lib.txl_lm_loss.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
     lib.txl_lm_loss.restype = st
-    del i64
     return lib
 
 
@@ -351,15 +350,20 @@ def _structs(mems: Sequence[TxlMem]):
 
 def txl_mem_update(mems: Sequence[TxlMem], hs: Sequence[torch.Tensor],
                    stream=None) -> None:
-    """Append segment hs[n] ([B,L,d] contiguous) to ring mems[n]; heads advance."""
+    """Append segment hs[n] ([B,L,d]) to ring mems[n]; heads advance. The
+    segments may be views with any row stride (row (b, l) at
+    (b*L + l) * stride(1) elements, so stride(0) must be L * stride(1)) and
+    a contiguous last dimension; all share that row stride."""
     assert len(mems) == len(hs)
     L = hs[0].shape[1] if hs else 0
+    row = hs[0].stride(1) if hs else 0
     for h in hs:
-        assert h.is_contiguous() and h.shape[1] == L
+        assert h.dim() == 3 and h.shape[1] == L and h.stride(2) == 1 and h.stride(1) == row
+        assert h.shape[0] <= 1 or h.stride(0) == L * row
     arr = _structs(mems)
     ptrs = (ctypes.c_void_p * max(1, len(hs)))(*[h.data_ptr() for h in hs])
     _check("txl_mem_update",
-           lib().txl_mem_update(arr, len(mems), ptrs, L, _stream(stream)))
+           lib().txl_mem_update(arr, len(mems), ptrs, row, L, _stream(stream)))
     for i, m in enumerate(mems):
         m.head = int(arr[i].head)
 

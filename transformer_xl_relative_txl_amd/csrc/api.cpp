@@ -225,7 +225,7 @@ TXL_API txl_status txl_rel_attn_fwd_mem_update(const txl_rel_attn_args *a, txl_m
     rb.valid[0] = mem->valid;
     rb.h[0] = h;
     rb.head[0] = mem->head;
-    st = launch_mem_update(rb, 1, B, M, L, row_bytes, stream);
+    st = launch_mem_update(rb, 1, B, M, L, row_bytes, row_bytes, stream);
   } else {
     RingAppend ra = {};
     ra.h = h;
@@ -350,16 +350,26 @@ static txl_status check_rings(const txl_mem *mems, int32_t n_mems, const char *w
 }
 
 TXL_API txl_status txl_mem_update(txl_mem *mems, int32_t n_mems,
-                                  const void *const *h, int32_t L,
+                                  const void *const *h, int64_t h_row_stride, int32_t L,
                                   hipStream_t stream) {
   clear_error();
   txl_status st = check_rings(mems, n_mems, "mem_update");
   if (st != TXL_OK) return st;
   if (L < 0) return fail(TXL_ERR_INVALID_ARG, "mem_update: L < 0");
+  if (h_row_stride < 0) return fail(TXL_ERR_INVALID_ARG, "mem_update: h_row_stride < 0");
   if (n_mems == 0 || L == 0 || mems[0].M == 0 || mems[0].B == 0) return TXL_OK;
   if (!h) return fail(TXL_ERR_INVALID_ARG, "mem_update: null h array");
   const int64_t row_bytes = static_cast<int64_t>(mems[0].d) * dtype_size(mems[0].dtype);
   if (row_bytes % 16) return fail(TXL_ERR_UNSUPPORTED, "mem_update: d * sizeof(dtype) must be a multiple of 16");
+  const int64_t stride = h_row_stride == 0 ? mems[0].d : h_row_stride;
+  if (stride < mems[0].d)
+    return fail(TXL_ERR_INVALID_ARG, "mem_update: h_row_stride %lld < d = %d",
+                static_cast<long long>(stride), mems[0].d);
+  const int64_t src_row_bytes = stride * static_cast<int64_t>(dtype_size(mems[0].dtype));
+  if (src_row_bytes % 16)
+    return fail(TXL_ERR_UNSUPPORTED, "mem_update: h_row_stride * sizeof(dtype) must be a multiple of 16");
+  if (src_row_bytes / 16 > 0xffffffffLL)
+    return fail(TXL_ERR_UNSUPPORTED, "mem_update: h_row_stride too large");
   for (int i = 0; i < n_mems; ++i) {
     if (!h[i]) return fail(TXL_ERR_INVALID_ARG, "mem_update: h[%d] is null", i);
     if (!aligned16(h[i]) || !aligned16(mems[i].data))
@@ -376,7 +386,7 @@ TXL_API txl_status txl_mem_update(txl_mem *mems, int32_t n_mems,
       rb.h[i] = h[base + i];
       rb.head[i] = mems[base + i].head;
     }
-    st = launch_mem_update(rb, n, mems[0].B, M, L, row_bytes, stream);
+    st = launch_mem_update(rb, n, mems[0].B, M, L, row_bytes, src_row_bytes, stream);
     if (st != TXL_OK) return st;
   }
   for (int i = 0; i < n_mems; ++i) mems[i].head = (mems[i].head + Lp) % M;

@@ -28,6 +28,7 @@ constexpr int kChunks = 1;  // 16-byte chunks per thread (more per thread measur
 struct RingMeta {
   int B, M, L, Lp;
   uint32_t cpr;         // 16-byte chunks per row
+  uint32_t src_cpr;     // 16-byte chunks between consecutive segment rows (>= cpr)
   FastDiv div_cpr, div_lp, div_b;
   uint32_t total;       // chunks in the launch
 };
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void mem_update_kernel(RingBatch rb, Ring
     int64_t slot = rb.head[ring] + k;
     if (slot >= mt.M) slot -= mt.M;
     const int64_t dst_row = static_cast<int64_t>(b) * mt.M + slot;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(rb.h[ring]) + src_row * mt.cpr + c;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(rb.h[ring]) + src_row * mt.src_cpr + c;
     dst[j] = reinterpret_cast<u32x4 *>(rb.data[ring]) + dst_row * mt.cpr + c;
     v[j] = __builtin_nontemporal_load(src);
     if (k == 0 && c == 0) {
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void mem_update_rows_kernel(RingBatch rb,
   int64_t slot = rb.head[ring] + k;
   if (slot >= mt.M) slot -= mt.M;
   const int64_t dst_row = static_cast<int64_t>(b) * mt.M + slot;
-  const u32x4 *src = reinterpret_cast<const u32x4 *>(rb.h[ring]) + src_row * mt.cpr + c;
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(rb.h[ring]) + src_row * mt.src_cpr + c;
   u32x4 *dst = reinterpret_cast<u32x4 *>(rb.data[ring]) + dst_row * mt.cpr + c;
   __builtin_nontemporal_store(__builtin_nontemporal_load(src), dst);
   if (k == 0 && c == 0) {
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void mem_update_one_kernel(u32x4 *__restr
   int64_t slot = head + k;
   if (slot >= mt.M) slot -= mt.M;
   const int64_t dst_row = static_cast<int64_t>(b) * mt.M + slot;
-  __builtin_nontemporal_store(__builtin_nontemporal_load(h + src_row * mt.cpr + c),
+  __builtin_nontemporal_store(__builtin_nontemporal_load(h + src_row * mt.src_cpr + c),
                               data + dst_row * mt.cpr + c);
   if (k == 0 && c == 0) {
     const int nv = valid[b] + mt.L;
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void mem_read_logical_kernel(
 }  // namespace
 
 txl_status launch_mem_update(const RingBatch &rb, int n, int B, int M, int L,
-                             int64_t row_bytes, hipStream_t s) {
+                             int64_t row_bytes, int64_t src_row_bytes, hipStream_t s) {
   RingMeta mt;
   mt.B = B;
   mt.M = M;
@@ -199,6 +200,7 @@ txl_status launch_mem_update(const RingBatch &rb, int n, int B, int M, int L,
   const int64_t total = static_cast<int64_t>(n) * B * mt.Lp * cpr;
   if (total >= (int64_t(1) << 31)) return fail(TXL_ERR_UNSUPPORTED, "mem_update: more than 2^31 chunks");
   mt.cpr = static_cast<uint32_t>(cpr);
+  mt.src_cpr = static_cast<uint32_t>(src_row_bytes / 16);
   mt.div_cpr = make_fastdiv(mt.cpr);
   mt.div_lp = make_fastdiv(static_cast<uint32_t>(mt.Lp));
   mt.div_b = make_fastdiv(static_cast<uint32_t>(B));

@@ -586,16 +586,30 @@ __global__ __launch_bounds__(256) void rel_attn_merge_kernel(AttnParams p) {
 
 }  // namespace
 
-// Raises the kernel's LDS limit once; checks the shapes the buffer loads
-// rely on and returns the grid (query tiles x splits x batch rows x heads).
-static txl_status prepare_launch(const void *kernel, bool *attr_set, const AttnParams &p,
-                                 int *n_qt, int64_t *blocks) {
+// Raises a kernel's LDS limit once per process.
+static txl_status raise_lds_limit(const void *kernel, bool *attr_set) {
   if (!*attr_set) {
     if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(kLdsTotal)) != hipSuccess)
       return fail(TXL_ERR_HIP, "rel_attn: cannot raise the LDS limit to %zu bytes", kLdsTotal);
     *attr_set = true;
   }
+  return TXL_OK;
+}
+static bool g_attr_plain = false, g_attr_append = false;
+
+txl_status rel_attn_mfma_setup() {
+  txl_status st = raise_lds_limit(reinterpret_cast<const void *>(rel_attn_mfma_kernel), &g_attr_plain);
+  if (st != TXL_OK) return st;
+  return raise_lds_limit(reinterpret_cast<const void *>(rel_attn_mfma_append_kernel), &g_attr_append);
+}
+
+// Raises the kernel's LDS limit once; checks the shapes the buffer loads
+// rely on and returns the grid (query tiles x splits x batch rows x heads).
+static txl_status prepare_launch(const void *kernel, bool *attr_set, const AttnParams &p,
+                                 int *n_qt, int64_t *blocks) {
+  txl_status st = raise_lds_limit(kernel, attr_set);
+  if (st != TXL_OK) return st;
   // buffer loads address rows by 32-bit byte offsets from the (batch, head)
   // base and rely on rows not overlapping for the out-of-range zero fill
   if (p.kv_sl < DH || p.r_sl < DH || p.q_sl < DH || p.o_sl < DH)
@@ -611,7 +625,7 @@ static txl_status prepare_launch(const void *kernel, bool *attr_set, const AttnP
 }
 
 txl_status launch_rel_attn_mfma_append(const AttnParams &p, const RingAppend &ra, hipStream_t s) {
-  static bool attr_set = false;
+  bool &attr_set = g_attr_append;
   if (p.n_split > 1) return fail(TXL_ERR_UNSUPPORTED, "rel_attn_append: key splits are not served");
   int n_qt;
   int64_t blocks;
@@ -636,7 +650,8 @@ txl_status launch_rel_attn_mfma_append(const AttnParams &p, const RingAppend &ra
     rb.valid[0] = ra.valid;
     rb.h[0] = ra.h;
     rb.head[0] = ra.head;
-    return launch_mem_update(rb, 1, ra.B, ra.M, ra.L, static_cast<int64_t>(ra.cpr) * 16, s);
+    return launch_mem_update(rb, 1, ra.B, ra.M, ra.L, static_cast<int64_t>(ra.cpr) * 16,
+                             static_cast<int64_t>(ra.cpr) * 16, s);
   }
   RingAppend a = ra;
   a.copy_pos0 = copy_pos0;
@@ -650,7 +665,7 @@ txl_status launch_rel_attn_mfma_append(const AttnParams &p, const RingAppend &ra
 }
 
 txl_status launch_rel_attn_mfma(const AttnParams &p, hipStream_t s) {
-  static bool attr_set = false;
+  bool &attr_set = g_attr_plain;
   int n_qt;
   int64_t blocks;
   txl_status st0 = prepare_launch(reinterpret_cast<const void *>(rel_attn_mfma_kernel), &attr_set,

@@ -56,6 +56,10 @@ txl_status check_config(const txl_stack_config *c) {
   if (c->d > widest) widest = c->d;
   if (krows * widest >= (int64_t(1) << 31) || static_cast<int64_t>(c->vocab) * c->d >= (int64_t(1) << 40))
     return fail(TXL_ERR_UNSUPPORTED, "stack: tensors too large for 32-bit row indexing");
+  // the attention's buffer loads address a head's keys and R rows (plus a
+  // tile of margin) with 32-bit byte offsets
+  if ((static_cast<int64_t>(c->M) + c->L + 96) * hd * 2 >= (int64_t(1) << 31))
+    return fail(TXL_ERR_UNSUPPORTED, "stack: key rows of one head span more than 2 GiB");
   return TXL_OK;
 }
 
@@ -306,6 +310,10 @@ TXL_API txl_status txl_stack_create(const txl_stack_config *c, const txl_stack_w
   const size_t need = txl_stack_persistent_bytes(c);
   if (persistent_bytes < need)
     return fail(TXL_ERR_WORKSPACE, "stack_create: persistent buffer %zu < %zu bytes", persistent_bytes, need);
+  // the attention kernels' LDS limits are raised here, so that a segment
+  // step makes no HIP call but its launches
+  st = rel_attn_mfma_setup();
+  if (st != TXL_OK) return st;
   txl_stack *s = new (std::nothrow) txl_stack;
   if (!s) return fail(TXL_ERR_INVALID_ARG, "stack_create: out of host memory");
   s->cfg = *c;
@@ -399,20 +407,20 @@ TXL_API txl_status txl_segment_step(txl_stack *st, const int32_t *tokens, txl_me
     if (s != TXL_OK) return s;
     if (!batched && !fused) {
       const void *hptr = hc;
-      s = txl_mem_update(&ring, 1, &hptr, c.L, stream);
+      s = txl_mem_update(&ring, 1, &hptr, 0, c.L, stream);
       if (s != TXL_OK) return s;
     }
   }
   if (!batched) {
     const void *top = h_out;
-    return txl_mem_update(&mems[c.n_layer], 1, &top, c.L, stream);
+    return txl_mem_update(&mems[c.n_layer], 1, &top, 0, c.L, stream);
   }
   // every ring takes its H^(n) at once, now that every layer has read its
   // memory and valid counts (ring n is read only by layer n+1)
   std::vector<const void *> hp(c.n_layer + 1);
   for (int n = 0; n < c.n_layer; ++n) hp[n] = slot(n);
   hp[c.n_layer] = h_out;
-  return txl_mem_update(mems, c.n_layer + 1, hp.data(), c.L, stream);
+  return txl_mem_update(mems, c.n_layer + 1, hp.data(), 0, c.L, stream);
 }
 
 TXL_API int32_t txl_kv_cache_min_capacity(const txl_stack_config *c) {

@@ -38,6 +38,10 @@ txl_status launch_rel_attn_valu(const AttnParams &p, txl_dtype dt,
                                 hipStream_t s);
 // bf16 MFMA kernel.
 txl_status launch_rel_attn_mfma(const AttnParams &p, hipStream_t s);
+// Raises the LDS limits of the bf16 attention kernels (done by their first
+// launch otherwise), so that a caller can take this HIP call out of a
+// sequence of launches.
+txl_status rel_attn_mfma_setup();
 
 // floor(n / d) = (umulhi(n, m) + n) >> s for 0 <= n < 2^31, d >= 1
 struct FastDiv {
@@ -104,8 +108,9 @@ struct RingBatch {
   const void *h[kMaxRingsPerLaunch];
   int64_t head[kMaxRingsPerLaunch];
 };
+// segment rows are src_row_bytes apart (>= row_bytes, a multiple of 16)
 txl_status launch_mem_update(const RingBatch &rb, int n, int B, int M, int L,
-                             int64_t row_bytes, hipStream_t s);
+                             int64_t row_bytes, int64_t src_row_bytes, hipStream_t s);
 txl_status launch_mem_reset(int32_t *const *valid, int n, int B,
                             const uint8_t *reset, hipStream_t s);
 txl_status launch_valid_advance(int32_t *const *valid, int n, int B, int M, int L,
