@@ -17,7 +17,9 @@ Prints one JSON line. `value` is attention TFLOP/s over the whole step
 (algorithmic flops: 6*d_h per visible (query, key) pair, masked pairs not
 counted). Every figure replays a captured HIP graph of K launches between
 two HIP events on the launch stream; per-kernel figures come from graphs that
-hold only that kernel.
+hold only that kernel. Before each timed replay the same graph is replayed
+back to back, untimed, for at least SETTLE_MS of GPU time (independent of
+--warmup), so the timed region starts with settled clocks.
 """
 from __future__ import annotations
 
@@ -35,11 +37,14 @@ METRIC = "rel-pos memory attention TFLOP/s (% bf16 MFMA peak) + mem-update GB/s,
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 N_RING_SETS = 16
+# untimed back-to-back replays before every timed figure (GPU time, ms)
+SETTLE_MS = 150.0
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by the
 # same counters' reading of a plain copy of known size), valid only for the
 # kernel source they were taken on.
 ATTN_TRAFFIC = {"source_sha1": "68bf396aa18ddc953739b97cc49ff93dcbfb5f44",
+                "profile": "profiles/rel_attn_B8_H16_L512_M512_hbm_traffic.md",
                 "rel_attn_mfma_append_kernel": 69.25e6, "rel_attn_mfma_kernel": 52.44e6}
 
 
@@ -54,35 +59,83 @@ def attn_hbm_bytes(B, H, L, M, d_h):
     return 2.0 * d_h * (2 * B * H * L + 2 * B * H * (M + L) + H * (M + L))
 
 
-def cpu_baseline(x, cfg, seconds: float):
-    """Time the fp64 oracle on a bounded sample of the same workload: whole
-    (batch row, head) slices, all queries each, cycling over the slices until
-    `seconds` pass."""
-    import numpy as np
+def _oracle_slices_worker(args):
+    """Run the fp64 oracle on whole (batch row, head) slices, cycling over the
+    given slices until `seconds` pass; returns (slices done, flops, seconds).
+    Runs in a fresh process with its math libraries held to one thread."""
+    slices, L, M, d_h, seconds = args
+    import time as _t
+
     from threadpoolctl import threadpool_limits
 
     from oracle import attention as oa
+    done, flops = 0, 0.0
+    t0 = _t.perf_counter()
+    with threadpool_limits(limits=1):
+        while _t.perf_counter() - t0 < seconds:
+            q, k, v, r, u, vb = slices[done % len(slices)]
+            oa.rel_attn(q, k, v, r, u, vb, valid=[M])
+            done += 1
+            flops += attn_flops(1, 1, L, M, d_h)
+    return done, flops, _t.perf_counter() - t0
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(x, cfg, seconds: float):
+    """Time the fp64 oracle as it stands on a bounded sample of the same
+    workload: whole (batch row, head) slices, all queries each. Two runs:
+    one process with one math-library thread, and one process per available
+    core (os.sched_getaffinity, at most 16), each with one thread, on
+    disjoint slices, for `seconds` each; the oracle's rate is the sum."""
+    import multiprocessing as mp
+
+    import numpy as np
+
     from oracle import stack as ost
 
     r = ost.rel_pos_table(x["w_r"].double().numpy(), cfg.M, cfg.L, cfg.H, cfg.d_h)
-    r = r.astype(np.float64)
     q, k, v = (x[n].double().numpy() for n in ("q", "k", "v"))
     u, vb = x["u"].double().numpy(), x["vb"].double().numpy()
-    slices = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
-    done, flops = 0, 0.0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        while time.perf_counter() - t0 < seconds:
-            b, h = slices[done % len(slices)]
-            oa.rel_attn(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
-                        r[h:h + 1], u[h:h + 1], vb[h:h + 1], valid=[cfg.M])
-            done += 1
-            flops += attn_flops(1, 1, cfg.L, cfg.M, cfg.d_h)
-    el = time.perf_counter() - t0
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 oracle rel-attn on {done} (batch row, head) slices of the same "
-                      f"workload ({cfg.B * cfg.H} slices per step), all {cfg.L} queries each, "
-                      f"{el:.1f} s, 1 thread"}
+    order = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+
+    def piece(b, h):
+        return (q[b:b + 1, h:h + 1].copy(), k[b:b + 1, h:h + 1].copy(),
+                v[b:b + 1, h:h + 1].copy(), r[h:h + 1].copy(), u[h:h + 1].copy(),
+                vb[h:h + 1].copy())
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    ctx = mp.get_context("spawn")     # fresh interpreters: no GPU state in the workers
+    runs = {}
+    for n_proc in sorted({1, cores}):
+        parts = []
+        for w in range(n_proc):
+            mine = order[w::n_proc][:max(1, 48 // n_proc)]
+            parts.append(([piece(b, h) for b, h in mine], cfg.L, cfg.M, cfg.d_h, seconds))
+        with ctx.Pool(n_proc) as pool:
+            res = pool.map(_oracle_slices_worker, parts)
+        done = sum(d for d, _, _ in res)
+        flops = sum(f for _, f, _ in res)
+        el = max(e for _, _, e in res)
+        runs[n_proc] = {"value": flops / el / 1e12, "slices": done, "seconds": round(el, 1)}
+    best = runs[cores]
+    return {"value": best["value"], "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 oracle rel-attn on {best['slices']} whole (batch row, head) slices "
+                      f"of the same workload ({cfg.B * cfg.H} slices per step, all {cfg.L} "
+                      f"queries each) in {best['seconds']} s: {cores} processes x 1 thread",
+            "one_thread": {"value": runs[1]["value"], "slices": runs[1]["slices"],
+                           "seconds": runs[1]["seconds"]},
+            "threads_per_process": 1, "affinity_cores": len(os.sched_getaffinity(0)),
+            "cpu_model": _cpu_model()}
 
 
 def stack_flops(c, m_eff, kv=False):
@@ -155,6 +208,13 @@ def stack_bench(name: str, steps: int, warmup: int, kv: bool = False) -> dict:
     g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    for _ in range(int(SETTLE_MS / max(e0.elapsed_time(e1), 1e-3)) + 1):   # settle the clocks
+        g.replay()
+    torch.cuda.synchronize()
     e0.record()
     for _ in range(steps):
         g.replay()
@@ -295,9 +355,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="budget of the oracle CPU baseline (0 skips it)")
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="budget of each of the two oracle CPU baseline runs (0 skips them)")
     ap.add_argument("--stack", choices=["16layer_d512", "18layer_d1024"], default=None,
                     help="measure the N-layer segment step instead (16-layer d=512 "
                          "workload or 18-layer d=1024 long-memory workload)")
@@ -413,8 +473,7 @@ def main() -> int:
     g_attn = capture(lambda i: attn())
     g_mem = capture(lambda i: mem(i))
     g_multi = capture(mem_multi)
-    # W untimed warmup steps, replayed from a graph so the GPU runs them
-    # back to back (its clocks settle before the timed region)
+    # W untimed warmup steps (as passed), replayed from a graph
     if args.warmup > 0:
         g_warm = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_warm):
@@ -423,19 +482,33 @@ def main() -> int:
         g_warm.replay()
         torch.cuda.synchronize()
 
-    def timed(g):
-        for _ in range(3):  # untimed replays: cache state, and >= 25 ms of back-to-back work
+    def settle(g, ms):
+        """Replay g back to back for at least `ms` of GPU time, untimed: a
+        cold or idle GPU needs tens of ms of continuous work before its
+        clocks settle, whatever the warm-up count."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        once = max(e0.elapsed_time(e1), 1e-3)
+        n = max(1, int(ms / once + 0.999))
+        for _ in range(n):
             g.replay()
         torch.cuda.synchronize()
+        return once * (n + 1)
+
+    def timed(g, settle_ms=SETTLE_MS):
+        settled = settle(g, settle_ms)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t = time.perf_counter()
         e0.record()
         g.replay()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / K, time.perf_counter() - t
+        return e0.elapsed_time(e1) / K, time.perf_counter() - t, settled
 
-    step_ms, wall = timed(g_step)
+    step_ms, wall, settled_ms = timed(g_step)
     sep_ms = timed(g_sep)[0]
     attn_ms = timed(g_attn)[0]
     mem_ms = timed(g_mem)[0]
@@ -447,6 +520,10 @@ def main() -> int:
         same_kernel = hashlib.sha1(fh.read()).hexdigest() == ATTN_TRAFFIC["source_sha1"]
     traffic = ATTN_TRAFFIC["rel_attn_mfma_append_kernel"] if same_kernel else None
     attn_traffic = ATTN_TRAFFIC["rel_attn_mfma_kernel"] if same_kernel else None
+    traffic_src = (f"not measured by this run: rocprofv3 FETCH_SIZE and WRITE_SIZE of this "
+                   f"kernel source (sha1 {ATTN_TRAFFIC['source_sha1'][:12]}), scaled by the "
+                   f"same counters' reading of a plain copy; {ATTN_TRAFFIC['profile']}"
+                   if same_kernel else "null: the kernel source differs from the profiled one")
 
     flops = attn_flops(B, H, L, M, dh)
     attn_bytes = attn_hbm_bytes(B, H, L, M, dh)
@@ -476,7 +553,9 @@ def main() -> int:
         "roofline": {"kernel": "rel_attn_mfma_append_kernel", "bound": "mfma",
                      "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "traffic_source": traffic_src,
                      "algorithmic_bytes": round(attn_bytes + mem_bytes)},
+        "settle_ms_before_each_figure": round(settled_ms, 1),
         "step_two_launches_ms": round(sep_ms, 5),
         "attention_alone": {"kernel": "rel_attn_mfma_kernel", "ms": round(attn_ms, 5),
                             "achieved": round(attn_tflops, 2), "unit": "TFLOP/s",
