@@ -83,11 +83,20 @@ def test_bf16_layer_without_memory():
     check(cfg, attn_case(cfg), "B4 H8 L128 M0")
 
 
-def test_bf16_large_layer_full_size_sampled():
-    """The large layer at full size, launched whole; the oracle checks two
-    batch rows x three heads (all 512 queries each)."""
+def test_bf16_large_layer_full_size_every_slice():
+    """The large layer at full size, launched whole as the benchmark launches
+    it; the oracle checks every (batch row, head) slice, all 512 queries
+    each (the tile dealing, XCD placement and copy workers all depend on the
+    workgroup index, so no slice is left out)."""
     cfg = txl_synth.ATTN_CONFIGS["B8_H16_L512_M512"]
-    check(cfg, attn_case(cfg), "B8_H16_L512_M512", b_idx=[0, 7], h_idx=[0, 5, 15])
+    check(cfg, attn_case(cfg), "B8_H16_L512_M512")
+
+
+def test_bf16_large_layer_mixed_valid_every_slice():
+    """The large layer's shape with per-row valid counts (row 0 full, row 1
+    empty, the rest random): every slice against the oracle."""
+    cfg = txl_synth.ATTN_CONFIGS["B8_H16_L512_M512"]
+    check(cfg, attn_case(cfg, seed=21, valid_mode="mixed"), "B8_H16_L512_M512 mixed valid")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -130,9 +130,11 @@ def test_fused_without_mem_valid():
 
 
 def test_fused_bench_layer():
+    """The benchmark's step at full size (B8 H16 L512 M512): bit-identical
+    to the two calls, every (batch row, head) slice against the oracle, the
+    ring against Tail_M, over two consecutive steps."""
     cfg = txl_synth.ATTN_CONFIGS["B8_H16_L512_M512"]
-    _run_case(cfg, B=8, L=512, M=512, H=16, valid_mode="full", head=0, steps=2, seed=1,
-              oracle=False)
+    _run_case(cfg, B=8, L=512, M=512, H=16, valid_mode="full", head=0, steps=2, seed=1)
 
 
 def test_fused_fp32_attention_falls_back():

@@ -81,17 +81,22 @@ class Oracle:
         return ost.layer_forward(h, mem, self.layer(n), self.r(n), c.M, c.H, c.d_h)
 
 
-def run_stream(cfg, w, tokens, resets, check, n_layer, rows_to_check, layers_to_check):
+def run_stream(cfg, w, tokens, resets, check, n_layer, rows_to_check, layers_to_check,
+               all_rows_layer=None):
     """Stream the segments through the GPU stack; at segments in `check`
-    compare memories (all rows, all rings, bit-exact) and the sampled layer
-    outputs (teacher-forced) with the oracle. Returns the max errors."""
+    compare memories (all rows, all rings, bit-exact) and layer outputs
+    (teacher-forced) with the oracle: rows `rows_to_check` at layers
+    `layers_to_check`, and, when `all_rows_layer(s)` is given, every row at
+    that layer of segment s. Returns the worst errors and the number of
+    compared elements beyond 1.5e-2 absolute (the bf16 attention figure)."""
     st, keep = make_stack(cfg, w)
     orc = Oracle(cfg, w)
     M, L, B, d = cfg.M, cfg.L, cfg.B, cfg.d
     assert L <= M, "the last L ring rows hold H^(n) only when L <= M"
     mems = [txl.TxlMem.empty(B, M, d) for _ in range(n_layer + 1)]
     h_out = torch.empty((B, L, d), dtype=torch.bfloat16, device=DEV)
-    worst = {"layer_abs": 0.0, "layer_excess": -1.0}
+    worst = {"layer_abs": 0.0, "layer_excess": -1.0, "n_compared": 0, "n_over_1.5e-2": 0,
+             "min_mem": M, "max_mem": 0}
     tok_d = tokens.to(DEV)
     for s in range(tokens.shape[0]):
         if resets[s].any():
@@ -102,7 +107,7 @@ def run_stream(cfg, w, tokens, resets, check, n_layer, rows_to_check, layers_to_
         if s not in check:
             continue
         after = read_rings(mems)
-        say(f"segment {s}: valid {[int(v) for v in after[0][1][:4]]}...")
+        say(f"segment {s}: valid {[int(v) for v in before[0][1]]} before the step")
         # H^(0) is the embedding of the tokens, exactly
         emb_ref = orc.emb[tokens[s].numpy()]
         assert np.array_equal(after[0][0][:, M - L:], emb_ref)
@@ -116,22 +121,30 @@ def run_stream(cfg, w, tokens, resets, check, n_layer, rows_to_check, layers_to_
                 want = om.tail(np.concatenate([old, hs[b]], axis=0), M)
                 assert valid_a[b] == want.shape[0], (s, n, b)
                 assert np.array_equal(data_a[b, M - valid_a[b]:], want), (s, n, b)
-        for n in layers_to_check:       # layer n maps H^(n-1) -> H^(n), 1-based
-            for b in rows_to_check:
-                data_b, valid_b = before[n - 1]
-                mem = data_b[b, M - valid_b[b]:]
-                h_in = after[n - 1][0][b, M - L:]
-                ref = orc.forward(n - 1, h_in, mem)
-                got = after[n][0][b, M - L:]
-                err = np.abs(got - ref)
-                excess = float((err - (ATOL + RTOL * np.abs(ref))).max())
-                worst["layer_abs"] = max(worst["layer_abs"], float(err.max()))
-                worst["layer_excess"] = max(worst["layer_excess"], excess)
-                say(f"  seg {s} layer {n} row {b} (mem {mem.shape[0]}): max abs err "
-                    f"{err.max():.3e}, mean {err.mean():.2e}")
-                assert excess <= 0.0, (s, n, b, float(err.max()))
+        pairs = {(n, b) for n in layers_to_check for b in rows_to_check}
+        if all_rows_layer is not None:
+            pairs |= {(all_rows_layer(s), b) for b in range(B)}
+        for n, b in sorted(pairs):          # layer n maps H^(n-1) -> H^(n), 1-based
+            data_b, valid_b = before[n - 1]
+            mem = data_b[b, M - valid_b[b]:]
+            h_in = after[n - 1][0][b, M - L:]
+            ref = orc.forward(n - 1, h_in, mem)
+            got = after[n][0][b, M - L:]
+            err = np.abs(got - ref)
+            excess = float((err - (ATOL + RTOL * np.abs(ref))).max())
+            worst["layer_abs"] = max(worst["layer_abs"], float(err.max()))
+            worst["layer_excess"] = max(worst["layer_excess"], excess)
+            worst["n_compared"] += int(err.size)
+            worst["n_over_1.5e-2"] += int((err > ATOL).sum())
+            worst["min_mem"] = min(worst["min_mem"], int(mem.shape[0]))
+            worst["max_mem"] = max(worst["max_mem"], int(mem.shape[0]))
+            say(f"  seg {s} layer {n} row {b} (mem {mem.shape[0]}): max abs err "
+                f"{err.max():.3e}, mean {err.mean():.2e}, beyond 1.5e-2: {int((err > ATOL).sum())}")
+            assert excess <= 0.0, (s, n, b, float(err.max()))
     st.close()
     del keep
+    say(f"  compared {worst['n_compared']} layer-output elements, "
+        f"{worst['n_over_1.5e-2']} beyond 1.5e-2 absolute, worst {worst['layer_abs']:.3e}")
     return worst
 
 
@@ -298,29 +311,73 @@ def test_stack_rejects_bad_arguments():
 
 
 # ----------------------------------------------------------------------------
-# the full-size workloads, sampled
+# the full-size workloads
 # ----------------------------------------------------------------------------
-def test_sixteen_layers_full_size_sampled():
+def test_sixteen_layers_full_size():
     """16 layers, d=512, B=16, L=M=384, 8 segments streamed (full size on the
-    GPU); memories checked for every row and ring at segments 0, 1, 7, layer
-    outputs teacher-forced for rows 0 and 15 at layers 1, 2, 8, 16."""
+    GPU); memories checked for every row and ring at segments 0, 1, 7; every
+    row teacher-forced at one layer per checked segment (16, 8, 1), rows 0
+    and 15 also at layers 1, 2, 8, 16."""
     cfg = txl_synth.STACK_CONFIGS["16layer_d512"]
     w = txl_synth.stack_weights(cfg)
     tokens = txl_synth.stack_tokens(cfg)
     resets = txl_synth.reset_schedule(cfg)
-    worst = run_stream(cfg, w, tokens, resets, check={0, 1, 7}, n_layer=cfg.n_layer,
-                       rows_to_check=[0, cfg.B - 1], layers_to_check=[1, 2, 8, 16])
+    layer_of = {0: 16, 1: 8, 7: 1}
+    worst = run_stream(cfg, w, tokens, resets, check=set(layer_of), n_layer=cfg.n_layer,
+                       rows_to_check=[0, cfg.B - 1], layers_to_check=[1, 2, 8, 16],
+                       all_rows_layer=layer_of.get)
     say(f"16 layers worst: {worst}")
 
 
-def test_eighteen_layers_long_memory_with_resets_sampled():
+def test_eighteen_layers_long_memory_with_resets():
     """18 layers, d=1024, B=8, L=128, M=640, 16 segments with every row
     resetting at segments 0, 4, 8, 12; checks at segments 1, 3, 4 and 15
-    (memories of 128, 384, 0 and 384 states)."""
+    (memories of 128, 384, 0 and 384 states): every row at one layer per
+    checked segment, rows 0 and 7 at layers 1, 9, 18."""
     cfg = txl_synth.STACK_CONFIGS["18layer_d1024"]
     w = txl_synth.stack_weights(cfg)
     tokens = txl_synth.stack_tokens(cfg)
     resets = txl_synth.reset_schedule(cfg)
-    worst = run_stream(cfg, w, tokens, resets, check={1, 3, 4, 15}, n_layer=cfg.n_layer,
-                       rows_to_check=[0, cfg.B - 1], layers_to_check=[1, 9, 18])
+    layer_of = {1: 18, 3: 9, 4: 5, 15: 1}
+    worst = run_stream(cfg, w, tokens, resets, check=set(layer_of), n_layer=cfg.n_layer,
+                       rows_to_check=[0, cfg.B - 1], layers_to_check=[1, 9, 18],
+                       all_rows_layer=layer_of.get)
     say(f"18 layers worst: {worst}")
+
+
+def test_eighteen_layers_steady_state_wrapped_ring():
+    """The 18-layer workload's labelled steady state: 16 segments with no
+    reset after the first, so from segment 5 on every layer attends over a
+    full memory of 640 states and each ring has wrapped (head moves 128 per
+    segment over 640 slots); this is the state the stack benchmark times.
+    Checks at segments 5, 9 and 15: every ring and row bit-exact, every row
+    at one layer per checked segment, rows 0 and 7 at layers 1, 9, 18."""
+    cfg = txl_synth.STACK_CONFIGS["18layer_d1024"]
+    w = txl_synth.stack_weights(cfg)
+    tokens = txl_synth.stack_tokens(cfg)
+    resets = torch.zeros((cfg.n_seg, cfg.B), dtype=torch.uint8)
+    resets[0] = 1
+    layer_of = {5: 18, 9: 2, 15: 10}
+    worst = run_stream(cfg, w, tokens, resets, check=set(layer_of), n_layer=cfg.n_layer,
+                       rows_to_check=[0, cfg.B - 1], layers_to_check=[1, 9, 18],
+                       all_rows_layer=layer_of.get)
+    assert worst["min_mem"] == cfg.M, worst
+    say(f"18 layers steady state worst: {worst}")
+
+
+def test_eighteen_layers_staggered_resets():
+    """The 18-layer workload with the staggered per-row reset schedule: row
+    b resets when (s + b) mod 4 == 0, so the rows of one step hold memories
+    of different lengths (0, 128, 256, 384 states side by side). Checks at
+    segments 2, 5 and 9: every row at one layer, rows 0 and 7 at layers 1
+    and 18."""
+    cfg = txl_synth.STACK_CONFIGS["18layer_d1024"]
+    w = txl_synth.stack_weights(cfg)
+    tokens = txl_synth.stack_tokens(cfg, n_seg=10)
+    resets = txl_synth.reset_schedule(cfg, n_seg=10, staggered=True)
+    layer_of = {2: 1, 5: 12, 9: 18}
+    worst = run_stream(cfg, w, tokens, resets, check=set(layer_of), n_layer=cfg.n_layer,
+                       rows_to_check=[0, cfg.B - 1], layers_to_check=[1, 18],
+                       all_rows_layer=layer_of.get)
+    assert worst["min_mem"] == 0 and worst["max_mem"] == 384, worst
+    say(f"18 layers staggered resets worst: {worst}")
