@@ -265,6 +265,29 @@ TXL_API txl_status txl_rel_attn_fwd_mem_update(const txl_rel_attn_args *a, txl_m
                                                const void *h, void *workspace,
                                                size_t ws_bytes, hipStream_t stream);
 
+/* txl_rel_attn_fwd_mem_update for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same launch and the same results, bit for bit, with the
+ * per-row counters in a static array of the library instead of a workspace.
+ * The call allocates nothing and calls no allocating routine; the caller
+ * still passes every input and output.
+ *
+ * The array is a file-scope device array of 4096 counters 256 bytes apart
+ * (1 MiB), one copy per GPU the library runs on, held until the process
+ * ends; its address is looked up once per device (hipGetSymbolAddress) on
+ * the first call with that device current, so the stream must belong to
+ * the current device. Each call first zeroes the counters of its B rows
+ * with a kernel on `stream` (graph-capturable; no memset) and the attention
+ * launch leaves them zero. Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (on different streams, or two graphs
+ * replayed concurrently) race and must not be made.
+ * Errors: those of txl_rel_attn_fwd_mem_update except WORKSPACE;
+ * UNSUPPORTED when B > 4096; HIP when the device or the symbol cannot be
+ * resolved. */
+TXL_API txl_status txl_rel_attn_fwd_mem_update_noalloc(const txl_rel_attn_args *a,
+                                                       txl_mem *mem, const void *h,
+                                                       hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * One segment through an N-layer stack ([P2] "019 Transformer-XL", section 3
  * pseudo-code; [P1] "Segment-Level Recurrence" and "Training and Inference"):

@@ -218,3 +218,25 @@ def test_mem_update_row_stride_checks_without_gpu(lib):
     assert lib.txl_mem_update(ctypes.byref(ring), 1, h, 18, 3, None) == 2     # 72-byte rows
     assert lib.txl_mem_update(ctypes.byref(ring), 1, h, -1, 3, None) == 1
     assert ring.head == 0
+
+
+def test_noalloc_attention_append_host_checks_without_gpu(lib):
+    """The no-alloc entry point rejects batch counts beyond its static
+    counters, and the usual argument errors, before anything is launched
+    (the pointers below are never dereferenced)."""
+    from transformer_xl_relative_txl_amd import _binding as bd
+    a = bd.RelAttnArgs()
+    a.dtype, a.B, a.H, a.L, a.M, a.d_h = bd.TXL_BF16, 4097, 1, 8, 8, 64
+    for n in ("q", "k", "v", "r", "u", "vb", "out"):
+        setattr(a, n, 4096)
+    a.q_sl = a.kv_sl = a.r_sl = a.o_sl = 64
+    ring = bd.TxlMemStruct()
+    ring.data, ring.valid, ring.head = 4096, 4096, 0
+    ring.B, ring.M, ring.d, ring.dtype = 4097, 8, 64, bd.TXL_BF16
+    st = lib.txl_rel_attn_fwd_mem_update_noalloc(ctypes.byref(a), ctypes.byref(ring), 8192, None)
+    assert st == 2 and b"4096" in lib.txl_last_error()
+    ring.M = 9                                          # ring differs from the attention
+    assert lib.txl_rel_attn_fwd_mem_update_noalloc(ctypes.byref(a), ctypes.byref(ring),
+                                                   8192, None) == 1
+    assert lib.txl_rel_attn_fwd_mem_update_noalloc(None, None, None, None) == 1
+    assert ring.head == 0

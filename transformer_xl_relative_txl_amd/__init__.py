@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     txl_rel_attn_bwd_workspace_bytes,
     txl_rel_attn_fwd,
     txl_rel_attn_fwd_mem_update,
+    txl_rel_attn_fwd_mem_update_noalloc,
     txl_rel_attn_mem_update_workspace,
     txl_rel_pos_table,
     txl_version,

@@ -131,6 +131,9 @@ def _load() -> ctypes.CDLL:
     lib.txl_rel_attn_fwd_mem_update.argtypes = [ctypes.POINTER(RelAttnArgs),
                                                 ctypes.POINTER(TxlMemStruct), vp, vp, sz, vp]
     lib.txl_rel_attn_fwd_mem_update.restype = st
+    lib.txl_rel_attn_fwd_mem_update_noalloc.argtypes = [ctypes.POINTER(RelAttnArgs),
+                                                        ctypes.POINTER(TxlMemStruct), vp, vp]
+    lib.txl_rel_attn_fwd_mem_update_noalloc.restype = st
     lib.txl_rel_attn_mem_update_workspace_bytes.argtypes = [i32]
     lib.txl_rel_attn_mem_update_workspace_bytes.restype = sz
     lib.txl_mem_reset_rows.argtypes = [ctypes.POINTER(TxlMemStruct), i32, vp, vp]
@@ -393,6 +396,25 @@ def txl_rel_attn_fwd_mem_update(q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
     return out
 
 
+def txl_rel_attn_fwd_mem_update_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                        r: torch.Tensor, u: torch.Tensor, vb: torch.Tensor,
+                                        out: torch.Tensor, mem: TxlMem, h: torch.Tensor,
+                                        mem_valid: Optional[torch.Tensor] = None,
+                                        lse: Optional[torch.Tensor] = None, scale: float = 0.0,
+                                        stream=None) -> torch.Tensor:
+    """txl_rel_attn_fwd_mem_update with the library's static counters: the
+    call allocates nothing (for graph capture and serving loops). Calls that
+    overlap on one GPU race."""
+    assert h.is_contiguous()
+    a = _attn_args(q, k, v, r, u, vb, out, mem_valid, lse, scale)
+    s = mem._struct()
+    _check("txl_rel_attn_fwd_mem_update_noalloc",
+           lib().txl_rel_attn_fwd_mem_update_noalloc(ctypes.byref(a), ctypes.byref(s), _ptr(h),
+                                                     _stream(stream)))
+    mem.head = int(s.head)
+    return out
+
+
 def txl_rel_attn_mem_update_workspace(B: int, device="cuda") -> torch.Tensor:
     """Zeroed counters for txl_rel_attn_fwd_mem_update (keep and reuse them)."""
     n = int(lib().txl_rel_attn_mem_update_workspace_bytes(B))
@@ -616,7 +638,7 @@ def exported_symbols() -> List[str]:
     return ["txl_rel_pos_table", "txl_rel_attn_fwd", "txl_rel_attn_split_workspace_bytes",
             "txl_rel_attn_fwd_split", "txl_rel_attn_bwd_workspace_bytes", "txl_rel_attn_bwd",
             "txl_mem_update", "txl_rel_attn_fwd_mem_update",
-            "txl_rel_attn_mem_update_workspace_bytes",
+            "txl_rel_attn_fwd_mem_update_noalloc", "txl_rel_attn_mem_update_workspace_bytes",
             "txl_mem_reset_rows", "txl_mem_read_logical", "txl_stack_persistent_bytes",
             "txl_stack_create", "txl_segment_step_workspace_bytes", "txl_segment_step",
             "txl_stack_destroy", "txl_kv_cache_min_capacity", "txl_segment_step_kv",

@@ -181,42 +181,50 @@ TXL_API size_t txl_rel_attn_mem_update_workspace_bytes(int32_t B) {
   return B > 0 ? static_cast<size_t>(B) * 256 : 0;
 }
 
-TXL_API txl_status txl_rel_attn_fwd_mem_update(const txl_rel_attn_args *a, txl_mem *mem,
-                                               const void *h, void *workspace, size_t ws_bytes,
-                                               hipStream_t stream) {
-  clear_error();
+// The attention and the ring append, with the per-row counters either in
+// the caller's workspace (counters != null, checked by the caller) or in the
+// library's static array (counters == null: no-alloc entry point).
+static txl_status attn_mem_update(const txl_rel_attn_args *a, txl_mem *mem, const void *h,
+                                  void *workspace, size_t ws_bytes, bool noalloc,
+                                  hipStream_t stream) {
+  const char *who = noalloc ? "rel_attn_mem_update_noalloc" : "rel_attn_mem_update";
   AttnParams p;
   bool nothing;
   txl_status st = attn_params(a, &p, &nothing);
   if (st != TXL_OK) return st;
-  if (!mem) return fail(TXL_ERR_INVALID_ARG, "rel_attn_mem_update: null ring");
-  st = check_rings(mem, 1, "rel_attn_mem_update");
+  if (!mem) return fail(TXL_ERR_INVALID_ARG, "%s: null ring", who);
+  st = check_rings(mem, 1, who);
   if (st != TXL_OK) return st;
   if (mem->B != a->B || mem->M != a->M)
-    return fail(TXL_ERR_INVALID_ARG, "rel_attn_mem_update: ring B, M (%d, %d) differ from the "
-                "attention's (%d, %d)", mem->B, mem->M, a->B, a->M);
+    return fail(TXL_ERR_INVALID_ARG, "%s: ring B, M (%d, %d) differ from the "
+                "attention's (%d, %d)", who, mem->B, mem->M, a->B, a->M);
   if (nothing) return TXL_OK;  // B == 0 or L == 0: no attention and no append
   if (mem->M == 0)             // nothing to append
     return a->dtype == TXL_BF16 ? launch_rel_attn_mfma(p, stream)
                                 : launch_rel_attn_valu(p, a->dtype, stream);
-  if (!h) return fail(TXL_ERR_INVALID_ARG, "rel_attn_mem_update: null h");
+  if (!h) return fail(TXL_ERR_INVALID_ARG, "%s: null h", who);
   const int64_t row_bytes = static_cast<int64_t>(mem->d) * dtype_size(mem->dtype);
   if (row_bytes % 16)
-    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_mem_update: d * sizeof(dtype) must be a multiple of 16");
+    return fail(TXL_ERR_UNSUPPORTED, "%s: d * sizeof(dtype) must be a multiple of 16", who);
   if (!aligned16(h) || !aligned16(mem->data))
-    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_mem_update: ring or h not 16-byte aligned");
+    return fail(TXL_ERR_UNSUPPORTED, "%s: ring or h not 16-byte aligned", who);
   const int B = mem->B, M = mem->M, L = a->L;
-  const size_t need = txl_rel_attn_mem_update_workspace_bytes(B);
-  if (!workspace || ws_bytes < need)
-    return fail(TXL_ERR_WORKSPACE, "rel_attn_mem_update: workspace %zu < %zu bytes", ws_bytes, need);
-  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-    return fail(TXL_ERR_UNSUPPORTED, "rel_attn_mem_update: workspace not 256-byte aligned");
+  if (!noalloc) {
+    const size_t need = txl_rel_attn_mem_update_workspace_bytes(B);
+    if (!workspace || ws_bytes < need)
+      return fail(TXL_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(TXL_ERR_UNSUPPORTED, "%s: workspace not 256-byte aligned", who);
+  } else if (B > kNoAllocMaxRows) {
+    return fail(TXL_ERR_UNSUPPORTED, "%s: B = %d exceeds the %d batch rows of the static counters",
+                who, B, kNoAllocMaxRows);
+  }
   const int Lp = L < M ? L : M;
   const int64_t h_bytes = static_cast<int64_t>(B) * L * row_bytes;
   const int64_t data_bytes = static_cast<int64_t>(B) * M * row_bytes;
   const int64_t limit = (int64_t(1) << 31) - 16;
   if (a->dtype != TXL_BF16 || h_bytes >= limit || data_bytes >= limit) {
-    // the two as separate launches (same results)
+    // the two as separate launches (same results, no counters)
     st = a->dtype == TXL_BF16 ? launch_rel_attn_mfma(p, stream)
                               : launch_rel_attn_valu(p, a->dtype, stream);
     if (st != TXL_OK) return st;
@@ -227,11 +235,16 @@ TXL_API txl_status txl_rel_attn_fwd_mem_update(const txl_rel_attn_args *a, txl_m
     rb.head[0] = mem->head;
     st = launch_mem_update(rb, 1, B, M, L, row_bytes, row_bytes, stream);
   } else {
+    uint32_t *done = static_cast<uint32_t *>(workspace);
+    if (noalloc) {
+      st = noalloc_counters(B, stream, &done);
+      if (st != TXL_OK) return st;
+    }
     RingAppend ra = {};
     ra.h = h;
     ra.data = mem->data;
     ra.valid = mem->valid;
-    ra.done = static_cast<uint32_t *>(workspace);
+    ra.done = done;
     ra.head = mem->head;
     ra.B = B;
     ra.M = M;
@@ -248,6 +261,19 @@ TXL_API txl_status txl_rel_attn_fwd_mem_update(const txl_rel_attn_args *a, txl_m
   if (st != TXL_OK) return st;
   mem->head = (mem->head + Lp) % M;
   return TXL_OK;
+}
+
+TXL_API txl_status txl_rel_attn_fwd_mem_update(const txl_rel_attn_args *a, txl_mem *mem,
+                                               const void *h, void *workspace, size_t ws_bytes,
+                                               hipStream_t stream) {
+  clear_error();
+  return attn_mem_update(a, mem, h, workspace, ws_bytes, false, stream);
+}
+
+TXL_API txl_status txl_rel_attn_fwd_mem_update_noalloc(const txl_rel_attn_args *a, txl_mem *mem,
+                                                       const void *h, hipStream_t stream) {
+  clear_error();
+  return attn_mem_update(a, mem, h, nullptr, 0, true, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -54,6 +54,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "txl_internal.h"
 
@@ -584,7 +585,57 @@ __global__ __launch_bounds__(256) void rel_attn_merge_kernel(AttnParams p) {
   if (p.lse && c == 0) p.lse[row] = (m + log2f(l)) * 0.6931471805599453f;
 }
 
+// Zeroes the counters of n batch rows (kCounterStride apart).
+__global__ __launch_bounds__(256) void counters_clear_kernel(uint32_t *done, int n) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b < n) done[b * kCounterStride] = 0u;
+}
+
 }  // namespace
+
+// The per-row counters of txl_rel_attn_fwd_mem_update_noalloc, for callers
+// that cannot allocate: a file-scope device array, one copy per GPU, held
+// until the process ends. Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol); it uses the
+// device address hipGetSymbolAddress returns, looked up once per device.
+static __device__ __align__(256) uint32_t scratch[kNoAllocMaxRows * kCounterStride];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+txl_status noalloc_counters(int B, hipStream_t s, uint32_t **out) {
+  if (B > kNoAllocMaxRows)
+    return fail(TXL_ERR_UNSUPPORTED,
+                "rel_attn_mem_update_noalloc: B = %d exceeds the %d batch rows of the static counters",
+                B, kNoAllocMaxRows);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(TXL_ERR_HIP, "rel_attn_mem_update_noalloc: no usable current device (%d)", dev);
+  uint32_t *ptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void *p = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return fail(TXL_ERR_HIP, "rel_attn_mem_update_noalloc: hipGetSymbolAddress: %s",
+                    hipGetErrorString(e));
+      g_scratch_ptr[dev] = static_cast<uint32_t *>(p);
+    }
+    ptr = g_scratch_ptr[dev];
+  }
+  // every call starts from zeroed counters (a kernel, not a memset, so the
+  // call can be captured in a graph); the attention launch leaves them zero
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(counters_clear_kernel, dim3((B + 255) / 256), dim3(256), 0, s, ptr, B);
+  const txl_status st = check_launch("counters_clear_kernel");
+  if (st != TXL_OK) return st;
+  *out = ptr;
+  return TXL_OK;
+}
 
 // Raises a kernel's LDS limit once per process.
 static txl_status raise_lds_limit(const void *kernel, bool *attr_set) {

@@ -80,6 +80,11 @@ struct RingAppend {
 };
 // The attention of p (n_split must be 1) and the append of ra in one launch.
 txl_status launch_rel_attn_mfma_append(const AttnParams &p, const RingAppend &ra, hipStream_t s);
+// Batch rows served by the static counters of the no-alloc entry point.
+constexpr int kNoAllocMaxRows = 4096;
+// The static counters of the current device for B batch rows (B <=
+// kNoAllocMaxRows), zeroed by a kernel enqueued on s.
+txl_status noalloc_counters(int B, hipStream_t s, uint32_t **out);
 
 // gradients (bf16 inputs): p holds the forward's arguments (out = the
 // forward's output); g the incoming gradient, the forward's lse, the fp32
