@@ -17,9 +17,10 @@ Prints one JSON line. `value` is attention TFLOP/s over the whole step
 (algorithmic flops: 6*d_h per visible (query, key) pair, masked pairs not
 counted). Every figure replays a captured HIP graph of K launches between
 two HIP events on the launch stream; per-kernel figures come from graphs that
-hold only that kernel. Before each timed replay the same graph is replayed
-back to back, untimed, for at least SETTLE_MS of GPU time (independent of
---warmup), so the timed region starts with settled clocks.
+hold only that kernel. Before each figure the same graph is replayed back to
+back, untimed, for at least SETTLE_MS of GPU time (independent of --warmup),
+so the timed regions start with settled clocks; each figure is the median of
+TIMED_REPEATS timed replays of exactly K steps.
 """
 from __future__ import annotations
 
@@ -39,6 +40,8 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 N_RING_SETS = 16
 # untimed back-to-back replays before every timed figure (GPU time, ms)
 SETTLE_MS = 150.0
+# timed replays of K steps per figure; the median is reported
+TIMED_REPEATS = 5
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by the
 # same counters' reading of a plain copy of known size), valid only for the
@@ -499,16 +502,27 @@ def main() -> int:
         return once * (n + 1)
 
     def timed(g, settle_ms=SETTLE_MS):
+        """Settle, then TIMED_REPEATS timed replays of exactly K steps, each
+        between a synchronize and two HIP events on the launch stream; the
+        figure is their median (a rare multi-microsecond stall of the device
+        lands in one repeat, not in the figure), all repeats are reported."""
         settled = settle(g, settle_ms)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t = time.perf_counter()
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / K, time.perf_counter() - t, settled
+        reps, walls = [], []
+        for _ in range(TIMED_REPEATS):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            walls.append(time.perf_counter() - t)
+            reps.append(e0.elapsed_time(e1) / K)
+        order = sorted(range(len(reps)), key=lambda j: reps[j])
+        mid = order[len(order) // 2]
+        return reps[mid], walls[mid], settled, reps
 
-    step_ms, wall, settled_ms = timed(g_step)
+    step_ms, wall, settled_ms, step_reps = timed(g_step)
     sep_ms = timed(g_sep)[0]
     attn_ms = timed(g_attn)[0]
     mem_ms = timed(g_mem)[0]
@@ -556,6 +570,7 @@ def main() -> int:
                      "traffic_source": traffic_src,
                      "algorithmic_bytes": round(attn_bytes + mem_bytes)},
         "settle_ms_before_each_figure": round(settled_ms, 1),
+        "ms_per_step_repeats": [round(x, 5) for x in step_reps],
         "step_two_launches_ms": round(sep_ms, 5),
         "attention_alone": {"kernel": "rel_attn_mfma_kernel", "ms": round(attn_ms, 5),
                             "achieved": round(attn_tflops, 2), "unit": "TFLOP/s",

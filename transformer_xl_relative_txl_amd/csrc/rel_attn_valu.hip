@@ -31,9 +31,7 @@ constexpr int RT = KT + QT - 1;    // R rows one tile needs
 constexpr int RP = DH + 1;         // padded R row: conflict-free skewed reads
 
 __device__ inline float ld(const float *p) { return *p; }
-__device__ inline float ld(const __bf16 *p) { return static_cast<float>(*p); }
 __device__ inline void st(float *p, float x) { *p = x; }
-__device__ inline void st(__bf16 *p, float x) { *p = static_cast<__bf16>(x); }
 
 template <typename T>
 __global__ __launch_bounds__(QT) void rel_attn_valu_kernel(AttnParams p) {
@@ -137,12 +135,11 @@ __global__ __launch_bounds__(QT) void rel_attn_valu_kernel(AttnParams p) {
 txl_status launch_rel_attn_valu(const AttnParams &p, txl_dtype dt,
                                 hipStream_t s) {
   if (p.H > 65535 || p.B > 65535) return fail(TXL_ERR_UNSUPPORTED, "rel_attn: B or H > 65535");
+  // fp32 only: bf16 attention always runs the MFMA kernel
+  if (dt != TXL_F32) return fail(TXL_ERR_UNSUPPORTED, "rel_attn: the VALU kernel serves fp32 only");
   const dim3 grid((p.L + QT - 1) / QT, p.H, p.B);
   (void)hipGetLastError();
-  if (dt == TXL_F32)
-    hipLaunchKernelGGL(rel_attn_valu_kernel<float>, grid, dim3(QT), 0, s, p);
-  else
-    hipLaunchKernelGGL(rel_attn_valu_kernel<__bf16>, grid, dim3(QT), 0, s, p);
+  hipLaunchKernelGGL(rel_attn_valu_kernel<float>, grid, dim3(QT), 0, s, p);
   return check_launch("rel_attn_valu_kernel");
 }
 
