@@ -8,8 +8,8 @@ resident in HBM before timing starts; the relative-position table R (a
 function of the weights and of M, L only) is built once by the library
 before timing. Each timed step is txl_rel_attn_fwd_mem_update: the
 attention, masked by the ring's valid counts, and the append of the segment
-to that ring, in one launch; the step rotates over 16 ring/segment buffer
-pairs (268 MB) so that the append is not served from the 256 MB last-level
+to that ring, in one launch; the step rotates over 32 ring/segment buffer
+pairs (537 MB) so that the append is not served from the 256 MB last-level
 cache. The same step as two launches (txl_rel_attn_fwd, then txl_mem_update)
 and each of those alone are timed as well.
 
@@ -37,7 +37,7 @@ if ROOT not in sys.path:
 METRIC = "rel-pos memory attention TFLOP/s (% bf16 MFMA peak) + mem-update GB/s, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-N_RING_SETS = 16
+N_RING_SETS = 32   # rotating ring / segment pairs: 537 MB, past the 256 MB last-level cache twice
 # untimed back-to-back replays before every timed figure (GPU time, ms)
 SETTLE_MS = 150.0
 # timed replays of K steps per figure; the median is reported
@@ -354,6 +354,68 @@ def bwd_bench(steps: int, warmup: int) -> dict:
             "gflop_per_step": round(fl / 1e9, 2)}
 
 
+def mem_sweep_bench(steps: int) -> dict:
+    """The single-ring update (txl_mem_update of one ring) at segment sizes
+    moving 4 to 134 MB per launch: B=8, d=1024 bf16, L = M = 128 .. 4096
+    (every slot replaced), each size rotating over ring / segment pairs that
+    span at least 1 GiB (cold last-level cache), replayed as a captured graph
+    of `steps` launches after a settle; the median of five timed replays."""
+    import torch
+
+    import transformer_xl_relative_txl_amd as txl
+
+    dev = torch.device("cuda:0")
+    B, d = 8, 1024
+    rows = []
+    for L in (128, 256, 512, 1024, 2048, 4096):
+        moved = 2.0 * B * L * d * 2
+        n_sets = max(4, int((1 << 30) // moved) + 1)
+        rings = [txl.TxlMem(torch.zeros((B, L, d), dtype=torch.bfloat16, device=dev),
+                            torch.full((B,), L, dtype=torch.int32, device=dev), 0)
+                 for _ in range(n_sets)]
+        segs = [torch.ones((B, L, d), dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
+
+        def upd(i):
+            txl.txl_mem_update([rings[i % n_sets]], [segs[i % n_sets]])
+
+        for i in range(n_sets):
+            upd(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                upd(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        for _ in range(int(SETTLE_MS / max(e0.elapsed_time(e1), 1e-3)) + 1):
+            g.replay()
+        reps = []
+        for _ in range(TIMED_REPEATS):
+            torch.cuda.synchronize()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1) / steps)
+        ms = sorted(reps)[len(reps) // 2]
+        gbps = moved / (ms * 1e-3) / 1e9
+        rows.append({"L": L, "MB_per_launch": round(moved / 1e6, 1), "us": round(ms * 1e3, 2),
+                     "GB_per_s": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "rotating_MB": round(n_sets * moved / 1e6)})
+        del rings, segs, g
+        torch.cuda.empty_cache()
+    return {"metric": "single-ring memory update GB/s by size (cold cache), 1 GPU",
+            "value": rows[2]["GB_per_s"], "unit": "GB/s", "n_gpus": 1, "steps": steps,
+            "warmup": 0, "ms_per_step": rows[2]["us"] / 1e3, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "txl_mem_update of one ring [8, L, 1024], L = M, value at "
+                                   "L = 512 (16.8 MB)"},
+            "sweep": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -370,6 +432,8 @@ def main() -> int:
                     help="measure the segment loss (logits + cross entropy) instead")
     ap.add_argument("--bwd", action="store_true",
                     help="measure the attention gradients (txl_rel_attn_bwd) instead")
+    ap.add_argument("--mem-sweep", action="store_true",
+                    help="measure the single-ring update at 4 to 134 MB per launch instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not run. The step shards "
@@ -382,6 +446,9 @@ def main() -> int:
         return 0
     if args.bwd:
         print(json.dumps(bwd_bench(args.steps, args.warmup)), flush=True)
+        return 0
+    if args.mem_sweep:
+        print(json.dumps(mem_sweep_bench(args.steps)), flush=True)
         return 0
     if args.stack:
         print(json.dumps(stack_bench(args.stack, args.steps, args.warmup, args.kv)), flush=True)
