@@ -44,6 +44,12 @@ Parity status of each function (what pins it is listed in the tests):
       pins fix how it is composed, not that the pages prescribe it.
   stack.segment_step_row, stack.stream                    pinned (the
       hand-unrolled recurrence; reset equals a fresh stream)
+  stack.layer_backward, segment_backward_row,
+      layer_norm_backward, gelu_grad                      pinned (central
+      finite differences of the pinned forward for every entry of every
+      weight, the segment input and the embedding rows, with the memory held
+      fixed as the stop-gradient input it is; planted mistakes in the
+      LayerNorm and GELU derivatives fail them)
   evaluation.row_streams                                   pinned (hand-worked
       example from the stream-state contract, stream invariants)
   evaluation.segment_nll                                   pinned (closed form,

@@ -31,7 +31,7 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 from scipy.special import erf
 
-from .attention import rel_attn
+from .attention import rel_attn, rel_attn_bwd
 from .memory import tail_rows
 
 LN_EPS = 1e-5
@@ -202,3 +202,116 @@ def stream(tokens: np.ndarray, resets: np.ndarray, emb: np.ndarray,
             seg[b] = hs
         out.append(seg)
     return out
+
+
+# ----------------------------------------------------------------------------
+# gradients of one segment (training)
+# ----------------------------------------------------------------------------
+def gelu_grad(x: np.ndarray) -> np.ndarray:
+    """d/dx of the exact GELU x Phi(x): Phi(x) + x phi(x)."""
+    return 0.5 * (1.0 + erf(x / math.sqrt(2.0))) + x * np.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+
+
+def layer_norm_backward(x: np.ndarray, g: np.ndarray, dy: np.ndarray, eps: float = LN_EPS):
+    """Gradients of y = layer_norm(x, g, b) over the last axis: returns
+    (dx, dg, db) for the incoming dy, written out by the chain rule through
+    the mean and the biased variance (xhat = (x - mean) r, r = 1/sqrt(var+eps)):
+        dg = sum_rows dy xhat,   db = sum_rows dy,
+        dx = r (gdy - mean(gdy) - xhat mean(gdy xhat)),  gdy = dy g."""
+    x = np.asarray(x, dtype=np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    r = 1.0 / np.sqrt(((x - mu) ** 2).mean(axis=-1, keepdims=True) + eps)
+    xhat = (x - mu) * r
+    gdy = dy * g
+    dx = r * (gdy - gdy.mean(axis=-1, keepdims=True)
+              - xhat * (gdy * xhat).mean(axis=-1, keepdims=True))
+    return dx, (dy * xhat).sum(axis=0), dy.sum(axis=0)
+
+
+def layer_backward(h: np.ndarray, mem: np.ndarray, lw: Dict[str, np.ndarray],
+                   wr: np.ndarray, M: int, H: int, dh: int, dy: np.ndarray):
+    """Gradients of one layer (layer_forward) for one batch row.
+
+    dy [L, d] is the gradient arriving at the layer's output. The memory is
+    a stop-gradient input ([P1] "Why Stop Gradient"; [P2] section
+    "stop-gradient到底切断哪里"): nothing is returned for it, but the keys and
+    values projected from its rows are part of this segment's computation,
+    so W^K and W^V receive their gradient from the memory rows as well.
+    R is built from the layer's W_R (wr [d, H*dh], math orientation) as in
+    rel_pos_table, so W_R gets its gradient through R.
+
+    Returns (dh_in [L, d], grads) with grads holding one array per weight of
+    layer_forward (wq, wk, wv, wo, wr, u, vb, ln1_g, ln1_b, w1, w2, ln2_g,
+    ln2_b), each the exact derivative of sum(dy * out) in float64.
+    """
+    lw = _f64(lw)
+    h = np.asarray(h, dtype=np.float64)
+    mem = np.asarray(mem, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    L, d = h.shape
+    m = mem.shape[0]
+    # forward, keeping what the backward needs
+    r_table = rel_pos_table(wr, M, L, H, dh)
+    ext = context(mem, h)
+    q = split_heads(h @ lw["wq"], H, dh)[None]
+    k = split_heads(ext @ lw["wk"], H, dh)[None]
+    v = split_heads(ext @ lw["wv"], H, dh)[None]
+    r = r_for_memory(r_table, M, m)
+    att = rel_attn(q, k, v, r, lw["u"], lw["vb"], valid=[m])["out"][0]
+    o = merge_heads(att)
+    x1 = h + o @ lw["wo"]
+    h1 = layer_norm(x1, lw["ln1_g"], lw["ln1_b"])
+    fpre = h1 @ lw["w1"]
+    f = gelu(fpre)
+    x2 = h1 + f @ lw["w2"]
+    # backward
+    g = {}
+    dx2, g["ln2_g"], g["ln2_b"] = layer_norm_backward(x2, lw["ln2_g"], dy)
+    g["w2"] = f.T @ dx2
+    dfpre = (dx2 @ lw["w2"].T) * gelu_grad(fpre)
+    g["w1"] = h1.T @ dfpre
+    dh1 = dfpre @ lw["w1"].T + dx2
+    dx1, g["ln1_g"], g["ln1_b"] = layer_norm_backward(x1, lw["ln1_g"], dh1)
+    g["wo"] = o.T @ dx1
+    datt = split_heads(dx1 @ lw["wo"].T, H, dh)[None]
+    ag = rel_attn_bwd(q, k, v, r, lw["u"], lw["vb"], datt, valid=[m])
+    dq = merge_heads(ag["dq"][0])
+    dk = merge_heads(ag["dk"][0])
+    dv = merge_heads(ag["dv"][0])
+    g["wq"] = h.T @ dq
+    g["wk"] = ext.T @ dk          # memory rows included: they feed W^K ...
+    g["wv"] = ext.T @ dv
+    g["u"] = ag["du"]
+    g["vb"] = ag["dvb"]
+    # ... but the gradient stops there: only the segment rows reach h
+    dh_in = dq @ lw["wq"].T + dk[m:] @ lw["wk"].T + dv[m:] @ lw["wv"].T + dx1
+    # W_R: R[h] = S W_R[:, head h] with S the sinusoid of distances M+L-1..0;
+    # the table rows a memory of m states uses are its last m+L
+    dr_full = np.zeros_like(r_table)
+    dr_full[:, M - m:, :] = ag["dr"]
+    s = sinusoid(np.arange(M + L - 1, -1, -1), d)
+    g["wr"] = s.T @ merge_heads(dr_full)
+    return dh_in, g
+
+
+def segment_backward_row(tokens: np.ndarray, mems: Sequence[np.ndarray], emb: np.ndarray,
+                         layers: Sequence[Dict[str, np.ndarray]], M: int, H: int, dh: int,
+                         dy: np.ndarray):
+    """Gradients of one segment of one batch row through the stack for the
+    gradient dy [L, d] arriving at H^(N): runs the forward (segment_step_row,
+    R built from each layer's W_R), then the layers in reverse, and
+    scatters the gradient reaching H^(0) into the embedding rows of the
+    tokens (a token that occurs twice adds twice). The memories are
+    stop-gradient inputs. Returns (demb [vocab, d], [grads of layer 1 .. N])."""
+    emb = np.asarray(emb, dtype=np.float64)
+    L = len(tokens)
+    r_tables = [rel_pos_table(lw["wr"], M, L, H, dh) for lw in layers]
+    hs, _ = segment_step_row(tokens, mems, emb, layers, r_tables, M, H, dh)
+    grads = [None] * len(layers)
+    g_h = np.asarray(dy, dtype=np.float64)
+    for n in range(len(layers) - 1, -1, -1):
+        g_h, grads[n] = layer_backward(hs[n], mems[n], layers[n], layers[n]["wr"], M, H, dh, g_h)
+    demb = np.zeros_like(emb)
+    for pos, t in enumerate(np.asarray(tokens, dtype=np.int64)):
+        demb[t] += g_h[pos]
+    return demb, grads
