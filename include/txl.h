@@ -106,6 +106,10 @@ typedef struct {
   int64_t o_sb, o_sh, o_sl;
   float *lse;                    /* [B, H, L] contiguous fp32, natural-log
                                     log-sum-exp of scaled visible scores; NULL = skip */
+  float *out_f32;                /* [B, H, L, d_h] contiguous fp32: out before
+                                    its rounding to bf16 (bf16 only, 16-byte
+                                    aligned); NULL = skip. Training records it
+                                    for txl_rel_attn_bwd (see there). */
 } txl_rel_attn_args;
 
 /* Shapes: d_h must be 64 (else UNSUPPORTED). B == 0 or L == 0: nothing to
@@ -150,7 +154,12 @@ TXL_API txl_status txl_rel_attn_fwd_split(const txl_rel_attn_args *a, int32_t kv
  *
  * a      : the arguments of the forward call that produced out and lse
  *          (bf16 only, else UNSUPPORTED); a->out and a->lse are read, both
- *          required.
+ *          required. When a->out_f32 is set (the forward wrote it), D_i is
+ *          formed from that unrounded output instead of the bf16 out: the
+ *          score gradient g_ij = p_ij (dp_ij - D_i) cancels to a small
+ *          difference when the probabilities are spread evenly, so D's
+ *          rounding error (2^-9 of |dout_i| |out_i|) would come back
+ *          magnified in du, dvb and dR.
  * grads  : dout [B, H, L, d_h] bf16 (strided, 16-byte rows), and the fp32
  *          outputs, all contiguous: dq [B, H, L, d_h], dk and dv
  *          [B, H, M+L, d_h] (logical key order), dr [H, M+L, d_h] (row t <->
@@ -358,6 +367,60 @@ TXL_API txl_status txl_segment_step(txl_stack *st, const int32_t *tokens, txl_me
                                     void *h_out, void *workspace, size_t ws_bytes,
                                     hipStream_t stream);
 TXL_API void txl_stack_destroy(txl_stack *st);
+
+/* ------------------------------------------------------------------------
+ * Training: gradients of one segment with the memory as a constant.
+ * [P1] "Why Stop Gradient" and "Training Loop Sketch", [P2] section
+ * "stop-gradient到底切断哪里": the memory enters the segment's graph as a
+ * stop-gradient input, so backpropagation ends at this segment. The memory's
+ * rows still feed the segment's keys and values, hence the W^K and W^V
+ * gradients, but no gradient leaves through them toward the earlier segment
+ * that wrote them (there is no memory gradient output).
+ *
+ * txl_segment_step_train is txl_segment_step (same arguments, same rings
+ * update, same h_out) that also records in `tape` what the backward reads:
+ * per layer its input H, the memory and valid counts as the layer read them,
+ * Q, K, V, the attention's output and log-sum-exp, the fp32 inputs of both
+ * LayerNorms, H1, the feed-forward's pre-activation and GELU output; and the
+ * token ids. tape: txl_segment_tape_bytes(c) device bytes, 256-byte aligned,
+ * owned by the caller; its layout is private to the library.
+ *
+ * txl_segment_backward: given dy = d loss / d h_out ([B, L, d] fp32 device,
+ * contiguous, 16-byte aligned) and the tape of the matching training step,
+ * writes (overwrites, never accumulates) every parameter gradient as fp32 in
+ * the layout of the weight it belongs to (txl_layer_weights above):
+ *   grads->emb [vocab, d] (rows of tokens absent from the segment are 0)
+ *   grads->layers[n].wq, wk, wv, wr [H*d_h, d], wo [d, H*d_h], w1 [d_ff, d],
+ *     w2 [d, d_ff], u, vb [H, d_h], ln1_g, ln1_b, ln2_g, ln2_b [d]
+ * all device, 16-byte aligned (emb 4-byte), host array of n_layer entries.
+ * The stack's weights must be the ones the training step ran with. The
+ * position table's gradient goes through R = S W_R^T to W_R (S: the fixed
+ * sinusoid rows of distances M+L-1 .. 0). Products run in bf16 with fp32
+ * accumulation; every reduction has a fixed order, so repeated calls give
+ * identical bits.
+ * workspace: txl_segment_backward_workspace_bytes(c) device bytes, 256-byte
+ * aligned. Calls sharing a workspace or a tape must not overlap; the tape is
+ * read only. Errors: INVALID_ARG (null pointers), WORKSPACE (tape or
+ * workspace too small), UNSUPPORTED (alignment), HIP; all but HIP are
+ * reported before anything is enqueued.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  float *wq, *wk, *wv, *wo, *wr, *u, *vb, *ln1_g, *ln1_b, *w1, *w2, *ln2_g, *ln2_b;
+} txl_layer_grads;
+
+typedef struct {
+  float *emb;
+  const txl_layer_grads *layers;   /* n_layer entries, host array */
+} txl_stack_grads;
+
+TXL_API size_t txl_segment_tape_bytes(const txl_stack_config *c);
+TXL_API txl_status txl_segment_step_train(txl_stack *st, const int32_t *tokens, txl_mem *mems,
+                                          void *h_out, void *tape, size_t tape_bytes,
+                                          void *workspace, size_t ws_bytes, hipStream_t stream);
+TXL_API size_t txl_segment_backward_workspace_bytes(const txl_stack_config *c);
+TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t tape_bytes,
+                                        const float *dy, const txl_stack_grads *grads,
+                                        void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Evaluation with projected memory ([P1] "Relation to KV Cache": the pages'

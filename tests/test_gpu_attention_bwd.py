@@ -161,3 +161,41 @@ def test_workspace_reuse_and_repeat_bitwise():
     b = run(part, None)
     for n in NAMES:
         assert torch.equal(a[n], b[n]), n
+
+
+def test_unrounded_output_and_gradients_from_it():
+    """The forward's out_f32 is the output before its rounding: the bf16 out
+    is its rounding bit for bit (plain and key-split kernels), and it is
+    closer to the oracle's output than out is (it lacks out's own rounding,
+    2^-9 relative). The backward forming D from it meets the same bound.
+    (In a deep stack this matters: with values grown alike, p (dp - D) is a
+    small difference and out's rounding in D comes back magnified in du,
+    dvb and dR; the stack's gradient tests show it.)"""
+    cfg = txl_synth.ATTN_CONFIGS["B4_H8_L128_M128"]
+    x = attn_case(cfg, B=2, H=2, L=128, M=384, seed=11, valid_mode="random")
+    dout = draw_dout(x["q"].shape, 11)
+    q, k, v = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
+    r, u, vb = x["r"].to(DEV), x["u"].to(DEV), x["vb"].to(DEV)
+    valid = x["valid"].to(DEV)
+    B, H, L, dh = q.shape
+    ref_out = oa.rel_attn(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["r"]), f64(x["u"]),
+                          f64(x["vb"]), valid=x["valid"].numpy())["out"]
+    ref = oracle(x, dout)
+    for splits in (1, 2):
+        out = torch.empty_like(q)
+        o32 = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=DEV)
+        txl.txl_rel_attn_fwd(q, k, v, r, u, vb, out, mem_valid=valid, lse=lse, out_f32=o32,
+                             kv_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(o32.to(torch.bfloat16), out), splits
+        e32 = err_report(f64(o32), ref_out)["rel_norm"]
+        e16 = err_report(f64(out), ref_out)["rel_norm"]
+        say(f"  splits={splits}: out_f32 rel_norm {e32:.2e}, bf16 out {e16:.2e}")
+        assert e32 < e16
+        g = txl.txl_rel_attn_bwd(q, k, v, r, u, vb, out, lse, dout.to(DEV), {},
+                                 mem_valid=valid, out_f32=o32)
+        torch.cuda.synchronize()
+        got = {n: f64(g[n]) for n in NAMES}
+        check(got, ref, f"splits={splits} out_f32")
+        hidden_rows_zero(got, x)

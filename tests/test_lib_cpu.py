@@ -167,6 +167,14 @@ def test_attention_backward_checks_without_gpu(lib):
     ldp = (32 + 64 + 7) // 8 * 8
     assert need >= 2 * 2 * 3 * 64 * ldp * 2
     assert lib.txl_rel_attn_bwd_workspace_bytes(-1, 3, 64, 32) == 0
+    # the unrounded output: bf16 only, 16-byte aligned
+    a.out_f32 = fake + 4
+    a.dtype = 1
+    assert lib.txl_rel_attn_fwd(ctypes.byref(a), None) == 2
+    assert b"out_f32" in lib.txl_last_error()
+    a.out_f32, a.dtype = fake, 0
+    assert lib.txl_rel_attn_fwd(ctypes.byref(a), None) == 2
+    assert b"out_f32" in lib.txl_last_error()
 
 
 def test_attention_with_ring_append_checks_without_gpu(lib):
@@ -240,3 +248,23 @@ def test_noalloc_attention_append_host_checks_without_gpu(lib):
                                                    8192, None) == 1
     assert lib.txl_rel_attn_fwd_mem_update_noalloc(None, None, None, None) == 1
     assert ring.head == 0
+
+
+def test_training_entry_points_host_checks_without_gpu(lib):
+    from transformer_xl_relative_txl_amd import _binding as bd
+    cfg = bd.StackConfig(2, 256, 4, 64, 512, 50, 2, 32, 64, 1e-5, bd.TXL_BF16)
+    tape = lib.txl_segment_tape_bytes(ctypes.byref(cfg))
+    ws = lib.txl_segment_backward_workspace_bytes(ctypes.byref(cfg))
+    rows, krows, hd = 2 * 32, 2 * (64 + 32), 256
+    # the tape holds at least H, Q, K, V, A, both LayerNorm inputs and the
+    # feed-forward's two [rows, d_ff] products of every layer
+    per_layer = rows * 256 * 2 + rows * hd * 2 * 2 + krows * hd * 2 * 2 + rows * 256 * 4 * 2 \
+        + rows * 512 * 2 * 2
+    assert tape >= 2 * per_layer and tape % 256 == 0
+    assert ws > 0 and ws % 256 == 0
+    bad = bd.StackConfig(2, 256, 4, 32, 256, 50, 2, 32, 64, 1e-5, bd.TXL_BF16)  # d_h 32
+    assert lib.txl_segment_tape_bytes(ctypes.byref(bad)) == 0
+    assert lib.txl_segment_backward_workspace_bytes(ctypes.byref(bad)) == 0
+    assert lib.txl_segment_step_train(None, None, None, None, None, 0, None, 0, None) == 1
+    assert lib.txl_segment_backward(None, None, 0, None, None, None, 0, None) == 1
+    assert b"null" in lib.txl_last_error()

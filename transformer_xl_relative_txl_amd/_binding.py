@@ -48,6 +48,7 @@ class RelAttnArgs(ctypes.Structure):
         ("out", ctypes.c_void_p),
         ("o_sb", ctypes.c_int64), ("o_sh", ctypes.c_int64), ("o_sl", ctypes.c_int64),
         ("lse", ctypes.c_void_p),
+        ("out_f32", ctypes.c_void_p),
     ]
 
 
@@ -96,6 +97,14 @@ class LayerWeights(ctypes.Structure):
 
 class StackWeights(ctypes.Structure):
     _fields_ = [("emb", ctypes.c_void_p), ("layers", ctypes.POINTER(LayerWeights))]
+
+
+class LayerGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_FIELDS]
+
+
+class StackGrads(ctypes.Structure):
+    _fields_ = [("emb", ctypes.c_void_p), ("layers", ctypes.POINTER(LayerGrads))]
 
 
 def _load() -> ctypes.CDLL:
@@ -151,6 +160,15 @@ def _load() -> ctypes.CDLL:
     lib.txl_segment_step.restype = st
     lib.txl_stack_destroy.argtypes = [vp]
     lib.txl_stack_destroy.restype = None
+    lib.txl_segment_tape_bytes.argtypes = [ctypes.POINTER(StackConfig)]
+    lib.txl_segment_tape_bytes.restype = sz
+    lib.txl_segment_step_train.argtypes = [vp, vp, ctypes.POINTER(TxlMemStruct), vp, vp, sz,
+                                           vp, sz, vp]
+    lib.txl_segment_step_train.restype = st
+    lib.txl_segment_backward_workspace_bytes.argtypes = [ctypes.POINTER(StackConfig)]
+    lib.txl_segment_backward_workspace_bytes.restype = sz
+    lib.txl_segment_backward.argtypes = [vp, vp, sz, vp, ctypes.POINTER(StackGrads), vp, sz, vp]
+    lib.txl_segment_backward.restype = st
     lib.txl_kv_cache_min_capacity.argtypes = [ctypes.POINTER(StackConfig)]
     lib.txl_kv_cache_min_capacity.restype = i32
     lib.txl_segment_step_kv.argtypes = [vp, vp, ctypes.POINTER(TxlKVCacheStruct), vp, vp, sz, vp]
@@ -226,14 +244,16 @@ def txl_rel_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      out: torch.Tensor, mem_valid: Optional[torch.Tensor] = None,
                      lse: Optional[torch.Tensor] = None, scale: float = 0.0,
                      stream=None, kv_splits: int = 1,
-                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     workspace: Optional[torch.Tensor] = None,
+                     out_f32: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Relative attention. q [B,H,L,d_h]; k, v [B,H,M+L,d_h] (same strides);
     r [H,M+L,d_h]; u, vb [H,d_h] contiguous; out [B,H,L,d_h]; mem_valid [B]
-    int32; lse [B,H,L] float32. Any element strides with a contiguous last
+    int32; lse [B,H,L] float32; out_f32 [B,H,L,d_h] contiguous float32 (the
+    unrounded output, bf16 only). Any element strides with a contiguous last
     dimension. kv_splits > 1 calls txl_rel_attn_fwd_split (workspace
     allocated here when not given)."""
     B, H, L, d_h = q.shape
-    a = _attn_args(q, k, v, r, u, vb, out, mem_valid, lse, scale)
+    a = _attn_args(q, k, v, r, u, vb, out, mem_valid, lse, scale, out_f32)
     if kv_splits == 1:
         _check("txl_rel_attn_fwd", lib().txl_rel_attn_fwd(ctypes.byref(a), _stream(stream)))
         return out
@@ -246,7 +266,7 @@ def txl_rel_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out
 
 
-def _attn_args(q, k, v, r, u, vb, out, mem_valid, lse, scale) -> RelAttnArgs:
+def _attn_args(q, k, v, r, u, vb, out, mem_valid, lse, scale, out_f32=None) -> RelAttnArgs:
     B, H, L, d_h = q.shape
     M = k.shape[2] - L
     if k.stride() != v.stride():
@@ -266,6 +286,10 @@ def _attn_args(q, k, v, r, u, vb, out, mem_valid, lse, scale) -> RelAttnArgs:
     a.out = _ptr(out)
     a.o_sb, a.o_sh, a.o_sl = out.stride(0), out.stride(1), out.stride(2)
     a.lse = _ptr(lse)
+    if out_f32 is not None:
+        assert out_f32.dtype == torch.float32 and out_f32.is_contiguous()
+        assert tuple(out_f32.shape) == tuple(out.shape)
+    a.out_f32 = _ptr(out_f32)
     return a
 
 
@@ -278,15 +302,16 @@ def txl_rel_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
                      grads: dict, mem_valid: Optional[torch.Tensor] = None,
                      scale: float = 0.0, workspace: Optional[torch.Tensor] = None,
-                     stream=None) -> dict:
+                     stream=None, out_f32: Optional[torch.Tensor] = None) -> dict:
     """Gradients of txl_rel_attn_fwd (bf16). q..lse are the forward call's
-    tensors (out and lse as it wrote them); dout [B,H,L,d_h] bf16; grads
+    tensors (out and lse as it wrote them, and out_f32 when it kept the
+    unrounded output); dout [B,H,L,d_h] bf16; grads
     holds contiguous float32 outputs dq [B,H,L,d_h], dk, dv [B,H,M+L,d_h],
     dr [H,M+L,d_h], du, dvb [H,d_h] (allocated here when missing); the
     workspace is allocated here when not given."""
     B, H, L, d_h = q.shape
     M = k.shape[2] - L
-    a = _attn_args(q, k, v, r, u, vb, out, mem_valid, lse, scale)
+    a = _attn_args(q, k, v, r, u, vb, out, mem_valid, lse, scale, out_f32)
     shapes = {"dq": (B, H, L, d_h), "dk": (B, H, M + L, d_h), "dv": (B, H, M + L, d_h),
               "dr": (H, M + L, d_h), "du": (H, d_h), "dvb": (H, d_h)}
     for name, shp in shapes.items():
@@ -535,6 +560,68 @@ class TxlStack:
             m.head = int(arr[i].head)
         return h_out
 
+    def tape_bytes(self) -> int:
+        """txl_segment_tape_bytes of this stack's configuration."""
+        return int(lib().txl_segment_tape_bytes(ctypes.byref(self.cfg)))
+
+    def new_tape(self) -> torch.Tensor:
+        """A device buffer of txl_segment_tape_bytes (uint8)."""
+        return torch.empty(self.tape_bytes(), dtype=torch.uint8, device=self.persistent.device)
+
+    def step_train(self, tokens: torch.Tensor, mems: Sequence[TxlMem], h_out: torch.Tensor,
+                   tape: torch.Tensor, stream=None) -> torch.Tensor:
+        """txl_segment_step_train: txl_segment_step that also fills `tape`."""
+        assert tokens.dtype == torch.int32 and tokens.is_contiguous()
+        assert len(mems) == self.cfg.n_layer + 1 and h_out.is_contiguous()
+        assert tape.dtype == torch.uint8 and tape.is_contiguous()
+        arr = _structs(mems)
+        _check("txl_segment_step_train",
+               lib().txl_segment_step_train(self._h, tokens.data_ptr(), arr, h_out.data_ptr(),
+                                            tape.data_ptr(), tape.numel(),
+                                            self.workspace.data_ptr(), self.workspace.numel(),
+                                            _stream(stream)))
+        for i, m in enumerate(mems):
+            m.head = int(arr[i].head)
+        return h_out
+
+    def new_grads(self) -> dict:
+        """fp32 device gradient buffers in the weights' layout:
+        {"emb": [vocab, d], "layers": [ {name: tensor} per layer ]}."""
+        c = self.cfg
+        hd = c.n_head * c.d_h
+        shapes = {"wq": (hd, c.d), "wk": (hd, c.d), "wv": (hd, c.d), "wr": (hd, c.d),
+                  "wo": (c.d, hd), "u": (c.n_head, c.d_h), "vb": (c.n_head, c.d_h),
+                  "ln1_g": (c.d,), "ln1_b": (c.d,), "ln2_g": (c.d,), "ln2_b": (c.d,),
+                  "w1": (c.d_ff, c.d), "w2": (c.d, c.d_ff)}
+        dev = self.persistent.device
+        return {"emb": torch.empty(c.vocab, c.d, dtype=torch.float32, device=dev),
+                "layers": [{n: torch.empty(*shapes[n], dtype=torch.float32, device=dev)
+                            for n in LAYER_FIELDS} for _ in range(c.n_layer)]}
+
+    def backward(self, tape: torch.Tensor, dy: torch.Tensor, grads: dict,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+        """txl_segment_backward: dy [B, L, d] fp32 (gradient at h_out) and the
+        tape of the matching step_train; fills `grads` (see new_grads)."""
+        assert dy.dtype == torch.float32 and dy.is_contiguous()
+        assert tape.dtype == torch.uint8 and tape.is_contiguous()
+        if workspace is None:
+            if getattr(self, "_bwd_ws", None) is None:
+                nb = int(lib().txl_segment_backward_workspace_bytes(ctypes.byref(self.cfg)))
+                self._bwd_ws = torch.empty(nb, dtype=torch.uint8, device=self.persistent.device)
+            workspace = self._bwd_ws
+        tensors = [grads["emb"]] + [t for lg in grads["layers"] for t in lg.values()]
+        for t in tensors:
+            assert t.is_cuda and t.is_contiguous() and t.dtype == torch.float32
+        layers = (LayerGrads * self.cfg.n_layer)()
+        for i, lg in enumerate(grads["layers"]):
+            layers[i] = LayerGrads(*[lg[n].data_ptr() for n in LAYER_FIELDS])
+        sg = StackGrads(grads["emb"].data_ptr(), layers)
+        _check("txl_segment_backward",
+               lib().txl_segment_backward(self._h, tape.data_ptr(), tape.numel(), dy.data_ptr(),
+                                          ctypes.byref(sg), workspace.data_ptr(), workspace.numel(),
+                                          _stream(stream)))
+        return grads
+
     def kv_min_capacity(self) -> int:
         """txl_kv_cache_min_capacity: 2*M + L."""
         return int(lib().txl_kv_cache_min_capacity(ctypes.byref(self.cfg)))
@@ -641,7 +728,9 @@ def exported_symbols() -> List[str]:
             "txl_rel_attn_fwd_mem_update_noalloc", "txl_rel_attn_mem_update_workspace_bytes",
             "txl_mem_reset_rows", "txl_mem_read_logical", "txl_stack_persistent_bytes",
             "txl_stack_create", "txl_segment_step_workspace_bytes", "txl_segment_step",
-            "txl_stack_destroy", "txl_kv_cache_min_capacity", "txl_segment_step_kv",
+            "txl_stack_destroy", "txl_segment_tape_bytes", "txl_segment_step_train",
+            "txl_segment_backward_workspace_bytes", "txl_segment_backward",
+            "txl_kv_cache_min_capacity", "txl_segment_step_kv",
             "txl_kv_cache_reset_rows", "txl_sampler_create", "txl_sampler_next",
             "txl_sampler_destroy", "txl_lm_loss_workspace_bytes", "txl_lm_loss",
             "txl_status_str", "txl_last_error", "txl_version"]

@@ -27,6 +27,7 @@ SOURCES = [
     "rel_attn_mfma.hip",
     "rel_attn_bwd.hip",
     "gemm.hip",
+    "bwd.hip",
     "stack.cpp",
     "sampler.cpp",
     "loss.cpp",

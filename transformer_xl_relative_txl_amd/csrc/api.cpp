@@ -111,12 +111,17 @@ static txl_status attn_params(const txl_rel_attn_args *a, AttnParams *out, bool 
                   static_cast<long long>(s));
   if (a->lse && (reinterpret_cast<uintptr_t>(a->lse) & 3u))
     return fail(TXL_ERR_INVALID_ARG, "rel_attn: lse not 4-byte aligned");
+  if (a->out_f32 && a->dtype != TXL_BF16)
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn: out_f32 is built for bf16 only");
+  if (a->out_f32 && (reinterpret_cast<uintptr_t>(a->out_f32) & 15u))
+    return fail(TXL_ERR_UNSUPPORTED, "rel_attn: out_f32 not 16-byte aligned");
   if (a->mem_valid && (reinterpret_cast<uintptr_t>(a->mem_valid) & 3u))
     return fail(TXL_ERR_INVALID_ARG, "rel_attn: mem_valid not 4-byte aligned");
 
   AttnParams p = {};
   p.q = a->q; p.k = a->k; p.v = a->v; p.r = a->r; p.u = a->u; p.vb = a->vb;
   p.out = a->out; p.lse = a->lse; p.valid = a->mem_valid;
+  p.out32 = a->out_f32;
   p.q_sb = a->q_sb; p.q_sh = a->q_sh; p.q_sl = a->q_sl;
   p.kv_sb = a->kv_sb; p.kv_sh = a->kv_sh; p.kv_sl = a->kv_sl;
   p.r_sh = a->r_sh; p.r_sl = a->r_sl;
@@ -341,6 +346,7 @@ TXL_API txl_status txl_rel_attn_bwd(const txl_rel_attn_args *a, const txl_rel_at
   g.dout = static_cast<const __bf16 *>(gr->dout);
   g.do_sb = gr->do_sb; g.do_sh = gr->do_sh; g.do_sl = gr->do_sl;
   g.lse = a->lse;
+  g.out32 = a->out_f32;
   g.dq = gr->dq; g.dk = gr->dk; g.dv = gr->dv; g.dr = gr->dr; g.du = gr->du; g.dvb = gr->dvb;
   g.qv = reinterpret_cast<__bf16 *>(base + w.qv);
   g.dd = reinterpret_cast<float *>(base + w.dd);

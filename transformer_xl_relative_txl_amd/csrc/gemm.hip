@@ -54,6 +54,18 @@ __device__ inline float gelu_erf(float v) {
   return 0.5f * v * (1.0f + erf_x);
 }
 
+// d/dv GELU(v) = Phi(v) + v phi(v), Phi from the same erf.
+__device__ inline float gelu_erf_grad(float v) {
+  const float x = v * 0.7071067811865476f;
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
+  const float poly =
+      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);  // exp(-v^2/2)
+  const float erf_x = copysignf(1.0f - poly * e, x);
+  return 0.5f * (1.0f + erf_x) + v * e * 0.3989422804014327f;
+}
+
 // Tile BM x BN (each 64 or 128) per workgroup of 4 waves arranged 2 x 2; a
 // wave computes (BM/2) x (BN/2) as blocks of 32 x 32. K runs in slabs of BKS
 // (32 or 64) through two LDS buffers: the next slab is loaded into registers while the
@@ -259,7 +271,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
   // block remapped once, instead of one 2-byte or 4-byte store per element.
   constexpr bool kStaged = BKS == 64 && (E == kEpiStoreBf16 || E == kEpiGeluBf16 ||
                                          ((E == kEpiResidualF32 || E == kEpiPartialF32) && BN == 64));
-  if constexpr (kStaged) {
+  // the pre-activation store and the fp32 residual take the direct path
+  const bool direct_only = (E == kEpiGeluBf16 && p.pre_out) || (E == kEpiResidualF32 && p.res32);
+  if constexpr (kStaged) if (!direct_only) {
     typedef typename std::conditional<(E == kEpiStoreBf16 || E == kEpiGeluBf16), __bf16, float>::type OT;
     constexpr int VE = 16 / static_cast<int>(sizeof(OT));       // elements per 16-byte chunk
     constexpr int OS = BN + VE;                                  // LDS row stride (elements)
@@ -337,10 +351,16 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
           if (E == kEpiPartialF32) {
             static_cast<float *>(p.c0)[split * p.c_split_stride + mo * p.ldc + nc] = v;
           } else if (E == kEpiResidualF32) {
-            v += static_cast<float>(p.res[static_cast<int64_t>(m) * p.ldres + nc]);
+            v += p.res32 ? p.res32[static_cast<int64_t>(m) * p.ldres + nc]
+                         : static_cast<float>(p.res[static_cast<int64_t>(m) * p.ldres + nc]);
             static_cast<float *>(second ? p.c1 : p.c0)[mo * p.ldc + nc] = v;
           } else {
-            if (E == kEpiGeluBf16) v = gelu_erf(v);
+            if (E == kEpiGeluBf16) {
+              if (p.pre_out) p.pre_out[mo * p.ldc + nc] = static_cast<__bf16>(v);
+              v = gelu_erf(v);
+            }
+            if (E == kEpiGeluGradBf16)
+              v *= gelu_erf_grad(static_cast<float>(p.pre_in[mo * p.ldc + nc]));
             static_cast<__bf16 *>(second ? p.c1 : p.c0)[mo * p.ldc + nc] = static_cast<__bf16>(v);
           }
         }
@@ -359,7 +379,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
                                                         const __bf16 *__restrict__ gamma,
                                                         const __bf16 *__restrict__ beta,
                                                         __bf16 *__restrict__ y, int rows, int d,
-                                                        float eps) {
+                                                        float eps, float *__restrict__ x_out) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
@@ -381,6 +401,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[c][e] += static_cast<float>(rr[e]);
       }
+      if (x_out) *reinterpret_cast<f32x4 *>(x_out + static_cast<int64_t>(row) * d + 256 * c + 4 * lane) = v[c];
       s += (v[c][0] + v[c][1]) + (v[c][2] + v[c][3]);
     }
   }
@@ -538,6 +559,8 @@ txl_status launch_gemm(const GemmParams &p, int epi, hipStream_t s) {
     launch_epi<kEpiResidualF32>(p, s);
   else if (epi == kEpiPartialF32)
     launch_epi<kEpiPartialF32>(p, s);
+  else if (epi == kEpiGeluGradBf16)
+    launch_epi<kEpiGeluGradBf16>(p, s);
   else
     launch_epi<kEpiLse>(p, s);
   return check_launch("gemm_kernel");
@@ -545,7 +568,7 @@ txl_status launch_gemm(const GemmParams &p, int epi, hipStream_t s) {
 
 txl_status launch_layernorm(const float *x, int n_parts, int64_t part_stride, const void *res,
                             const void *gamma, const void *beta, void *y, int rows, int d,
-                            float eps, hipStream_t s) {
+                            float eps, hipStream_t s, float *x_out) {
   if (rows <= 0) return TXL_OK;
   (void)hipGetLastError();
   const dim3 grid((rows + 3) / 4);
@@ -554,11 +577,11 @@ txl_status launch_layernorm(const float *x, int n_parts, int64_t part_stride, co
   const __bf16 *b = static_cast<const __bf16 *>(beta);
   __bf16 *o = static_cast<__bf16 *>(y);
   if (n_parts == 1)
-    hipLaunchKernelGGL(layernorm_kernel<1>, grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps);
+    hipLaunchKernelGGL(layernorm_kernel<1>, grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps, x_out);
   else if (n_parts == 2)
-    hipLaunchKernelGGL(layernorm_kernel<2>, grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps);
+    hipLaunchKernelGGL(layernorm_kernel<2>, grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps, x_out);
   else if (n_parts == 4)
-    hipLaunchKernelGGL(layernorm_kernel<4>, grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps);
+    hipLaunchKernelGGL(layernorm_kernel<4>, grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps, x_out);
   else
     return fail(TXL_ERR_UNSUPPORTED, "layernorm: %d partial sums (1, 2 or 4 are built)", n_parts);
   return check_launch("layernorm_kernel");

@@ -82,8 +82,9 @@ __device__ inline void bstore16(__bf16 v, rsrc_t rs, int voff, int soff) {
 constexpr int kDropOffset = 0x40000000;   // past any p / g slice (slices stay below 1 GiB)
 
 // ---------------------------------------------------------------------------
-// D_i = dout_i . out_i (fp32) and qv = bf16(q + v) (the dR product's operand);
-// one thread per query row and 8 dimensions.
+// D_i = dout_i . out_i (fp32; out unrounded when the forward kept it) and
+// qv = bf16(q + v) (the dR product's operand); one thread per query row and
+// 8 dimensions.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnParams p, BwdParams g) {
   const int64_t BHL = static_cast<int64_t>(p.B) * p.H * p.L;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -99,11 +100,24 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnParams p, BwdParams g
     const __bf16 *dp = g.dout + b * g.do_sb + h * g.do_sh + i * g.do_sl + 8 * c;
     const bf16x8 qv = load8(qp), ov = load8(op), dv = load8(dp);
     const bf16x8 vv = load8(static_cast<const __bf16 *>(p.vb) + h * DH + 8 * c);
+    float of[8];
+    if (g.out32) {  // the unrounded output, when the forward kept it
+      const f32x4 lo = *reinterpret_cast<const f32x4 *>(g.out32 + row * DH + 8 * c);
+      const f32x4 hi = *reinterpret_cast<const f32x4 *>(g.out32 + row * DH + 8 * c + 4);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        of[x] = lo[x];
+        of[x + 4] = hi[x];
+      }
+    } else {
+#pragma unroll
+      for (int x = 0; x < 8; ++x) of[x] = static_cast<float>(ov[x]);
+    }
     bf16x8 bq;
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       bq[x] = static_cast<__bf16>(static_cast<float>(qv[x]) + static_cast<float>(vv[x]));
-      acc += static_cast<float>(dv[x]) * static_cast<float>(ov[x]);
+      acc += static_cast<float>(dv[x]) * of[x];
     }
     *reinterpret_cast<bf16x8 *>(g.qv + row * DH + 8 * c) = bq;
   }

@@ -527,14 +527,21 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
   }
   const float inv = 1.0f / l_tot;
   __bf16 *op = static_cast<__bf16 *>(p.out) + b * p.o_sb + h * p.o_sh + static_cast<int64_t>(i) * p.o_sl;
+  // training also keeps the unrounded output
+  float *o32 = p.out32 ? p.out32 + ((static_cast<int64_t>(b) * p.H + h) * L + i) * DH : nullptr;
 #pragma unroll
   for (int db = 0; db < 2; ++db)
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
+      f32x4 of;
       bf16x4 o4;
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) o4[cc] = static_cast<__bf16>(o_acc[db][4 * a4 + cc] * inv);
+      for (int cc = 0; cc < 4; ++cc) {
+        of[cc] = o_acc[db][4 * a4 + cc] * inv;
+        o4[cc] = static_cast<__bf16>(of[cc]);
+      }
       *reinterpret_cast<bf16x4 *>(op + db * 32 + 8 * a4 + 4 * hh) = o4;
+      if (o32) *reinterpret_cast<f32x4 *>(o32 + db * 32 + 8 * a4 + 4 * hh) = of;
     }
   if (p.lse && hh == 0)
     p.lse[(static_cast<int64_t>(b) * p.H + h) * L + i] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
@@ -579,9 +586,13 @@ __global__ __launch_bounds__(256) void rel_attn_merge_kernel(AttnParams p) {
   const float inv = 1.0f / l;
   bf16x4 o4;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) o4[q] = static_cast<__bf16>(o[q] * inv);
+  for (int q = 0; q < 4; ++q) {
+    o[q] *= inv;
+    o4[q] = static_cast<__bf16>(o[q]);
+  }
   __bf16 *op = static_cast<__bf16 *>(p.out) + b * p.o_sb + h * p.o_sh + static_cast<int64_t>(i) * p.o_sl;
   *reinterpret_cast<bf16x4 *>(op + 4 * c) = o4;
+  if (p.out32) *reinterpret_cast<f32x4 *>(p.out32 + row * DH + 4 * c) = o;
   if (p.lse && c == 0) p.lse[row] = (m + log2f(l)) * 0.6931471805599453f;
 }
 

@@ -184,8 +184,9 @@ txl_status check_workspace(const WsLayout &ws, const void *workspace, size_t ws_
 // fp32 scratch x): one GEMM with the residual in its epilogue, or, when the
 // tiles cannot fill the chip, a split-K GEMM writing fp32 partials that the
 // LayerNorm adds up in split order before the residual.
+// x_out (training) receives the fp32 sum the LayerNorm normalises.
 txl_status residual_ln(GemmParams p, const __bf16 *res, const void *gamma, const void *beta,
-                       void *y, float eps, hipStream_t stream) {
+                       void *y, float eps, hipStream_t stream, float *x_out = nullptr) {
   const int splits = residual_splits(p.rows, p.N, p.K);
   txl_status s;
   if (splits > 1) {
@@ -194,14 +195,181 @@ txl_status residual_ln(GemmParams p, const __bf16 *res, const void *gamma, const
     s = launch_gemm(p, kEpiPartialF32, stream);
     if (s != TXL_OK) return s;
     return launch_layernorm(static_cast<const float *>(p.c0), splits, p.c_split_stride, res, gamma,
-                            beta, y, p.rows, p.N, eps, stream);
+                            beta, y, p.rows, p.N, eps, stream, x_out);
   }
   p.res = res;
   p.ldres = p.N;
   s = launch_gemm(p, kEpiResidualF32, stream);
   if (s != TXL_OK) return s;
   return launch_layernorm(static_cast<const float *>(p.c0), 1, 0, nullptr, gamma, beta, y, p.rows,
-                          p.N, eps, stream);
+                          p.N, eps, stream, x_out);
+}
+
+// What the training step records of layer n for the backward (all device
+// pointers into the caller's tape).
+struct TapeLayer {
+  __bf16 *hin;   // H^(n) [B*L, d], the layer's input
+  __bf16 *mem;   // ring n before the step, logical order [B, M, d]
+  int32_t *valid;  // its valid counts [B]
+  __bf16 *q;     // [B*L, HD]
+  __bf16 *k, *v; // [B*(M+L), HD]
+  __bf16 *o;     // attention output [B*L, HD]
+  float *o32;    // the same before its rounding, [B, H, L, 64]
+  float *lse;    // [B, H, L]
+  float *x1;     // H + A W^O before LN1 [B*L, d]
+  __bf16 *h1;    // LN1 output [B*L, d]
+  __bf16 *fpre;  // H1 W1 before GELU [B*L, d_ff]
+  __bf16 *f;     // GELU output [B*L, d_ff]
+  float *x2;     // H1 + F W2 before LN2 [B*L, d]
+};
+
+struct TapeLayout {
+  size_t hin, mem, valid, q, k, v, o, o32, lse, x1, h1, fpre, f, x2, per_layer, tokens, total;
+};
+
+TapeLayout tape_layout(const txl_stack_config &c) {
+  const size_t hd = static_cast<size_t>(c.n_head) * c.d_h;
+  const size_t rows = static_cast<size_t>(c.B) * c.L;
+  const size_t krows = static_cast<size_t>(c.B) * (c.M + c.L);
+  TapeLayout t;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  t.hin = take(rows * c.d * 2);
+  t.mem = take(static_cast<size_t>(c.B) * c.M * c.d * 2);
+  t.valid = take(static_cast<size_t>(c.B) * 4);
+  t.q = take(rows * hd * 2);
+  t.k = take(krows * hd * 2);
+  t.v = take(krows * hd * 2);
+  t.o = take(rows * hd * 2);
+  t.o32 = take(rows * hd * 4);
+  t.lse = take(static_cast<size_t>(c.B) * c.n_head * c.L * 4);
+  t.x1 = take(rows * c.d * 4);
+  t.h1 = take(rows * c.d * 2);
+  t.fpre = take(rows * c.d_ff * 2);
+  t.f = take(rows * c.d_ff * 2);
+  t.x2 = take(rows * c.d * 4);
+  t.per_layer = off;
+  t.tokens = off * c.n_layer;  // after the layers: the segment's token ids
+  t.total = t.tokens + align256(rows * 4);
+  return t;
+}
+
+TapeLayer tape_at(const TapeLayout &t, const void *tape, int n) {
+  char *base = const_cast<char *>(static_cast<const char *>(tape)) + t.per_layer * n;
+  TapeLayer l;
+  l.hin = reinterpret_cast<__bf16 *>(base + t.hin);
+  l.mem = reinterpret_cast<__bf16 *>(base + t.mem);
+  l.valid = reinterpret_cast<int32_t *>(base + t.valid);
+  l.q = reinterpret_cast<__bf16 *>(base + t.q);
+  l.k = reinterpret_cast<__bf16 *>(base + t.k);
+  l.v = reinterpret_cast<__bf16 *>(base + t.v);
+  l.o = reinterpret_cast<__bf16 *>(base + t.o);
+  l.o32 = reinterpret_cast<float *>(base + t.o32);
+  l.lse = reinterpret_cast<float *>(base + t.lse);
+  l.x1 = reinterpret_cast<float *>(base + t.x1);
+  l.h1 = reinterpret_cast<__bf16 *>(base + t.h1);
+  l.fpre = reinterpret_cast<__bf16 *>(base + t.fpre);
+  l.f = reinterpret_cast<__bf16 *>(base + t.f);
+  l.x2 = reinterpret_cast<float *>(base + t.x2);
+  return l;
+}
+
+int round64(int64_t x) { return static_cast<int>((x + 63) / 64 * 64); }
+
+// K splits of a weight-gradient product (output rows x N, reduction K over
+// the segment's rows): enough workgroups to fill the chip (about 512 tiles
+// of 64 x 64), each split keeping at least 256 of K.
+int dw_splits(int rows, int N, int K) {
+  const int64_t tiles = static_cast<int64_t>((rows + 63) / 64) * (N / 64);
+  int s = 1;
+  while (s < 16 && tiles * s < 512 && K / (2 * s) >= 256) s *= 2;
+  return s;
+}
+
+// out [rows, N] fp32 = A [rows, K] W [N, K]^T (both bf16, row stride K): one
+// GEMM storing fp32, or split-K partials added in split order.
+txl_status dw_gemm(const __bf16 *a, int rows, const __bf16 *w, int N, int K, float *out,
+                   float *part, hipStream_t stream) {
+  const int splits = dw_splits(rows, N, K);
+  GemmParams p = dense(a, K, rows, N, K, w, splits > 1 ? part : out, N);
+  p.k_splits = splits;
+  p.c_split_stride = static_cast<int64_t>(rows) * N;
+  txl_status s = launch_gemm(p, kEpiPartialF32, stream);
+  if (s != TXL_OK || splits == 1) return s;
+  return launch_reduce_parts(part, splits, p.c_split_stride, p.c_split_stride, out, stream);
+}
+
+// Workspace of the segment backward (one layer's intermediates, reused from
+// the top layer down).
+struct BwdWs {
+  int r_pad, e_pad, t_pad;  // segment rows, [memory; segment] rows, R rows, padded to 64
+  size_t g0, g1, dx2, dx2b, dh1, dx1, dx1b, dfpre, dfpreT, xT, aT, dout, dq, dk, dv, dr, attn,
+      attn_bytes, gT, acat, wT, wcatT, st, pg, pb, part, total;
+};
+
+BwdWs bwd_ws(const txl_stack_config &c) {
+  const size_t hd = static_cast<size_t>(c.n_head) * c.d_h;
+  const int HD = static_cast<int>(hd);
+  const size_t rows = static_cast<size_t>(c.B) * c.L;
+  const size_t krows = static_cast<size_t>(c.B) * (c.M + c.L);
+  BwdWs w;
+  w.r_pad = round64(static_cast<int64_t>(rows));
+  w.e_pad = round64(static_cast<int64_t>(krows));
+  w.t_pad = round64(c.M + c.L);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  const size_t rd = rows * c.d;
+  w.g0 = take(rd * 4);
+  w.g1 = take(rd * 4);
+  w.dx2 = take(rd * 4);
+  w.dx2b = take(rd * 2);
+  w.dh1 = take(rd * 4);
+  w.dx1 = take(rd * 4);
+  w.dx1b = take(rd * 2);
+  w.dfpre = take(rows * c.d_ff * 2);
+  w.dfpreT = take(static_cast<size_t>(c.d_ff) * w.r_pad * 2);
+  w.xT = take(static_cast<size_t>(c.d) * w.r_pad * 2);
+  w.aT = take(std::max({static_cast<size_t>(c.d_ff) * w.r_pad, static_cast<size_t>(c.d) * w.e_pad,
+                        hd * w.r_pad}) * 2);
+  w.dout = take(rows * hd * 2);
+  w.dq = take(rows * hd * 4);
+  w.dk = take(krows * hd * 4);
+  w.dv = take(krows * hd * 4);
+  w.dr = take(static_cast<size_t>(c.M + c.L) * hd * 4);
+  w.attn_bytes = txl_rel_attn_bwd_workspace_bytes(c.B, c.n_head, c.L, c.M);
+  w.attn = take(w.attn_bytes);
+  w.gT = take(hd * std::max(w.e_pad, w.t_pad) * 2);
+  w.acat = take(rows * 3 * hd * 2);
+  w.wT = take(static_cast<size_t>(std::max(c.d_ff, HD)) * c.d * 2);
+  w.wcatT = take(static_cast<size_t>(c.d) * 3 * hd * 2);
+  w.st = take(static_cast<size_t>(c.d) * w.t_pad * 2);
+  int rpb;
+  const size_t ln_blocks = ln_backward_blocks(static_cast<int>(rows), &rpb);
+  w.pg = take(ln_blocks * c.d * 4);
+  w.pb = take(ln_blocks * c.d * 4);
+  // the largest split-K partial set of the weight-gradient products
+  size_t part = 0;
+  auto need = [&](int r, int n, int k) {
+    const int s = dw_splits(r, n, k);
+    if (s > 1) part = std::max(part, static_cast<size_t>(s) * r * n);
+  };
+  need(c.d, c.d_ff, w.r_pad);
+  need(c.d_ff, c.d, w.r_pad);
+  need(c.d, HD, w.r_pad);
+  need(HD, c.d, w.r_pad);
+  need(HD, c.d, w.e_pad);
+  need(HD, c.d, w.t_pad);
+  w.part = take(part * 4);
+  w.total = off;
+  return w;
 }
 
 // The part of layer n that does not depend on how memory is kept: Q = H W^Q,
@@ -213,12 +381,18 @@ txl_status residual_ln(GemmParams p, const __bf16 *res, const void *gamma, const
 // layer's input once the attention has read its valid counts).
 txl_status layer_body(const txl_stack *st, int n, const __bf16 *hc, void *dst, const void *k,
                       const void *v, int64_t kv_sb, const int32_t *valid, const StepBufs &b,
-                      hipStream_t stream, txl_mem *append = nullptr) {
+                      hipStream_t stream, txl_mem *append = nullptr,
+                      const TapeLayer *tl = nullptr) {
   const txl_stack_config &c = st->cfg;
   const txl_layer_weights &lw = st->layers[n];
   const int HD = c.n_head * c.d_h;
   const int rows = c.B * c.L;
-  txl_status s = launch_gemm(dense(hc, c.d, rows, HD, c.d, lw.wq, b.q, HD), kEpiStoreBf16, stream);
+  // with a tape, the products that the backward reads land in it
+  __bf16 *q_out = tl ? tl->q : b.q;
+  __bf16 *o_out = tl ? tl->o : b.o;
+  __bf16 *h1_out = tl ? tl->h1 : b.h1;
+  __bf16 *f_out = tl ? tl->f : b.f;
+  txl_status s = launch_gemm(dense(hc, c.d, rows, HD, c.d, lw.wq, q_out, HD), kEpiStoreBf16, stream);
   if (s != TXL_OK) return s;
   txl_rel_attn_args a = {};
   a.dtype = TXL_BF16;
@@ -227,7 +401,7 @@ txl_status layer_body(const txl_stack *st, int n, const __bf16 *hc, void *dst, c
   a.L = c.L;
   a.M = c.M;
   a.d_h = c.d_h;
-  a.q = b.q;
+  a.q = q_out;
   a.q_sb = static_cast<int64_t>(c.L) * HD;
   a.q_sh = c.d_h;
   a.q_sl = HD;
@@ -243,11 +417,12 @@ txl_status layer_body(const txl_stack *st, int n, const __bf16 *hc, void *dst, c
   a.vb = lw.vb;
   a.mem_valid = valid;
   a.scale = 0.0f;
-  a.out = b.o;
+  a.out = o_out;
   a.o_sb = static_cast<int64_t>(c.L) * HD;
   a.o_sh = c.d_h;
   a.o_sl = HD;
-  a.lse = nullptr;
+  a.lse = tl ? tl->lse : nullptr;
+  a.out_f32 = tl ? tl->o32 : nullptr;
   const int splits = attn_splits(c);
   if (append)
     s = txl_rel_attn_fwd_mem_update(&a, append, hc, st->counters, st->counter_bytes, stream);
@@ -256,14 +431,16 @@ txl_status layer_body(const txl_stack *st, int n, const __bf16 *hc, void *dst, c
                    : txl_rel_attn_fwd(&a, stream);
   if (s != TXL_OK) return s;
   // X = H + A W^O; H1 = LN1(X)
-  s = residual_ln(dense(b.o, HD, rows, c.d, HD, lw.wo, b.x, c.d), hc, lw.ln1_g, lw.ln1_b, b.h1,
-                  c.ln_eps, stream);
+  s = residual_ln(dense(o_out, HD, rows, c.d, HD, lw.wo, b.x, c.d), hc, lw.ln1_g, lw.ln1_b, h1_out,
+                  c.ln_eps, stream, tl ? tl->x1 : nullptr);
   if (s != TXL_OK) return s;
   // F = GELU(H1 W1); X = H1 + F W2; H^(n) = LN2(X)
-  s = launch_gemm(dense(b.h1, c.d, rows, c.d_ff, c.d, lw.w1, b.f, c.d_ff), kEpiGeluBf16, stream);
+  GemmParams p1 = dense(h1_out, c.d, rows, c.d_ff, c.d, lw.w1, f_out, c.d_ff);
+  p1.pre_out = tl ? tl->fpre : nullptr;
+  s = launch_gemm(p1, kEpiGeluBf16, stream);
   if (s != TXL_OK) return s;
-  return residual_ln(dense(b.f, c.d_ff, rows, c.d, c.d_ff, lw.w2, b.x, c.d), b.h1, lw.ln2_g,
-                     lw.ln2_b, dst, c.ln_eps, stream);
+  return residual_ln(dense(f_out, c.d_ff, rows, c.d, c.d_ff, lw.w2, b.x, c.d), h1_out, lw.ln2_g,
+                     lw.ln2_b, dst, c.ln_eps, stream, tl ? tl->x2 : nullptr);
 }
 
 }  // namespace
@@ -346,9 +523,229 @@ TXL_API txl_status txl_stack_create(const txl_stack_config *c, const txl_stack_w
 
 TXL_API void txl_stack_destroy(txl_stack *st) { delete st; }
 
+static txl_status segment_step(txl_stack *st, const int32_t *tokens, txl_mem *mems, void *h_out,
+                               void *workspace, size_t ws_bytes, void *tape, size_t tape_bytes,
+                               hipStream_t stream);
+
 TXL_API txl_status txl_segment_step(txl_stack *st, const int32_t *tokens, txl_mem *mems,
                                     void *h_out, void *workspace, size_t ws_bytes,
                                     hipStream_t stream) {
+  return segment_step(st, tokens, mems, h_out, workspace, ws_bytes, nullptr, 0, stream);
+}
+
+TXL_API size_t txl_segment_tape_bytes(const txl_stack_config *c) {
+  if (check_config(c) != TXL_OK) return 0;
+  return tape_layout(*c).total;
+}
+
+TXL_API txl_status txl_segment_step_train(txl_stack *st, const int32_t *tokens, txl_mem *mems,
+                                          void *h_out, void *tape, size_t tape_bytes,
+                                          void *workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!tape) return fail(TXL_ERR_INVALID_ARG, "segment_step_train: null tape");
+  return segment_step(st, tokens, mems, h_out, workspace, ws_bytes, tape, tape_bytes, stream);
+}
+
+TXL_API size_t txl_segment_backward_workspace_bytes(const txl_stack_config *c) {
+  if (check_config(c) != TXL_OK) return 0;
+  return bwd_ws(*c).total;
+}
+
+// Layer n from the top down (each product C = A B^T on the stack's GEMM):
+//   LN2:  dX2 = LN2'(X2, dH^(n)),  dg2, db2
+//   FFN:  dW2 = dX2^T F,  dFpre = (dX2 W2) * GELU'(Fpre),  dW1 = dFpre^T H1,
+//         dH1 = dX2 + dFpre W1
+//   LN1:  dX1 = LN1'(X1, dH1),  dg1, db1
+//   out:  dW^O = dX1^T A,  dA = dX1 W^O
+//   attention backward: dQ, dK, dV over [memory; segment], dR, du, dv
+//   dW^Q = dQ^T H,  dW^K = dK^T [mem; H],  dW^V = dV^T [mem; H],  dW_R = dR^T S
+//   dH^(n-1) = dX1 + dQ W^Q + dK_seg W^K + dV_seg W^V   (one GEMM over [dQ|dK|dV])
+// The memory rows enter dW^K and dW^V only: no gradient leaves through them.
+TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t tape_bytes,
+                                        const float *dy, const txl_stack_grads *grads,
+                                        void *workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!st || !tape || !dy || !grads || !grads->layers || !grads->emb || !workspace)
+    return fail(TXL_ERR_INVALID_ARG, "segment_backward: null argument");
+  const txl_stack_config &c = st->cfg;
+  const TapeLayout tlay = tape_layout(c);
+  if (tape_bytes < tlay.total)
+    return fail(TXL_ERR_WORKSPACE, "segment_backward: tape %zu < %zu bytes", tape_bytes, tlay.total);
+  const BwdWs w = bwd_ws(c);
+  if (ws_bytes < w.total)
+    return fail(TXL_ERR_WORKSPACE, "segment_backward: workspace %zu < %zu bytes", ws_bytes, w.total);
+  if ((reinterpret_cast<uintptr_t>(tape) & 255u) || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
+      (reinterpret_cast<uintptr_t>(dy) & 15u))
+    return fail(TXL_ERR_UNSUPPORTED,
+                "segment_backward: tape and workspace must be 256-byte, dy 16-byte aligned");
+  for (int n = 0; n < c.n_layer; ++n) {
+    const txl_layer_grads &g = grads->layers[n];
+    float *outs[] = {g.wq, g.wk, g.wv, g.wo, g.wr, g.u, g.vb, g.ln1_g, g.ln1_b, g.w1, g.w2, g.ln2_g, g.ln2_b};
+    for (float *o : outs) {
+      if (!o) return fail(TXL_ERR_INVALID_ARG, "segment_backward: layer %d has a null gradient", n);
+      if (reinterpret_cast<uintptr_t>(o) & 15u)
+        return fail(TXL_ERR_UNSUPPORTED, "segment_backward: layer %d gradient not 16-byte aligned", n);
+    }
+  }
+  if (reinterpret_cast<uintptr_t>(grads->emb) & 3u)
+    return fail(TXL_ERR_INVALID_ARG, "segment_backward: emb gradient not 4-byte aligned");
+
+  char *base = static_cast<char *>(workspace);
+  auto f32 = [&](size_t off) { return reinterpret_cast<float *>(base + off); };
+  auto b16 = [&](size_t off) { return reinterpret_cast<__bf16 *>(base + off); };
+  const int HD = c.n_head * c.d_h;
+  const int R = c.B * c.L;
+  const int KR = c.B * (c.M + c.L);
+  const int ML = c.M + c.L;
+  float *part = f32(w.part);
+  int rpb;
+  const int ln_blocks = ln_backward_blocks(R, &rpb);
+  __bf16 *xT = b16(w.xT), *aT = b16(w.aT), *gT = b16(w.gT), *wT = b16(w.wT);
+  __bf16 *wcatT = b16(w.wcatT), *acat = b16(w.acat), *stT = b16(w.st);
+
+  // S^T [d, t_pad]: the sinusoid rows of distances M+L-1 .. 0, shared by every layer
+  txl_status s = launch_sinusoid_t(c.M, c.L, c.d, w.t_pad, stT, stream);
+  if (s != TXL_OK) return s;
+
+  auto ln_bwd = [&](const float *x, const void *gamma, const float *dyv, float *dx, __bf16 *dxb,
+                    float *dg, float *db) {
+    txl_status r = launch_ln_backward(x, gamma, dyv, dx, dxb, f32(w.pg), f32(w.pb), R, c.d,
+                                      c.ln_eps, stream);
+    if (r != TXL_OK) return r;
+    r = launch_reduce_parts(f32(w.pg), ln_blocks, c.d, c.d, dg, stream);
+    if (r != TXL_OK) return r;
+    return launch_reduce_parts(f32(w.pb), ln_blocks, c.d, c.d, db, stream);
+  };
+  // y [C, r_pad] = x^T for a plain [R rows, C] matrix
+  auto tr = [&](const void *x, bool x_f32, int rows, int cols, int r_pad, __bf16 *y) {
+    return launch_transpose_bf16(x, rows, nullptr, nullptr, 0, cols, x_f32, rows, cols, r_pad, y,
+                                 r_pad, 0, stream);
+  };
+
+  const float *gin = dy;
+  for (int n = c.n_layer - 1; n >= 0; --n) {
+    const txl_layer_weights &lw = st->layers[n];
+    const txl_layer_grads &g = grads->layers[n];
+    const TapeLayer tl = tape_at(tlay, tape, n);
+    float *gout = f32((c.n_layer - 1 - n) % 2 ? w.g1 : w.g0);
+    float *dx2 = f32(w.dx2), *dh1 = f32(w.dh1), *dx1 = f32(w.dx1);
+    __bf16 *dx2b = b16(w.dx2b), *dx1b = b16(w.dx1b), *dfpre = b16(w.dfpre), *dfpreT = b16(w.dfpreT);
+
+    // LN2
+    s = ln_bwd(tl.x2, lw.ln2_g, gin, dx2, dx2b, g.ln2_g, g.ln2_b);
+    if (s != TXL_OK) return s;
+    // dW2 = dX2^T F
+    if ((s = tr(dx2, true, R, c.d, w.r_pad, xT)) != TXL_OK) return s;
+    if ((s = tr(tl.f, false, R, c.d_ff, w.r_pad, aT)) != TXL_OK) return s;
+    if ((s = dw_gemm(xT, c.d, aT, c.d_ff, w.r_pad, g.w2, part, stream)) != TXL_OK) return s;
+    // dFpre = (dX2 W2) * GELU'(Fpre)
+    if ((s = tr(lw.w2, false, c.d, c.d_ff, c.d, wT)) != TXL_OK) return s;
+    GemmParams pf = dense(dx2b, c.d, R, c.d_ff, c.d, wT, dfpre, c.d_ff);
+    pf.pre_in = tl.fpre;
+    if ((s = launch_gemm(pf, kEpiGeluGradBf16, stream)) != TXL_OK) return s;
+    // dW1 = dFpre^T H1
+    if ((s = tr(dfpre, false, R, c.d_ff, w.r_pad, dfpreT)) != TXL_OK) return s;
+    if ((s = tr(tl.h1, false, R, c.d, w.r_pad, aT)) != TXL_OK) return s;
+    if ((s = dw_gemm(dfpreT, c.d_ff, aT, c.d, w.r_pad, g.w1, part, stream)) != TXL_OK) return s;
+    // dH1 = dX2 + dFpre W1
+    if ((s = tr(lw.w1, false, c.d_ff, c.d, c.d_ff, wT)) != TXL_OK) return s;
+    GemmParams ph = dense(dfpre, c.d_ff, R, c.d, c.d_ff, wT, dh1, c.d);
+    ph.res32 = dx2;
+    ph.ldres = c.d;
+    if ((s = launch_gemm(ph, kEpiResidualF32, stream)) != TXL_OK) return s;
+    // LN1
+    if ((s = ln_bwd(tl.x1, lw.ln1_g, dh1, dx1, dx1b, g.ln1_g, g.ln1_b)) != TXL_OK) return s;
+    // dW^O = dX1^T A;  dA = dX1 W^O
+    if ((s = tr(dx1, true, R, c.d, w.r_pad, xT)) != TXL_OK) return s;
+    if ((s = tr(tl.o, false, R, HD, w.r_pad, aT)) != TXL_OK) return s;
+    if ((s = dw_gemm(xT, c.d, aT, HD, w.r_pad, g.wo, part, stream)) != TXL_OK) return s;
+    if ((s = tr(lw.wo, false, c.d, HD, c.d, wT)) != TXL_OK) return s;
+    if ((s = launch_gemm(dense(dx1b, c.d, R, HD, c.d, wT, b16(w.dout), HD), kEpiStoreBf16, stream)) != TXL_OK)
+      return s;
+    // attention backward, with the forward's arguments as the tape holds them
+    txl_rel_attn_args a = {};
+    a.dtype = TXL_BF16;
+    a.B = c.B;
+    a.H = c.n_head;
+    a.L = c.L;
+    a.M = c.M;
+    a.d_h = c.d_h;
+    a.q = tl.q;
+    a.q_sb = static_cast<int64_t>(c.L) * HD;
+    a.q_sh = c.d_h;
+    a.q_sl = HD;
+    a.k = tl.k;
+    a.v = tl.v;
+    a.kv_sb = static_cast<int64_t>(ML) * HD;
+    a.kv_sh = c.d_h;
+    a.kv_sl = HD;
+    a.r = static_cast<const char *>(st->persistent) + n * st->r_bytes;
+    a.r_sh = c.d_h;
+    a.r_sl = HD;
+    a.u = lw.u;
+    a.vb = lw.vb;
+    a.mem_valid = tl.valid;
+    a.scale = 0.0f;
+    a.out = tl.o;
+    a.o_sb = static_cast<int64_t>(c.L) * HD;
+    a.o_sh = c.d_h;
+    a.o_sl = HD;
+    a.lse = tl.lse;
+    a.out_f32 = tl.o32;
+    txl_rel_attn_grads ag = {};
+    ag.dout = b16(w.dout);
+    ag.do_sb = static_cast<int64_t>(c.L) * HD;
+    ag.do_sh = c.d_h;
+    ag.do_sl = HD;
+    ag.dq = f32(w.dq);
+    ag.dk = f32(w.dk);
+    ag.dv = f32(w.dv);
+    ag.dr = f32(w.dr);
+    ag.du = g.u;
+    ag.dvb = g.vb;
+    if ((s = txl_rel_attn_bwd(&a, &ag, base + w.attn, w.attn_bytes, stream)) != TXL_OK) return s;
+    // dW^Q = dQ^T H  (dQ also into acat's first HD columns)
+    if ((s = launch_head_grad_pack(f32(w.dq), c.B, c.n_head, c.L, gT, w.r_pad, acat, c.L, 3 * HD, 0,
+                                   stream)) != TXL_OK)
+      return s;
+    if ((s = launch_zero_cols(gT, HD, w.r_pad, R, w.r_pad, stream)) != TXL_OK) return s;
+    if ((s = tr(tl.hin, false, R, c.d, w.r_pad, aT)) != TXL_OK) return s;
+    if ((s = dw_gemm(gT, HD, aT, c.d, w.r_pad, g.wq, part, stream)) != TXL_OK) return s;
+    // dW^K = dK^T [mem; H], dW^V = dV^T [mem; H] (slots a row does not hold read as 0)
+    if ((s = launch_transpose_bf16(tl.mem, c.M, tl.valid, tl.hin, c.L, c.d, false, KR, c.d,
+                                   w.e_pad, aT, w.e_pad, 0, stream)) != TXL_OK)
+      return s;
+    for (int kv = 0; kv < 2; ++kv) {
+      if ((s = launch_head_grad_pack(f32(kv ? w.dv : w.dk), c.B, c.n_head, ML, gT, w.e_pad, acat,
+                                     c.L, 3 * HD, (1 + kv) * HD, stream)) != TXL_OK)
+        return s;
+      if ((s = launch_zero_cols(gT, HD, w.e_pad, KR, w.e_pad, stream)) != TXL_OK) return s;
+      if ((s = dw_gemm(gT, HD, aT, c.d, w.e_pad, kv ? g.wv : g.wk, part, stream)) != TXL_OK) return s;
+    }
+    // dW_R = dR^T S (R = S W_R^T for distances M+L-1 .. 0)
+    if ((s = launch_head_grad_pack(f32(w.dr), 1, c.n_head, ML, gT, w.t_pad, nullptr, 0, 0, 0,
+                                   stream)) != TXL_OK)
+      return s;
+    if ((s = launch_zero_cols(gT, HD, w.t_pad, ML, w.t_pad, stream)) != TXL_OK) return s;
+    if ((s = dw_gemm(gT, HD, stT, c.d, w.t_pad, g.wr, part, stream)) != TXL_OK) return s;
+    // dH^(n-1) = dX1 + [dQ | dK_seg | dV_seg] [W^Q; W^K; W^V]
+    const void *wqkv[3] = {lw.wq, lw.wk, lw.wv};
+    for (int j = 0; j < 3; ++j)
+      if ((s = launch_transpose_bf16(wqkv[j], HD, nullptr, nullptr, 0, c.d, false, HD, c.d, HD,
+                                     wcatT, 3 * HD, j * HD, stream)) != TXL_OK)
+        return s;
+    GemmParams pi = dense(acat, 3 * HD, R, c.d, 3 * HD, wcatT, gout, c.d);
+    pi.res32 = dx1;
+    pi.ldres = c.d;
+    if ((s = launch_gemm(pi, kEpiResidualF32, stream)) != TXL_OK) return s;
+    gin = gout;
+  }
+  // H^(0) = Emb[tokens]: each position's gradient goes to its token's row
+  const int32_t *tok = reinterpret_cast<const int32_t *>(static_cast<const char *>(tape) + tlay.tokens);
+  return launch_embed_backward(tok, R, gin, c.d, c.vocab, grads->emb, stream);
+}
+
+static txl_status segment_step(txl_stack *st, const int32_t *tokens, txl_mem *mems, void *h_out,
+                               void *workspace, size_t ws_bytes, void *tape, size_t tape_bytes,
+                               hipStream_t stream) {
   if (!st || !tokens || !mems || !h_out || !workspace)
     return fail(TXL_ERR_INVALID_ARG, "segment_step: null argument");
   const txl_stack_config &c = st->cfg;
@@ -367,24 +764,52 @@ TXL_API txl_status txl_segment_step(txl_stack *st, const int32_t *tokens, txl_me
       return fail(TXL_ERR_UNSUPPORTED, "segment_step: ring %d misaligned", n);
   }
 
+  const TapeLayout tlay = tape_layout(c);
+  if (tape) {
+    if (tape_bytes < tlay.total)
+      return fail(TXL_ERR_WORKSPACE, "segment_step_train: tape %zu < %zu bytes", tape_bytes, tlay.total);
+    if (reinterpret_cast<uintptr_t>(tape) & 255u)
+      return fail(TXL_ERR_UNSUPPORTED, "segment_step_train: tape not 256-byte aligned");
+  }
+
   StepBufs b = bufs(ws, workspace);
   const int HD = c.n_head * c.d_h;
   const int rows = c.B * c.L;
   const int ML = c.M + c.L;
   // H^(n), the input of layer n, lives in slot n until the end of the step
-  // (batched ring update) or in slot n mod 2 (ring updated after the layer)
+  // (batched ring update) or in slot n mod 2 (ring updated after the layer);
+  // with a tape, in the tape's record of layer n
   const bool batched = batch_rings(c);
   auto slot = [&](int n) {
+    if (tape) return tape_at(tlay, tape, n).hin;
     return b.hs + static_cast<size_t>(batched ? n : (n & 1)) * rows * c.d;
   };
   s = launch_embed(tokens, st->emb, slot(0), rows, c.d, c.vocab, stream);
   if (s != TXL_OK) return s;
+  if (tape) {
+    s = launch_copy_i32(tokens, reinterpret_cast<int32_t *>(static_cast<char *>(tape) + tlay.tokens),
+                        rows, stream);
+    if (s != TXL_OK) return s;
+  }
   for (int n = 0; n < c.n_layer; ++n) {
     const txl_layer_weights &lw = st->layers[n];
     txl_mem &ring = mems[n];
     const __bf16 *hc = slot(n);
+    TapeLayer tl;
+    if (tape) {  // the memory as this layer reads it, before any update
+      tl = tape_at(tlay, tape, n);
+      if (c.M > 0) {
+        s = launch_mem_read_logical(ring.data, tl.mem, c.B, c.M, ring.head,
+                                    static_cast<int64_t>(c.d) * 2, stream);
+        if (s != TXL_OK) return s;
+      }
+      s = launch_copy_i32(ring.valid, tl.valid, c.B, stream);
+      if (s != TXL_OK) return s;
+    }
+    __bf16 *k_out = tape ? tl.k : b.k;
+    __bf16 *v_out = tape ? tl.v : b.v;
     // [K | V] = [ring; H] [W^K | W^V], memory rows gathered in logical order
-    GemmParams pkv = dense(nullptr, c.d, c.B * ML, 2 * HD, c.d, lw.wk, b.k, HD);
+    GemmParams pkv = dense(nullptr, c.d, c.B * ML, 2 * HD, c.d, lw.wk, k_out, HD);
     pkv.gather = 1;
     pkv.ring = static_cast<const __bf16 *>(ring.data);
     pkv.seg = hc;
@@ -394,7 +819,7 @@ TXL_API txl_status txl_segment_step(txl_stack *st, const int32_t *tokens, txl_me
     pkv.segL = c.L;
     pkv.w1 = static_cast<const __bf16 *>(lw.wv);
     pkv.n_split = HD;
-    pkv.c1 = b.v;
+    pkv.c1 = v_out;
     s = launch_gemm(pkv, kEpiStoreBf16, stream);
     if (s != TXL_OK) return s;
     void *dst = (n + 1 == c.n_layer) ? h_out : static_cast<void *>(slot(n + 1));
@@ -402,8 +827,8 @@ TXL_API txl_status txl_segment_step(txl_stack *st, const int32_t *tokens, txl_me
     // read it: inside the attention's launch when it runs unsplit (the copy
     // then runs in the shadow of the latency-bound attention), else after it.
     const bool fused = !batched && attn_splits(c) == 1;
-    s = layer_body(st, n, hc, dst, b.k, b.v, static_cast<int64_t>(ML) * HD, ring.valid, b, stream,
-                   fused ? &ring : nullptr);
+    s = layer_body(st, n, hc, dst, k_out, v_out, static_cast<int64_t>(ML) * HD, ring.valid, b,
+                   stream, fused ? &ring : nullptr, tape ? &tl : nullptr);
     if (s != TXL_OK) return s;
     if (!batched && !fused) {
       const void *hptr = hc;

@@ -22,6 +22,7 @@ struct AttnParams {
   const void *q, *k, *v, *r, *u, *vb;
   void *out;
   float *lse;
+  float *out32;  // optional fp32 copy of out, [B*H*L, 64] contiguous (bf16 path only)
   const int32_t *valid;
   int64_t q_sb, q_sh, q_sl, kv_sb, kv_sh, kv_sl, r_sh, r_sl, o_sb, o_sh, o_sl;
   int32_t B, H, L, M;
@@ -93,6 +94,7 @@ struct BwdParams {
   const __bf16 *dout;
   int64_t do_sb, do_sh, do_sl;
   const float *lse;
+  const float *out32;     // the forward's unrounded out [B*H*L, 64], or null
   float *dq, *dk, *dv, *dr, *du, *dvb;
   __bf16 *qv;             // [B*H*L, 64]: q + v
   float *dd;              // [B*H*L]: dout . out
@@ -133,13 +135,43 @@ txl_status launch_mem_read_logical(const void *data, void *out, int B, int M,
 // ---- relative-position table ---------------------------------------------
 txl_status launch_rel_pos_table(txl_dtype dt, int M, int L, int d, int HD,
                                 const void *w_r, void *r, hipStream_t s);
+// st [d, t_pad] bf16: st[k, t] = S(M+L-1-t, k) for t < M+L, 0 beyond
+txl_status launch_sinusoid_t(int M, int L, int d, int t_pad, void *st, hipStream_t s);
+
+// ---- segment gradients (bwd.hip) -------------------------------------------
+// y[c, col0 + q] = row q of the source, bf16, zero for R <= q < r_pad; source
+// row q is, with G = g1 + g2, row (q/G)*g1 + q%G of x1 when q%G < g1, else
+// row (q/G)*g2 + q%G - g1 of x2 (row stride ldx; fp32 or bf16 source); with
+// valid1 set, x1 rows j = q%G < g1 - valid1[q/G] read as 0
+txl_status launch_transpose_bf16(const void *x1, int g1, const int32_t *valid1, const void *x2,
+                                 int g2, int64_t ldx, bool src_f32, int R, int C, int r_pad,
+                                 void *y, int64_t ldy, int col0, hipStream_t s);
+// g [B, H, T, 64] fp32 -> yt[h*64 + e, b*T + j] bf16 (row stride ldt) and,
+// when y2 is set, y2[b*L + j - (T-L), col0 + h*64 + e] for j >= T - L
+txl_status launch_head_grad_pack(const float *g, int B, int H, int T, void *yt, int64_t ldt,
+                                 void *y2, int L, int64_t ld2, int col0, hipStream_t s);
+txl_status launch_zero_cols(void *y, int n_rows, int64_t ldy, int c_from, int c_to, hipStream_t s);
+// out[i] = sum over s < S of part[s*stride + i] (n a multiple of 4, 16-byte aligned)
+txl_status launch_reduce_parts(const float *part, int S, int64_t stride, int64_t n, float *out,
+                               hipStream_t s);
+int ln_backward_blocks(int rows, int *rpb);
+txl_status launch_ln_backward(const float *x, const void *gamma, const float *dy, float *dx,
+                              void *dxb, float *part_g, float *part_b, int rows, int d, float eps,
+                              hipStream_t s);
+txl_status launch_embed_backward(const int32_t *tokens, int n_tok, const float *dh0, int d,
+                                 int vocab, float *demb, hipStream_t s);
+txl_status launch_copy_i32(const int32_t *src, int32_t *dst, int n, hipStream_t s);
 
 // ---- dense layers of the stack ---------------------------------------------
 // kEpiPartialF32: split-K, split s stores its fp32 partial at c0 + s*c_split_stride
 // kEpiLse: C is not stored; per row tile tm and column n the tile's maximum
 //          and sum of exponentials over its rows go to part_m/part_s[tm*N + n],
 //          and C[targets[n]][n] to tgt[n] (rows = vocabulary, columns = tokens)
-enum { kEpiStoreBf16 = 0, kEpiGeluBf16 = 1, kEpiResidualF32 = 2, kEpiPartialF32 = 3, kEpiLse = 4 };
+// kEpiGeluGradBf16: C = acc * GELU'(pre_in) stored bf16 (the backward of the
+//          feed-forward's activation); kEpiGeluBf16 also stores the
+//          pre-activation acc (bf16) to pre_out when it is set
+enum { kEpiStoreBf16 = 0, kEpiGeluBf16 = 1, kEpiResidualF32 = 2, kEpiPartialF32 = 3, kEpiLse = 4,
+       kEpiGeluGradBf16 = 5 };
 // C[m, n] = sum_k A[m, k] W[n, k]; N split at n_split between (w0, c0) and
 // (w1, c1); n_split and N are multiples of 128, K a multiple of 32.
 struct GemmParams {
@@ -163,6 +195,9 @@ struct GemmParams {
   int64_t c_bstride, c_row0;
   const __bf16 *res;  // residual [rows, ldres] for kEpiResidualF32
   int64_t ldres;
+  const float *res32; // fp32 residual [rows, ldres] instead of res (kEpiResidualF32)
+  __bf16 *pre_out;    // kEpiGeluBf16: pre-activation [rows, ldc] (null = not stored)
+  const __bf16 *pre_in;  // kEpiGeluGradBf16: pre-activation [rows, ldc]
   // split-K (kEpiPartialF32 only): k_splits workgroups per tile, each over a
   // contiguous range of K slabs
   int k_splits;
@@ -174,9 +209,10 @@ struct GemmParams {
 txl_status launch_gemm(const GemmParams &p, int epi, hipStream_t s);
 // y = LN(x) over rows of d, x = sum of n_parts fp32 buffers (part_stride
 // elements apart, added in order) plus the bf16 residual res (may be null)
+// x_out (may be null) receives the summed fp32 x (the LayerNorm's input)
 txl_status launch_layernorm(const float *x, int n_parts, int64_t part_stride, const void *res,
                             const void *gamma, const void *beta, void *y, int rows, int d,
-                            float eps, hipStream_t s);
+                            float eps, hipStream_t s, float *x_out = nullptr);
 // row tiles the kEpiLse GEMM uses for `rows` rows (its part_m/part_s height)
 int lse_row_tiles(int rows, int N);
 // nll[n] = log(sum_t part_s[t][n] exp(part_m[t][n] - m)) + m - tgt[n] for

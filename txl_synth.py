@@ -163,14 +163,17 @@ LAYER_KEYS = ("wq", "wk", "wv", "wo", "wr", "u", "vb", "ln1_g", "ln1_b",
               "w1", "w2", "ln2_g", "ln2_b")
 
 
-def stack_weights(cfg: StackConfig, *, n_layer: Optional[int] = None
-                  ) -> Dict[str, object]:
+def stack_weights(cfg: StackConfig, *, n_layer: Optional[int] = None,
+                  ln_std: float = 0.0) -> Dict[str, object]:
     """Draw the stack's weights (CPU tensors, rounded to the workload dtype).
 
     Math orientation: a projection ``y = x W`` stores W as [in, out].
     Draw order: emb [vocab, d], then per layer wq, wk, wv [d, H*d_h],
     wo [H*d_h, d], wr [d, H*d_h], u [H, d_h], vb [H, d_h], w1 [d, d_ff],
-    w2 [d_ff, d]. LayerNorm gains are 1 and shifts 0 (not drawn).
+    w2 [d_ff, d]. LayerNorm gains are 1 and shifts 0 (not drawn), unless
+    ``ln_std`` > 0: then, after all of the above, per layer ln1_g, ln1_b,
+    ln2_g, ln2_b are drawn as 1 + N(0, ln_std^2), N(0, ln_std^2) (gains)
+    and N(0, ln_std^2) (shifts), so that gradients see gains other than 1.
     """
     n_layer = cfg.n_layer if n_layer is None else n_layer
     g = torch.Generator("cpu").manual_seed(cfg.seed)
@@ -193,7 +196,14 @@ def stack_weights(cfg: StackConfig, *, n_layer: Optional[int] = None
             "ln1_g": torch.ones(d), "ln1_b": torch.zeros(d),
             "ln2_g": torch.ones(d), "ln2_b": torch.zeros(d),
         }
-        layers.append({k: t.to(dt) for k, t in lw.items()})
+        layers.append(lw)
+    if ln_std > 0:
+        for lw in layers:
+            lw["ln1_g"] = 1.0 + _normal(g, (d,), ln_std)
+            lw["ln1_b"] = _normal(g, (d,), ln_std)
+            lw["ln2_g"] = 1.0 + _normal(g, (d,), ln_std)
+            lw["ln2_b"] = _normal(g, (d,), ln_std)
+    layers = [{k: t.to(dt) for k, t in lw.items()} for lw in layers]
     return {"emb": emb, "layers": layers}
 
 
@@ -207,6 +217,16 @@ def stack_tokens(cfg: StackConfig, *, n_seg: Optional[int] = None,
     g = torch.Generator("cpu").manual_seed(cfg.seed + 1)
     return torch.randint(0, cfg.vocab, (n_seg, B, L), generator=g,
                          dtype=torch.int32)
+
+
+def stack_dy(cfg: StackConfig, *, B: Optional[int] = None, L: Optional[int] = None,
+             seed_offset: int = 2) -> torch.Tensor:
+    """A gradient arriving at the stack's output: N(0, 1) fp32 [B, L, d]
+    (seed = cfg.seed + seed_offset)."""
+    B = cfg.B if B is None else B
+    L = cfg.L if L is None else L
+    g = torch.Generator("cpu").manual_seed(cfg.seed + seed_offset)
+    return _normal(g, (B, L, cfg.d), 1.0)
 
 
 def reset_schedule(cfg: StackConfig, n_seg: Optional[int] = None,
