@@ -156,6 +156,98 @@ def stack_flops(c, m_eff, kv=False):
     return c.n_layer * per_layer
 
 
+def stack_train_flops(c, m_eff):
+    """Algorithmic flops of one training step: the forward (stack_flops) and
+    the backward: per dense product C = A W its two gradients dA = dC W^T and
+    dW = A^T dC, except that dA of the K/V projection covers the segment rows
+    only (the memory is a stop-gradient input), the W_R gradient through
+    R = S W_R^T, and the attention backward (16 d_h per visible pair)."""
+    hd = c.H * c.d_h
+    rows = c.B * c.L
+    kv_rows = c.B * (m_eff + c.L)
+    ml = m_eff + c.L
+    dw = (2 * rows * c.d * hd + 4 * kv_rows * c.d * hd + 2 * rows * hd * c.d
+          + 4 * rows * c.d * c.d_ff + 2 * ml * c.d * hd)
+    dx = 2 * rows * c.d * hd + 4 * rows * c.d * hd + 2 * rows * hd * c.d + 4 * rows * c.d * c.d_ff
+    attn_b = attn_flops(c.B, c.H, c.L, m_eff, c.d_h) * 8.0 / 3.0
+    return stack_flops(c, m_eff) + c.n_layer * (dw + dx + attn_b)
+
+
+def stack_train_bench(name: str, steps: int, warmup: int) -> dict:
+    """One training step of the stack with a full memory: the recording
+    forward (txl_segment_step_train, rings advanced) and the segment
+    backward (txl_segment_backward: every weight gradient, the embedding
+    gradient), for a fixed gradient at the output, captured once as a HIP
+    graph and replayed `steps` times between events."""
+    import torch
+
+    import txl_synth
+    import transformer_xl_relative_txl_amd as txl
+
+    c = txl_synth.STACK_CONFIGS[name]
+    dev = torch.device("cuda:0")
+    w = txl_synth.stack_weights(c, ln_std=0.1)
+    out_major = ("wq", "wk", "wv", "wo", "wr", "w1", "w2")
+    emb = w["emb"].to(dev).contiguous()
+    layers = [{k: (t.t() if k in out_major else t).contiguous().to(dev) for k, t in lw.items()}
+              for lw in w["layers"]]
+    st = txl.TxlStack(n_layer=c.n_layer, d=c.d, n_head=c.H, d_h=c.d_h, d_ff=c.d_ff,
+                      vocab=c.vocab, B=c.B, L=c.L, M=c.M, emb=emb, layers=layers)
+    tokens = txl_synth.stack_tokens(c).to(dev)
+    dy = txl_synth.stack_dy(c).to(dev).contiguous()
+    h = torch.empty((c.B, c.L, c.d), dtype=torch.bfloat16, device=dev)
+    mems = [txl.TxlMem.empty(c.B, c.M, c.d, device=dev) for _ in range(c.n_layer + 1)]
+    tape = st.new_tape()
+    grads = st.new_grads()
+
+    def step(i):
+        st.step_train(tokens[i % c.n_seg].contiguous(), mems, h, tape)
+        st.backward(tape, dy, grads)
+
+    s = 0
+    while int(mems[0].valid.min().item()) < c.M or s < warmup:   # fill the memory
+        step(s)
+        s += 1
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(0)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    for _ in range(int(SETTLE_MS / max(e0.elapsed_time(e1), 1e-3)) + 1):   # settle the clocks
+        g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fl = stack_train_flops(c, c.M)
+    tape_mb = tape.numel() / 1e6
+    ws_mb = st._bwd_ws.numel() / 1e6
+    st.close()
+    tflops = fl / (ms * 1e-3) / 1e12
+    return {"metric": "training step TFLOP/s (N-layer stack forward + segment backward), 1 GPU",
+            "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+            "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"{c.n_layer}-layer stack training step, d={c.d} H={c.H} "
+                                   f"d_ff={c.d_ff} B={c.B} L={c.L} M={c.M} (memory full, "
+                                   "stop-gradient; all weight and embedding gradients)",
+                       "tokens_per_s": round(c.B * c.L / (ms * 1e-3), 1),
+                       "tape_MB": round(tape_mb, 1), "backward_workspace_MB": round(ws_mb, 1)},
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None},
+            "gflop_per_step": round(fl / 1e9, 2)}
+
+
 def stack_bench(name: str, steps: int, warmup: int, kv: bool = False) -> dict:
     """One segment step of the stack with a full memory (steady state),
     captured once as a HIP graph and replayed `steps` times between events.
@@ -428,6 +520,8 @@ def main() -> int:
                          "workload or 18-layer d=1024 long-memory workload)")
     ap.add_argument("--kv", action="store_true",
                     help="with --stack: keep memory as projected keys / values")
+    ap.add_argument("--train", action="store_true",
+                    help="with --stack: the training step (recording forward + segment backward)")
     ap.add_argument("--loss", action="store_true",
                     help="measure the segment loss (logits + cross entropy) instead")
     ap.add_argument("--bwd", action="store_true",
@@ -449,6 +543,9 @@ def main() -> int:
         return 0
     if args.mem_sweep:
         print(json.dumps(mem_sweep_bench(args.steps)), flush=True)
+        return 0
+    if args.stack and args.train:
+        print(json.dumps(stack_train_bench(args.stack, args.steps, args.warmup)), flush=True)
         return 0
     if args.stack:
         print(json.dumps(stack_bench(args.stack, args.steps, args.warmup, args.kv)), flush=True)

@@ -113,6 +113,32 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(const float *__restri
   reinterpret_cast<f32x4 *>(out)[e] = acc;
 }
 
+// The same sum for many parts over few columns (the LayerNorm parameter
+// partials: hundreds of parts, d columns): a workgroup owns 16 columns, its
+// 16 thread groups each add every 16th part in order, and the 16 group sums
+// are added in group order.
+constexpr int kColGroups = 16;
+__global__ __launch_bounds__(256) void reduce_cols_kernel(const float *__restrict__ part, int S,
+                                                          int64_t stride, int64_t n,
+                                                          float *__restrict__ out) {
+  __shared__ float red[kColGroups][16];
+  const int cl = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  const int64_t col = static_cast<int64_t>(blockIdx.x) * 16 + cl;
+  float acc = 0.0f;
+  if (col < n) {
+#pragma unroll 8
+    for (int s = grp; s < S; s += kColGroups) acc += part[s * stride + col];
+  }
+  red[grp][cl] = acc;
+  __syncthreads();
+  if (grp == 0 && col < n) {
+    float t = red[0][cl];
+#pragma unroll
+    for (int gq = 1; gq < kColGroups; ++gq) t += red[gq][cl];
+    out[col] = t;
+  }
+}
+
 // LayerNorm backward, one wave per row, rows [blockIdx.x * rpb, ...) per
 // workgroup: dx = r (gdy - mean(gdy) - xhat mean(gdy xhat)), gdy = dy gamma,
 // xhat = (x - mean) r; dx in fp32 and, when dxb is set, bf16. The gamma and
@@ -307,8 +333,13 @@ txl_status launch_head_grad_pack(const float *g, int B, int H, int T, void *yt, 
 txl_status launch_reduce_parts(const float *part, int S, int64_t stride, int64_t n, float *out,
                                hipStream_t s) {
   if (n == 0) return TXL_OK;
-  const int64_t n4 = n / 4;
   (void)hipGetLastError();
+  if (S > 16) {  // many parts: split them over thread groups
+    hipLaunchKernelGGL(reduce_cols_kernel, dim3(static_cast<unsigned>((n + 15) / 16)), dim3(256), 0, s,
+                       part, S, stride, n, out);
+    return check_launch("reduce_cols_kernel");
+  }
+  const int64_t n4 = n / 4;
   hipLaunchKernelGGL(reduce_parts_kernel, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, s,
                      part, S, stride, n4, out);
   return check_launch("reduce_parts_kernel");

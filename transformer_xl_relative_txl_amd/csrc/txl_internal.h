@@ -151,7 +151,8 @@ txl_status launch_transpose_bf16(const void *x1, int g1, const int32_t *valid1, 
 txl_status launch_head_grad_pack(const float *g, int B, int H, int T, void *yt, int64_t ldt,
                                  void *y2, int L, int64_t ld2, int col0, hipStream_t s);
 txl_status launch_zero_cols(void *y, int n_rows, int64_t ldy, int c_from, int c_to, hipStream_t s);
-// out[i] = sum over s < S of part[s*stride + i] (n a multiple of 4, 16-byte aligned)
+// out[i] = sum over s < S of part[s*stride + i], in a fixed order (n a multiple
+// of 4, 16-byte aligned)
 txl_status launch_reduce_parts(const float *part, int S, int64_t stride, int64_t n, float *out,
                                hipStream_t s);
 int ln_backward_blocks(int rows, int *rpb);
