@@ -72,16 +72,15 @@ constexpr int QW = 32;         // queries per wave (MFMA N)
 constexpr int NW = 4;          // waves per workgroup
 constexpr int BQ = QW * NW;    // queries per workgroup
 constexpr int BK = 64;         // keys per tile
-constexpr int KS = DH + 8;     // K tile row stride (bf16 elements)
-constexpr int VS = BK + 8;     // V^T tile row stride (bf16 elements)
 constexpr int NU = 3 * QW;     // band rows of a tile: key c of half kb reads u = c + 31 - r + 32kb < 95
-constexpr int US = QW + 2;     // band row stride (floats); odd multiple of 2 -> conflict-free skew
+constexpr int US = QW;         // band row stride (floats): the diagonal read puts lane r on bank r
 constexpr float kPsumLimit = 256.0f;  // a tile keeps the running max while each lane's sum of p stays <= 2^8
 
-constexpr size_t kLdsK = size_t(BK) * KS * 2;   // one K tile
-constexpr size_t kLdsV = size_t(DH) * VS * 2;   // one V^T tile
-constexpr size_t kLdsBand = size_t(NW) * NU * US * 4;
-constexpr size_t kLdsTotal = (kLdsK + kLdsV) + kLdsBand;  // 70656 bytes: two workgroups per CU
+// LDS: two K/V tile buffers (K [64 keys][64 dims] then V [64 keys][64 dims],
+// bf16, 16-byte chunks swizzled: chunk c of key row n sits in slot c ^ (n & 7))
+// and the waves' bands; 81920 bytes, two workgroups per CU.
+constexpr int kTileElems = BK * DH;            // one K or V tile
+constexpr int kBandFloats = NW * NU * US;
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -138,42 +137,31 @@ __device__ inline void bstore_nt(rsrc_t rs, int byte_off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, rs, byte_off, 0, kNonTemporal);
 }
 
-// One tile of K (two 16-byte chunks per thread) and V (two keys x 8 dims
-// per thread), held in registers between the global load and the LDS store.
-struct KVRegs {
-  u32x4 k[2];
-  u32x4 va, vb;
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ inline void load_kv(KVRegs &x, rsrc_t krs, rsrc_t vrs, int row_bytes, int j0, int tid) {
+// Tile [j0, j0 + 64) of K and of V into an LDS buffer with direct
+// buffer-to-LDS loads (no registers): wave w's instruction t = 2w + rep fills
+// key rows 8t .. 8t+7, lane l landing at byte 16 l of that 1 KiB (row
+// 8t + l/8, slot l % 8), so the lane loads source chunk (l % 8) ^ (l / 8) of
+// its row. Rows past the buffer's range load zeros.
+__device__ inline void dma_kv(rsrc_t krs, rsrc_t vrs, int row_bytes, int j0, __bf16 *buf, int wave,
+                              int lane) {
 #pragma unroll
   for (int rep = 0; rep < 2; ++rep) {
-    const int cidx = tid + rep * 256;
-    const int row = cidx >> 3, col = (cidx & 7) * 8;
-    x.k[rep] = bload(krs, (j0 + row) * row_bytes + col * 2);
+    const int t = 2 * wave + rep;
+    const int row = 8 * t + (lane >> 3);
+    const int off = (j0 + row) * row_bytes + 16 * ((lane & 7) ^ (lane >> 3));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void *)(buf + 512 * t), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(buf + kTileElems + 512 * t), 16, off,
+                                             0, 0, 0);
   }
-  const int kq = tid & 31, dc = tid >> 5;
-  const int ja = j0 + 2 * kq;
-  x.va = bload(vrs, ja * row_bytes + 16 * dc);
-  x.vb = bload(vrs, (ja + 1) * row_bytes + 16 * dc);
 }
 
-__device__ inline void store_kv(const KVRegs &x, __bf16 *sk, __bf16 *svt, int tid) {
-#pragma unroll
-  for (int rep = 0; rep < 2; ++rep) {
-    const int cidx = tid + rep * 256;
-    const int row = cidx >> 3, col = (cidx & 7) * 8;
-    *reinterpret_cast<u32x4 *>(sk + row * KS + col) = x.k[rep];
-  }
-  // V^T: 32-bit word w of a V row holds dims 2w (low half) and 2w+1 (high half)
-  const int kq = tid & 31, dc = tid >> 5;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t even = (x.va[w] & 0xffffu) | (x.vb[w] << 16);
-    const uint32_t odd = (x.va[w] >> 16) | (x.vb[w] & 0xffff0000u);
-    *reinterpret_cast<uint32_t *>(svt + (8 * dc + 2 * w) * VS + 2 * kq) = even;
-    *reinterpret_cast<uint32_t *>(svt + (8 * dc + 2 * w + 1) * VS + 2 * kq) = odd;
-  }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+// Transposing LDS read: within each 16-lane group, element k of lane j is the
+// 16-bit value at (address of lane 4k + j/4) + j % 4.
+__device__ inline v4i16 lds_read_tr(const __bf16 *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)p);
 }
 
 // The attention of one query tile; with kAppend the workgroups of the lighter
@@ -187,9 +175,8 @@ __device__ inline void store_kv(const KVRegs &x, __bf16 *sk, __bf16 *svt, int ti
 // their end put the contended atomic's return on their first tile's wait.)
 template <bool kAppend>
 __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, const RingAppend &ra,
-                                              unsigned char *smem) {
-  // the K tile at smem, the V^T tile right after it, then the waves' bands
-  float *sband = reinterpret_cast<float *>(smem + (kLdsK + kLdsV));
+                                              __bf16 *__restrict__ kv0, __bf16 *__restrict__ kv1,
+                                              float *__restrict__ sband) {
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -249,8 +236,7 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
   const rsrc_t vrs = make_rsrc(vp, static_cast<uint32_t>((j_end - 1) * kv_row_bytes + 2 * DH));
   const rsrc_t rrs = make_rsrc(rp, static_cast<uint32_t>((ML - 1) * r_row_bytes + 2 * DH));
 
-  KVRegs nxt;
-  load_kv(nxt, krs, vrs, kv_row_bytes, j_lo, tid);
+  dma_kv(krs, vrs, kv_row_bytes, j_lo, kv0, wave, lane);
 
   // Q' = (q+u) c and Q'' = (q+v) c as B operands: k-step s holds dims 16s+8hh..+7
   const float c2 = p.scale * 1.4426950408889634f;
@@ -276,11 +262,14 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
 #pragma unroll
     for (int x = 0; x < 16; ++x) o_acc[db][x] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
-  float *band = sband + wave * (NU * US);
-  // band[u][r] for this lane: written at u*US + r, the shifted read of key c
-  // is band[(c + 31 - r)][r]
-  float *band_w = band + 4 * hh * US + r;
-  const float *band_r = band + (31 - r + 4 * hh) * US + r;
+  // This wave's band [u][r] starts at sband[band0]: written at u*US + r, the
+  // shifted read of key c is [(c + 31 - r)][r]. LDS accesses index the
+  // kernel's LDS arrays directly (one offset from the array), which lets the
+  // compiler tell them apart from the tile buffer the loads are filling and
+  // not wait for those loads before reading the band or the other buffer.
+  const int band0 = wave * (NU * US);
+  const int band_w = band0 + 4 * hh * US + r;
+  const int band_r = band0 + (31 - r + 4 * hh) * US + r;
 
   // Band row u of the tile starting at key j0 is R row t = j0 + u + L - 32 - iw.
   // rr holds band blocks 1 and 2 (u = 32 + r, 64 + r) of the next tile, loaded
@@ -310,20 +299,35 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
   }
   load_r(j_lo);
 
-  // tile 0 into buffer 0, tile 1 in flight
-  store_kv(nxt, reinterpret_cast<__bf16 *>(smem), reinterpret_cast<__bf16 *>(smem + kLdsK), tid);
-  load_kv(nxt, krs, vrs, kv_row_bytes, j_lo + BK, tid);
+  // V operand reads (transposing): lane l = 16g + 4k + q supplies the
+  // address of V[key][d0 + 4q], key = 4hh + k (+ the k-step's base), so that
+  // lane j of its group receives V[keys][d0 + j]; d0 = 32db + 16(g & 1).
+  // Slot offsets of the swizzle (key & 7 = 4hh + k at every base).
+  int v_off[2];
+  {
+    const int x = 4 * hh + ((lane >> 2) & 3);
+    const int q = lane & 3;
+    const int cc = 2 * ((lane >> 4) & 1) + (q >> 1);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) v_off[db] = x * DH + 8 * ((4 * db + cc) ^ x) + 4 * (q & 1);
+  }
+  // K operand reads: key row n = 32kb + r, chunk 2s + hh in slot (2s + hh) ^ (r & 7)
+  const int k_row = r * DH;
+
+  // tile 0 in buffer 0 before the loop; every tile's loads are waited for
+  // (with the R rows of the next tile) at the end of the tile before
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
+  auto run_tile = [&](int kt, const __bf16 *sk, __bf16 *nxt) {
     const int j0 = j_lo + kt * BK;
+    // tile kt+1 into the other buffer (freed by the last barrier); past the
+    // last tile the loads read zeros into a buffer nobody reads
+    dma_kv(krs, vrs, kv_row_bytes, j0 + BK, nxt, wave, lane);
     // Every wave runs every tile of its workgroup (no branch, so the compiler
     // can count outstanding loads): a tile past a wave's diagonal is fully
     // masked and leaves (m, l, O) unchanged, and the wave would otherwise wait
     // at the barrier.
-    unsigned char *buf = smem;
-    const __bf16 *sk = reinterpret_cast<const __bf16 *>(buf);
-    const __bf16 *svt = reinterpret_cast<const __bf16 *>(buf + kLdsK);
 
     {
       // ---- position band P[u][query] = R[t(u)] (Q'')^T, three blocks of 32 rows ----
@@ -350,8 +354,7 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
       // register 4a+c' of block bb holds band row u = 32bb + 8a + 4hh + c'; the
       // three blocks go to rows 0..95 once, and the 32-key half kb reads rows
       // u = c + 31 - r + 32kb. Rows past the diagonal become -inf (masked keys
-      // get weight exactly 0); rounding the fill's start down to 4 floats only
-      // touches the padding columns of row ul0 (US = 34 is 2 mod 4).
+      // get weight exactly 0).
       f32x16 s_acc[2];
 #pragma unroll
       for (int bb = 0; bb < 3; ++bb)
@@ -359,12 +362,12 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
         for (int a4 = 0; a4 < 4; ++a4)
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc)
-            band_w[(32 * bb + 8 * a4 + cc) * US] = b_acc[bb][4 * a4 + cc];
+            sband[band_w + (32 * bb + 8 * a4 + cc) * US] = b_acc[bb][4 * a4 + cc];
       if (ul0 < NU - 1) {
-        const int start = ((ul0 + 1 > 0 ? ul0 + 1 : 0) * US) & ~3;
+        const int start = (ul0 + 1 > 0 ? ul0 + 1 : 0) * US;
         const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         for (int f = start + 4 * lane; f < NU * US; f += 256)
-          *reinterpret_cast<f32x4 *>(band + f) = ninf;
+          *reinterpret_cast<f32x4 *>(&sband[band0 + f]) = ninf;
       }
       wave_lds_sync();
 #pragma unroll
@@ -372,13 +375,13 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int c = 8 * (x >> 2) + (x & 3);
-          s_acc[kb][x] = band_r[(c + 32 * kb) * US];
+          s_acc[kb][x] = sband[band_r + (c + 32 * kb) * US];
         }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const bf16x8 a = load8(sk + (kb * 32 + r) * KS + 16 * s + 8 * hh);
+          const bf16x8 a = load8(&sk[kb * 32 * DH + k_row + 8 * ((2 * s + hh) ^ (r & 7))]);
           s_acc[kb] = mfma32(a, qa[s], s_acc[kb]);
         }
 
@@ -434,24 +437,23 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
-            const __bf16 *vrow = svt + (db * 32 + r) * VS + kb * 32 + 16 * s2 + 4 * hh;
-            const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vrow);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vrow + 8);
-            bf16x8 a;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              a[e] = lo[e];
-              a[e + 4] = hi[e];
-            }
+            const int vk = kTileElems + (kb * 32 + 16 * s2) * DH + v_off[db];
+            const v4i16 lo = lds_read_tr(&sk[vk]);
+            const v4i16 hi = lds_read_tr(&sk[vk + 8 * DH]);
+            // whole-vector cast: a per-element bit cast of these vectors was
+            // folded to element 0 by the compiler
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             o_acc[db] = mfma32(a, pb[kb][s2], o_acc[db]);
           }
     }
-    // refill the K / V^T buffer with tile kt+1 once every wave has finished
-    // reading tile kt, and start loading tile kt+2
+    // tile kt+1 (and the next R rows) landed; once every wave is here, it is
+    // visible to all and tile kt's buffer is free for tile kt+2
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    store_kv(nxt, reinterpret_cast<__bf16 *>(smem), reinterpret_cast<__bf16 *>(smem + kLdsK), tid);
-    load_kv(nxt, krs, vrs, kv_row_bytes, j0 + 2 * BK, tid);
-    __syncthreads();
+  };
+  for (int kt = 0; kt < n_tiles; kt += 2) {
+    run_tile(kt, kv0, kv1);
+    if (kt + 1 < n_tiles) run_tile(kt + 1, kv1, kv0);
   }
 
   if constexpr (kAppend) {
@@ -547,16 +549,22 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
     p.lse[(static_cast<int64_t>(b) * p.H + h) * L + i] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
 }
 
+#define TXL_ATTN_LDS                                                  \
+  __shared__ __attribute__((aligned(4096))) __bf16 kv0[2 * kTileElems]; \
+  __shared__ __attribute__((aligned(4096))) __bf16 kv1[2 * kTileElems]; \
+  __shared__ __attribute__((aligned(16))) float sband[kBandFloats];
+
 __global__ __launch_bounds__(256, 2) void rel_attn_mfma_kernel(AttnParams p, int n_qt) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  rel_attn_tile<false>(p, n_qt, RingAppend{}, smem);
+  TXL_ATTN_LDS
+  rel_attn_tile<false>(p, n_qt, RingAppend{}, kv0, kv1, sband);
 }
 
 __global__ __launch_bounds__(256, 2) void rel_attn_mfma_append_kernel(AttnParams p, int n_qt,
                                                                       RingAppend ra) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  rel_attn_tile<true>(p, n_qt, ra, smem);
+  TXL_ATTN_LDS
+  rel_attn_tile<true>(p, n_qt, ra, kv0, kv1, sband);
 }
+#undef TXL_ATTN_LDS
 
 // Merge of the key-range splits: per query, m = max_s m_s and
 // O = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s (a split that saw no key
@@ -648,36 +656,20 @@ txl_status noalloc_counters(int B, hipStream_t s, uint32_t **out) {
   return TXL_OK;
 }
 
-// Raises a kernel's LDS limit once per process.
-static txl_status raise_lds_limit(const void *kernel, bool *attr_set) {
-  if (!*attr_set) {
-    if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(kLdsTotal)) != hipSuccess)
-      return fail(TXL_ERR_HIP, "rel_attn: cannot raise the LDS limit to %zu bytes", kLdsTotal);
-    *attr_set = true;
-  }
-  return TXL_OK;
-}
-static bool g_attr_plain = false, g_attr_append = false;
+// The kernels' LDS is static (81920 bytes, within the 160 KB of a CU for two
+// workgroups); nothing to set up.
+txl_status rel_attn_mfma_setup() { return TXL_OK; }
 
-txl_status rel_attn_mfma_setup() {
-  txl_status st = raise_lds_limit(reinterpret_cast<const void *>(rel_attn_mfma_kernel), &g_attr_plain);
-  if (st != TXL_OK) return st;
-  return raise_lds_limit(reinterpret_cast<const void *>(rel_attn_mfma_append_kernel), &g_attr_append);
-}
-
-// Raises the kernel's LDS limit once; checks the shapes the buffer loads
-// rely on and returns the grid (query tiles x splits x batch rows x heads).
-static txl_status prepare_launch(const void *kernel, bool *attr_set, const AttnParams &p,
-                                 int *n_qt, int64_t *blocks) {
-  txl_status st = raise_lds_limit(kernel, attr_set);
-  if (st != TXL_OK) return st;
+// Checks the shapes the buffer loads rely on and returns the grid (query
+// tiles x splits x batch rows x heads).
+static txl_status prepare_launch(const AttnParams &p, int *n_qt, int64_t *blocks) {
   // buffer loads address rows by 32-bit byte offsets from the (batch, head)
   // base and rely on rows not overlapping for the out-of-range zero fill
   if (p.kv_sl < DH || p.r_sl < DH || p.q_sl < DH || p.o_sl < DH)
     return fail(TXL_ERR_UNSUPPORTED, "rel_attn: bf16 row strides must be >= d_h");
   const int64_t ML = static_cast<int64_t>(p.M) + p.L;
-  if ((ML + BK) * p.kv_sl * 2 >= (int64_t(1) << 31) || (ML + BK + QW) * p.r_sl * 2 >= (int64_t(1) << 31))
+  // (the last tile's look-ahead loads reach up to two tiles past the keys)
+  if ((ML + 2 * BK) * p.kv_sl * 2 >= (int64_t(1) << 31) || (ML + BK + QW) * p.r_sl * 2 >= (int64_t(1) << 31))
     return fail(TXL_ERR_UNSUPPORTED, "rel_attn: key / R rows span more than 2 GiB per head");
   *n_qt = (p.L + BQ - 1) / BQ;
   const int S = p.n_split > 1 ? p.n_split : 1;
@@ -687,12 +679,10 @@ static txl_status prepare_launch(const void *kernel, bool *attr_set, const AttnP
 }
 
 txl_status launch_rel_attn_mfma_append(const AttnParams &p, const RingAppend &ra, hipStream_t s) {
-  bool &attr_set = g_attr_append;
   if (p.n_split > 1) return fail(TXL_ERR_UNSUPPORTED, "rel_attn_append: key splits are not served");
   int n_qt;
   int64_t blocks;
-  txl_status st = prepare_launch(reinterpret_cast<const void *>(rel_attn_mfma_append_kernel),
-                                 &attr_set, p, &n_qt, &blocks);
+  txl_status st = prepare_launch(p, &n_qt, &blocks);
   if (st != TXL_OK) return st;
   // Copy workers: the lighter half of the query tiles (dealt after the
   // heavier half), or every tile when there is one. (Measured at B8 H16
@@ -722,21 +712,19 @@ txl_status launch_rel_attn_mfma_append(const AttnParams &p, const RingAppend &ra
   a.rounds = static_cast<uint32_t>((static_cast<int64_t>(a.total) + workers - 1) / workers);
   (void)hipGetLastError();
   hipLaunchKernelGGL(rel_attn_mfma_append_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256),
-                     kLdsTotal, s, p, n_qt, a);
+                     0, s, p, n_qt, a);
   return check_launch("rel_attn_mfma_append_kernel");
 }
 
 txl_status launch_rel_attn_mfma(const AttnParams &p, hipStream_t s) {
-  bool &attr_set = g_attr_plain;
   int n_qt;
   int64_t blocks;
-  txl_status st0 = prepare_launch(reinterpret_cast<const void *>(rel_attn_mfma_kernel), &attr_set,
-                                  p, &n_qt, &blocks);
+  txl_status st0 = prepare_launch(p, &n_qt, &blocks);
   if (st0 != TXL_OK) return st0;
   const int S = p.n_split > 1 ? p.n_split : 1;
   (void)hipGetLastError();
   hipLaunchKernelGGL(rel_attn_mfma_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256),
-                     kLdsTotal, s, p, n_qt);
+                     0, s, p, n_qt);
   txl_status st = check_launch("rel_attn_mfma_kernel");
   if (st != TXL_OK || S == 1) return st;
   const int64_t threads = static_cast<int64_t>(p.B) * p.H * p.L * (DH / 4);
