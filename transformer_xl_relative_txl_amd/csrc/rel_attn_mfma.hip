@@ -355,7 +355,20 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
       // three blocks go to rows 0..95 once, and the 32-key half kb reads rows
       // u = c + 31 - r + 32kb. Rows past the diagonal become -inf (masked keys
       // get weight exactly 0).
+      // content scores first (their operands are in LDS since the tile
+      // began), so they run while the band's results drain and its LDS
+      // round trip completes; the shifted position term is added after
       f32x16 s_acc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int x = 0; x < 16; ++x) s_acc[kb][x] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 a = load8(&sk[kb * 32 * DH + k_row + 8 * ((2 * s + hh) ^ (r & 7))]);
+          s_acc[kb] = mfma32(a, qa[s], s_acc[kb]);
+        }
+      }
 #pragma unroll
       for (int bb = 0; bb < 3; ++bb)
 #pragma unroll
@@ -375,14 +388,7 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int c = 8 * (x >> 2) + (x & 3);
-          s_acc[kb][x] = sband[band_r + (c + 32 * kb) * US];
-        }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 a = load8(&sk[kb * 32 * DH + k_row + 8 * ((2 * s + hh) ^ (r & 7))]);
-          s_acc[kb] = mfma32(a, qa[s], s_acc[kb]);
+          s_acc[kb][x] += sband[band_r + (c + 32 * kb) * US];
         }
 
       // ---- online softmax in base 2 ----
