@@ -324,12 +324,12 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
     // tile kt+1 into the other buffer (freed by the last barrier); past the
     // last tile the loads read zeros into a buffer nobody reads
     dma_kv(krs, vrs, kv_row_bytes, j0 + BK, nxt, wave, lane);
-    // Every wave runs every tile of its workgroup (no branch, so the compiler
-    // can count outstanding loads): a tile past a wave's diagonal is fully
-    // masked and leaves (m, l, O) unchanged, and the wave would otherwise wait
-    // at the barrier.
+    // Every wave takes part in every tile's loads and barrier; a wave skips
+    // the arithmetic of a tile past its last query's diagonal (the tile is
+    // fully masked for it and would leave (m, l, O) unchanged; so are all
+    // later tiles, so the band carry and the R prefetch are not needed).
 
-    {
+    if (j0 <= M + iw + QW - 1) {  // some key of the tile is visible to this wave
       // ---- position band P[u][query] = R[t(u)] (Q'')^T, three blocks of 32 rows ----
       f32x16 b_acc[3];
       b_acc[0] = b_carry;
