@@ -28,6 +28,7 @@ SOURCES = [
     "rel_attn_bwd.hip",
     "gemm.hip",
     "bwd.hip",
+    "dw_gemm.hip",
     "stack.cpp",
     "sampler.cpp",
     "loss.cpp",

@@ -1,7 +1,9 @@
 // Kernels of the stack's segment gradients (the layer GEMMs themselves run on
-// the GEMM of gemm.hip): tiled transposes into bf16 GEMM operands, the
-// packing of the attention's per-head gradients, deterministic sums of
-// split-K partials, the LayerNorm backward and the embedding scatter.
+// the GEMM of gemm.hip, which reads K-major operands directly): the weight
+// transposes of the input-gradient product over [dQ | dK | dV], the
+// [memory; segment] rows as one matrix, the merge of the attention's
+// per-head gradients into rows, deterministic sums of split-K partials, the
+// LayerNorm backward and the embedding scatter.
 //
 // [P1] "Transformer-XL" notes, "Why Stop Gradient" and "Training Loop
 // Sketch"; [P2] "019 Transformer-XL", section "stop-gradient到底切断哪里":
@@ -20,86 +22,85 @@ namespace {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kT = 64;  // transpose tile
 
 __device__ inline float to_f(float x) { return x; }
 __device__ inline float to_f(__bf16 x) { return static_cast<float>(x); }
 
-// y[c, col0 + q] = x_row(q)[c] for source rows q in [0, R) and 0 for
-// R <= q < r_pad, columns c in [0, C). Source row q sits in group
-// g = q / (g1 + g2) at j = q mod (g1 + g2): row g*g1 + j of x1 when j < g1,
-// else row g*g2 + (j - g1) of x2, both with row stride ldx (a plain matrix
-// is g1 = R, g2 = 0; [memory; segment] of every batch row is g1 = M,
-// g2 = L). With valid1 set, x1 rows j < g1 - valid1[g] (memory slots a
-// batch row does not hold) read as 0. 64 x 64 tiles through LDS, both sides
-// coalesced.
+// y[c, col0 + q] = x[q, c] (bf16) for rows q < R and columns c < C of a
+// row-major x (row stride ldx, fp32 or bf16). 64 x 64 tiles through LDS,
+// both sides coalesced.
 template <typename T>
-__global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ x1, int g1,
-                                                        const int32_t *__restrict__ valid1,
-                                                        const T *__restrict__ x2, int g2,
-                                                        int64_t ldx, int R, int C, int r_pad,
-                                                        __bf16 *__restrict__ y, int64_t ldy,
+__global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ x, int64_t ldx, int R,
+                                                        int C, __bf16 *__restrict__ y, int64_t ldy,
                                                         int col0) {
   __shared__ float tile[kT][kT + 1];
   const int c0 = blockIdx.x * kT, q0 = blockIdx.y * kT;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const int gs = g1 + g2;
 #pragma unroll 4
   for (int k = 0; k < kT / 4; ++k) {
     const int qq = ty + 4 * k, q = q0 + qq, c = c0 + tx;
-    float v = 0.0f;
-    if (q < R && c < C) {
-      const int g = q / gs, j = q - g * gs;
-      bool held = true;
-      if (j < g1 && valid1) {
-        const int vl = min(max(valid1[g], 0), g1);
-        held = j >= g1 - vl;
-      }
-      const T *row = j < g1 ? x1 + (static_cast<int64_t>(g) * g1 + j) * ldx
-                            : x2 + (static_cast<int64_t>(g) * g2 + (j - g1)) * ldx;
-      if (held) v = to_f(row[c]);
-    }
-    tile[qq][tx] = v;
+    tile[qq][tx] = (q < R && c < C) ? to_f(x[static_cast<int64_t>(q) * ldx + c]) : 0.0f;
   }
   __syncthreads();
 #pragma unroll 4
   for (int k = 0; k < kT / 4; ++k) {
     const int cc = ty + 4 * k, c = c0 + cc, q = q0 + tx;
-    if (c < C && q < r_pad) y[static_cast<int64_t>(c) * ldy + col0 + q] = static_cast<__bf16>(tile[tx][cc]);
+    if (c < C && q < R) y[static_cast<int64_t>(c) * ldy + col0 + q] = static_cast<__bf16>(tile[tx][cc]);
   }
 }
 
+// [memory; segment] rows of every batch row as one matrix, y [B*(M+L), d]:
+// row b*(M+L) + j is memory row j of batch row b (logical order) when j < M
+// and the row holds it (j >= M - valid[b]), zero for a slot it does not
+// hold, and segment row j - M otherwise. 16-byte chunks.
+__global__ __launch_bounds__(256) void gather_ext_kernel(const u32x4 *__restrict__ mem,
+                                                         const int32_t *__restrict__ valid,
+                                                         const u32x4 *__restrict__ seg, int B, int M,
+                                                         int L, int cpr, u32x4 *__restrict__ y) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(B) * (M + L) * cpr;
+  if (e >= total) return;
+  const int64_t row = e / cpr;
+  const int c = static_cast<int>(e - row * cpr);
+  const int b = static_cast<int>(row / (M + L)), j = static_cast<int>(row - static_cast<int64_t>(b) * (M + L));
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (j >= M) {
+    v = seg[(static_cast<int64_t>(b) * L + (j - M)) * cpr + c];
+  } else {
+    const int vl = min(max(valid[b], 0), M);
+    if (j >= M - vl) v = mem[(static_cast<int64_t>(b) * M + j) * cpr + c];
+  }
+  y[e] = v;
+}
+
 // Per-head fp32 gradients g [B, H, T, 64] (T keys or queries per batch row)
-// into bf16 GEMM operands: the transposed merge yt[h*64 + e, b*T + j] (row
-// stride ldt; columns from B*T on are left to the caller) and, when y2 is
-// set, the merged rows of the last L entries of every batch row,
-// y2[b*L + j - (T-L), col0 + h*64 + e] (row stride ld2).
-__global__ __launch_bounds__(256) void head_grad_pack_kernel(const float *__restrict__ g, int B,
-                                                             int H, int T, __bf16 *__restrict__ yt,
-                                                             int64_t ldt, __bf16 *__restrict__ y2,
-                                                             int L, int64_t ld2, int col0) {
-  __shared__ float tile[kT][kT + 1];
-  const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
-  const int j0 = blockIdx.x * kT;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const float *src = g + static_cast<int64_t>(bh) * T * 64;
-#pragma unroll 4
-  for (int k = 0; k < kT / 4; ++k) {
-    const int jj = ty + 4 * k, j = j0 + jj;
-    const float v = j < T ? src[static_cast<int64_t>(j) * 64 + tx] : 0.0f;
-    tile[jj][tx] = v;
-    if (y2 && j < T && j >= T - L)
-      y2[(static_cast<int64_t>(b) * L + (j - (T - L))) * ld2 + col0 + h * 64 + tx] = static_cast<__bf16>(v);
-  }
-  __syncthreads();
-#pragma unroll 4
-  for (int k = 0; k < kT / 4; ++k) {
-    const int e = ty + 4 * k, j = j0 + tx;
-    if (j < T)
-      yt[static_cast<int64_t>(h * 64 + e) * ldt + static_cast<int64_t>(b) * T + j] =
-          static_cast<__bf16>(tile[tx][e]);
-  }
+// merged over heads into bf16 rows: y_all[(b*T + j)*ld_all + h*64 + e] for
+// every j when y_all is set, and y_last[(b*L + j - (T-L))*ld_last + col0 +
+// h*64 + e] for the last L entries of every batch row when y_last is set.
+// Four elements a thread.
+__global__ __launch_bounds__(256) void head_grad_merge_kernel(const float *__restrict__ g, int B,
+                                                              int H, int T, __bf16 *__restrict__ y_all,
+                                                              int64_t ld_all, __bf16 *__restrict__ y_last,
+                                                              int L, int64_t ld_last, int col0) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // one per 4 elements
+  const int64_t total = static_cast<int64_t>(B) * H * T * 16;
+  if (e >= total) return;
+  const int q = static_cast<int>(e & 15);
+  const int64_t row = e >> 4;                      // (b, h, j)
+  const int j = static_cast<int>(row % T);
+  const int64_t bh = row / T;
+  const int h = static_cast<int>(bh % H), b = static_cast<int>(bh / H);
+  const f32x4 v = reinterpret_cast<const f32x4 *>(g)[e];
+  bf16x4 o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o[k] = static_cast<__bf16>(v[k]);
+  const int col = h * 64 + 4 * q;
+  if (y_all) *reinterpret_cast<bf16x4 *>(y_all + (static_cast<int64_t>(b) * T + j) * ld_all + col) = o;
+  if (y_last && j >= T - L)
+    *reinterpret_cast<bf16x4 *>(y_last + (static_cast<int64_t>(b) * L + (j - (T - L))) * ld_last + col0 + col) = o;
 }
 
 // out[i] = sum_{s < S} part[s * stride + i], s ascending (4 floats a thread)
@@ -285,16 +286,6 @@ __global__ __launch_bounds__(256) void embed_backward_kernel(const int32_t *__re
     if (v0 + r < vocab) demb[static_cast<int64_t>(v0 + r) * d + col] = acc[r][tid];
 }
 
-// y[r, c] = 0 for rows r < n_rows and columns c in [c_from, c_to) (row stride ldy)
-__global__ __launch_bounds__(256) void zero_cols_kernel(__bf16 *__restrict__ y, int n_rows, int64_t ldy,
-                                                        int c_from, int c_to) {
-  const int w = c_to - c_from;
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (e >= static_cast<int64_t>(n_rows) * w) return;
-  const int64_t r = e / w;
-  y[r * ldy + c_from + (e - r * w)] = static_cast<__bf16>(0.0f);
-}
-
 __global__ void copy_i32_kernel(const int32_t *__restrict__ src, int32_t *__restrict__ dst, int n) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e < n) dst[e] = src[e];
@@ -302,32 +293,42 @@ __global__ void copy_i32_kernel(const int32_t *__restrict__ src, int32_t *__rest
 
 }  // namespace
 
-txl_status launch_transpose_bf16(const void *x1, int g1, const int32_t *valid1, const void *x2,
-                                 int g2, int64_t ldx, bool src_f32, int R, int C, int r_pad,
-                                 void *y, int64_t ldy, int col0, hipStream_t s) {
-  if (C <= 0 || r_pad <= 0) return TXL_OK;
-  if (g1 + g2 <= 0) return fail(TXL_ERR_INVALID_ARG, "transpose: empty row groups");
-  const dim3 grid((C + kT - 1) / kT, (r_pad + kT - 1) / kT);
+txl_status launch_transpose_bf16(const void *x, int64_t ldx, bool src_f32, int R, int C, void *y,
+                                 int64_t ldy, int col0, hipStream_t s) {
+  if (C <= 0 || R <= 0) return TXL_OK;
+  const dim3 grid((C + kT - 1) / kT, (R + kT - 1) / kT);
   (void)hipGetLastError();
   if (src_f32)
-    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s, static_cast<const float *>(x1), g1,
-                       valid1, static_cast<const float *>(x2), g2, ldx, R, C, r_pad,
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s, static_cast<const float *>(x), ldx, R, C,
                        static_cast<__bf16 *>(y), ldy, col0);
   else
-    hipLaunchKernelGGL(transpose_kernel<__bf16>, grid, dim3(256), 0, s, static_cast<const __bf16 *>(x1), g1,
-                       valid1, static_cast<const __bf16 *>(x2), g2, ldx, R, C, r_pad,
-                       static_cast<__bf16 *>(y), ldy, col0);
+    hipLaunchKernelGGL(transpose_kernel<__bf16>, grid, dim3(256), 0, s, static_cast<const __bf16 *>(x), ldx, R,
+                       C, static_cast<__bf16 *>(y), ldy, col0);
   return check_launch("transpose_kernel");
 }
 
-txl_status launch_head_grad_pack(const float *g, int B, int H, int T, void *yt, int64_t ldt,
-                                 void *y2, int L, int64_t ld2, int col0, hipStream_t s) {
-  if (B == 0 || T == 0) return TXL_OK;
-  const dim3 grid((T + kT - 1) / kT, B * H);
+txl_status launch_gather_ext(const void *mem, const int32_t *valid, const void *seg, int B, int M, int L,
+                             int d, void *y, hipStream_t s) {
+  if (d % 8) return fail(TXL_ERR_UNSUPPORTED, "gather_ext: d must be a multiple of 8");
+  const int cpr = d / 8;
+  const int64_t total = static_cast<int64_t>(B) * (M + L) * cpr;
+  if (total == 0) return TXL_OK;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(head_grad_pack_kernel, grid, dim3(256), 0, s, g, B, H, T, static_cast<__bf16 *>(yt), ldt,
-                     static_cast<__bf16 *>(y2), L, ld2, col0);
-  return check_launch("head_grad_pack_kernel");
+  hipLaunchKernelGGL(gather_ext_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const u32x4 *>(mem), valid, static_cast<const u32x4 *>(seg), B, M, L, cpr,
+                     static_cast<u32x4 *>(y));
+  return check_launch("gather_ext_kernel");
+}
+
+txl_status launch_head_grad_merge(const float *g, int B, int H, int T, void *y_all, int64_t ld_all,
+                                  void *y_last, int L, int64_t ld_last, int col0, hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(B) * H * T * 16;
+  if (total == 0) return TXL_OK;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(head_grad_merge_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s,
+                     g, B, H, T, static_cast<__bf16 *>(y_all), ld_all, static_cast<__bf16 *>(y_last), L,
+                     ld_last, col0);
+  return check_launch("head_grad_merge_kernel");
 }
 
 txl_status launch_reduce_parts(const float *part, int S, int64_t stride, int64_t n, float *out,
@@ -372,15 +373,6 @@ txl_status launch_embed_backward(const int32_t *tokens, int n_tok, const float *
   (void)hipGetLastError();
   hipLaunchKernelGGL(embed_backward_kernel, grid, dim3(256), 0, s, tokens, n_tok, dh0, d, vocab, demb);
   return check_launch("embed_backward_kernel");
-}
-
-txl_status launch_zero_cols(void *y, int n_rows, int64_t ldy, int c_from, int c_to, hipStream_t s) {
-  const int64_t total = static_cast<int64_t>(n_rows) * (c_to - c_from);
-  if (total <= 0) return TXL_OK;
-  (void)hipGetLastError();
-  hipLaunchKernelGGL(zero_cols_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s,
-                     static_cast<__bf16 *>(y), n_rows, ldy, c_from, c_to);
-  return check_launch("zero_cols_kernel");
 }
 
 txl_status launch_copy_i32(const int32_t *src, int32_t *dst, int n, hipStream_t s) {

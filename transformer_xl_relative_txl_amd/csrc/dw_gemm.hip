@@ -1,0 +1,261 @@
+// Weight-gradient products of the stack's backward: out = X^T Y, where X
+// [K, rows] and Y [K, N] are activations or output gradients stored one
+// segment row per row (the reduction runs over the segment's rows, the
+// strided dimension of both operands).
+//
+// [P1] "Transformer-XL" notes, "Training Loop Sketch": a segment's loss is
+// back-propagated through the segment alone, so every weight gradient of a
+// layer is a sum over the segment's B*L rows (over the B*(M+L) key rows for
+// W^K and W^V, whose memory part is a constant input, and over the M+L
+// distances for W_R).
+//
+// Both operands stay in the layout the forward wrote: 64-row slabs of X
+// and Y go straight from global memory into LDS with direct buffer-to-LDS
+// loads (16 bytes a lane, [k][column] order, no registers), and the MFMA
+// operands, which need eight consecutive k of one column per lane, come out
+// of LDS with transposing reads (ds_read_b64_tr_b16). Workgroups of 4 waves
+// compute 128 x 128 (or 64 x 64) output tiles with v_mfma_f32_32x32x16_bf16,
+// two LDS buffers with one barrier per slab, and the K range split over
+// k_splits workgroups whose fp32 partials are added afterwards in split
+// order (a fixed order: the result does not depend on scheduling).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "txl_internal.h"
+
+namespace txl {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kXcds = 8;
+constexpr int KS = 64;  // k rows per slab
+
+__device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// Transposing LDS read: within each 16-lane group, element e of lane j is
+// the 16-bit value at (address of lane 4e + j/4) + j % 4.
+__device__ inline v4i16 lds_read_tr(const __bf16 *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)p);
+}
+
+// Slab layout in LDS: row k (KS rows) of W columns, the row's 16-byte
+// chunk c at slot c ^ swz(k). A transposing read of one MFMA operand
+// touches rows k0 + {0..3} and k0 + {8..11} (k0 a multiple of 4), four
+// chunks each; swz spreads the rows k0 + e over distinct banks, so every
+// bank serves four 4-byte reads, the minimum for 512 bytes.
+template <int W>
+__device__ inline int swz(int k) {
+  return (4 * (k & 3)) & (W / 8 - 1);
+}
+
+// One slab (rows [kb, kb + KS) of the operand, columns [c0, c0 + W)) into
+// LDS: instruction t of wave w fills bytes [1024 t, 1024 t + 1024) of the
+// slab, lane l landing at byte 16 l of them. Rows past the resource's range
+// load zeros.
+template <int W>
+__device__ inline void dma_slab(rsrc_t rs, int row_bytes, __bf16 *dst, int wave, int lane) {
+  constexpr int CPR = W / 8;          // chunks per row
+  constexpr int RPI = 512 / W;        // rows per instruction
+  constexpr int PER_WAVE = W / 32;    // instructions per wave (W / 8 in all)
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int t = wave * PER_WAVE + i;
+    const int row = t * RPI + lane / CPR;
+    const int slot = lane % CPR;
+    const int off = row * row_bytes + 16 * (slot ^ swz<W>(row));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + 512 * t), 16, off, 0, 0, 0);
+  }
+}
+
+// The slab rows [kb, kb + KS) of an operand whose rows [0, k_rows) exist:
+// a resource starting at row kb, column c0, covering up to the last
+// existing row's W columns (empty past the end).
+template <int W>
+__device__ inline rsrc_t slab_rsrc(const __bf16 *base, int64_t ld, int c0, int kb, int k_rows) {
+  const int rem = k_rows - kb;
+  const int n = rem < KS ? rem : KS;
+  const uint32_t bytes = n > 0 ? static_cast<uint32_t>((n - 1) * ld * 2 + W * 2) : 0u;
+  return make_rsrc(base + static_cast<int64_t>(kb) * ld + c0, bytes);
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(256, 2) void dw_kernel(const __bf16 *__restrict__ x, int64_t ldx,
+                                                    const __bf16 *__restrict__ y, int64_t ldy,
+                                                    int rows, int N, int k_rows, int k_splits,
+                                                    float *__restrict__ out, int64_t split_stride) {
+  constexpr int WM = BM / 64, WN = BN / 64;  // 32 x 32 blocks per wave
+  __shared__ __attribute__((aligned(4096))) __bf16 sx0[KS * BM];
+  __shared__ __attribute__((aligned(4096))) __bf16 sx1[KS * BM];
+  __shared__ __attribute__((aligned(4096))) __bf16 sy0[KS * BN];
+  __shared__ __attribute__((aligned(4096))) __bf16 sy1[KS * BN];
+
+  // XCD-contiguous tile assignment (a bijection on [0, T)); split s takes
+  // the tile indices [s T / k_splits, (s + 1) T / k_splits)
+  const int T = gridDim.x;
+  const int bid = blockIdx.x;
+  const int xc = bid % kXcds, local = bid / kXcds;
+  const int q = T / kXcds, rem = T % kXcds;
+  int tile = xc * q + (xc < rem ? xc : rem) + local;
+  const int per = T / k_splits;
+  const int split = tile / per;
+  tile -= split * per;
+  const int n_tn = N / BN;
+  const int tm = tile / n_tn, tn = tile - tm * n_tn;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int n_slabs = (k_rows + KS - 1) / KS;
+  const int ks0 = static_cast<int>(static_cast<int64_t>(split) * n_slabs / k_splits);
+  const int ks1 = static_cast<int>(static_cast<int64_t>(split + 1) * n_slabs / k_splits);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // transposing-read offsets (elements, k-step 0, first half): lane
+  // 16g + 4e + qq supplies row 8 (g >> 1) + e, columns 16 (g & 1) + 4 qq of
+  // a 32-column block; the second half reads rows + 4, k-step s rows + 16 s
+  const int g = lane >> 4, e = (lane >> 2) & 3, qq = lane & 3;
+  const int kr = 8 * (g >> 1) + e;
+  int xo[WM], yo[WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+    const int m = wm * (BM / 2) + 32 * i + 16 * (g & 1) + 4 * qq;
+    xo[i] = kr * BM + 8 * ((m >> 3) ^ swz<BM>(kr)) + (m & 7);
+  }
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    const int n = wn * (BN / 2) + 32 * j + 16 * (g & 1) + 4 * qq;
+    yo[j] = kr * BN + 8 * ((n >> 3) ^ swz<BN>(kr)) + (n & 7);
+  }
+  // rows kr + 4 h + 16 s all have (row & 3) == e: the swizzle is the same
+
+  f32x16 acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int xrb = static_cast<int>(ldx * 2), yrb = static_cast<int>(ldy * 2);
+  auto load = [&](int ks, __bf16 *dx, __bf16 *dy) {
+    dma_slab<BM>(slab_rsrc<BM>(x, ldx, m0, ks * KS, k_rows), xrb, dx, wave, lane);
+    dma_slab<BN>(slab_rsrc<BN>(y, ldy, n0, ks * KS, k_rows), yrb, dy, wave, lane);
+  };
+  auto compute = [&](const __bf16 *cx, const __bf16 *cy) {
+#pragma unroll
+    for (int s = 0; s < KS / 16; ++s) {
+      bf16x8 a[WM], b[WN];
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        const v4i16 lo = lds_read_tr(cx + xo[i] + 16 * s * BM);
+        const v4i16 hi = lds_read_tr(cx + xo[i] + (16 * s + 4) * BM);
+        a[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const v4i16 lo = lds_read_tr(cy + yo[j] + 16 * s * BN);
+        const v4i16 hi = lds_read_tr(cy + yo[j] + (16 * s + 4) * BN);
+        b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Slab ks sits in buffer (ks - ks0) % 2. The wait and barrier at the top
+  // of a slab make its loads visible and free the other buffer (read during
+  // the slab before), which then takes slab ks + 1 while this one computes.
+  if (ks0 < ks1) load(ks0, sx0, sy0);
+  for (int ks = ks0; ks < ks1; ks += 2) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (ks + 1 < ks1) load(ks + 1, sx1, sy1);
+    compute(sx0, sy0);
+    if (ks + 1 >= ks1) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (ks + 2 < ks1) load(ks + 2, sx0, sy0);
+    compute(sx1, sy1);
+  }
+
+  // register 4 a + c of block (i, j) holds out[m0 + wm BM/2 + 32 i + 8 a +
+  // 4 (lane / 32) + c][n0 + wn BN/2 + 32 j + lane % 32]
+  float *o = out + split * split_stride;
+  const int r = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int col = n0 + wn * (BN / 2) + 32 * j + r;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int row = m0 + wm * (BM / 2) + 32 * i + 8 * a + 4 * hh + c;
+          o[static_cast<int64_t>(row) * N + col] = acc[i][j][4 * a + c];
+        }
+    }
+}
+
+}  // namespace
+
+// 128 x 128 tiles when the output divides into them, else 64 x 64.
+static bool dw_big_tiles(int rows, int N) { return rows % 128 == 0 && N % 128 == 0; }
+
+int dw_gemm_splits(int rows, int N, int k_rows) {
+  const int tm = dw_big_tiles(rows, N) ? 128 : 64;
+  const int64_t tiles = static_cast<int64_t>(rows / tm) * (N / tm);
+  const int n_slabs = (k_rows + KS - 1) / KS;
+  // about two workgroups per CU, each split keeping at least 4 slabs
+  int s = 1;
+  while (s < 32 && tiles * s < 512 && n_slabs / (2 * s) >= 4) s *= 2;
+  return s;
+}
+
+txl_status launch_dw_gemm(const void *x, int64_t ldx, int rows, const void *y, int64_t ldy, int N,
+                          int k_rows, int k_splits, float *out, int64_t split_stride,
+                          hipStream_t s) {
+  if (rows == 0 || N == 0) return TXL_OK;
+  if (rows < 0 || N < 0 || k_rows < 0 || rows % 64 || N % 64)
+    return fail(TXL_ERR_INVALID_ARG, "dw_gemm: rows %d and N %d must be multiples of 64, k_rows %d >= 0",
+                rows, N, k_rows);
+  if (!x || !y || !out || ldx < rows || ldy < N || ldx % 8 || ldy % 8 ||
+      reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 16)
+    return fail(TXL_ERR_INVALID_ARG, "dw_gemm: operands must be 16-byte aligned with ldx >= rows, "
+                                 "ldy >= N, strides multiples of 8");
+  // a slab's resource spans up to 64 rows: offsets within it fit 32 bits
+  if (static_cast<int64_t>(KS) * (ldx > ldy ? ldx : ldy) * 2 >= (int64_t{1} << 31))
+    return fail(TXL_ERR_UNSUPPORTED, "dw_gemm: row stride too large");
+  if (k_splits < 1 || (k_splits > 1 && split_stride < static_cast<int64_t>(rows) * N))
+    return fail(TXL_ERR_INVALID_ARG, "dw_gemm: k_splits %d with split stride %lld", k_splits,
+                static_cast<long long>(split_stride));
+  const bool big = dw_big_tiles(rows, N);
+  const int tm = big ? 128 : 64;
+  const int64_t tiles = static_cast<int64_t>(rows / tm) * (N / tm) * k_splits;
+  if (tiles > 0x7fffffff) return fail(TXL_ERR_UNSUPPORTED, "dw_gemm: too many tiles");
+  const __bf16 *xb = static_cast<const __bf16 *>(x);
+  const __bf16 *yb = static_cast<const __bf16 *>(y);
+  (void)hipGetLastError();
+  if (big)
+    hipLaunchKernelGGL((dw_kernel<128, 128>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s,
+                       xb, ldx, yb, ldy, rows, N, k_rows, k_splits, out, split_stride);
+  else
+    hipLaunchKernelGGL((dw_kernel<64, 64>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s, xb,
+                       ldx, yb, ldy, rows, N, k_rows, k_splits, out, split_stride);
+  return check_launch("dw_kernel");
+}
+
+}  // namespace txl

@@ -140,36 +140,31 @@ __global__ __launch_bounds__(kThreads) void rel_pos_table_kernel(
   }
 }
 
-// The sinusoid transposed, for the gradient of W_R: st[k, t] = S(M+L-1-t, k)
-// in bf16 for t < M+L and 0 for M+L <= t < t_pad (the same evaluation as the
-// table above).
-__global__ __launch_bounds__(kThreads) void sinusoid_t_kernel(int ML, int d, int t_pad,
-                                                              __bf16 *__restrict__ st) {
+// The sinusoid rows, for the gradient of W_R: st[t, k] = S(M+L-1-t, k) in
+// bf16 (the same evaluation as the table above).
+__global__ __launch_bounds__(kThreads) void sinusoid_rows_kernel(int ML, int d,
+                                                                 __bf16 *__restrict__ st) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (e >= static_cast<int64_t>(d) * t_pad) return;
-  const int k = static_cast<int>(e / t_pad), t = static_cast<int>(e - static_cast<int64_t>(k) * t_pad);
-  float val = 0.0f;
-  if (t < ML) {
-    const int half = d / 2;
-    const bool is_sin = k < half;
-    constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
-    const double f = pow(10000.0, -2.0 * (is_sin ? k : k - half) / static_cast<double>(d)) * kInvTwoPi;
-    const double rev = static_cast<double>(ML - 1 - t) * f;
-    const float frac = static_cast<float>(rev - rint(rev));
-    val = is_sin ? __builtin_amdgcn_sinf(frac) : __builtin_amdgcn_cosf(frac);
-  }
-  st[e] = static_cast<__bf16>(val);
+  if (e >= static_cast<int64_t>(ML) * d) return;
+  const int t = static_cast<int>(e / d), k = static_cast<int>(e - static_cast<int64_t>(t) * d);
+  const int half = d / 2;
+  const bool is_sin = k < half;
+  constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
+  const double f = pow(10000.0, -2.0 * (is_sin ? k : k - half) / static_cast<double>(d)) * kInvTwoPi;
+  const double rev = static_cast<double>(ML - 1 - t) * f;
+  const float frac = static_cast<float>(rev - rint(rev));
+  st[e] = static_cast<__bf16>(is_sin ? __builtin_amdgcn_sinf(frac) : __builtin_amdgcn_cosf(frac));
 }
 
 }  // namespace
 
-txl_status launch_sinusoid_t(int M, int L, int d, int t_pad, void *st, hipStream_t s) {
-  const int64_t total = static_cast<int64_t>(d) * t_pad;
+txl_status launch_sinusoid_rows(int M, int L, int d, void *st, hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(M + L) * d;
   if (total == 0) return TXL_OK;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(sinusoid_t_kernel, dim3(static_cast<unsigned>((total + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, s, M + L, d, t_pad, static_cast<__bf16 *>(st));
-  return check_launch("sinusoid_t_kernel");
+  hipLaunchKernelGGL(sinusoid_rows_kernel, dim3(static_cast<unsigned>((total + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, M + L, d, static_cast<__bf16 *>(st));
+  return check_launch("sinusoid_rows_kernel");
 }
 
 txl_status launch_rel_pos_table(txl_dtype dt, int M, int L, int d, int HD,

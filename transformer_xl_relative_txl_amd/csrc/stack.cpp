@@ -278,37 +278,24 @@ TapeLayer tape_at(const TapeLayout &t, const void *tape, int n) {
   return l;
 }
 
-int round64(int64_t x) { return static_cast<int>((x + 63) / 64 * 64); }
-
-// K splits of a weight-gradient product (output rows x N, reduction K over
-// the segment's rows): enough workgroups to fill the chip (about 512 tiles
-// of 64 x 64), each split keeping at least 256 of K.
-int dw_splits(int rows, int N, int K) {
-  const int64_t tiles = static_cast<int64_t>((rows + 63) / 64) * (N / 64);
-  int s = 1;
-  while (s < 16 && tiles * s < 512 && K / (2 * s) >= 256) s *= 2;
-  return s;
-}
-
-// out [rows, N] fp32 = A [rows, K] W [N, K]^T (both bf16, row stride K): one
-// GEMM storing fp32, or split-K partials added in split order.
-txl_status dw_gemm(const __bf16 *a, int rows, const __bf16 *w, int N, int K, float *out,
-                   float *part, hipStream_t stream) {
-  const int splits = dw_splits(rows, N, K);
-  GemmParams p = dense(a, K, rows, N, K, w, splits > 1 ? part : out, N);
-  p.k_splits = splits;
-  p.c_split_stride = static_cast<int64_t>(rows) * N;
-  txl_status s = launch_gemm(p, kEpiPartialF32, stream);
+// out [rows, N] fp32 = X^T Y over the first K rows of X [*, ldx] and Y
+// [*, ldy] (bf16, one segment row per row): one product storing fp32, or
+// split-K partials added in split order.
+txl_status dw_gemm(const __bf16 *x, int64_t ldx, int rows, const __bf16 *y, int64_t ldy, int N, int K,
+                   float *out, float *part, hipStream_t stream) {
+  const int splits = dw_gemm_splits(rows, N, K);
+  const int64_t stride = static_cast<int64_t>(rows) * N;
+  txl_status s = launch_dw_gemm(x, ldx, rows, y, ldy, N, K, splits, splits > 1 ? part : out, stride,
+                                stream);
   if (s != TXL_OK || splits == 1) return s;
-  return launch_reduce_parts(part, splits, p.c_split_stride, p.c_split_stride, out, stream);
+  return launch_reduce_parts(part, splits, stride, stride, out, stream);
 }
 
 // Workspace of the segment backward (one layer's intermediates, reused from
 // the top layer down).
 struct BwdWs {
-  int r_pad, e_pad, t_pad;  // segment rows, [memory; segment] rows, R rows, padded to 64
-  size_t g0, g1, dx2, dx2b, dh1, dx1, dx1b, dfpre, dfpreT, xT, aT, dout, dq, dk, dv, dr, attn,
-      attn_bytes, gT, acat, wT, wcatT, st, pg, pb, part, total;
+  size_t g0, g1, dx2, dx2b, dh1, dx1, dx1b, dfpre, dout, dq, dk, dv, dr, attn, attn_bytes, ym, ext,
+      acat, wcatT, wT, st, pg, pb, part, total;
 };
 
 BwdWs bwd_ws(const txl_stack_config &c) {
@@ -316,10 +303,8 @@ BwdWs bwd_ws(const txl_stack_config &c) {
   const int HD = static_cast<int>(hd);
   const size_t rows = static_cast<size_t>(c.B) * c.L;
   const size_t krows = static_cast<size_t>(c.B) * (c.M + c.L);
+  const size_t ml = static_cast<size_t>(c.M + c.L);
   BwdWs w;
-  w.r_pad = round64(static_cast<int64_t>(rows));
-  w.e_pad = round64(static_cast<int64_t>(krows));
-  w.t_pad = round64(c.M + c.L);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -335,22 +320,19 @@ BwdWs bwd_ws(const txl_stack_config &c) {
   w.dx1 = take(rd * 4);
   w.dx1b = take(rd * 2);
   w.dfpre = take(rows * c.d_ff * 2);
-  w.dfpreT = take(static_cast<size_t>(c.d_ff) * w.r_pad * 2);
-  w.xT = take(static_cast<size_t>(c.d) * w.r_pad * 2);
-  w.aT = take(std::max({static_cast<size_t>(c.d_ff) * w.r_pad, static_cast<size_t>(c.d) * w.e_pad,
-                        hd * w.r_pad}) * 2);
   w.dout = take(rows * hd * 2);
   w.dq = take(rows * hd * 4);
   w.dk = take(krows * hd * 4);
   w.dv = take(krows * hd * 4);
-  w.dr = take(static_cast<size_t>(c.M + c.L) * hd * 4);
+  w.dr = take(ml * hd * 4);
   w.attn_bytes = txl_rel_attn_bwd_workspace_bytes(c.B, c.n_head, c.L, c.M);
   w.attn = take(w.attn_bytes);
-  w.gT = take(hd * std::max(w.e_pad, w.t_pad) * 2);
+  w.ym = take(std::max(krows, ml) * hd * 2);
+  w.ext = take(krows * c.d * 2);
   w.acat = take(rows * 3 * hd * 2);
-  w.wT = take(static_cast<size_t>(std::max(c.d_ff, HD)) * c.d * 2);
   w.wcatT = take(static_cast<size_t>(c.d) * 3 * hd * 2);
-  w.st = take(static_cast<size_t>(c.d) * w.t_pad * 2);
+  w.wT = take(static_cast<size_t>(c.d) * std::max(static_cast<size_t>(c.d_ff), hd) * 2);
+  w.st = take(ml * c.d * 2);
   int rpb;
   const size_t ln_blocks = ln_backward_blocks(static_cast<int>(rows), &rpb);
   w.pg = take(ln_blocks * c.d * 4);
@@ -358,15 +340,16 @@ BwdWs bwd_ws(const txl_stack_config &c) {
   // the largest split-K partial set of the weight-gradient products
   size_t part = 0;
   auto need = [&](int r, int n, int k) {
-    const int s = dw_splits(r, n, k);
+    const int s = dw_gemm_splits(r, n, k);
     if (s > 1) part = std::max(part, static_cast<size_t>(s) * r * n);
   };
-  need(c.d, c.d_ff, w.r_pad);
-  need(c.d_ff, c.d, w.r_pad);
-  need(c.d, HD, w.r_pad);
-  need(HD, c.d, w.r_pad);
-  need(HD, c.d, w.e_pad);
-  need(HD, c.d, w.t_pad);
+  const int R = static_cast<int>(rows), KR = static_cast<int>(krows), ML = static_cast<int>(ml);
+  need(c.d, c.d_ff, R);
+  need(c.d_ff, c.d, R);
+  need(c.d, HD, R);
+  need(HD, c.d, R);
+  need(HD, c.d, KR);
+  need(HD, c.d, ML);
   w.part = take(part * 4);
   w.total = off;
   return w;
@@ -598,11 +581,11 @@ TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t 
   float *part = f32(w.part);
   int rpb;
   const int ln_blocks = ln_backward_blocks(R, &rpb);
-  __bf16 *xT = b16(w.xT), *aT = b16(w.aT), *gT = b16(w.gT), *wT = b16(w.wT);
-  __bf16 *wcatT = b16(w.wcatT), *acat = b16(w.acat), *stT = b16(w.st);
+  __bf16 *wcatT = b16(w.wcatT), *acat = b16(w.acat), *st_rows = b16(w.st), *ym = b16(w.ym);
+  __bf16 *ext = b16(w.ext), *wT = b16(w.wT);
 
-  // S^T [d, t_pad]: the sinusoid rows of distances M+L-1 .. 0, shared by every layer
-  txl_status s = launch_sinusoid_t(c.M, c.L, c.d, w.t_pad, stT, stream);
+  // S [M+L, d]: the sinusoid rows of distances M+L-1 .. 0, shared by every layer
+  txl_status s = launch_sinusoid_rows(c.M, c.L, c.d, st_rows, stream);
   if (s != TXL_OK) return s;
 
   auto ln_bwd = [&](const float *x, const void *gamma, const float *dyv, float *dx, __bf16 *dxb,
@@ -614,11 +597,6 @@ TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t 
     if (r != TXL_OK) return r;
     return launch_reduce_parts(f32(w.pb), ln_blocks, c.d, c.d, db, stream);
   };
-  // y [C, r_pad] = x^T for a plain [R rows, C] matrix
-  auto tr = [&](const void *x, bool x_f32, int rows, int cols, int r_pad, __bf16 *y) {
-    return launch_transpose_bf16(x, rows, nullptr, nullptr, 0, cols, x_f32, rows, cols, r_pad, y,
-                                 r_pad, 0, stream);
-  };
 
   const float *gin = dy;
   for (int n = c.n_layer - 1; n >= 0; --n) {
@@ -627,38 +605,37 @@ TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t 
     const TapeLayer tl = tape_at(tlay, tape, n);
     float *gout = f32((c.n_layer - 1 - n) % 2 ? w.g1 : w.g0);
     float *dx2 = f32(w.dx2), *dh1 = f32(w.dh1), *dx1 = f32(w.dx1);
-    __bf16 *dx2b = b16(w.dx2b), *dx1b = b16(w.dx1b), *dfpre = b16(w.dfpre), *dfpreT = b16(w.dfpreT);
+    __bf16 *dx2b = b16(w.dx2b), *dx1b = b16(w.dx1b), *dfpre = b16(w.dfpre);
+    const __bf16 *w1 = static_cast<const __bf16 *>(lw.w1), *w2 = static_cast<const __bf16 *>(lw.w2);
+    const __bf16 *wo = static_cast<const __bf16 *>(lw.wo);
 
     // LN2
     s = ln_bwd(tl.x2, lw.ln2_g, gin, dx2, dx2b, g.ln2_g, g.ln2_b);
     if (s != TXL_OK) return s;
     // dW2 = dX2^T F
-    if ((s = tr(dx2, true, R, c.d, w.r_pad, xT)) != TXL_OK) return s;
-    if ((s = tr(tl.f, false, R, c.d_ff, w.r_pad, aT)) != TXL_OK) return s;
-    if ((s = dw_gemm(xT, c.d, aT, c.d_ff, w.r_pad, g.w2, part, stream)) != TXL_OK) return s;
-    // dFpre = (dX2 W2) * GELU'(Fpre)
-    if ((s = tr(lw.w2, false, c.d, c.d_ff, c.d, wT)) != TXL_OK) return s;
+    if ((s = dw_gemm(dx2b, c.d, c.d, tl.f, c.d_ff, c.d_ff, R, g.w2, part, stream)) != TXL_OK) return s;
+    // dFpre = (dX2 W2) * GELU'(Fpre), with W2 [d, d_ff] transposed
+    if ((s = launch_transpose_bf16(w2, c.d_ff, false, c.d, c.d_ff, wT, c.d, 0, stream)) != TXL_OK)
+      return s;
     GemmParams pf = dense(dx2b, c.d, R, c.d_ff, c.d, wT, dfpre, c.d_ff);
     pf.pre_in = tl.fpre;
     if ((s = launch_gemm(pf, kEpiGeluGradBf16, stream)) != TXL_OK) return s;
     // dW1 = dFpre^T H1
-    if ((s = tr(dfpre, false, R, c.d_ff, w.r_pad, dfpreT)) != TXL_OK) return s;
-    if ((s = tr(tl.h1, false, R, c.d, w.r_pad, aT)) != TXL_OK) return s;
-    if ((s = dw_gemm(dfpreT, c.d_ff, aT, c.d, w.r_pad, g.w1, part, stream)) != TXL_OK) return s;
-    // dH1 = dX2 + dFpre W1
-    if ((s = tr(lw.w1, false, c.d_ff, c.d, c.d_ff, wT)) != TXL_OK) return s;
+    if ((s = dw_gemm(dfpre, c.d_ff, c.d_ff, tl.h1, c.d, c.d, R, g.w1, part, stream)) != TXL_OK) return s;
+    // dH1 = dX2 + dFpre W1, with W1 [d_ff, d] transposed
+    if ((s = launch_transpose_bf16(w1, c.d, false, c.d_ff, c.d, wT, c.d_ff, 0, stream)) != TXL_OK)
+      return s;
     GemmParams ph = dense(dfpre, c.d_ff, R, c.d, c.d_ff, wT, dh1, c.d);
     ph.res32 = dx2;
     ph.ldres = c.d;
     if ((s = launch_gemm(ph, kEpiResidualF32, stream)) != TXL_OK) return s;
     // LN1
     if ((s = ln_bwd(tl.x1, lw.ln1_g, dh1, dx1, dx1b, g.ln1_g, g.ln1_b)) != TXL_OK) return s;
-    // dW^O = dX1^T A;  dA = dX1 W^O
-    if ((s = tr(dx1, true, R, c.d, w.r_pad, xT)) != TXL_OK) return s;
-    if ((s = tr(tl.o, false, R, HD, w.r_pad, aT)) != TXL_OK) return s;
-    if ((s = dw_gemm(xT, c.d, aT, HD, w.r_pad, g.wo, part, stream)) != TXL_OK) return s;
-    if ((s = tr(lw.wo, false, c.d, HD, c.d, wT)) != TXL_OK) return s;
-    if ((s = launch_gemm(dense(dx1b, c.d, R, HD, c.d, wT, b16(w.dout), HD), kEpiStoreBf16, stream)) != TXL_OK)
+    // dW^O = dX1^T A;  dA = dX1 W^O, with W^O [d, HD] transposed
+    if ((s = dw_gemm(dx1b, c.d, c.d, tl.o, HD, HD, R, g.wo, part, stream)) != TXL_OK) return s;
+    if ((s = launch_transpose_bf16(wo, HD, false, c.d, HD, wT, c.d, 0, stream)) != TXL_OK) return s;
+    if ((s = launch_gemm(dense(dx1b, c.d, R, HD, c.d, wT, b16(w.dout), HD), kEpiStoreBf16, stream)) !=
+        TXL_OK)
       return s;
     // attention backward, with the forward's arguments as the tape holds them
     txl_rel_attn_args a = {};
@@ -702,35 +679,29 @@ TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t 
     ag.du = g.u;
     ag.dvb = g.vb;
     if ((s = txl_rel_attn_bwd(&a, &ag, base + w.attn, w.attn_bytes, stream)) != TXL_OK) return s;
-    // dW^Q = dQ^T H  (dQ also into acat's first HD columns)
-    if ((s = launch_head_grad_pack(f32(w.dq), c.B, c.n_head, c.L, gT, w.r_pad, acat, c.L, 3 * HD, 0,
-                                   stream)) != TXL_OK)
+    // dW^Q = dQ^T H, dQ merged into acat's first HD columns
+    if ((s = launch_head_grad_merge(f32(w.dq), c.B, c.n_head, c.L, nullptr, 0, acat, c.L, 3 * HD, 0,
+                                    stream)) != TXL_OK)
       return s;
-    if ((s = launch_zero_cols(gT, HD, w.r_pad, R, w.r_pad, stream)) != TXL_OK) return s;
-    if ((s = tr(tl.hin, false, R, c.d, w.r_pad, aT)) != TXL_OK) return s;
-    if ((s = dw_gemm(gT, HD, aT, c.d, w.r_pad, g.wq, part, stream)) != TXL_OK) return s;
-    // dW^K = dK^T [mem; H], dW^V = dV^T [mem; H] (slots a row does not hold read as 0)
-    if ((s = launch_transpose_bf16(tl.mem, c.M, tl.valid, tl.hin, c.L, c.d, false, KR, c.d,
-                                   w.e_pad, aT, w.e_pad, 0, stream)) != TXL_OK)
+    if ((s = dw_gemm(acat, 3 * HD, HD, tl.hin, c.d, c.d, R, g.wq, part, stream)) != TXL_OK) return s;
+    // dW^K = dK^T [mem; H], dW^V = dV^T [mem; H] (slots a row does not hold read as 0);
+    // the segment rows of dK, dV also go to acat for the input gradient
+    if ((s = launch_gather_ext(tl.mem, tl.valid, tl.hin, c.B, c.M, c.L, c.d, ext, stream)) != TXL_OK)
       return s;
     for (int kv = 0; kv < 2; ++kv) {
-      if ((s = launch_head_grad_pack(f32(kv ? w.dv : w.dk), c.B, c.n_head, ML, gT, w.e_pad, acat,
-                                     c.L, 3 * HD, (1 + kv) * HD, stream)) != TXL_OK)
+      if ((s = launch_head_grad_merge(f32(kv ? w.dv : w.dk), c.B, c.n_head, ML, ym, HD, acat, c.L,
+                                      3 * HD, (1 + kv) * HD, stream)) != TXL_OK)
         return s;
-      if ((s = launch_zero_cols(gT, HD, w.e_pad, KR, w.e_pad, stream)) != TXL_OK) return s;
-      if ((s = dw_gemm(gT, HD, aT, c.d, w.e_pad, kv ? g.wv : g.wk, part, stream)) != TXL_OK) return s;
+      if ((s = dw_gemm(ym, HD, HD, ext, c.d, c.d, KR, kv ? g.wv : g.wk, part, stream)) != TXL_OK) return s;
     }
     // dW_R = dR^T S (R = S W_R^T for distances M+L-1 .. 0)
-    if ((s = launch_head_grad_pack(f32(w.dr), 1, c.n_head, ML, gT, w.t_pad, nullptr, 0, 0, 0,
-                                   stream)) != TXL_OK)
+    if ((s = launch_head_grad_merge(f32(w.dr), 1, c.n_head, ML, ym, HD, nullptr, 0, 0, 0, stream)) != TXL_OK)
       return s;
-    if ((s = launch_zero_cols(gT, HD, w.t_pad, ML, w.t_pad, stream)) != TXL_OK) return s;
-    if ((s = dw_gemm(gT, HD, stT, c.d, w.t_pad, g.wr, part, stream)) != TXL_OK) return s;
+    if ((s = dw_gemm(ym, HD, HD, st_rows, c.d, c.d, ML, g.wr, part, stream)) != TXL_OK) return s;
     // dH^(n-1) = dX1 + [dQ | dK_seg | dV_seg] [W^Q; W^K; W^V]
     const void *wqkv[3] = {lw.wq, lw.wk, lw.wv};
     for (int j = 0; j < 3; ++j)
-      if ((s = launch_transpose_bf16(wqkv[j], HD, nullptr, nullptr, 0, c.d, false, HD, c.d, HD,
-                                     wcatT, 3 * HD, j * HD, stream)) != TXL_OK)
+      if ((s = launch_transpose_bf16(wqkv[j], c.d, false, HD, c.d, wcatT, 3 * HD, j * HD, stream)) != TXL_OK)
         return s;
     GemmParams pi = dense(acat, 3 * HD, R, c.d, 3 * HD, wcatT, gout, c.d);
     pi.res32 = dx1;

@@ -135,22 +135,20 @@ txl_status launch_mem_read_logical(const void *data, void *out, int B, int M,
 // ---- relative-position table ---------------------------------------------
 txl_status launch_rel_pos_table(txl_dtype dt, int M, int L, int d, int HD,
                                 const void *w_r, void *r, hipStream_t s);
-// st [d, t_pad] bf16: st[k, t] = S(M+L-1-t, k) for t < M+L, 0 beyond
-txl_status launch_sinusoid_t(int M, int L, int d, int t_pad, void *st, hipStream_t s);
+// S [M+L, d] bf16: row t = the sinusoid of distance M+L-1-t
+txl_status launch_sinusoid_rows(int M, int L, int d, void *st, hipStream_t s);
 
 // ---- segment gradients (bwd.hip) -------------------------------------------
-// y[c, col0 + q] = row q of the source, bf16, zero for R <= q < r_pad; source
-// row q is, with G = g1 + g2, row (q/G)*g1 + q%G of x1 when q%G < g1, else
-// row (q/G)*g2 + q%G - g1 of x2 (row stride ldx; fp32 or bf16 source); with
-// valid1 set, x1 rows j = q%G < g1 - valid1[q/G] read as 0
-txl_status launch_transpose_bf16(const void *x1, int g1, const int32_t *valid1, const void *x2,
-                                 int g2, int64_t ldx, bool src_f32, int R, int C, int r_pad,
-                                 void *y, int64_t ldy, int col0, hipStream_t s);
-// g [B, H, T, 64] fp32 -> yt[h*64 + e, b*T + j] bf16 (row stride ldt) and,
-// when y2 is set, y2[b*L + j - (T-L), col0 + h*64 + e] for j >= T - L
-txl_status launch_head_grad_pack(const float *g, int B, int H, int T, void *yt, int64_t ldt,
-                                 void *y2, int L, int64_t ld2, int col0, hipStream_t s);
-txl_status launch_zero_cols(void *y, int n_rows, int64_t ldy, int c_from, int c_to, hipStream_t s);
+// y[c, col0 + q] = x[q, c] in bf16 for q < R, c < C (x row stride ldx)
+txl_status launch_transpose_bf16(const void *x, int64_t ldx, bool src_f32, int R, int C, void *y,
+                                 int64_t ldy, int col0, hipStream_t s);
+// y [B*(M+L), d] = [memory (logical order, unheld slots zero); segment] per batch row
+txl_status launch_gather_ext(const void *mem, const int32_t *valid, const void *seg, int B, int M, int L,
+                             int d, void *y, hipStream_t s);
+// g [B, H, T, 64] fp32 -> bf16 rows merged over heads: y_all [B*T, ld_all]
+// (all entries) and / or y_last rows b*L + j - (T-L), columns col0.. (the last L)
+txl_status launch_head_grad_merge(const float *g, int B, int H, int T, void *y_all, int64_t ld_all,
+                                  void *y_last, int L, int64_t ld_last, int col0, hipStream_t s);
 // out[i] = sum over s < S of part[s*stride + i], in a fixed order (n a multiple
 // of 4, 16-byte aligned)
 txl_status launch_reduce_parts(const float *part, int S, int64_t stride, int64_t n, float *out,
@@ -208,6 +206,14 @@ struct GemmParams {
   float *part_m, *part_s, *tgt;
 };
 txl_status launch_gemm(const GemmParams &p, int epi, hipStream_t s);
+// Weight gradients: out [rows, N] fp32 = X^T Y over the first k_rows rows of
+// X [*, ldx] bf16 (rows columns used) and Y [*, ldy] bf16 (N columns used),
+// split over k_splits contiguous K ranges whose fp32 results go to
+// out + s * split_stride (k_splits == 1: out). rows and N multiples of 64,
+// ldx, ldy and the base pointers 16-byte aligned in bf16 elements (x8).
+int dw_gemm_splits(int rows, int N, int k_rows);
+txl_status launch_dw_gemm(const void *x, int64_t ldx, int rows, const void *y, int64_t ldy, int N,
+                          int k_rows, int k_splits, float *out, int64_t split_stride, hipStream_t s);
 // y = LN(x) over rows of d, x = sum of n_parts fp32 buffers (part_stride
 // elements apart, added in order) plus the bf16 residual res (may be null)
 // x_out (may be null) receives the summed fp32 x (the LayerNorm's input)
