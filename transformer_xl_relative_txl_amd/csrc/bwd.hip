@@ -26,29 +26,45 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kT = 64;  // transpose tile
 
-__device__ inline float to_f(float x) { return x; }
-__device__ inline float to_f(__bf16 x) { return static_cast<float>(x); }
+// Up to kMaxTransposes bf16 transposes in one launch, y[c, col0 + q] =
+// x[q, c], R and C multiples of 64: workgroup t takes 64 x 64 tile t of the
+// job whose tile range holds it. Each thread loads two 16-byte row chunks
+// of the tile into LDS and stores two 16-byte chunks of the transposed
+// tile, eight rows of one column gathered from LDS.
+struct TransposeBatch {
+  TransposeJob job[kMaxTransposes];
+  int tile0[kMaxTransposes + 1];  // job k owns tiles [tile0[k], tile0[k + 1])
+  int n;
+};
 
-// y[c, col0 + q] = x[q, c] (bf16) for rows q < R and columns c < C of a
-// row-major x (row stride ldx, fp32 or bf16). 64 x 64 tiles through LDS,
-// both sides coalesced.
-template <typename T>
-__global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ x, int64_t ldx, int R,
-                                                        int C, __bf16 *__restrict__ y, int64_t ldy,
-                                                        int col0) {
-  __shared__ float tile[kT][kT + 1];
-  const int c0 = blockIdx.x * kT, q0 = blockIdx.y * kT;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-#pragma unroll 4
-  for (int k = 0; k < kT / 4; ++k) {
-    const int qq = ty + 4 * k, q = q0 + qq, c = c0 + tx;
-    tile[qq][tx] = (q < R && c < C) ? to_f(x[static_cast<int64_t>(q) * ldx + c]) : 0.0f;
+__global__ __launch_bounds__(256) void transpose_batch_kernel(TransposeBatch tb) {
+  __shared__ __bf16 tile[kT][kT + 2];
+  int k = 0;
+  while (k + 1 < tb.n && static_cast<int>(blockIdx.x) >= tb.tile0[k + 1]) ++k;
+  const TransposeJob &jb = tb.job[k];
+  const int t = blockIdx.x - tb.tile0[k];
+  const int n_tc = jb.C / kT;
+  const int q0 = (t / n_tc) * kT, c0 = (t % n_tc) * kT;
+  const int tid = threadIdx.x;
+  const __bf16 *x = static_cast<const __bf16 *>(jb.x);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = (tid >> 3) + 32 * i, ch = tid & 7;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(q0 + row) * jb.ldx + c0 + 8 * ch);
+    const __bf16 *e = reinterpret_cast<const __bf16 *>(&v);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) tile[row][8 * ch + m] = e[m];
   }
   __syncthreads();
-#pragma unroll 4
-  for (int k = 0; k < kT / 4; ++k) {
-    const int cc = ty + 4 * k, c = c0 + cc, q = q0 + tx;
-    if (c < C && q < R) y[static_cast<int64_t>(c) * ldy + col0 + q] = static_cast<__bf16>(tile[tx][cc]);
+  __bf16 *y = static_cast<__bf16 *>(jb.y);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int cc = (tid >> 3) + 32 * i, qc = tid & 7;
+    __bf16 e[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) e[m] = tile[8 * qc + m][cc];
+    *reinterpret_cast<u32x4 *>(y + static_cast<int64_t>(c0 + cc) * jb.ldy + jb.col0 + q0 + 8 * qc) =
+        __builtin_bit_cast(u32x4, e);
   }
 }
 
@@ -114,17 +130,22 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(const float *__restri
   reinterpret_cast<f32x4 *>(out)[e] = acc;
 }
 
-// The same sum for many parts over few columns (the LayerNorm parameter
-// partials: hundreds of parts, d columns): a workgroup owns 16 columns, its
-// 16 thread groups each add every 16th part in order, and the 16 group sums
-// are added in group order.
-constexpr int kColGroups = 16;
-__global__ __launch_bounds__(256) void reduce_cols_kernel(const float *__restrict__ part, int S,
-                                                          int64_t stride, int64_t n,
-                                                          float *__restrict__ out) {
-  __shared__ float red[kColGroups][16];
-  const int cl = threadIdx.x & 15, grp = threadIdx.x >> 4;
-  const int64_t col = static_cast<int64_t>(blockIdx.x) * 16 + cl;
+// The same sum for many parts over few columns, for two part sets at once
+// (the LayerNorm gamma and beta partials: hundreds of parts, d columns):
+// blockIdx.y picks the set, a workgroup owns 8 columns, its 32 thread
+// groups each add every 32nd part in order, and the 32 group sums are
+// added in group order.
+constexpr int kColGroups = 32, kColsPerBlock = 8;
+__global__ __launch_bounds__(256) void reduce_cols2_kernel(const float *__restrict__ part0,
+                                                           float *__restrict__ out0,
+                                                           const float *__restrict__ part1,
+                                                           float *__restrict__ out1, int S,
+                                                           int64_t stride, int64_t n) {
+  __shared__ float red[kColGroups][kColsPerBlock];
+  const float *part = blockIdx.y ? part1 : part0;
+  float *out = blockIdx.y ? out1 : out0;
+  const int cl = threadIdx.x % kColsPerBlock, grp = threadIdx.x / kColsPerBlock;
+  const int64_t col = static_cast<int64_t>(blockIdx.x) * kColsPerBlock + cl;
   float acc = 0.0f;
   if (col < n) {
 #pragma unroll 8
@@ -293,18 +314,26 @@ __global__ void copy_i32_kernel(const int32_t *__restrict__ src, int32_t *__rest
 
 }  // namespace
 
-txl_status launch_transpose_bf16(const void *x, int64_t ldx, bool src_f32, int R, int C, void *y,
-                                 int64_t ldy, int col0, hipStream_t s) {
-  if (C <= 0 || R <= 0) return TXL_OK;
-  const dim3 grid((C + kT - 1) / kT, (R + kT - 1) / kT);
+txl_status launch_transpose_batch(const TransposeJob *jobs, int n, hipStream_t s) {
+  if (n < 1 || n > kMaxTransposes) return fail(TXL_ERR_INVALID_ARG, "transpose_batch: %d jobs", n);
+  TransposeBatch tb = {};
+  tb.n = n;
+  int64_t tiles = 0;
+  for (int k = 0; k < n; ++k) {
+    const TransposeJob &j = jobs[k];
+    if (j.R <= 0 || j.C <= 0 || j.R % kT || j.C % kT || j.ldx % 8 || j.ldy % 8 || j.col0 % 8 ||
+        j.ldx < j.C || j.ldy < j.col0 + j.R || reinterpret_cast<uintptr_t>(j.x) % 16 ||
+        reinterpret_cast<uintptr_t>(j.y) % 16)
+      return fail(TXL_ERR_UNSUPPORTED, "transpose_batch: job %d shape or alignment", k);
+    tb.job[k] = j;
+    tb.tile0[k] = static_cast<int>(tiles);
+    tiles += static_cast<int64_t>(j.R / kT) * (j.C / kT);
+    if (tiles > 0x7fffffff) return fail(TXL_ERR_UNSUPPORTED, "transpose_batch: too many tiles");
+  }
+  tb.tile0[n] = static_cast<int>(tiles);
   (void)hipGetLastError();
-  if (src_f32)
-    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s, static_cast<const float *>(x), ldx, R, C,
-                       static_cast<__bf16 *>(y), ldy, col0);
-  else
-    hipLaunchKernelGGL(transpose_kernel<__bf16>, grid, dim3(256), 0, s, static_cast<const __bf16 *>(x), ldx, R,
-                       C, static_cast<__bf16 *>(y), ldy, col0);
-  return check_launch("transpose_kernel");
+  hipLaunchKernelGGL(transpose_batch_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s, tb);
+  return check_launch("transpose_batch_kernel");
 }
 
 txl_status launch_gather_ext(const void *mem, const int32_t *valid, const void *seg, int B, int M, int L,
@@ -334,16 +363,24 @@ txl_status launch_head_grad_merge(const float *g, int B, int H, int T, void *y_a
 txl_status launch_reduce_parts(const float *part, int S, int64_t stride, int64_t n, float *out,
                                hipStream_t s) {
   if (n == 0) return TXL_OK;
-  (void)hipGetLastError();
-  if (S > 16) {  // many parts: split them over thread groups
-    hipLaunchKernelGGL(reduce_cols_kernel, dim3(static_cast<unsigned>((n + 15) / 16)), dim3(256), 0, s,
-                       part, S, stride, n, out);
-    return check_launch("reduce_cols_kernel");
-  }
+  if (n % 4 || reinterpret_cast<uintptr_t>(part) % 16 || reinterpret_cast<uintptr_t>(out) % 16 ||
+      stride % 4)
+    return fail(TXL_ERR_UNSUPPORTED, "reduce_parts: n, stride multiples of 4, 16-byte aligned");
   const int64_t n4 = n / 4;
+  (void)hipGetLastError();
   hipLaunchKernelGGL(reduce_parts_kernel, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, s,
                      part, S, stride, n4, out);
   return check_launch("reduce_parts_kernel");
+}
+
+txl_status launch_reduce_cols2(const float *part0, float *out0, const float *part1, float *out1, int S,
+                               int64_t stride, int64_t n, hipStream_t s) {
+  if (n == 0) return TXL_OK;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(reduce_cols2_kernel,
+                     dim3(static_cast<unsigned>((n + kColsPerBlock - 1) / kColsPerBlock), 2), dim3(256), 0,
+                     s, part0, out0, part1, out1, S, stride, n);
+  return check_launch("reduce_cols2_kernel");
 }
 
 // rows per workgroup of the LayerNorm backward: at least 16, about 256 workgroups

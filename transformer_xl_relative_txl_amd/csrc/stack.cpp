@@ -331,7 +331,7 @@ BwdWs bwd_ws(const txl_stack_config &c) {
   w.ext = take(krows * c.d * 2);
   w.acat = take(rows * 3 * hd * 2);
   w.wcatT = take(static_cast<size_t>(c.d) * 3 * hd * 2);
-  w.wT = take(static_cast<size_t>(c.d) * std::max(static_cast<size_t>(c.d_ff), hd) * 2);
+  w.wT = take((2 * static_cast<size_t>(c.d) * c.d_ff + hd * c.d) * 2);
   w.st = take(ml * c.d * 2);
   int rpb;
   const size_t ln_blocks = ln_backward_blocks(static_cast<int>(rows), &rpb);
@@ -593,9 +593,7 @@ TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t 
     txl_status r = launch_ln_backward(x, gamma, dyv, dx, dxb, f32(w.pg), f32(w.pb), R, c.d,
                                       c.ln_eps, stream);
     if (r != TXL_OK) return r;
-    r = launch_reduce_parts(f32(w.pg), ln_blocks, c.d, c.d, dg, stream);
-    if (r != TXL_OK) return r;
-    return launch_reduce_parts(f32(w.pb), ln_blocks, c.d, c.d, db, stream);
+    return launch_reduce_cols2(f32(w.pg), dg, f32(w.pb), db, ln_blocks, c.d, c.d, stream);
   };
 
   const float *gin = dy;
@@ -609,32 +607,39 @@ TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t 
     const __bf16 *w1 = static_cast<const __bf16 *>(lw.w1), *w2 = static_cast<const __bf16 *>(lw.w2);
     const __bf16 *wo = static_cast<const __bf16 *>(lw.wo);
 
+    // the layer's weights transposed for the input-gradient products:
+    // W2^T [d_ff, d], W1^T [d, d_ff], W^O^T [HD, d], [W^Q; W^K; W^V]^T [d, 3 HD]
+    __bf16 *w2T = wT, *w1T = wT + static_cast<size_t>(c.d_ff) * c.d;
+    __bf16 *woT = w1T + static_cast<size_t>(c.d) * c.d_ff;
+    const TransposeJob jobs[6] = {
+        {w2, c.d_ff, c.d, c.d_ff, w2T, c.d, 0},
+        {w1, c.d, c.d_ff, c.d, w1T, c.d_ff, 0},
+        {wo, HD, c.d, HD, woT, c.d, 0},
+        {lw.wq, c.d, HD, c.d, wcatT, 3 * HD, 0},
+        {lw.wk, c.d, HD, c.d, wcatT, 3 * HD, HD},
+        {lw.wv, c.d, HD, c.d, wcatT, 3 * HD, 2 * HD}};
+    if ((s = launch_transpose_batch(jobs, 6, stream)) != TXL_OK) return s;
     // LN2
     s = ln_bwd(tl.x2, lw.ln2_g, gin, dx2, dx2b, g.ln2_g, g.ln2_b);
     if (s != TXL_OK) return s;
     // dW2 = dX2^T F
     if ((s = dw_gemm(dx2b, c.d, c.d, tl.f, c.d_ff, c.d_ff, R, g.w2, part, stream)) != TXL_OK) return s;
-    // dFpre = (dX2 W2) * GELU'(Fpre), with W2 [d, d_ff] transposed
-    if ((s = launch_transpose_bf16(w2, c.d_ff, false, c.d, c.d_ff, wT, c.d, 0, stream)) != TXL_OK)
-      return s;
-    GemmParams pf = dense(dx2b, c.d, R, c.d_ff, c.d, wT, dfpre, c.d_ff);
+    // dFpre = (dX2 W2) * GELU'(Fpre)
+    GemmParams pf = dense(dx2b, c.d, R, c.d_ff, c.d, w2T, dfpre, c.d_ff);
     pf.pre_in = tl.fpre;
     if ((s = launch_gemm(pf, kEpiGeluGradBf16, stream)) != TXL_OK) return s;
     // dW1 = dFpre^T H1
     if ((s = dw_gemm(dfpre, c.d_ff, c.d_ff, tl.h1, c.d, c.d, R, g.w1, part, stream)) != TXL_OK) return s;
-    // dH1 = dX2 + dFpre W1, with W1 [d_ff, d] transposed
-    if ((s = launch_transpose_bf16(w1, c.d, false, c.d_ff, c.d, wT, c.d_ff, 0, stream)) != TXL_OK)
-      return s;
-    GemmParams ph = dense(dfpre, c.d_ff, R, c.d, c.d_ff, wT, dh1, c.d);
+    // dH1 = dX2 + dFpre W1
+    GemmParams ph = dense(dfpre, c.d_ff, R, c.d, c.d_ff, w1T, dh1, c.d);
     ph.res32 = dx2;
     ph.ldres = c.d;
     if ((s = launch_gemm(ph, kEpiResidualF32, stream)) != TXL_OK) return s;
     // LN1
     if ((s = ln_bwd(tl.x1, lw.ln1_g, dh1, dx1, dx1b, g.ln1_g, g.ln1_b)) != TXL_OK) return s;
-    // dW^O = dX1^T A;  dA = dX1 W^O, with W^O [d, HD] transposed
+    // dW^O = dX1^T A;  dA = dX1 W^O
     if ((s = dw_gemm(dx1b, c.d, c.d, tl.o, HD, HD, R, g.wo, part, stream)) != TXL_OK) return s;
-    if ((s = launch_transpose_bf16(wo, HD, false, c.d, HD, wT, c.d, 0, stream)) != TXL_OK) return s;
-    if ((s = launch_gemm(dense(dx1b, c.d, R, HD, c.d, wT, b16(w.dout), HD), kEpiStoreBf16, stream)) !=
+    if ((s = launch_gemm(dense(dx1b, c.d, R, HD, c.d, woT, b16(w.dout), HD), kEpiStoreBf16, stream)) !=
         TXL_OK)
       return s;
     // attention backward, with the forward's arguments as the tape holds them
@@ -699,10 +704,6 @@ TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t 
       return s;
     if ((s = dw_gemm(ym, HD, HD, st_rows, c.d, c.d, ML, g.wr, part, stream)) != TXL_OK) return s;
     // dH^(n-1) = dX1 + [dQ | dK_seg | dV_seg] [W^Q; W^K; W^V]
-    const void *wqkv[3] = {lw.wq, lw.wk, lw.wv};
-    for (int j = 0; j < 3; ++j)
-      if ((s = launch_transpose_bf16(wqkv[j], c.d, false, HD, c.d, wcatT, 3 * HD, j * HD, stream)) != TXL_OK)
-        return s;
     GemmParams pi = dense(acat, 3 * HD, R, c.d, 3 * HD, wcatT, gout, c.d);
     pi.res32 = dx1;
     pi.ldres = c.d;

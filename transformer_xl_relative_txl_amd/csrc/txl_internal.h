@@ -139,9 +139,19 @@ txl_status launch_rel_pos_table(txl_dtype dt, int M, int L, int d, int HD,
 txl_status launch_sinusoid_rows(int M, int L, int d, void *st, hipStream_t s);
 
 // ---- segment gradients (bwd.hip) -------------------------------------------
-// y[c, col0 + q] = x[q, c] in bf16 for q < R, c < C (x row stride ldx)
-txl_status launch_transpose_bf16(const void *x, int64_t ldx, bool src_f32, int R, int C, void *y,
-                                 int64_t ldy, int col0, hipStream_t s);
+// bf16 transposes y[c, col0 + q] = x[q, c] for q < R, c < C (x row stride
+// ldx, y row stride ldy), up to kMaxTransposes in one launch; R and C
+// multiples of 64, pointers 16-byte aligned, ldx, ldy, col0 multiples of 8
+struct TransposeJob {
+  const void *x;
+  int64_t ldx;
+  int R, C;
+  void *y;
+  int64_t ldy;
+  int col0;
+};
+constexpr int kMaxTransposes = 8;
+txl_status launch_transpose_batch(const TransposeJob *jobs, int n, hipStream_t s);
 // y [B*(M+L), d] = [memory (logical order, unheld slots zero); segment] per batch row
 txl_status launch_gather_ext(const void *mem, const int32_t *valid, const void *seg, int B, int M, int L,
                              int d, void *y, hipStream_t s);
@@ -153,6 +163,10 @@ txl_status launch_head_grad_merge(const float *g, int B, int H, int T, void *y_a
 // of 4, 16-byte aligned)
 txl_status launch_reduce_parts(const float *part, int S, int64_t stride, int64_t n, float *out,
                                hipStream_t s);
+// the same for two part sets (out0 from part0, out1 from part1) in one
+// launch, for many parts over few columns (any n, 4-byte aligned)
+txl_status launch_reduce_cols2(const float *part0, float *out0, const float *part1, float *out1, int S,
+                               int64_t stride, int64_t n, hipStream_t s);
 int ln_backward_blocks(int rows, int *rpb);
 txl_status launch_ln_backward(const float *x, const void *gamma, const float *dy, float *dx,
                               void *dxb, float *part_g, float *part_b, int rows, int d, float eps,
