@@ -168,16 +168,19 @@ __global__ __launch_bounds__(256) void reduce_cols2_kernel(const float *__restri
 // order within a wave, the four waves added in order) go to
 // part_g / part_b [blockIdx.x, d].
 constexpr int kLnMaxChunks = 16;  // d <= 4096
+template <int NCH>
 __global__ __launch_bounds__(256) void ln_backward_kernel(
     const float *__restrict__ x, const __bf16 *__restrict__ gamma, const float *__restrict__ dy,
     float *__restrict__ dx, __bf16 *__restrict__ dxb, float *__restrict__ part_g,
     float *__restrict__ part_b, int rows, int d, int rpb, float eps) {
-  __shared__ float red[4][2][8 * 256];  // 8 of the row's 256-column chunks per pass (64 KB)
+  constexpr int MAXC = NCH > 0 ? NCH : kLnMaxChunks;
+  constexpr int RC = MAXC < 8 ? MAXC : 8;  // chunks per pass of the partial-sum exchange
+  __shared__ float red[4][2][RC * 256];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nch = d / 256;
-  f32x4 ag[kLnMaxChunks], ab[kLnMaxChunks];
+  const int nch = NCH > 0 ? NCH : d / 256;
+  f32x4 ag[MAXC], ab[MAXC];
 #pragma unroll
-  for (int c = 0; c < kLnMaxChunks; ++c) {
+  for (int c = 0; c < MAXC; ++c) {
     ag[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     ab[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
@@ -185,10 +188,10 @@ __global__ __launch_bounds__(256) void ln_backward_kernel(
   for (int row = r_lo + wave; row < r_hi; row += 4) {
     const float *xr = x + static_cast<int64_t>(row) * d;
     const float *gr = dy + static_cast<int64_t>(row) * d;
-    f32x4 xv[kLnMaxChunks], gv[kLnMaxChunks];
+    f32x4 xv[MAXC], gv[MAXC];
     float s = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kLnMaxChunks; ++c)
+    for (int c = 0; c < MAXC; ++c)
       if (c < nch) {
         xv[c] = *reinterpret_cast<const f32x4 *>(xr + 256 * c + 4 * lane);
         s += (xv[c][0] + xv[c][1]) + (xv[c][2] + xv[c][3]);
@@ -198,7 +201,7 @@ __global__ __launch_bounds__(256) void ln_backward_kernel(
     const float mean = s / d;
     float ss = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kLnMaxChunks; ++c)
+    for (int c = 0; c < MAXC; ++c)
       if (c < nch)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(256) void ln_backward_kernel(
     const float rs = 1.0f / sqrtf(ss / d + eps);
     float m1 = 0.0f, m2 = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kLnMaxChunks; ++c)
+    for (int c = 0; c < MAXC; ++c)
       if (c < nch) {
         const bf16x4 gm = *reinterpret_cast<const bf16x4 *>(gamma + 256 * c + 4 * lane);
         gv[c] = *reinterpret_cast<const f32x4 *>(gr + 256 * c + 4 * lane);
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(256) void ln_backward_kernel(
     m1 /= d;
     m2 /= d;
 #pragma unroll
-    for (int c = 0; c < kLnMaxChunks; ++c)
+    for (int c = 0; c < MAXC; ++c)
       if (c < nch) {
         f32x4 o4;
         bf16x4 ob;
@@ -248,25 +251,24 @@ __global__ __launch_bounds__(256) void ln_backward_kernel(
         if (dxb) *reinterpret_cast<bf16x4 *>(dxb + at) = ob;
       }
   }
-  // the four waves' partial sums, added in wave order
-  for (int half = 0; half < 2; ++half) {  // chunks [8 half, 8 half + 8): LDS holds half the row
-    if (half * 8 >= nch) break;
+  // the four waves' partial sums, added in wave order, RC chunks per pass
+  for (int base = 0; base < nch; base += RC) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      if (half * 8 + c < nch)
+    for (int c = 0; c < RC; ++c)
+      if (base + c < nch)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          red[wave][0][(c * 64 + lane) * 4 + e] = ag[half * 8 + c][e];
-          red[wave][1][(c * 64 + lane) * 4 + e] = ab[half * 8 + c][e];
+          red[wave][0][(c * 64 + lane) * 4 + e] = ag[base + c][e];
+          red[wave][1][(c * 64 + lane) * 4 + e] = ab[base + c][e];
         }
     __syncthreads();
-    const int n = (nch - half * 8 < 8 ? nch - half * 8 : 8) * 256;
+    const int n = (nch - base < RC ? nch - base : RC) * 256;
     for (int i = threadIdx.x; i < n; i += 256) {
       const float g = ((red[0][0][i] + red[1][0][i]) + red[2][0][i]) + red[3][0][i];
       const float bb = ((red[0][1][i] + red[1][1][i]) + red[2][1][i]) + red[3][1][i];
       // LDS index i = (c * 64 + lane) * 4 + e  <->  column 256 c + 4 lane + e
       const int c = i / 256, rem = i - c * 256;
-      const int col = 256 * (half * 8 + c) + rem;
+      const int col = 256 * (base + c) + rem;
       part_g[static_cast<int64_t>(blockIdx.x) * d + col] = g;
       part_b[static_cast<int64_t>(blockIdx.x) * d + col] = bb;
     }
@@ -383,10 +385,12 @@ txl_status launch_reduce_cols2(const float *part0, float *out0, const float *par
   return check_launch("reduce_cols2_kernel");
 }
 
-// rows per workgroup of the LayerNorm backward: at least 16, about 256 workgroups
+// rows per workgroup of the LayerNorm backward: at least kLnBwdMinRows, about
+// kLnBwdBlocks workgroups
+constexpr int kLnBwdBlocks = 512, kLnBwdMinRows = 8;
 int ln_backward_blocks(int rows, int *rpb) {
-  *rpb = (rows + 255) / 256;
-  if (*rpb < 16) *rpb = 16;
+  *rpb = (rows + kLnBwdBlocks - 1) / kLnBwdBlocks;
+  if (*rpb < kLnBwdMinRows) *rpb = kLnBwdMinRows;
   return (rows + *rpb - 1) / *rpb;
 }
 
@@ -398,9 +402,15 @@ txl_status launch_ln_backward(const float *x, const void *gamma, const float *dy
   int rpb;
   const int blocks = ln_backward_blocks(rows, &rpb);
   (void)hipGetLastError();
-  hipLaunchKernelGGL(ln_backward_kernel, dim3(blocks), dim3(256), 0, s, x,
-                     static_cast<const __bf16 *>(gamma), dy, dx, static_cast<__bf16 *>(dxb), part_g,
-                     part_b, rows, d, rpb, eps);
+  const __bf16 *g = static_cast<const __bf16 *>(gamma);
+  __bf16 *xb = static_cast<__bf16 *>(dxb);
+  switch (d / 256) {
+    case 1: hipLaunchKernelGGL(ln_backward_kernel<1>, dim3(blocks), dim3(256), 0, s, x, g, dy, dx, xb, part_g, part_b, rows, d, rpb, eps); break;
+    case 2: hipLaunchKernelGGL(ln_backward_kernel<2>, dim3(blocks), dim3(256), 0, s, x, g, dy, dx, xb, part_g, part_b, rows, d, rpb, eps); break;
+    case 3: hipLaunchKernelGGL(ln_backward_kernel<3>, dim3(blocks), dim3(256), 0, s, x, g, dy, dx, xb, part_g, part_b, rows, d, rpb, eps); break;
+    case 4: hipLaunchKernelGGL(ln_backward_kernel<4>, dim3(blocks), dim3(256), 0, s, x, g, dy, dx, xb, part_g, part_b, rows, d, rpb, eps); break;
+    default: hipLaunchKernelGGL(ln_backward_kernel<0>, dim3(blocks), dim3(256), 0, s, x, g, dy, dx, xb, part_g, part_b, rows, d, rpb, eps); break;
+  }
   return check_launch("ln_backward_kernel");
 }
 

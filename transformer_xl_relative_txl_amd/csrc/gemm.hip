@@ -372,7 +372,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
 // biased variance, one wave per row, result rounded to bf16.
 constexpr int kLnMaxChunks = 16;  // 4-float chunks per lane: d <= 4096
 
-template <int NP>
+// NCH: 256-column chunks of a row when known at compile time (registers
+// sized to the row), 0 for any d <= 4096.
+template <int NP, int NCH>
 __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict__ x,
                                                         int64_t part_stride,
                                                         const __bf16 *__restrict__ res,
@@ -383,12 +385,13 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
-  const int nch = d / 256;
+  constexpr int MAXC = NCH > 0 ? NCH : kLnMaxChunks;
+  const int nch = NCH > 0 ? NCH : d / 256;
   const float *xr = x + static_cast<int64_t>(row) * d;
-  f32x4 v[kLnMaxChunks];
+  f32x4 v[MAXC];
   float s = 0.0f;
 #pragma unroll
-  for (int c = 0; c < kLnMaxChunks; ++c) {
+  for (int c = 0; c < MAXC; ++c) {
     if (c < nch) {
       v[c] = *reinterpret_cast<const f32x4 *>(xr + 256 * c + 4 * lane);
       // split-K partials in order, then the residual
@@ -410,7 +413,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
   const float mean = s / d;
   float ss = 0.0f;
 #pragma unroll
-  for (int c = 0; c < kLnMaxChunks; ++c) {
+  for (int c = 0; c < MAXC; ++c) {
     if (c < nch) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -424,7 +427,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
   const float inv = 1.0f / sqrtf(ss / d + eps);
   __bf16 *yr = y + static_cast<int64_t>(row) * d;
 #pragma unroll
-  for (int c = 0; c < kLnMaxChunks; ++c) {
+  for (int c = 0; c < MAXC; ++c) {
     if (c < nch) {
       const int col = 256 * c + 4 * lane;
       const bf16x4 gm = *reinterpret_cast<const bf16x4 *>(gamma + col);
@@ -576,14 +579,24 @@ txl_status launch_layernorm(const float *x, int n_parts, int64_t part_stride, co
   const __bf16 *g = static_cast<const __bf16 *>(gamma);
   const __bf16 *b = static_cast<const __bf16 *>(beta);
   __bf16 *o = static_cast<__bf16 *>(y);
-  if (n_parts == 1)
-    hipLaunchKernelGGL(layernorm_kernel<1>, grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps, x_out);
-  else if (n_parts == 2)
-    hipLaunchKernelGGL(layernorm_kernel<2>, grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps, x_out);
-  else if (n_parts == 4)
-    hipLaunchKernelGGL(layernorm_kernel<4>, grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps, x_out);
-  else
+  if (n_parts != 1 && n_parts != 2 && n_parts != 4)
     return fail(TXL_ERR_UNSUPPORTED, "layernorm: %d partial sums (1, 2 or 4 are built)", n_parts);
+  auto go = [&](auto np) {
+    constexpr int NP = decltype(np)::value;
+    switch (d / 256) {
+      case 1: hipLaunchKernelGGL((layernorm_kernel<NP, 1>), grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps, x_out); break;
+      case 2: hipLaunchKernelGGL((layernorm_kernel<NP, 2>), grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps, x_out); break;
+      case 3: hipLaunchKernelGGL((layernorm_kernel<NP, 3>), grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps, x_out); break;
+      case 4: hipLaunchKernelGGL((layernorm_kernel<NP, 4>), grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps, x_out); break;
+      default: hipLaunchKernelGGL((layernorm_kernel<NP, 0>), grid, dim3(256), 0, s, x, part_stride, r, g, b, o, rows, d, eps, x_out); break;
+    }
+  };
+  if (n_parts == 1)
+    go(std::integral_constant<int, 1>{});
+  else if (n_parts == 2)
+    go(std::integral_constant<int, 2>{});
+  else
+    go(std::integral_constant<int, 4>{});
   return check_launch("layernorm_kernel");
 }
 

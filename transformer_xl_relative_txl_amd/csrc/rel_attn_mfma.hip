@@ -21,18 +21,21 @@
 //    new blocks (two 32-row R loads, 8 MFMAs).
 //  * The per-query diagonal read of the band (the relative shift, [P1]
 //    "Relative Shift Trick" replaced by index arithmetic) goes through a
-//    per-wave LDS band stored [u][query] with a row stride of 34 floats and
+//    per-wave LDS band stored [u][query] with a row stride of 32 floats and
 //    all 96 rows of the tile's three blocks (written once per tile, read by
 //    both 32-key halves): lane r reads row c + 31 - r (+32 for the second
-//    half) for key c, which is conflict-free.
-//  * K and V^T tiles are staged in LDS by the whole workgroup in a single
-//    buffer (a barrier before and after each refill; the next tile's K / V
-//    sit in registers meanwhile), which leaves room for the 96-row bands at
-//    two workgroups per CU; R rows go straight from L2 into the A operand,
-//    one tile ahead.
-//  * The shifted position term is read from LDS straight into the score
-//    accumulator, and the content MFMA K (Q')^T accumulates onto it, so the
-//    two terms are summed by the matrix unit, not by VALU adds.
+//    half) for key c, so both the write and the read put lane r on bank r.
+//  * K and V tiles go from HBM straight into LDS with buffer-to-LDS loads
+//    (16 bytes a lane, no registers), into two buffers: the next tile's
+//    loads are issued at the top of a tile and waited for, with one barrier,
+//    at its end. Rows are stored with their 16-byte chunks XOR-swizzled by
+//    the row, which makes the K operand reads (16 bytes of one key row per
+//    lane) and the transposing V reads (ds_read_b64_tr_b16, eight keys of
+//    one dimension per lane for the V^T operand) conflict-free. R rows go
+//    straight from L2 into the A operand, one tile ahead.
+//  * The content MFMAs run first (their operands are in LDS when the tile
+//    starts), while the band's results drain and its LDS round trip
+//    completes; the shifted position term is then added to the scores.
 //  * Masking: band row u of a tile is one distance for every query of the
 //    wave, and the rows of negative distance (key after query) are exactly
 //    the rows past a wave-uniform limit; on tiles that cross the diagonal
