@@ -312,6 +312,14 @@ TXL_API size_t txl_rel_attn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t L,
 TXL_API txl_status txl_rel_attn_bwd(const txl_rel_attn_args *a, const txl_rel_attn_grads *gr,
                                     void *workspace, size_t ws_bytes, hipStream_t stream) {
   clear_error();
+  return rel_attn_bwd_impl(a, gr, nullptr, workspace, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+txl_status txl::rel_attn_bwd_impl(const txl_rel_attn_args *a, const txl_rel_attn_grads *gr,
+                                  const BwdRows *rows, void *workspace, size_t ws_bytes,
+                                  hipStream_t stream) {
   AttnParams p;
   bool nothing;
   txl_status st = attn_params(a, &p, &nothing);
@@ -321,8 +329,18 @@ TXL_API txl_status txl_rel_attn_bwd(const txl_rel_attn_args *a, const txl_rel_at
     return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: gradients are built for bf16 inputs only");
   if (nothing) return TXL_OK;
   if (!a->lse) return fail(TXL_ERR_INVALID_ARG, "rel_attn_bwd: the forward's lse is required");
-  if (!gr->dout || !gr->dq || !gr->dk || !gr->dv || !gr->dr || !gr->du || !gr->dvb)
+  const BwdRows rw = rows ? *rows : BwdRows{};
+  if (!gr->dout || !(gr->dq || rw.dq) || !(gr->dk || rw.dk) || !(gr->dv || rw.dv) || !(gr->dr || rw.dr) ||
+      !gr->du || !gr->dvb)
     return fail(TXL_ERR_INVALID_ARG, "rel_attn_bwd: null gradient pointer");
+  {
+    const __bf16 *rp[] = {rw.dq, rw.dk, rw.dv, rw.dk_seg, rw.dv_seg, rw.dr};
+    const int64_t rl[] = {rw.dq_ld, rw.kv_ld, rw.kv_ld, rw.seg_ld, rw.seg_ld, rw.dr_ld};
+    const int64_t hd = static_cast<int64_t>(a->H) * a->d_h;
+    for (int i = 0; i < 6; ++i)
+      if (rp[i] && ((reinterpret_cast<uintptr_t>(rp[i]) & 7u) || rl[i] < hd || rl[i] % 4))
+        return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: bf16 row output %d misaligned or rows too short", i);
+  }
   if (!aligned16(gr->dout))
     return fail(TXL_ERR_UNSUPPORTED, "rel_attn_bwd: dout not 16-byte aligned");
   const int64_t dstr[] = {gr->do_sb, gr->do_sh, gr->do_sl};
@@ -356,8 +374,11 @@ TXL_API txl_status txl_rel_attn_bwd(const txl_rel_attn_args *a, const txl_rel_at
   g.part_u = reinterpret_cast<float *>(base + w.pu);
   g.part_v = reinterpret_cast<float *>(base + w.pv);
   g.part_r = reinterpret_cast<float *>(base + w.pr);
+  g.rows = rw;
   return launch_rel_attn_bwd(p, g, stream);
 }
+
+extern "C" {
 
 // ---------------------------------------------------------------------------
 static txl_status check_rings(const txl_mem *mems, int32_t n_mems, const char *who) {

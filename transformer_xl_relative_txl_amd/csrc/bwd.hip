@@ -1,9 +1,7 @@
-// Kernels of the stack's segment gradients (the layer GEMMs themselves run on
-// the GEMM of gemm.hip, which reads K-major operands directly): the weight
-// transposes of the input-gradient product over [dQ | dK | dV], the
-// [memory; segment] rows as one matrix, the merge of the attention's
-// per-head gradients into rows, deterministic sums of split-K partials, the
-// LayerNorm backward and the embedding scatter.
+// Kernels of the stack's segment gradients (the products run on gemm.hip and
+// dw_gemm.hip): the batched weight transposes of the input-gradient
+// products, the [memory; segment] rows as one matrix, deterministic sums of
+// split-K partials, the LayerNorm backward and the embedding scatter.
 //
 // [P1] "Transformer-XL" notes, "Why Stop Gradient" and "Training Loop
 // Sketch"; [P2] "019 Transformer-XL", section "stop-gradient到底切断哪里":
@@ -90,33 +88,6 @@ __global__ __launch_bounds__(256) void gather_ext_kernel(const u32x4 *__restrict
     if (j >= M - vl) v = mem[(static_cast<int64_t>(b) * M + j) * cpr + c];
   }
   y[e] = v;
-}
-
-// Per-head fp32 gradients g [B, H, T, 64] (T keys or queries per batch row)
-// merged over heads into bf16 rows: y_all[(b*T + j)*ld_all + h*64 + e] for
-// every j when y_all is set, and y_last[(b*L + j - (T-L))*ld_last + col0 +
-// h*64 + e] for the last L entries of every batch row when y_last is set.
-// Four elements a thread.
-__global__ __launch_bounds__(256) void head_grad_merge_kernel(const float *__restrict__ g, int B,
-                                                              int H, int T, __bf16 *__restrict__ y_all,
-                                                              int64_t ld_all, __bf16 *__restrict__ y_last,
-                                                              int L, int64_t ld_last, int col0) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // one per 4 elements
-  const int64_t total = static_cast<int64_t>(B) * H * T * 16;
-  if (e >= total) return;
-  const int q = static_cast<int>(e & 15);
-  const int64_t row = e >> 4;                      // (b, h, j)
-  const int j = static_cast<int>(row % T);
-  const int64_t bh = row / T;
-  const int h = static_cast<int>(bh % H), b = static_cast<int>(bh / H);
-  const f32x4 v = reinterpret_cast<const f32x4 *>(g)[e];
-  bf16x4 o;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) o[k] = static_cast<__bf16>(v[k]);
-  const int col = h * 64 + 4 * q;
-  if (y_all) *reinterpret_cast<bf16x4 *>(y_all + (static_cast<int64_t>(b) * T + j) * ld_all + col) = o;
-  if (y_last && j >= T - L)
-    *reinterpret_cast<bf16x4 *>(y_last + (static_cast<int64_t>(b) * L + (j - (T - L))) * ld_last + col0 + col) = o;
 }
 
 // out[i] = sum_{s < S} part[s * stride + i], s ascending (4 floats a thread)
@@ -349,17 +320,6 @@ txl_status launch_gather_ext(const void *mem, const int32_t *valid, const void *
                      static_cast<const u32x4 *>(mem), valid, static_cast<const u32x4 *>(seg), B, M, L, cpr,
                      static_cast<u32x4 *>(y));
   return check_launch("gather_ext_kernel");
-}
-
-txl_status launch_head_grad_merge(const float *g, int B, int H, int T, void *y_all, int64_t ld_all,
-                                  void *y_last, int L, int64_t ld_last, int col0, hipStream_t s) {
-  const int64_t total = static_cast<int64_t>(B) * H * T * 16;
-  if (total == 0) return TXL_OK;
-  (void)hipGetLastError();
-  hipLaunchKernelGGL(head_grad_merge_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s,
-                     g, B, H, T, static_cast<__bf16 *>(y_all), ld_all, static_cast<__bf16 *>(y_last), L,
-                     ld_last, col0);
-  return check_launch("head_grad_merge_kernel");
 }
 
 txl_status launch_reduce_parts(const float *part, int S, int64_t stride, int64_t n, float *out,

@@ -148,7 +148,29 @@ constexpr size_t kKvLdsTile = size_t(QT) * TS * 2;          // one [32][72] bf16
 constexpr size_t kKvLdsTr = size_t(DH) * TT * 2;            // one [64][40] bf16 tile
 constexpr size_t kKvLdsBand = size_t(NW) * QT * BS * 4;
 constexpr size_t kKvLdsTotal = 3 * kKvLdsTile + 2 * kKvLdsTr + 2 * QT * 4 + kKvLdsBand;
-static_assert(size_t(KW) * (DH + 4) * 4 <= size_t(QT) * BS * 4, "dK / dV staging must fit a wave's band");
+
+// Dims 4 c4 .. 4 c4 + 3 of key j's dK and dV (batch row b, head h): fp32
+// per head where dkp / dvp are set, and the bf16 rows of g.rows.
+__device__ inline void store_kv_grad(const BwdParams &g, float *dkp, float *dvp, int b, int h, int ML,
+                                     int M, int L, int j, int c4, f32x4 dk, f32x4 dv) {
+  if (dkp) *reinterpret_cast<f32x4 *>(dkp + static_cast<int64_t>(j) * DH + 4 * c4) = dk;
+  if (dvp) *reinterpret_cast<f32x4 *>(dvp + static_cast<int64_t>(j) * DH + 4 * c4) = dv;
+  bf16x4 kb4, vb4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    kb4[e] = static_cast<__bf16>(dk[e]);
+    vb4[e] = static_cast<__bf16>(dv[e]);
+  }
+  const int col = h * DH + 4 * c4;
+  const int64_t row = static_cast<int64_t>(b) * ML + j;
+  if (g.rows.dk) *reinterpret_cast<bf16x4 *>(g.rows.dk + row * g.rows.kv_ld + col) = kb4;
+  if (g.rows.dv) *reinterpret_cast<bf16x4 *>(g.rows.dv + row * g.rows.kv_ld + col) = vb4;
+  if (j >= M) {
+    const int64_t srow = static_cast<int64_t>(b) * L + (j - M);
+    if (g.rows.dk_seg) *reinterpret_cast<bf16x4 *>(g.rows.dk_seg + srow * g.rows.seg_ld + col) = kb4;
+    if (g.rows.dv_seg) *reinterpret_cast<bf16x4 *>(g.rows.dv_seg + srow * g.rows.seg_ld + col) = vb4;
+  }
+}
 
 __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams g, int n_kb) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -181,8 +203,8 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams 
   const __bf16 *vbp = static_cast<const __bf16 *>(p.vb) + h * DH;
   const __bf16 *dop = g.dout + b * g.do_sb + h * g.do_sh;
   const int64_t row_bh = static_cast<int64_t>(bh) * L;
-  float *dkp = g.dk + static_cast<int64_t>(bh) * ML * DH;
-  float *dvp = g.dv + static_cast<int64_t>(bh) * ML * DH;
+  float *dkp = g.dk ? g.dk + static_cast<int64_t>(bh) * ML * DH : nullptr;
+  float *dvp = g.dv ? g.dv + static_cast<int64_t>(bh) * ML * DH : nullptr;
   float *band = sband + wave * (QT * BS);
 
   // keys below the first valid one, or past the last, take no gradient; a
@@ -193,8 +215,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams 
       const int kk = e / (DH / 4), c4 = e - kk * (DH / 4);
       if (jb + kk < ML) {
         const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-        *reinterpret_cast<f32x4 *>(dkp + static_cast<int64_t>(jb + kk) * DH + 4 * c4) = z;
-        *reinterpret_cast<f32x4 *>(dvp + static_cast<int64_t>(jb + kk) * DH + 4 * c4) = z;
+        store_kv_grad(g, dkp, dvp, b, h, ML, M, L, jb + kk, c4, z, z);
       }
     }
     return;
@@ -392,8 +413,12 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams 
     __syncthreads();
   }
 
-  // ---- dK, dV rows through LDS (this wave's band area), 16-byte stores ----
+  // ---- dK, dV rows through LDS (this wave's band area, one after the
+  // other), four dims of a key a lane, then stored together ----
   float *st = band;   // [32 keys][64 + 4 dims]
+  static_assert(size_t(KW) * (DH + 4) * 4 <= size_t(QT) * BS * 4, "dK / dV staging must fit a wave's band");
+  constexpr int NIT = KW * DH / 4 / 64;
+  f32x4 kv4[2][NIT];
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -404,16 +429,19 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams 
         st[r * (DH + 4) + dh] = pass == 0 ? dk_acc[db][x] : dv_acc[db][x];
       }
     wave_lds_sync();
-    float *dst = pass == 0 ? dkp : dvp;
 #pragma unroll
-    for (int it = 0; it < KW * DH / 4 / 64; ++it) {
+    for (int it = 0; it < NIT; ++it) {
       const int e = lane + 64 * it;
       const int kk = e / (DH / 4), c4 = e - kk * (DH / 4);
-      if (jw + kk < ML)
-        *reinterpret_cast<f32x4 *>(dst + static_cast<int64_t>(jw + kk) * DH + 4 * c4) =
-            *reinterpret_cast<const f32x4 *>(st + kk * (DH + 4) + 4 * c4);
+      kv4[pass][it] = *reinterpret_cast<const f32x4 *>(st + kk * (DH + 4) + 4 * c4);
     }
     wave_lds_sync();
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int e = lane + 64 * it;
+    const int kk = e / (DH / 4), c4 = e - kk * (DH / 4);
+    if (jw + kk < ML) store_kv_grad(g, dkp, dvp, b, h, ML, M, L, jw + kk, c4, kv4[0][it], kv4[1][it]);
   }
   (void)n_kb;
 }
@@ -446,6 +474,7 @@ struct BgParams {
   int rows, n_phase;
   BgPhase ph[2];
   float *c;
+  __bf16 *c16;      // bf16 output instead of c when set (same strides)
   int64_t ldc, c_s1, c_s2;
   int Z2;
   const int32_t *valid;
@@ -633,11 +662,16 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
     }
   }
 
-  float *cp = q.c + z1 * q.c_s1 + z2 * q.c_s2;
+  const int64_t co = z1 * q.c_s1 + z2 * q.c_s2;
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
     const int m = m0 + wm * 32 + 8 * (x >> 2) + 4 * hh + (x & 3);
-    if (m < q.rows) cp[static_cast<int64_t>(m) * q.ldc + n] = acc[x];
+    if (m < q.rows) {
+      if (q.c16)
+        q.c16[co + static_cast<int64_t>(m) * q.ldc + n] = static_cast<__bf16>(acc[x]);
+      else
+        q.c[co + static_cast<int64_t>(m) * q.ldc + n] = acc[x];
+    }
   }
 }
 
@@ -647,7 +681,8 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
 // per (part, head): 4 groups of 64 lanes split the items, then combine.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *part_r, float *dr, int64_t n_r,
                                                          const float *part_u, const float *part_v,
-                                                         float *du, float *dvb, int B, int H, int n_mt) {
+                                                         float *du, float *dvb, int B, int H, int n_mt,
+                                                         __bf16 *dr_rows, int64_t dr_ld, int ml) {
   __shared__ float red[4][DH];
   const int tid = threadIdx.x;
   if (static_cast<int>(blockIdx.x) < 2 * H) {
@@ -681,7 +716,13 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *part_r, fl
   float s = 0.0f;
 #pragma unroll
   for (int x = 0; x < 8; ++x) s += acc[x];
-  dr[e] = s;
+  if (dr) dr[e] = s;
+  if (dr_rows) {  // e = (h (M+L) + t) 64 + n  ->  row t, column h 64 + n
+    const int64_t ht = e / DH;
+    const int n = static_cast<int>(e - ht * DH);
+    const int hh2 = static_cast<int>(ht / ml), t = static_cast<int>(ht - static_cast<int64_t>(hh2) * ml);
+    dr_rows[static_cast<int64_t>(t) * dr_ld + hh2 * DH + n] = static_cast<__bf16>(s);
+  }
 }
 
 }  // namespace
@@ -743,7 +784,11 @@ txl_status launch_rel_attn_bwd(const AttnParams &p, const BwdParams &g, hipStrea
   q.ph[1].a = g.pm; q.ph[1].lda = g.ldp; q.ph[1].a_s1 = H * pz; q.ph[1].a_s2 = pz;
   q.ph[1].b = static_cast<const __bf16 *>(p.r); q.ph[1].ldb = p.r_sl; q.ph[1].b_s1 = 0;
   q.ph[1].b_s2 = p.r_sh; q.ph[1].colsum = g.part_v;
-  q.c = g.dq; q.ldc = DH; q.c_s1 = static_cast<int64_t>(H) * L * DH; q.c_s2 = static_cast<int64_t>(L) * DH;
+  if (g.rows.dq) {   // bf16 rows b*L + i, column h*64 + e
+    q.c16 = g.rows.dq; q.ldc = g.rows.dq_ld; q.c_s1 = static_cast<int64_t>(L) * g.rows.dq_ld; q.c_s2 = DH;
+  } else {
+    q.c = g.dq; q.ldc = DH; q.c_s1 = static_cast<int64_t>(H) * L * DH; q.c_s2 = static_cast<int64_t>(L) * DH;
+  }
   q.Z2 = H;
   if ((st = run(q, B * H)) != TXL_OK) return st;
   // dR per batch row = sum over queries of g (q + v), by distance; summed over
@@ -759,7 +804,8 @@ txl_status launch_rel_attn_bwd(const AttnParams &p, const BwdParams &g, hipStrea
   if ((st = run(q, B * H)) != TXL_OK) return st;
   const int64_t n_r = static_cast<int64_t>(H) * ml * DH;
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>(2 * H + (n_r + 255) / 256)), dim3(256), 0, s,
-                     g.part_r, g.dr, n_r, g.part_u, g.part_v, g.du, g.dvb, B, H, n_mt_q);
+                     g.part_r, g.dr, n_r, g.part_u, g.part_v, g.du, g.dvb, B, H, n_mt_q, g.rows.dr,
+                     g.rows.dr_ld, ml);
   return check_launch("bwd_reduce_kernel");
 }
 

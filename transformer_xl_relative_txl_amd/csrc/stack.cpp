@@ -294,8 +294,8 @@ txl_status dw_gemm(const __bf16 *x, int64_t ldx, int rows, const __bf16 *y, int6
 // Workspace of the segment backward (one layer's intermediates, reused from
 // the top layer down).
 struct BwdWs {
-  size_t g0, g1, dx2, dx2b, dh1, dx1, dx1b, dfpre, dout, dq, dk, dv, dr, attn, attn_bytes, ym, ext,
-      acat, wcatT, wT, st, pg, pb, part, total;
+  size_t g0, g1, dx2, dx2b, dh1, dx1, dx1b, dfpre, dout, kvg, drb, attn, attn_bytes, ext, acat, wcatT,
+      wT, st, pg, pb, part, total;
 };
 
 BwdWs bwd_ws(const txl_stack_config &c) {
@@ -321,13 +321,10 @@ BwdWs bwd_ws(const txl_stack_config &c) {
   w.dx1b = take(rd * 2);
   w.dfpre = take(rows * c.d_ff * 2);
   w.dout = take(rows * hd * 2);
-  w.dq = take(rows * hd * 4);
-  w.dk = take(krows * hd * 4);
-  w.dv = take(krows * hd * 4);
-  w.dr = take(ml * hd * 4);
+  w.kvg = take(krows * 2 * hd * 2);
+  w.drb = take(ml * hd * 2);
   w.attn_bytes = txl_rel_attn_bwd_workspace_bytes(c.B, c.n_head, c.L, c.M);
   w.attn = take(w.attn_bytes);
-  w.ym = take(std::max(krows, ml) * hd * 2);
   w.ext = take(krows * c.d * 2);
   w.acat = take(rows * 3 * hd * 2);
   w.wcatT = take(static_cast<size_t>(c.d) * 3 * hd * 2);
@@ -581,7 +578,8 @@ TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t 
   float *part = f32(w.part);
   int rpb;
   const int ln_blocks = ln_backward_blocks(R, &rpb);
-  __bf16 *wcatT = b16(w.wcatT), *acat = b16(w.acat), *st_rows = b16(w.st), *ym = b16(w.ym);
+  __bf16 *wcatT = b16(w.wcatT), *acat = b16(w.acat), *st_rows = b16(w.st);
+  __bf16 *kvg = b16(w.kvg), *drb = b16(w.drb);
   __bf16 *ext = b16(w.ext), *wT = b16(w.wT);
 
   // S [M+L, d]: the sinusoid rows of distances M+L-1 .. 0, shared by every layer
@@ -672,37 +670,37 @@ TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t 
     a.o_sl = HD;
     a.lse = tl.lse;
     a.out_f32 = tl.o32;
+    // the gradients arrive as bf16 rows: dQ in acat's first HD columns, dK
+    // and dV of every key in kvg ([B*(M+L), 2 HD]) and of the segment's keys
+    // in acat's other columns, dR in drb [M+L, HD]
     txl_rel_attn_grads ag = {};
     ag.dout = b16(w.dout);
     ag.do_sb = static_cast<int64_t>(c.L) * HD;
     ag.do_sh = c.d_h;
     ag.do_sl = HD;
-    ag.dq = f32(w.dq);
-    ag.dk = f32(w.dk);
-    ag.dv = f32(w.dv);
-    ag.dr = f32(w.dr);
     ag.du = g.u;
     ag.dvb = g.vb;
-    if ((s = txl_rel_attn_bwd(&a, &ag, base + w.attn, w.attn_bytes, stream)) != TXL_OK) return s;
-    // dW^Q = dQ^T H, dQ merged into acat's first HD columns
-    if ((s = launch_head_grad_merge(f32(w.dq), c.B, c.n_head, c.L, nullptr, 0, acat, c.L, 3 * HD, 0,
-                                    stream)) != TXL_OK)
-      return s;
+    BwdRows rows = {};
+    rows.dq = acat;
+    rows.dq_ld = 3 * HD;
+    rows.dk = kvg;
+    rows.dv = kvg + HD;
+    rows.kv_ld = 2 * HD;
+    rows.dk_seg = acat + HD;
+    rows.dv_seg = acat + 2 * HD;
+    rows.seg_ld = 3 * HD;
+    rows.dr = drb;
+    rows.dr_ld = HD;
+    if ((s = rel_attn_bwd_impl(&a, &ag, &rows, base + w.attn, w.attn_bytes, stream)) != TXL_OK) return s;
+    // dW^Q = dQ^T H
     if ((s = dw_gemm(acat, 3 * HD, HD, tl.hin, c.d, c.d, R, g.wq, part, stream)) != TXL_OK) return s;
-    // dW^K = dK^T [mem; H], dW^V = dV^T [mem; H] (slots a row does not hold read as 0);
-    // the segment rows of dK, dV also go to acat for the input gradient
+    // dW^K = dK^T [mem; H], dW^V = dV^T [mem; H] (slots a row does not hold read as 0)
     if ((s = launch_gather_ext(tl.mem, tl.valid, tl.hin, c.B, c.M, c.L, c.d, ext, stream)) != TXL_OK)
       return s;
-    for (int kv = 0; kv < 2; ++kv) {
-      if ((s = launch_head_grad_merge(f32(kv ? w.dv : w.dk), c.B, c.n_head, ML, ym, HD, acat, c.L,
-                                      3 * HD, (1 + kv) * HD, stream)) != TXL_OK)
-        return s;
-      if ((s = dw_gemm(ym, HD, HD, ext, c.d, c.d, KR, kv ? g.wv : g.wk, part, stream)) != TXL_OK) return s;
-    }
+    if ((s = dw_gemm(kvg, 2 * HD, HD, ext, c.d, c.d, KR, g.wk, part, stream)) != TXL_OK) return s;
+    if ((s = dw_gemm(kvg + HD, 2 * HD, HD, ext, c.d, c.d, KR, g.wv, part, stream)) != TXL_OK) return s;
     // dW_R = dR^T S (R = S W_R^T for distances M+L-1 .. 0)
-    if ((s = launch_head_grad_merge(f32(w.dr), 1, c.n_head, ML, ym, HD, nullptr, 0, 0, 0, stream)) != TXL_OK)
-      return s;
-    if ((s = dw_gemm(ym, HD, HD, st_rows, c.d, c.d, ML, g.wr, part, stream)) != TXL_OK) return s;
+    if ((s = dw_gemm(drb, HD, HD, st_rows, c.d, c.d, ML, g.wr, part, stream)) != TXL_OK) return s;
     // dH^(n-1) = dX1 + [dQ | dK_seg | dV_seg] [W^Q; W^K; W^V]
     GemmParams pi = dense(acat, 3 * HD, R, c.d, 3 * HD, wcatT, gout, c.d);
     pi.res32 = dx1;

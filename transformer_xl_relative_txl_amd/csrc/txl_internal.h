@@ -90,6 +90,20 @@ txl_status noalloc_counters(int B, hipStream_t s, uint32_t **out);
 // gradients (bf16 inputs): p holds the forward's arguments (out = the
 // forward's output); g the incoming gradient, the forward's lse, the fp32
 // gradient outputs (contiguous) and the workspace pieces
+// The attention gradients as bf16 rows for the stack's products (each null
+// pointer: not written): column h*64 + e of row b*L + i (dq), b*(M+L) + j
+// (dk, dv: every key), b*L + j - M (dk_seg, dv_seg: the segment's keys) or
+// t (dr: distance row t, summed over batch rows).
+struct BwdRows {
+  __bf16 *dq;
+  int64_t dq_ld;
+  __bf16 *dk, *dv;
+  int64_t kv_ld;
+  __bf16 *dk_seg, *dv_seg;
+  int64_t seg_ld;
+  __bf16 *dr;
+  int64_t dr_ld;
+};
 struct BwdParams {
   const __bf16 *dout;
   int64_t do_sb, do_sh, do_sl;
@@ -102,10 +116,15 @@ struct BwdParams {
   int64_t ldp;
   float *part_u, *part_v; // [B*H][ceil(L/64)][64] column sums of dq's two parts
   float *part_r;          // [B][H][M+L][64] dR of each batch row
+  BwdRows rows;           // bf16 row outputs (the fp32 dq, dk, dv, dr may then be null)
 };
 // row length of pm / gm for M memory slots and L queries
 size_t rel_attn_bwd_ldp(int M, int L);
 txl_status launch_rel_attn_bwd(const AttnParams &p, const BwdParams &g, hipStream_t s);
+// txl_rel_attn_bwd with the bf16 row outputs of `rows` (null: none); where a
+// row output is given, the matching fp32 output of `gr` may be null
+txl_status rel_attn_bwd_impl(const txl_rel_attn_args *a, const txl_rel_attn_grads *gr,
+                             const BwdRows *rows, void *workspace, size_t ws_bytes, hipStream_t stream);
 
 // ---- memory ring ---------------------------------------------------------
 constexpr int kMaxRingsPerLaunch = 32;
@@ -155,10 +174,6 @@ txl_status launch_transpose_batch(const TransposeJob *jobs, int n, hipStream_t s
 // y [B*(M+L), d] = [memory (logical order, unheld slots zero); segment] per batch row
 txl_status launch_gather_ext(const void *mem, const int32_t *valid, const void *seg, int B, int M, int L,
                              int d, void *y, hipStream_t s);
-// g [B, H, T, 64] fp32 -> bf16 rows merged over heads: y_all [B*T, ld_all]
-// (all entries) and / or y_last rows b*L + j - (T-L), columns col0.. (the last L)
-txl_status launch_head_grad_merge(const float *g, int B, int H, int T, void *y_all, int64_t ld_all,
-                                  void *y_last, int L, int64_t ld_last, int col0, hipStream_t s);
 // out[i] = sum over s < S of part[s*stride + i], in a fixed order (n a multiple
 // of 4, 16-byte aligned)
 txl_status launch_reduce_parts(const float *part, int S, int64_t stride, int64_t n, float *out,
