@@ -386,13 +386,23 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
           *reinterpret_cast<f32x4 *>(&sband[band0 + f]) = ninf;
       }
       wave_lds_sync();
+      // all 16 two-dword diagonal reads are issued before the first add (left
+      // to itself the compiler issued them two or three at a time, each
+      // batch waiting for the LDS round trip of the one before)
+      float dg[2][16];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int c = 8 * (x >> 2) + (x & 3);
-          s_acc[kb][x] += sband[band_r + (c + 32 * kb) * US];
+          dg[kb][x] = sband[band_r + (c + 32 * kb) * US];
         }
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);  // then the VALU adds
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) s_acc[kb][x] += dg[kb][x];
 
       // ---- online softmax in base 2 ----
       // p = 2^(s - m) with the running max m kept while every p of the tile
