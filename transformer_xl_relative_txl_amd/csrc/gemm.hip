@@ -143,21 +143,32 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
   }
   if (p.gather && !__syncthreads_or(any_valid)) return;  // all rows are empty memory slots
 
+  // Every load is issued unconditionally, so the compiler counts the loads
+  // in flight exactly and a slab's LDS store waits only for its own loads
+  // (loads behind branches had made it wait for all of them, the prefetch
+  // included): a row without data reads a W row instead and is zeroed when
+  // stored, and past the last slab the last one is read again, unused.
+  uint32_t a_ok = 0;
+#pragma unroll
+  for (int j = 0; j < A_CH; ++j) {
+    if (arow[j]) a_ok |= 1u << j;
+    else arow[j] = wrow[0];
+  }
+
   // two register sets: slab ks+2 is loaded while slab ks is multiplied and
   // slab ks+1 waits in the other set for its LDS buffer
   u32x4 av[2][A_CH], wv[2][B_CH];
   auto load = [&](int set, int k0) {
 #pragma unroll
-    for (int j = 0; j < A_CH; ++j)
-      av[set][j] = arow[j] ? *reinterpret_cast<const u32x4 *>(arow[j] + k0 + 8 * kc)
-                           : u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < A_CH; ++j) av[set][j] = *reinterpret_cast<const u32x4 *>(arow[j] + k0 + 8 * kc);
 #pragma unroll
     for (int j = 0; j < B_CH; ++j) wv[set][j] = *reinterpret_cast<const u32x4 *>(wrow[j] + k0 + 8 * kc);
   };
   auto store = [&](int set, int buf) {
 #pragma unroll
     for (int j = 0; j < A_CH; ++j)
-      *reinterpret_cast<u32x4 *>(&sa[buf][(tid / CPR + RPP * j) * AS + 8 * kc]) = av[set][j];
+      *reinterpret_cast<u32x4 *>(&sa[buf][(tid / CPR + RPP * j) * AS + 8 * kc]) =
+          (a_ok >> j) & 1u ? av[set][j] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < B_CH; ++j)
       *reinterpret_cast<u32x4 *>(&sb[buf][(tid / CPR + RPP * j) * AS + 8 * kc]) = wv[set][j];
@@ -194,17 +205,18 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
   };
   // slab ks lives in LDS buffer (ks - ks0) & 1 and register set (ks - ks0) & 1;
   // a buffer is refilled only after the barrier that ends its last readers
+  const int ks_last = ks1 - 1;  // ks1 > ks0: every split holds a slab
   load(0, ks0 * BKS);
-  if (ks0 + 1 < ks1) load(1, (ks0 + 1) * BKS);
+  load(1, min(ks0 + 1, ks_last) * BKS);
   store(0, 0);
   __syncthreads();
   for (int ks = ks0; ks < ks1; ks += 2) {
-    if (ks + 2 < ks1) load(0, (ks + 2) * BKS);
+    load(0, min(ks + 2, ks_last) * BKS);
     compute(0);
     if (ks + 1 < ks1) store(1, 1);
     __syncthreads();
     if (ks + 1 >= ks1) break;
-    if (ks + 3 < ks1) load(1, (ks + 3) * BKS);
+    load(1, min(ks + 3, ks_last) * BKS);
     compute(1);
     if (ks + 2 < ks1) store(0, 0);
     __syncthreads();
