@@ -147,7 +147,7 @@ constexpr int BS = 2 * QT + 4;    // band row stride (floats): [query][u], u < 6
 constexpr size_t kKvLdsTile = size_t(QT) * TS * 2;          // one [32][72] bf16 tile
 constexpr size_t kKvLdsTr = size_t(DH) * TT * 2;            // one [64][40] bf16 tile
 constexpr size_t kKvLdsBand = size_t(NW) * QT * BS * 4;
-constexpr size_t kKvLdsTotal = 3 * kKvLdsTile + 2 * kKvLdsTr + 2 * QT * 4 + kKvLdsBand;
+constexpr size_t kKvLdsTotal = 3 * kKvLdsTile + 2 * kKvLdsTr + 2 * QT * 4 + kKvLdsBand + 2 * DH * 2;
 
 // Dims 4 c4 .. 4 c4 + 3 of key j's dK and dV (batch row b, head h): fp32
 // per head where dkp / dvp are set, and the bf16 rows of g.rows.
@@ -182,6 +182,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams 
   float *sLse = reinterpret_cast<float *>(sDoT + DH * TT);
   float *sD = sLse + QT;
   float *sband = sD + QT;
+  __bf16 *sUV = reinterpret_cast<__bf16 *>(sband + NW * QT * BS);  // u [64] then v [64]
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const int BH = p.B * p.H;
@@ -235,20 +236,35 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams 
   // query-tile staging: thread -> (query row, 8-dim chunk)
   const int st_row = tid >> 3, st_c = (tid & 7) * 8;
   const float c2 = p.scale * 1.4426950408889634f;
+  // The next query tile's loads are issued unconditionally (rows past L
+  // read row L-1) and nothing is computed from them before stage(): with
+  // the loads behind branches, or scaled right after loading, the compiler
+  // waited for them (and so for every load before them) at once.
   bf16x8 nq, ndo;
   float nlse = 0.0f, nd = 0.0f;
+  bool nq_ok = false, nl_ok = false;
   auto fetch = [&](int i0) {
     const int i = i0 + st_row;
-    nq = i < L ? load8(qp + static_cast<int64_t>(i) * p.q_sl + st_c) : zero8();
-    ndo = i < L ? load8(dop + static_cast<int64_t>(i) * g.do_sl + st_c) : zero8();
-    if (tid < QT) {
-      const int ii = i0 + tid;
-      nlse = ii < L ? g.lse[row_bh + ii] * 1.4426950408889634f : 0.0f;
-      nd = ii < L ? g.dd[row_bh + ii] * p.scale : 0.0f;   // scale * D
-    }
+    nq_ok = i < L;
+    const int64_t ic = nq_ok ? i : L - 1;
+    nq = load8(qp + ic * p.q_sl + st_c);
+    ndo = load8(dop + ic * g.do_sl + st_c);
+    const int ii = i0 + (tid & (QT - 1));
+    nl_ok = ii < L;
+    const int64_t iic = nl_ok ? ii : L - 1;
+    nlse = g.lse[row_bh + iic];
+    nd = g.dd[row_bh + iic];
   };
+  // u and v of the head, read by every stage, sit in LDS (written before
+  // the first stage's barrier)
+  if (tid < 16) *reinterpret_cast<bf16x8 *>(sUV + 8 * tid) = load8((tid < 8 ? up : vbp) + 8 * (tid & 7));
   auto stage = [&]() {
-    const bf16x8 u8 = load8(up + st_c), v8 = load8(vbp + st_c);
+    const bf16x8 u8 = *reinterpret_cast<const bf16x8 *>(sUV + st_c);
+    const bf16x8 v8 = *reinterpret_cast<const bf16x8 *>(sUV + DH + st_c);
+    if (!nq_ok) {
+      nq = zero8();
+      ndo = zero8();
+    }
     bf16x8 a, bq, qu;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -267,8 +283,8 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams 
       sDoT[(st_c + e) * TT + st_row] = ndo[e];
     }
     if (tid < QT) {
-      sLse[tid] = nlse;
-      sD[tid] = nd;
+      sLse[tid] = nl_ok ? nlse * 1.4426950408889634f : 0.0f;
+      sD[tid] = nl_ok ? nd * p.scale : 0.0f;   // scale * D
     }
   };
 
@@ -306,7 +322,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams 
   __syncthreads();
   const float scale = p.scale;
   for (int i0 = q_first; i0 < L; i0 += QT) {
-    if (i0 + QT < L) fetch(i0 + QT);
+    fetch(i0 + QT);  // past the last tile: loaded, never staged
 
     // ---- the band Q'' R^T, one 32-column block at a time, to LDS as
     // band[q][u] (u = t - t0); the next tile's band starts 32 rows lower, so
