@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
   // in flight exactly and a slab's LDS store waits only for its own loads
   // (loads behind branches had made it wait for all of them, the prefetch
   // included): a row without data reads a W row instead and is zeroed when
-  // stored, and past the last slab the last one is read again, unused.
+  // stored.
   uint32_t a_ok = 0;
 #pragma unroll
   for (int j = 0; j < A_CH; ++j) {
@@ -205,22 +205,42 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
   };
   // slab ks lives in LDS buffer (ks - ks0) & 1 and register set (ks - ks0) & 1;
   // a buffer is refilled only after the barrier that ends its last readers
-  const int ks_last = ks1 - 1;  // ks1 > ks0: every split holds a slab
+  // The loop runs while both of its loads are in range; the last one to
+  // three slabs are peeled off with at most one more load.
   load(0, ks0 * BKS);
-  load(1, min(ks0 + 1, ks_last) * BKS);
+  load(1, min(ks0 + 1, ks1 - 1) * BKS);  // ks1 > ks0: every split holds a slab
   store(0, 0);
   __syncthreads();
-  for (int ks = ks0; ks < ks1; ks += 2) {
-    load(0, min(ks + 2, ks_last) * BKS);
+  int ks = ks0;
+  for (; ks + 3 < ks1; ks += 2) {
+    load(0, (ks + 2) * BKS);
     compute(0);
-    if (ks + 1 < ks1) store(1, 1);
+    store(1, 1);
     __syncthreads();
-    if (ks + 1 >= ks1) break;
-    load(1, min(ks + 3, ks_last) * BKS);
+    load(1, (ks + 3) * BKS);
     compute(1);
-    if (ks + 2 < ks1) store(0, 0);
+    store(0, 0);
     __syncthreads();
   }
+  const int left = ks1 - ks;  // 1, 2 or 3 slabs: ks in buffer 0, ks + 1 in set 1
+  if (left == 3) {
+    load(0, (ks + 2) * BKS);
+    compute(0);
+    store(1, 1);
+    __syncthreads();
+    compute(1);
+    store(0, 0);
+    __syncthreads();
+    compute(0);
+  } else if (left == 2) {
+    compute(0);
+    store(1, 1);
+    __syncthreads();
+    compute(1);
+  } else {
+    compute(0);
+  }
+  __syncthreads();  // the epilogues reuse the LDS buffers
 
   // epilogue: register 4a+c of block (i, jn) holds
   // C[wm*BM/2 + 32i + 8a + 4g + c][wn*BN/2 + 32jn + r]
