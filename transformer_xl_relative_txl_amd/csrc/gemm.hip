@@ -555,17 +555,20 @@ void launch_epi(const GemmParams &p, hipStream_t s) {
     return;
   }
   // by measurement on the stack's shapes: 128x128 tiles when they alone give
-  // about two tiles per CU, except under the GELU epilogue (its per-output
-  // cost favours more, smaller tiles); split-K products 128x64 when the splits
-  // fill the chip; otherwise 64x64
+  // about two tiles per CU; split-K products 128x64 when the splits fill the
+  // chip; the GELU product without the pre-activation store 128x128, else
+  // 128x64, when they fill the chip (with the store, whose per-element
+  // writes favour more, smaller tiles, 64x64); otherwise 64x64
   auto tiles = [&](int bm, int bn) {
     return static_cast<int64_t>((p.rows + bm - 1) / bm) * (p.N / bn) *
            (E == kEpiPartialF32 ? p.k_splits : 1);
   };
   const int64_t want = 512;
-  if (E != kEpiGeluBf16 && E != kEpiPartialF32 && p.N % 128 == 0 && tiles(128, 128) >= want)
+  const bool gelu_plain = E == kEpiGeluBf16 && !p.pre_out;
+  if ((E != kEpiGeluBf16 || gelu_plain) && E != kEpiPartialF32 && p.N % 128 == 0 &&
+      tiles(128, 128) >= want)
     launch_shape<E, 128, 128>(p, s);
-  else if (E == kEpiPartialF32 && tiles(128, 64) >= want)
+  else if ((E == kEpiPartialF32 || gelu_plain) && tiles(128, 64) >= want)
     launch_shape<E, 128, 64>(p, s);
   else
     launch_shape<E, 64, 64>(p, s);
