@@ -360,6 +360,50 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
       return;
     }
   }
+  // The residual and the stored pre-activation are loaded for all of the
+  // lane's outputs before the first store, branch-free (rows past the end
+  // read the first element): loaded one at a time, behind the row check and
+  // after stores they might alias, each load was waited for on its own.
+  constexpr bool kReads = E == kEpiResidualF32 || E == kEpiGeluGradBf16;
+  float xin[kReads ? WN : 1][kReads ? WM : 1][kReads ? 16 : 1];
+  if constexpr (kReads) {
+    // element offset of output x of block (jn, i), or 0 past the last row
+    auto at = [&](int jn, int i, int x) -> int64_t {
+      const int nc = (second ? n0 - p.n_split : n0) + wn * (BN / 2) + jn * 32 + r;
+      const int mb = m0 + wm * (BM / 2) + i * 32;
+      const int mi = 8 * (x >> 2) + 4 * g + (x & 3);
+      if (mb + mi >= p.rows) return 0;
+      if (E == kEpiGeluGradBf16) {
+        const int64_t ob = p.c_seg > 0 ? (mb / p.c_seg) * p.c_bstride + p.c_row0 + mb % p.c_seg
+                                       : static_cast<int64_t>(mb);
+        return (ob + mi) * p.ldc + nc;
+      }
+      return static_cast<int64_t>(mb + mi) * p.ldres + nc;
+    };
+    if (E == kEpiResidualF32 && p.res32) {
+#pragma unroll
+      for (int jn = 0; jn < WN; ++jn)
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) xin[jn][i][x] = p.res32[at(jn, i, x)];
+    } else {
+      const __bf16 *src = E == kEpiGeluGradBf16 ? p.pre_in : p.res;
+      __bf16 raw[kReads ? WN : 1][kReads ? WM : 1][16];
+#pragma unroll
+      for (int jn = 0; jn < WN; ++jn)
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) raw[jn][i][x] = src[at(jn, i, x)];
+#pragma unroll
+      for (int jn = 0; jn < WN; ++jn)
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) xin[jn][i][x] = static_cast<float>(raw[jn][i][x]);
+    }
+  }
 #pragma unroll
   for (int jn = 0; jn < WN; ++jn) {
     const int n = n0 + wn * (BN / 2) + jn * 32 + r;
@@ -383,16 +427,14 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
           if (E == kEpiPartialF32) {
             static_cast<float *>(p.c0)[split * p.c_split_stride + mo * p.ldc + nc] = v;
           } else if (E == kEpiResidualF32) {
-            v += p.res32 ? p.res32[static_cast<int64_t>(m) * p.ldres + nc]
-                         : static_cast<float>(p.res[static_cast<int64_t>(m) * p.ldres + nc]);
+            v += xin[kReads ? jn : 0][kReads ? i : 0][kReads ? 4 * a4 + c : 0];
             static_cast<float *>(second ? p.c1 : p.c0)[mo * p.ldc + nc] = v;
           } else {
             if (E == kEpiGeluBf16) {
               if (p.pre_out) p.pre_out[mo * p.ldc + nc] = static_cast<__bf16>(v);
               v = gelu_erf(v);
             }
-            if (E == kEpiGeluGradBf16)
-              v *= gelu_erf_grad(static_cast<float>(p.pre_in[mo * p.ldc + nc]));
+            if (E == kEpiGeluGradBf16) v *= gelu_erf_grad(xin[kReads ? jn : 0][kReads ? i : 0][kReads ? 4 * a4 + c : 0]);
             static_cast<__bf16 *>(second ? p.c1 : p.c0)[mo * p.ldc + nc] = static_cast<__bf16>(v);
           }
         }
