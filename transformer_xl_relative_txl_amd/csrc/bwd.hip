@@ -159,14 +159,21 @@ __global__ __launch_bounds__(256) void ln_backward_kernel(
   for (int row = r_lo + wave; row < r_hi; row += 4) {
     const float *xr = x + static_cast<int64_t>(row) * d;
     const float *gr = dy + static_cast<int64_t>(row) * d;
+    // x, dy and gamma of the row are loaded before any arithmetic: one
+    // memory round trip per row
     f32x4 xv[MAXC], gv[MAXC];
-    float s = 0.0f;
+    bf16x4 gmv[MAXC];
 #pragma unroll
     for (int c = 0; c < MAXC; ++c)
       if (c < nch) {
         xv[c] = *reinterpret_cast<const f32x4 *>(xr + 256 * c + 4 * lane);
-        s += (xv[c][0] + xv[c][1]) + (xv[c][2] + xv[c][3]);
+        gv[c] = *reinterpret_cast<const f32x4 *>(gr + 256 * c + 4 * lane);
+        gmv[c] = *reinterpret_cast<const bf16x4 *>(gamma + 256 * c + 4 * lane);
       }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c)
+      if (c < nch) s += (xv[c][0] + xv[c][1]) + (xv[c][2] + xv[c][3]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
     const float mean = s / d;
@@ -186,8 +193,7 @@ __global__ __launch_bounds__(256) void ln_backward_kernel(
 #pragma unroll
     for (int c = 0; c < MAXC; ++c)
       if (c < nch) {
-        const bf16x4 gm = *reinterpret_cast<const bf16x4 *>(gamma + 256 * c + 4 * lane);
-        gv[c] = *reinterpret_cast<const f32x4 *>(gr + 256 * c + 4 * lane);
+        const bf16x4 gm = gmv[c];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float xh = (xv[c][e] - mean) * rs;

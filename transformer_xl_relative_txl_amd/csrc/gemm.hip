@@ -462,21 +462,33 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
   constexpr int MAXC = NCH > 0 ? NCH : kLnMaxChunks;
   const int nch = NCH > 0 ? NCH : d / 256;
   const float *xr = x + static_cast<int64_t>(row) * d;
-  f32x4 v[MAXC];
+  // every input of the row (x and its split-K partials, the residual, gamma
+  // and beta) is loaded before any arithmetic: one memory round trip per row
+  f32x4 v[MAXC], pv[MAXC][NP > 1 ? NP - 1 : 1];
+  bf16x4 rr[MAXC], gm[MAXC], bt[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    if (c < nch) {
+      const int col = 256 * c + 4 * lane;
+      v[c] = *reinterpret_cast<const f32x4 *>(xr + col);
+#pragma unroll
+      for (int part = 1; part < NP; ++part)
+        pv[c][part - 1] = *reinterpret_cast<const f32x4 *>(xr + part * part_stride + col);
+      if (res) rr[c] = *reinterpret_cast<const bf16x4 *>(res + static_cast<int64_t>(row) * d + col);
+      gm[c] = *reinterpret_cast<const bf16x4 *>(gamma + col);
+      bt[c] = *reinterpret_cast<const bf16x4 *>(beta + col);
+    }
+  }
   float s = 0.0f;
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
     if (c < nch) {
-      v[c] = *reinterpret_cast<const f32x4 *>(xr + 256 * c + 4 * lane);
       // split-K partials in order, then the residual
 #pragma unroll
-      for (int part = 1; part < NP; ++part)
-        v[c] += *reinterpret_cast<const f32x4 *>(xr + part * part_stride + 256 * c + 4 * lane);
+      for (int part = 1; part < NP; ++part) v[c] += pv[c][part - 1];
       if (res) {
-        const bf16x4 rr = *reinterpret_cast<const bf16x4 *>(res + static_cast<int64_t>(row) * d +
-                                                            256 * c + 4 * lane);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[c][e] += static_cast<float>(rr[e]);
+        for (int e = 0; e < 4; ++e) v[c][e] += static_cast<float>(rr[c][e]);
       }
       if (x_out) *reinterpret_cast<f32x4 *>(x_out + static_cast<int64_t>(row) * d + 256 * c + 4 * lane) = v[c];
       s += (v[c][0] + v[c][1]) + (v[c][2] + v[c][3]);
@@ -504,13 +516,11 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
   for (int c = 0; c < MAXC; ++c) {
     if (c < nch) {
       const int col = 256 * c + 4 * lane;
-      const bf16x4 gm = *reinterpret_cast<const bf16x4 *>(gamma + col);
-      const bf16x4 bt = *reinterpret_cast<const bf16x4 *>(beta + col);
       bf16x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        o[e] = static_cast<__bf16>((v[c][e] - mean) * inv * static_cast<float>(gm[e]) +
-                                   static_cast<float>(bt[e]));
+        o[e] = static_cast<__bf16>((v[c][e] - mean) * inv * static_cast<float>(gm[c][e]) +
+                                   static_cast<float>(bt[c][e]));
       *reinterpret_cast<bf16x4 *>(yr + col) = o;
     }
   }
