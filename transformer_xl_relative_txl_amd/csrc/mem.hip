@@ -186,7 +186,9 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(KVBuffers kb, KVCo
 
 __global__ __launch_bounds__(kThreads) void mem_read_logical_kernel(
     const u32x4 *data, u32x4 *out, int M, int64_t head, uint32_t cpr, FastDiv div_cpr,
-    FastDiv div_m, uint32_t total) {
+    FastDiv div_m, uint32_t total, const int32_t *valid_src, int32_t *valid_dst, int B) {
+  if (valid_src && blockIdx.x == 0)  // the valid counts too, by the first workgroup
+    for (int i = threadIdx.x; i < B; i += kThreads) valid_dst[i] = valid_src[i];
   const uint32_t base = blockIdx.x * (kThreads * kChunks) + threadIdx.x;
 #pragma unroll
   for (int j = 0; j < kChunks; ++j) {
@@ -286,7 +288,7 @@ txl_status launch_kv_compact(const KVBuffers &kb, int n, int B, int M, int64_t c
 
 txl_status launch_mem_read_logical(const void *data, void *out, int B, int M,
                                    int64_t head, int64_t row_bytes,
-                                   hipStream_t s) {
+                                   hipStream_t s, const int32_t *valid_src, int32_t *valid_dst) {
   const int64_t cpr = row_bytes / 16;
   const int64_t total = static_cast<int64_t>(B) * M * cpr;
   if (total >= (int64_t(1) << 31)) return fail(TXL_ERR_UNSUPPORTED, "mem_read_logical: more than 2^31 chunks");
@@ -296,7 +298,8 @@ txl_status launch_mem_read_logical(const void *data, void *out, int B, int M,
   hipLaunchKernelGGL(mem_read_logical_kernel, dim3(blocks), dim3(kThreads), 0, s,
                      reinterpret_cast<const u32x4 *>(data), reinterpret_cast<u32x4 *>(out), M,
                      head, static_cast<uint32_t>(cpr), make_fastdiv(static_cast<uint32_t>(cpr)),
-                     make_fastdiv(static_cast<uint32_t>(M)), static_cast<uint32_t>(total));
+                     make_fastdiv(static_cast<uint32_t>(M)), static_cast<uint32_t>(total), valid_src,
+                     valid_dst, B);
   return check_launch("mem_read_logical_kernel");
 }
 

@@ -768,12 +768,11 @@ static txl_status segment_step(txl_stack *st, const int32_t *tokens, txl_mem *me
     TapeLayer tl;
     if (tape) {  // the memory as this layer reads it, before any update
       tl = tape_at(tlay, tape, n);
-      if (c.M > 0) {
+      if (c.M > 0)
         s = launch_mem_read_logical(ring.data, tl.mem, c.B, c.M, ring.head,
-                                    static_cast<int64_t>(c.d) * 2, stream);
-        if (s != TXL_OK) return s;
-      }
-      s = launch_copy_i32(ring.valid, tl.valid, c.B, stream);
+                                    static_cast<int64_t>(c.d) * 2, stream, ring.valid, tl.valid);
+      else
+        s = launch_copy_i32(ring.valid, tl.valid, c.B, stream);
       if (s != TXL_OK) return s;
     }
     __bf16 *k_out = tape ? tl.k : b.k;

@@ -147,9 +147,12 @@ struct KVBuffers {
 };
 txl_status launch_kv_compact(const KVBuffers &kb, int n, int B, int M, int64_t cap,
                              int64_t start, int64_t row_bytes, hipStream_t s);
+// the ring's slots in logical order into out [B, M, row]; with valid_src
+// set, also the B valid counts into valid_dst
 txl_status launch_mem_read_logical(const void *data, void *out, int B, int M,
                                    int64_t head, int64_t row_bytes,
-                                   hipStream_t s);
+                                   hipStream_t s, const int32_t *valid_src = nullptr,
+                                   int32_t *valid_dst = nullptr);
 
 // ---- relative-position table ---------------------------------------------
 txl_status launch_rel_pos_table(txl_dtype dt, int M, int L, int d, int HD,
