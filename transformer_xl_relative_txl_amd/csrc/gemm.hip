@@ -108,6 +108,18 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
   const __bf16 *arow[A_CH];
   const __bf16 *wrow[B_CH];
   int any_valid = 0;
+  // gather mode: the valid counts of the rows' batch rows are loaded first,
+  // all at once (rows past the end read the last row's): loaded inside the
+  // row logic, each was waited for on its own before the next
+  int vrow[A_CH];
+  if (p.gather) {
+    const int ml = p.memM + p.segL;
+#pragma unroll
+    for (int j = 0; j < A_CH; ++j) {
+      const int m = min(m0 + tid / CPR + RPP * j, p.rows - 1);
+      vrow[j] = p.valid[m / ml];
+    }
+  }
 #pragma unroll
   for (int j = 0; j < A_CH; ++j) {
     const int row = tid / CPR + RPP * j;
@@ -122,7 +134,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
         if (jl >= p.memM) {
           src = p.seg + (static_cast<int64_t>(b) * p.segL + (jl - p.memM)) * p.lda;
         } else {
-          int valid = p.valid[b];
+          int valid = vrow[j];
           valid = valid < 0 ? 0 : (valid > p.memM ? p.memM : valid);
           if (jl >= p.memM - valid) {
             int64_t slot = p.head + jl;
