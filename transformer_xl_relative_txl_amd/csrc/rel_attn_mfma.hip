@@ -31,8 +31,10 @@
 //    at its end. Rows are stored with their 16-byte chunks XOR-swizzled by
 //    the row, which makes the K operand reads (16 bytes of one key row per
 //    lane) and the transposing V reads (ds_read_b64_tr_b16, eight keys of
-//    one dimension per lane for the V^T operand) conflict-free. R rows go
-//    straight from L2 into the A operand, one tile ahead.
+//    one dimension per lane for the V^T operand) free of LDS bank conflicts
+//    (64 banks: 16 lanes of a 16-byte read, or 32 of an 8-byte read, must
+//    cover all of them). R rows go straight from L2 into the A operand, one
+//    tile ahead.
 //  * The content MFMAs run first (their operands are in LDS when the tile
 //    starts), while the band's results drain and its LDS round trip
 //    completes; the shifted position term is then added to the scores.
@@ -80,7 +82,7 @@ constexpr int US = QW;         // band row stride (floats): the diagonal read pu
 constexpr float kPsumLimit = 256.0f;  // a tile keeps the running max while each lane's sum of p stays <= 2^8
 
 // LDS: two K/V tile buffers (K [64 keys][64 dims] then V [64 keys][64 dims],
-// bf16, 16-byte chunks swizzled: chunk c of key row n sits in slot c ^ (n & 7))
+// bf16, 16-byte chunks swizzled: chunk c of key row n sits in slot c ^ kv_swz(n))
 // and the waves' bands; 81920 bytes, two workgroups per CU.
 constexpr int kTileElems = BK * DH;            // one K or V tile
 constexpr int kBandFloats = NW * NU * US;
@@ -142,18 +144,26 @@ __device__ inline void bstore_nt(rsrc_t rs, int byte_off, u32x4 v) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Slot of chunk c of key row n (a row is 128 bytes, 8 slots; two rows span
+// the 64 banks): c ^ kv_swz(n). The K operand read has 16 lanes read chunk c
+// of rows n0 .. n0+15 at once, so the 8 even and the 8 odd rows each need 8
+// distinct slots (bit 3 of n enters); the V read has 32 lanes read chunks
+// 4db .. 4db+3 of rows n0+k, k < 4, so rows k and k+2 (same bank half) need
+// slots in different groups of four (bit 1 of n flips bit 2).
+__device__ inline int kv_swz(int n) { return (n & 7) ^ ((n << 1) & 4) ^ ((n >> 3) & 1); }
+
 // Tile [j0, j0 + 64) of K and of V into an LDS buffer with direct
 // buffer-to-LDS loads (no registers): wave w's instruction t = 2w + rep fills
 // key rows 8t .. 8t+7, lane l landing at byte 16 l of that 1 KiB (row
-// 8t + l/8, slot l % 8), so the lane loads source chunk (l % 8) ^ (l / 8) of
-// its row. Rows past the buffer's range load zeros.
+// n = 8t + l/8, slot l % 8), so the lane loads source chunk
+// (l % 8) ^ kv_swz(n) of its row. Rows past the buffer's range load zeros.
 __device__ inline void dma_kv(rsrc_t krs, rsrc_t vrs, int row_bytes, int j0, __bf16 *buf, int wave,
                               int lane) {
 #pragma unroll
   for (int rep = 0; rep < 2; ++rep) {
     const int t = 2 * wave + rep;
     const int row = 8 * t + (lane >> 3);
-    const int off = (j0 + row) * row_bytes + 16 * ((lane & 7) ^ (lane >> 3));
+    const int off = (j0 + row) * row_bytes + 16 * ((lane & 7) ^ kv_swz(row));
     __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void *)(buf + 512 * t), 16, off, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(buf + kTileElems + 512 * t), 16, off,
                                              0, 0, 0);
@@ -305,16 +315,20 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
   // V operand reads (transposing): lane l = 16g + 4k + q supplies the
   // address of V[key][d0 + 4q], key = 4hh + k (+ the k-step's base), so that
   // lane j of its group receives V[keys][d0 + j]; d0 = 32db + 16(g & 1).
-  // Slot offsets of the swizzle (key & 7 = 4hh + k at every base).
-  int v_off[2];
+  // Slot offsets of the swizzle: key = 4hh + k at the k-step's first eight
+  // keys (a base that is a multiple of 16), 8 + 4hh + k at its second eight.
+  int v_off[2], v_offh[2];
   {
     const int x = 4 * hh + ((lane >> 2) & 3);
     const int q = lane & 3;
     const int cc = 2 * ((lane >> 4) & 1) + (q >> 1);
 #pragma unroll
-    for (int db = 0; db < 2; ++db) v_off[db] = x * DH + 8 * ((4 * db + cc) ^ x) + 4 * (q & 1);
+    for (int db = 0; db < 2; ++db) {
+      v_off[db] = x * DH + 8 * ((4 * db + cc) ^ kv_swz(x)) + 4 * (q & 1);
+      v_offh[db] = x * DH + 8 * ((4 * db + cc) ^ kv_swz(x + 8)) + 4 * (q & 1);
+    }
   }
-  // K operand reads: key row n = 32kb + r, chunk 2s + hh in slot (2s + hh) ^ (r & 7)
+  // K operand reads: key row n = 32kb + r, chunk 2s + hh in slot (2s + hh) ^ kv_swz(r)
   const int k_row = r * DH;
 
   // tile 0 in buffer 0 before the loop; every tile's loads are waited for
@@ -368,7 +382,7 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
         for (int x = 0; x < 16; ++x) s_acc[kb][x] = 0.0f;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const bf16x8 a = load8(&sk[kb * 32 * DH + k_row + 8 * ((2 * s + hh) ^ (r & 7))]);
+          const bf16x8 a = load8(&sk[kb * 32 * DH + k_row + 8 * ((2 * s + hh) ^ kv_swz(r))]);
           s_acc[kb] = mfma32(a, qa[s], s_acc[kb]);
         }
       }
@@ -456,9 +470,9 @@ __device__ __forceinline__ void rel_attn_tile(const AttnParams &p, int n_qt, con
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
-            const int vk = kTileElems + (kb * 32 + 16 * s2) * DH + v_off[db];
-            const v4i16 lo = lds_read_tr(&sk[vk]);
-            const v4i16 hi = lds_read_tr(&sk[vk + 8 * DH]);
+            const int vk = kTileElems + (kb * 32 + 16 * s2) * DH;
+            const v4i16 lo = lds_read_tr(&sk[vk + v_off[db]]);
+            const v4i16 hi = lds_read_tr(&sk[vk + 8 * DH + v_offh[db]]);
             // whole-vector cast: a per-element bit cast of these vectors was
             // folded to element 0 by the compiler
             const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
