@@ -90,14 +90,27 @@ __global__ __launch_bounds__(256) void gather_ext_kernel(const u32x4 *__restrict
   y[e] = v;
 }
 
-// out[i] = sum_{s < S} part[s * stride + i], s ascending (4 floats a thread)
+// out[i] = sum_{s < S} part[s * stride + i], s ascending (4 floats a thread).
+// The parts are loaded eight at a time (the index clamped to the last part,
+// so the loads need no branch) before any of them is added: one load at a
+// time left a thread waiting a full memory round trip per part.
+constexpr int kPartBatch = 8;
 __global__ __launch_bounds__(256) void reduce_parts_kernel(const float *__restrict__ part, int S,
                                                            int64_t stride, int64_t n4,
                                                            float *__restrict__ out) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (e >= n4) return;
-  f32x4 acc = reinterpret_cast<const f32x4 *>(part)[e];
-  for (int s = 1; s < S; ++s) acc += reinterpret_cast<const f32x4 *>(part + s * stride)[e];
+  const f32x4 *p = reinterpret_cast<const f32x4 *>(part) + e;
+  const int64_t st4 = stride / 4;
+  f32x4 acc = p[0];
+  for (int s0 = 1; s0 < S; s0 += kPartBatch) {
+    f32x4 v[kPartBatch];
+#pragma unroll
+    for (int t = 0; t < kPartBatch; ++t) v[t] = p[(s0 + t < S ? s0 + t : S - 1) * st4];
+#pragma unroll
+    for (int t = 0; t < kPartBatch; ++t)
+      if (s0 + t < S) acc += v[t];
+  }
   reinterpret_cast<f32x4 *>(out)[e] = acc;
 }
 

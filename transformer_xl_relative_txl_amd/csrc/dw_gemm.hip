@@ -219,10 +219,12 @@ int dw_gemm_splits(int rows, int N, int k_rows) {
   const int tm = dw_big_tiles(rows, N) ? 128 : 64;
   const int64_t tiles = static_cast<int64_t>(rows / tm) * (N / tm);
   const int n_slabs = (k_rows + KS - 1) / KS;
-  // up to about two workgroups per CU, each split keeping at least 8 slabs
-  // (fewer, longer splits: the partial sums cost more than the occupancy)
+  // up to about two workgroups per CU, each split keeping at least 4 slabs
+  // (the 16-layer training step: 8 slabs per split 10.36 ms, 4 slabs
+  // 10.28, 3 slabs 10.36 - the partial sums then cost more than the
+  // occupancy brings)
   int s = 1;
-  while (s < 32 && tiles * s < 512 && n_slabs / (2 * s) >= 8) s *= 2;
+  while (s < 32 && tiles * s < 512 && n_slabs / (2 * s) >= 4) s *= 2;
   return s;
 }
 
