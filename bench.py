@@ -46,9 +46,9 @@ TIMED_REPEATS = 5
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by the
 # same counters' reading of a plain copy of known size), valid only for the
 # kernel source they were taken on.
-ATTN_TRAFFIC = {"source_sha1": "7b235ef082385ff67d6150f00376a1528a70cf6d",
+ATTN_TRAFFIC = {"source_sha1": "678a1c745e8105dbe5abfb71aa1b700c6ba464e1",
                 "profile": "profiles/rel_attn_B8_H16_L512_M512_hbm_traffic.md",
-                "rel_attn_mfma_append_kernel": 69.29e6, "rel_attn_mfma_kernel": 52.49e6}
+                "rel_attn_mfma_append_kernel": 69.32e6, "rel_attn_mfma_kernel": 52.52e6}
 
 
 def attn_flops(B, H, L, M_eff, d_h):
