@@ -310,6 +310,89 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
     return;
   }
   const bool second = n0 >= p.n_split;
+  // fp32-staged epilogue of the two GELU products that also touch a second
+  // bf16 matrix of the output's shape (the stored pre-activation, or the
+  // pre-activation the derivative is taken at): the tile goes to LDS as fp32
+  // in two row halves (half a tile fits the A buffers) and every thread then
+  // handles 8 consecutive columns of a row, with one 16-byte load of the
+  // pre-activation and 16-byte stores, instead of one 2-byte access per
+  // element. The arithmetic per element is the direct path's.
+  constexpr bool kStagedF32 = BKS == 64 && (E == kEpiGeluGradBf16 || E == kEpiGeluBf16);
+  if constexpr (kStagedF32) {
+    const __bf16 *pre_in = E == kEpiGeluGradBf16 ? p.pre_in : nullptr;
+    __bf16 *pre_out = E == kEpiGeluBf16 ? p.pre_out : nullptr;
+    const uintptr_t al = reinterpret_cast<uintptr_t>(p.c0) | reinterpret_cast<uintptr_t>(p.c1) |
+                         reinterpret_cast<uintptr_t>(pre_in) | reinterpret_cast<uintptr_t>(pre_out);
+    if ((pre_in || pre_out) && (al & 15) == 0 && p.ldc % 8 == 0) {
+      constexpr int HB = BM / 2;                 // rows per half (one wave row)
+      constexpr int OSf = BN + 4;                // LDS row stride (floats)
+      constexpr int CPR8 = BN / 8, RP8 = 256 / CPR8, IT8 = HB / RP8;
+      static_assert(size_t(HB) * OSf * 4 <= sizeof(sa), "half a tile must fit the A buffers");
+      static_assert(RP8 <= 32 && 32 % RP8 == 0, "row passes must tile 32-row blocks");
+      float *ct = reinterpret_cast<float *>(&sa[0][0]);
+      const int cc = tid % CPR8, rr0 = tid / CPR8;
+      const int nc0 = (second ? n0 - p.n_split : n0) + cc * 8;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // output row offsets of this thread's rows of the half (a 32-row
+        // block never straddles an output segment: c_seg % 32 == 0), and the
+        // pre-activation loaded before the barrier
+        int64_t mo[IT8];
+        bool ok[IT8];
+        bf16x8 pin[IT8];
+#pragma unroll
+        for (int it = 0; it < IT8; ++it) {
+          const int row = rr0 + RP8 * it;
+          const int m = m0 + h * HB + row;
+          ok[it] = m < p.rows;
+          const int mb = m0 + h * HB + (RP8 * it / 32) * 32;
+          mo[it] = (p.c_seg > 0 ? (mb / p.c_seg) * p.c_bstride + p.c_row0 + mb % p.c_seg
+                                : static_cast<int64_t>(mb)) + (row & 31);
+          if (E == kEpiGeluGradBf16)
+            pin[it] = *reinterpret_cast<const bf16x8 *>(pre_in + (ok[it] ? mo[it] * p.ldc + nc0 : 0));
+        }
+        if (wm == h) {
+#pragma unroll
+          for (int jn = 0; jn < WN; ++jn)
+#pragma unroll
+            for (int i = 0; i < WM; ++i)
+#pragma unroll
+              for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                  const int row = i * 32 + 8 * a4 + 4 * g + c;
+                  const int col = wn * (BN / 2) + jn * 32 + r;
+                  ct[row * OSf + col] = acc[i][jn][4 * a4 + c];
+                }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < IT8; ++it) {
+          const int row = rr0 + RP8 * it;
+          const f32x4 lo = *reinterpret_cast<const f32x4 *>(ct + row * OSf + cc * 8);
+          const f32x4 hi = *reinterpret_cast<const f32x4 *>(ct + row * OSf + cc * 8 + 4);
+          bf16x8 o, pre;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float v = e < 4 ? lo[e] : hi[e - 4];
+            if (E == kEpiGeluBf16) {
+              pre[e] = static_cast<__bf16>(v);
+              v = gelu_erf(v);
+            } else {
+              v *= gelu_erf_grad(static_cast<float>(pin[it][e]));
+            }
+            o[e] = static_cast<__bf16>(v);
+          }
+          if (!ok[it]) continue;
+          __bf16 *dst = static_cast<__bf16 *>(second ? p.c1 : p.c0) + mo[it] * p.ldc + nc0;
+          *reinterpret_cast<bf16x8 *>(dst) = o;
+          if (E == kEpiGeluBf16) *reinterpret_cast<bf16x8 *>(pre_out + mo[it] * p.ldc + nc0) = pre;
+        }
+        __syncthreads();  // the next half reuses the LDS rows
+      }
+      return;
+    }
+  }
   // Staged epilogue: the tile goes to LDS (free after the last barrier of the
   // loop) and leaves as 16-byte row chunks, the output row of each 32-row
   // block remapped once, instead of one 2-byte or 4-byte store per element.
