@@ -398,8 +398,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
   // block remapped once, instead of one 2-byte or 4-byte store per element.
   constexpr bool kStaged = BKS == 64 && (E == kEpiStoreBf16 || E == kEpiGeluBf16 ||
                                          ((E == kEpiResidualF32 || E == kEpiPartialF32) && BN == 64));
-  // the pre-activation store and the fp32 residual take the direct path
-  const bool direct_only = (E == kEpiGeluBf16 && p.pre_out) || (E == kEpiResidualF32 && p.res32);
+  // the pre-activation store takes the fp32-staged path above (or, unaligned,
+  // the direct path)
+  const bool direct_only = E == kEpiGeluBf16 && p.pre_out;
   if constexpr (kStaged) if (!direct_only) {
     typedef typename std::conditional<(E == kEpiStoreBf16 || E == kEpiGeluBf16), __bf16, float>::type OT;
     constexpr int VE = 16 / static_cast<int>(sizeof(OT));       // elements per 16-byte chunk
@@ -409,10 +410,35 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
     static_assert(32 % RP == 0 || RP % 32 == 0, "row passes must tile 32-row blocks");
     const uintptr_t al = reinterpret_cast<uintptr_t>(p.c0) | reinterpret_cast<uintptr_t>(p.c1);
     bool vec_ok = (al & 15) == 0 && p.ldc % VE == 0;
-    if (E == kEpiResidualF32) vec_ok = vec_ok && p.ldres % 4 == 0 && (reinterpret_cast<uintptr_t>(p.res) & 7) == 0;
+    if (E == kEpiResidualF32)
+      vec_ok = vec_ok && p.ldres % 4 == 0 &&
+               (p.res32 ? (reinterpret_cast<uintptr_t>(p.res32) & 15) == 0
+                        : (reinterpret_cast<uintptr_t>(p.res) & 7) == 0);
     if (E == kEpiPartialF32) vec_ok = vec_ok && p.c_split_stride % 4 == 0;
     if (vec_ok) {
       OT *ct = reinterpret_cast<OT *>(&sa[0][0]);
+      const int cc = tid % CPRo, rr0 = tid / CPRo;
+      const int nc0 = (second ? n0 - p.n_split : n0) + cc * VE;
+      // the residual of this thread's rows, loaded before the tile is staged
+      // (rows past the end read row 0) and converted only where it is added
+      constexpr int RI = E == kEpiResidualF32 ? IT : 1;
+      f32x4 r32[RI];
+      bf16x4 r16[RI];
+      if constexpr (E == kEpiResidualF32) {
+        if (p.res32) {
+#pragma unroll
+          for (int it = 0; it < IT; ++it) {
+            const int m = m0 + rr0 + RP * it;
+            r32[it] = *reinterpret_cast<const f32x4 *>(p.res32 + static_cast<int64_t>(m < p.rows ? m : 0) * p.ldres + nc0);
+          }
+        } else {
+#pragma unroll
+          for (int it = 0; it < IT; ++it) {
+            const int m = m0 + rr0 + RP * it;
+            r16[it] = *reinterpret_cast<const bf16x4 *>(p.res + static_cast<int64_t>(m < p.rows ? m : 0) * p.ldres + nc0);
+          }
+        }
+      }
 #pragma unroll
       for (int jn = 0; jn < WN; ++jn)
 #pragma unroll
@@ -428,8 +454,6 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
               ct[row * OS + col] = static_cast<OT>(v);
             }
       __syncthreads();
-      const int cc = tid % CPRo, rr0 = tid / CPRo;
-      const int nc0 = (second ? n0 - p.n_split : n0) + cc * VE;
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
         const int row = rr0 + RP * it;
@@ -443,10 +467,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
         if (E == kEpiPartialF32) {
           *reinterpret_cast<u32x4 *>(static_cast<float *>(p.c0) + split * p.c_split_stride + mo * p.ldc + nc0) = v;
         } else if (E == kEpiResidualF32) {
-          const bf16x4 rv = *reinterpret_cast<const bf16x4 *>(p.res + static_cast<int64_t>(m) * p.ldres + nc0);
           f32x4 o = __builtin_bit_cast(f32x4, v);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] += static_cast<float>(rv[e]);
+          for (int e = 0; e < 4; ++e) o[e] += p.res32 ? r32[RI > 1 ? it : 0][e] : static_cast<float>(r16[RI > 1 ? it : 0][e]);
           *reinterpret_cast<f32x4 *>(static_cast<float *>(second ? p.c1 : p.c0) + mo * p.ldc + nc0) = o;
         } else {
           *reinterpret_cast<u32x4 *>(static_cast<__bf16 *>(second ? p.c1 : p.c0) + mo * p.ldc + nc0) = v;
