@@ -187,8 +187,7 @@ __global__ __launch_bounds__(256) void ln_backward_kernel(
 #pragma unroll
     for (int c = 0; c < MAXC; ++c)
       if (c < nch) s += (xv[c][0] + xv[c][1]) + (xv[c][2] + xv[c][3]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    s = wave_sum(s);
     const float mean = s / d;
     float ss = 0.0f;
 #pragma unroll
@@ -199,8 +198,7 @@ __global__ __launch_bounds__(256) void ln_backward_kernel(
           const float t = xv[c][e] - mean;
           ss += t * t;
         }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    ss = wave_sum(ss);
     const float rs = 1.0f / sqrtf(ss / d + eps);
     float m1 = 0.0f, m2 = 0.0f;
 #pragma unroll
@@ -219,11 +217,8 @@ __global__ __launch_bounds__(256) void ln_backward_kernel(
           m2 += gdy * xh;
         }
       }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      m1 += __shfl_xor(m1, o);
-      m2 += __shfl_xor(m2, o);
-    }
+    m1 = wave_sum(m1);
+    m2 = wave_sum(m2);
     m1 /= d;
     m2 /= d;
 #pragma unroll

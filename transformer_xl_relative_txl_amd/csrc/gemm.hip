@@ -612,8 +612,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
       s += (v[c][0] + v[c][1]) + (v[c][2] + v[c][3]);
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  s = wave_sum(s);
   const float mean = s / d;
   float ss = 0.0f;
 #pragma unroll
@@ -626,8 +625,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
       }
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / d + eps);
   __bf16 *yr = y + static_cast<int64_t>(row) * d;
 #pragma unroll

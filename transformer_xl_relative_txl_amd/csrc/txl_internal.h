@@ -58,6 +58,25 @@ __device__ inline uint32_t fdiv(uint32_t n, FastDiv f) {
   return (__umulhi(n, f.m) + n) >> f.s;
 }
 
+// Sum over the 64 lanes of a wave, returned to every lane, with DPP moves
+// instead of LDS permutes: pairs and quads, half-rows and rows of 16 lanes
+// (each lane then holds its row's sum), then the row broadcasts that carry
+// rows 0-2 into row 3; lane 63 holds the total, read out as a scalar.
+template <int Ctrl, int RowMask>
+__device__ inline float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), Ctrl,
+                                                                   RowMask, 0xF, false));
+}
+__device__ inline float wave_sum(float v) {
+  v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1, 0, 3, 2]
+  v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2, 3, 0, 1]
+  v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_add<0x140, 0xF>(v);  // row_mirror
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 // One ring's append (txl_mem_update of a single ring) carried out by the bf16
 // attention kernel in the same launch: the 16-byte chunks of the L' = min(L, M)
 // new rows are spread over the threads of the workgroups with the lighter
