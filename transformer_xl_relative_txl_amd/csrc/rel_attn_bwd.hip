@@ -706,15 +706,20 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *part_r, fl
     const float *src = which ? part_v : part_u;
     const int n = tid & 63, grp = tid >> 6, items = B * n_mt;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // the four items of a round are loaded before any is added (items past
+    // the end load the last item and add nothing): loads behind the item
+    // test were waited for one at a time
     for (int it0 = grp; it0 < items; it0 += 16) {
+      float v[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const int it = it0 + 4 * x;
-        if (it < items) {
-          const int b = it / n_mt, t = it - b * n_mt;
-          acc[x] += src[((static_cast<int64_t>(b) * H + h) * n_mt + t) * DH + n];
-        }
+        const int it = it0 + 4 * x < items ? it0 + 4 * x : items - 1;
+        const int b = it / n_mt, t = it - b * n_mt;
+        v[x] = src[((static_cast<int64_t>(b) * H + h) * n_mt + t) * DH + n];
       }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        if (it0 + 4 * x < items) acc[x] += v[x];
     }
     red[grp][n] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     __syncthreads();
@@ -725,9 +730,12 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *part_r, fl
   if (e >= n_r) return;
   float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   for (int b0 = 0; b0 < B; b0 += 8) {
+    float v[8];  // loaded together, as above
+#pragma unroll
+    for (int x = 0; x < 8; ++x) v[x] = part_r[(b0 + x < B ? b0 + x : B - 1) * n_r + e];
 #pragma unroll
     for (int x = 0; x < 8; ++x)
-      if (b0 + x < B) acc[x] += part_r[(b0 + x) * n_r + e];
+      if (b0 + x < B) acc[x] += v[x];
   }
   float s = 0.0f;
 #pragma unroll
