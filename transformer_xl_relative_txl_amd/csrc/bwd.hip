@@ -265,8 +265,11 @@ __global__ __launch_bounds__(256) void ln_backward_kernel(
 // position order (rows of v with no token are 0; ids outside [0, vocab) add
 // nothing). A workgroup owns 32 vocabulary rows and 256 columns: every wave
 // scans the tokens 64 at a time with one ballot, and the matches are added
-// to an LDS accumulator in position order.
-constexpr int kEmbRows = 32;
+// to an LDS accumulator in position order. The tokens of eight such rounds
+// are loaded together (clamped to the last position, so the loads need no
+// branch): a scan that loaded one round at a time waited a memory round trip
+// per 64 tokens.
+constexpr int kEmbRows = 32, kEmbRounds = 8;
 __global__ __launch_bounds__(256) void embed_backward_kernel(const int32_t *__restrict__ tokens,
                                                              int n_tok, const float *__restrict__ dh0,
                                                              int d, int vocab,
@@ -277,15 +280,24 @@ __global__ __launch_bounds__(256) void embed_backward_kernel(const int32_t *__re
   const int col = c0 + tid;
 #pragma unroll
   for (int r = 0; r < kEmbRows; ++r) acc[r][tid] = 0.0f;
-  for (int p0 = 0; p0 < n_tok; p0 += 64) {
-    const int p = p0 + lane;
-    const int t = p < n_tok ? tokens[p] : -1;
-    uint64_t hit = __builtin_amdgcn_ballot_w64(t >= v0 && t < v0 + kEmbRows && t < vocab);
-    while (hit) {                       // the same mask in every wave: uniform
-      const int k = __builtin_ctzll(hit);
-      hit &= hit - 1;
-      const int tk = __shfl(t, k);
-      if (col < d) acc[tk - v0][tid] += dh0[static_cast<int64_t>(p0 + k) * d + col];
+  for (int pb = 0; pb < n_tok; pb += 64 * kEmbRounds) {
+    int tv[kEmbRounds];
+#pragma unroll
+    for (int s = 0; s < kEmbRounds; ++s) {
+      const int p = pb + 64 * s + lane;
+      tv[s] = tokens[p < n_tok ? p : n_tok - 1];
+    }
+#pragma unroll
+    for (int s = 0; s < kEmbRounds; ++s) {
+      const int p0 = pb + 64 * s;
+      const int t = p0 + lane < n_tok ? tv[s] : -1;
+      uint64_t hit = __builtin_amdgcn_ballot_w64(t >= v0 && t < v0 + kEmbRows && t < vocab);
+      while (hit) {                     // the same mask in every wave: uniform
+        const int k = __builtin_ctzll(hit);
+        hit &= hit - 1;
+        const int tk = __shfl(t, k);
+        if (col < d) acc[tk - v0][tid] += dh0[static_cast<int64_t>(p0 + k) * d + col];
+      }
     }
   }
   if (col >= d) return;
