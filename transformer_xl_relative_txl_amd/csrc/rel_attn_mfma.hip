@@ -602,6 +602,10 @@ __global__ __launch_bounds__(256, 2) void rel_attn_mfma_append_kernel(AttnParams
 // Merge of the key-range splits: per query, m = max_s m_s and
 // O = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s (a split that saw no key
 // has m_s = -inf and adds nothing). One thread per query and 4 dimensions.
+// NS > 0: exactly NS splits, every split's m, l and O loaded before any is
+// used (a loop over a run-time count waited for them one split at a time);
+// NS = 0: any count. The sums run in split order either way.
+template <int NS>
 __global__ __launch_bounds__(256) void rel_attn_merge_kernel(AttnParams p) {
   const int64_t BHL = static_cast<int64_t>(p.B) * p.H * p.L;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -609,17 +613,38 @@ __global__ __launch_bounds__(256) void rel_attn_merge_kernel(AttnParams p) {
   const int64_t row = e / (DH / 4);
   const int c = static_cast<int>(e - row * (DH / 4));
   float m = -INFINITY;
-  for (int sp = 0; sp < p.n_split; ++sp) m = fmaxf(m, p.part_m[sp * BHL + row]);
   float l = 0.0f;
   f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int sp = 0; sp < p.n_split; ++sp) {
-    const float ms = p.part_m[sp * BHL + row];
-    if (!(ms > -INFINITY)) continue;
-    const float w = __builtin_amdgcn_exp2f(ms - m);
-    l += w * p.part_l[sp * BHL + row];
-    const f32x4 os = *reinterpret_cast<const f32x4 *>(p.part_o + (sp * BHL + row) * DH + 4 * c);
+  if constexpr (NS > 0) {
+    float ms[NS], ls[NS];
+    f32x4 os[NS];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] += w * os[q];
+    for (int sp = 0; sp < NS; ++sp) {
+      ms[sp] = p.part_m[sp * BHL + row];
+      ls[sp] = p.part_l[sp * BHL + row];
+      os[sp] = *reinterpret_cast<const f32x4 *>(p.part_o + (sp * BHL + row) * DH + 4 * c);
+    }
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp) m = fmaxf(m, ms[sp]);
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp) {
+      if (!(ms[sp] > -INFINITY)) continue;
+      const float w = __builtin_amdgcn_exp2f(ms[sp] - m);
+      l += w * ls[sp];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] += w * os[sp][q];
+    }
+  } else {
+    for (int sp = 0; sp < p.n_split; ++sp) m = fmaxf(m, p.part_m[sp * BHL + row]);
+    for (int sp = 0; sp < p.n_split; ++sp) {
+      const float ms = p.part_m[sp * BHL + row];
+      if (!(ms > -INFINITY)) continue;
+      const float w = __builtin_amdgcn_exp2f(ms - m);
+      l += w * p.part_l[sp * BHL + row];
+      const f32x4 os = *reinterpret_cast<const f32x4 *>(p.part_o + (sp * BHL + row) * DH + 4 * c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] += w * os[q];
+    }
   }
   const int64_t bh = row / p.L;
   const int i = static_cast<int>(row - bh * p.L);
@@ -761,8 +786,15 @@ txl_status launch_rel_attn_mfma(const AttnParams &p, hipStream_t s) {
   txl_status st = check_launch("rel_attn_mfma_kernel");
   if (st != TXL_OK || S == 1) return st;
   const int64_t threads = static_cast<int64_t>(p.B) * p.H * p.L * (DH / 4);
-  hipLaunchKernelGGL(rel_attn_merge_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)),
-                     dim3(256), 0, s, p);
+  const dim3 mgrid(static_cast<unsigned>((threads + 255) / 256));
+  if (S == 2)
+    hipLaunchKernelGGL(rel_attn_merge_kernel<2>, mgrid, dim3(256), 0, s, p);
+  else if (S == 3)
+    hipLaunchKernelGGL(rel_attn_merge_kernel<3>, mgrid, dim3(256), 0, s, p);
+  else if (S == 4)
+    hipLaunchKernelGGL(rel_attn_merge_kernel<4>, mgrid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(rel_attn_merge_kernel<0>, mgrid, dim3(256), 0, s, p);
   return check_launch("rel_attn_merge_kernel");
 }
 
