@@ -657,15 +657,27 @@ __global__ __launch_bounds__(256) void lse_finish_kernel(const float *__restrict
   const int n = blockIdx.x * kFinTok + tl;
   float m = -INFINITY, s = 0.0f;
   if (n < N) {
-    for (int t = grp; t < n_tiles; t += kFinGrp) {
-      const float mt = part_m[static_cast<int64_t>(t) * N + n];
-      const float st = part_s[static_cast<int64_t>(t) * N + n];
-      if (st <= 0.0f) continue;
-      if (mt > m) {
-        s = s * __expf(m - mt) + st;
-        m = mt;
-      } else {
-        s += st * __expf(mt - m);
+    // four of the group's tiles loaded before the first is combined (tiles
+    // past the end load the group's first and are skipped); the tiles are
+    // combined in the same order as one at a time
+    constexpr int kFinBatch = 4;
+    for (int t0 = grp; t0 < n_tiles; t0 += kFinBatch * kFinGrp) {
+      float mt[kFinBatch], st[kFinBatch];
+#pragma unroll
+      for (int u = 0; u < kFinBatch; ++u) {
+        const int t = t0 + u * kFinGrp < n_tiles ? t0 + u * kFinGrp : t0;
+        mt[u] = part_m[static_cast<int64_t>(t) * N + n];
+        st[u] = part_s[static_cast<int64_t>(t) * N + n];
+      }
+#pragma unroll
+      for (int u = 0; u < kFinBatch; ++u) {
+        if (t0 + u * kFinGrp >= n_tiles || st[u] <= 0.0f) continue;
+        if (mt[u] > m) {
+          s = s * __expf(m - mt[u]) + st[u];
+          m = mt[u];
+        } else {
+          s += st[u] * __expf(mt[u] - m);
+        }
       }
     }
   }
