@@ -46,9 +46,9 @@ TIMED_REPEATS = 5
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by the
 # same counters' reading of a plain copy of known size), valid only for the
 # kernel source they were taken on.
-ATTN_TRAFFIC = {"source_sha1": "678a1c745e8105dbe5abfb71aa1b700c6ba464e1",
+ATTN_TRAFFIC = {"source_sha1": "c5fc50ea69f27a4d5908780d34fbfb51d4dd27d4",
                 "profile": "profiles/rel_attn_B8_H16_L512_M512_hbm_traffic.md",
-                "rel_attn_mfma_append_kernel": 69.32e6, "rel_attn_mfma_kernel": 52.52e6}
+                "rel_attn_mfma_append_kernel": 69.34e6, "rel_attn_mfma_kernel": 52.53e6}
 
 
 def attn_flops(B, H, L, M_eff, d_h):
