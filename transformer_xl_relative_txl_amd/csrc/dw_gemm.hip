@@ -17,7 +17,9 @@
 // compute 128 x 128 (or 64 x 64) output tiles with v_mfma_f32_32x32x16_bf16,
 // two LDS buffers with one barrier per slab, and the K range split over
 // k_splits workgroups whose fp32 partials are added afterwards in split
-// order (a fixed order: the result does not depend on scheduling).
+// order (a fixed order: the result does not depend on scheduling). The
+// products of a layer run as one batch: a launch's workgroups are dealt to
+// the products in turn, so the splits need only fill the chip together.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -35,6 +37,19 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kXcds = 8;
 constexpr int KS = 64;  // k rows per slab
+
+// One product of a launch: its workgroups are [wg_begin, wg_begin + tiles
+// k_splits) of the grid, split s taking [wg_begin + s tiles, ...).
+struct DwJob {
+  const __bf16 *x, *y;
+  float *out;
+  int64_t ldx, ldy, split_stride;
+  int rows, N, k_rows, k_splits, tiles, wg_begin;
+};
+struct DwBatch {
+  DwJob job[kMaxDwProblems];
+  int n;
+};
 
 __device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
@@ -88,26 +103,32 @@ __device__ inline rsrc_t slab_rsrc(const __bf16 *base, int64_t ld, int c0, int k
 }
 
 template <int BM, int BN>
-__global__ __launch_bounds__(256, 2) void dw_kernel(const __bf16 *__restrict__ x, int64_t ldx,
-                                                    const __bf16 *__restrict__ y, int64_t ldy,
-                                                    int rows, int N, int k_rows, int k_splits,
-                                                    float *__restrict__ out, int64_t split_stride) {
+__global__ __launch_bounds__(256, 2) void dw_kernel(DwBatch bt) {
   constexpr int WM = BM / 64, WN = BN / 64;  // 32 x 32 blocks per wave
   __shared__ __attribute__((aligned(4096))) __bf16 sx0[KS * BM];
   __shared__ __attribute__((aligned(4096))) __bf16 sx1[KS * BM];
   __shared__ __attribute__((aligned(4096))) __bf16 sy0[KS * BN];
   __shared__ __attribute__((aligned(4096))) __bf16 sy1[KS * BN];
 
-  // XCD-contiguous tile assignment (a bijection on [0, T)); split s takes
-  // the tile indices [s T / k_splits, (s + 1) T / k_splits)
+  // XCD-contiguous workgroup order (a bijection on [0, T)), then the
+  // product owning the index (a wave-uniform choice among the batch's
+  // entries, made with constant indices so the entries stay scalar)
   const int T = gridDim.x;
   const int bid = blockIdx.x;
   const int xc = bid % kXcds, local = bid / kXcds;
   const int q = T / kXcds, rem = T % kXcds;
-  int tile = xc * q + (xc < rem ? xc : rem) + local;
-  const int per = T / k_splits;
-  const int split = tile / per;
-  tile -= split * per;
+  const int gidx = xc * q + (xc < rem ? xc : rem) + local;
+  DwJob J = bt.job[0];
+#pragma unroll
+  for (int k = 1; k < kMaxDwProblems; ++k)
+    if (k < bt.n && gidx >= bt.job[k].wg_begin) J = bt.job[k];
+  const __bf16 *__restrict__ x = J.x;
+  const __bf16 *__restrict__ y = J.y;
+  const int64_t ldx = J.ldx, ldy = J.ldy;
+  const int N = J.N, k_rows = J.k_rows, k_splits = J.k_splits;
+  int tile = gidx - J.wg_begin;
+  const int split = tile / J.tiles;
+  tile -= split * J.tiles;
   const int n_tn = N / BN;
   const int tm = tile / n_tn, tn = tile - tm * n_tn;
   const int m0 = tm * BM, n0 = tn * BN;
@@ -193,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void dw_kernel(const __bf16 *__restrict__ x
 
   // register 4 a + c of block (i, j) holds out[m0 + wm BM/2 + 32 i + 8 a +
   // 4 (lane / 32) + c][n0 + wn BN/2 + 32 j + lane % 32]
-  float *o = out + split * split_stride;
+  float *o = J.out + split * J.split_stride;
   const int r = lane & 31, hh = lane >> 5;
 #pragma unroll
   for (int i = 0; i < WM; ++i)
@@ -215,50 +236,109 @@ __global__ __launch_bounds__(256, 2) void dw_kernel(const __bf16 *__restrict__ x
 // 128 x 128 tiles when the output divides into them, else 64 x 64.
 static bool dw_big_tiles(int rows, int N) { return rows % 128 == 0 && N % 128 == 0; }
 
-int dw_gemm_splits(int rows, int N, int k_rows) {
-  const int tm = dw_big_tiles(rows, N) ? 128 : 64;
-  const int64_t tiles = static_cast<int64_t>(rows / tm) * (N / tm);
-  const int n_slabs = (k_rows + KS - 1) / KS;
-  // up to about two workgroups per CU, each split keeping at least 4 slabs
-  // (the 16-layer training step: 8 slabs per split 10.36 ms, 4 slabs
-  // 10.28, 3 slabs 10.36 - the partial sums then cost more than the
-  // occupancy brings)
-  int s = 1;
-  while (s < 32 && tiles * s < 512 && n_slabs / (2 * s) >= 4) s *= 2;
-  return s;
+// Splits of a batch: every split of every product should carry about the
+// same work, total / kDwTargetWgs, where a product's work is its tiles x K
+// slabs (a 64 x 64 tile counts a quarter of a 128 x 128 one); at least one
+// slab per split, at most 64 splits.
+constexpr int64_t kDwTargetWgs = 512;
+static void dw_plan(const DwProblem *p, int n, int *splits) {
+  int64_t total = 0;  // in quarter tile-slabs (a 64 x 64 tile and one slab)
+  for (int j = 0; j < n; ++j) {
+    const int tm = dw_big_tiles(p[j].rows, p[j].N) ? 128 : 64;
+    const int64_t tiles = static_cast<int64_t>(p[j].rows / tm) * (p[j].N / tm);
+    const int64_t slabs = (p[j].k_rows + KS - 1) / KS;
+    total += tiles * slabs * (tm == 128 ? 4 : 1);
+  }
+  int64_t per = total / kDwTargetWgs;  // quarter tile-slabs per workgroup
+  if (per < 1) per = 1;
+  for (int j = 0; j < n; ++j) {
+    const int q = dw_big_tiles(p[j].rows, p[j].N) ? 4 : 1;
+    const int64_t slabs = (p[j].k_rows + KS - 1) / KS;
+    int64_t sp = (slabs * q + per / 2) / per;
+    if (sp > slabs) sp = slabs;
+    if (sp > 64) sp = 64;
+    splits[j] = sp < 1 ? 1 : static_cast<int>(sp);
+  }
 }
 
-txl_status launch_dw_gemm(const void *x, int64_t ldx, int rows, const void *y, int64_t ldy, int N,
-                          int k_rows, int k_splits, float *out, int64_t split_stride,
-                          hipStream_t s) {
-  if (rows == 0 || N == 0) return TXL_OK;
-  if (rows < 0 || N < 0 || k_rows < 0 || rows % 64 || N % 64)
-    return fail(TXL_ERR_INVALID_ARG, "dw_gemm: rows %d and N %d must be multiples of 64, k_rows %d >= 0",
-                rows, N, k_rows);
-  if (!x || !y || !out || ldx < rows || ldy < N || ldx % 8 || ldy % 8 ||
-      reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 16)
-    return fail(TXL_ERR_INVALID_ARG, "dw_gemm: operands must be 16-byte aligned with ldx >= rows, "
-                                 "ldy >= N, strides multiples of 8");
-  // a slab's resource spans up to 64 rows: offsets within it fit 32 bits
-  if (static_cast<int64_t>(KS) * (ldx > ldy ? ldx : ldy) * 2 >= (int64_t{1} << 31))
-    return fail(TXL_ERR_UNSUPPORTED, "dw_gemm: row stride too large");
-  if (k_splits < 1 || (k_splits > 1 && split_stride < static_cast<int64_t>(rows) * N))
-    return fail(TXL_ERR_INVALID_ARG, "dw_gemm: k_splits %d with split stride %lld", k_splits,
-                static_cast<long long>(split_stride));
-  const bool big = dw_big_tiles(rows, N);
-  const int tm = big ? 128 : 64;
-  const int64_t tiles = static_cast<int64_t>(rows / tm) * (N / tm) * k_splits;
-  if (tiles > 0x7fffffff) return fail(TXL_ERR_UNSUPPORTED, "dw_gemm: too many tiles");
-  const __bf16 *xb = static_cast<const __bf16 *>(x);
-  const __bf16 *yb = static_cast<const __bf16 *>(y);
+size_t dw_batch_part_floats(const DwProblem *p, int n) {
+  if (n < 1 || n > kMaxDwProblems) return 0;
+  int sp[kMaxDwProblems];
+  dw_plan(p, n, sp);
+  size_t f = 0;
+  for (int j = 0; j < n; ++j)
+    if (sp[j] > 1) f += static_cast<size_t>(sp[j]) * p[j].rows * p[j].N;
+  return f;
+}
+
+txl_status launch_dw_batch(const DwProblem *p, int n, float *part, size_t part_floats,
+                           hipStream_t s) {
+  if (n < 1 || n > kMaxDwProblems) return fail(TXL_ERR_INVALID_ARG, "dw_batch: %d products", n);
+  for (int j = 0; j < n; ++j) {
+    const DwProblem &d = p[j];
+    if (d.rows < 0 || d.N < 0 || d.k_rows < 0 || d.rows % 64 || d.N % 64)
+      return fail(TXL_ERR_INVALID_ARG, "dw_gemm: rows %d and N %d must be multiples of 64, k_rows %d >= 0",
+                  d.rows, d.N, d.k_rows);
+    if (d.rows == 0 || d.N == 0) continue;
+    if (!d.x || !d.y || !d.out || d.ldx < d.rows || d.ldy < d.N || d.ldx % 8 || d.ldy % 8 ||
+        reinterpret_cast<uintptr_t>(d.x) % 16 || reinterpret_cast<uintptr_t>(d.y) % 16)
+      return fail(TXL_ERR_INVALID_ARG, "dw_gemm: operands must be 16-byte aligned with ldx >= rows, "
+                                   "ldy >= N, strides multiples of 8");
+    // a slab's resource spans up to 64 rows: offsets within it fit 32 bits
+    if (static_cast<int64_t>(KS) * (d.ldx > d.ldy ? d.ldx : d.ldy) * 2 >= (int64_t{1} << 31))
+      return fail(TXL_ERR_UNSUPPORTED, "dw_gemm: row stride too large");
+  }
+  const size_t need = dw_batch_part_floats(p, n);
+  if (need > 0 && (!part || part_floats < need))
+    return fail(TXL_ERR_WORKSPACE, "dw_batch: %zu partial floats < %zu", part_floats, need);
+  int sp[kMaxDwProblems];
+  dw_plan(p, n, sp);
+  // one launch per tile shape
+  DwBatch big = {}, small = {};
+  int64_t wg_big = 0, wg_small = 0;
+  size_t poff = 0;
+  for (int j = 0; j < n; ++j) {
+    const DwProblem &d = p[j];
+    if (d.rows == 0 || d.N == 0) continue;
+    const bool b = dw_big_tiles(d.rows, d.N);
+    const int tm = b ? 128 : 64;
+    DwJob J;
+    J.x = static_cast<const __bf16 *>(d.x);
+    J.y = static_cast<const __bf16 *>(d.y);
+    J.ldx = d.ldx;
+    J.ldy = d.ldy;
+    J.rows = d.rows;
+    J.N = d.N;
+    J.k_rows = d.k_rows;
+    J.k_splits = sp[j];
+    J.tiles = (d.rows / tm) * (d.N / tm);
+    J.split_stride = static_cast<int64_t>(d.rows) * d.N;
+    J.out = sp[j] > 1 ? part + poff : d.out;
+    if (sp[j] > 1) poff += static_cast<size_t>(sp[j]) * d.rows * d.N;
+    DwBatch &B = b ? big : small;
+    int64_t &wg = b ? wg_big : wg_small;
+    J.wg_begin = static_cast<int>(wg);
+    wg += static_cast<int64_t>(J.tiles) * sp[j];
+    B.job[B.n++] = J;
+  }
+  if (wg_big > 0x7fffffff || wg_small > 0x7fffffff) return fail(TXL_ERR_UNSUPPORTED, "dw_gemm: too many tiles");
   (void)hipGetLastError();
-  if (big)
-    hipLaunchKernelGGL((dw_kernel<128, 128>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s,
-                       xb, ldx, yb, ldy, rows, N, k_rows, k_splits, out, split_stride);
-  else
-    hipLaunchKernelGGL((dw_kernel<64, 64>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s, xb,
-                       ldx, yb, ldy, rows, N, k_rows, k_splits, out, split_stride);
-  return check_launch("dw_kernel");
+  if (big.n)
+    hipLaunchKernelGGL((dw_kernel<128, 128>), dim3(static_cast<unsigned>(wg_big)), dim3(256), 0, s, big);
+  if (small.n)
+    hipLaunchKernelGGL((dw_kernel<64, 64>), dim3(static_cast<unsigned>(wg_small)), dim3(256), 0, s, small);
+  txl_status st = check_launch("dw_kernel");
+  if (st != TXL_OK) return st;
+  // the split products' partials, each summed in split order
+  poff = 0;
+  for (int j = 0; j < n; ++j) {
+    const DwProblem &d = p[j];
+    if (d.rows == 0 || d.N == 0 || sp[j] == 1) continue;
+    const int64_t stride = static_cast<int64_t>(d.rows) * d.N;
+    if ((st = launch_reduce_parts(part + poff, sp[j], stride, stride, d.out, s)) != TXL_OK) return st;
+    poff += static_cast<size_t>(sp[j]) * d.rows * d.N;
+  }
+  return TXL_OK;
 }
 
 }  // namespace txl

@@ -278,24 +278,34 @@ TapeLayer tape_at(const TapeLayout &t, const void *tape, int n) {
   return l;
 }
 
-// out [rows, N] fp32 = X^T Y over the first K rows of X [*, ldx] and Y
-// [*, ldy] (bf16, one segment row per row): one product storing fp32, or
-// split-K partials added in split order.
-txl_status dw_gemm(const __bf16 *x, int64_t ldx, int rows, const __bf16 *y, int64_t ldy, int N, int K,
-                   float *out, float *part, hipStream_t stream) {
-  const int splits = dw_gemm_splits(rows, N, K);
-  const int64_t stride = static_cast<int64_t>(rows) * N;
-  txl_status s = launch_dw_gemm(x, ldx, rows, y, ldy, N, K, splits, splits > 1 ? part : out, stride,
-                                stream);
-  if (s != TXL_OK || splits == 1) return s;
-  return launch_reduce_parts(part, splits, stride, stride, out, stream);
+// A layer's seven weight-gradient products, out [rows, N] fp32 = X^T Y over
+// the first K rows of X [*, ldx] and Y [*, ldy] (bf16, one segment row per
+// row), in the order W2, W1, W^O, W^Q, W^K, W^V, W_R. Only the shapes matter
+// for sizing (null pointers).
+struct LayerDw {
+  DwProblem p[7];
+};
+LayerDw layer_dw(const txl_stack_config &c, int R, int KR, int ML, const __bf16 *dx2b, const __bf16 *f,
+                 const __bf16 *dfpre, const __bf16 *h1, const __bf16 *dx1b, const __bf16 *o,
+                 const __bf16 *acat, const __bf16 *hin, const __bf16 *kvg, const __bf16 *ext,
+                 const __bf16 *drb, const __bf16 *st_rows, const txl_layer_grads *g) {
+  const int HD = c.n_head * c.d_h;
+  LayerDw L;
+  L.p[0] = {dx2b, c.d, c.d, f, c.d_ff, c.d_ff, R, g ? g->w2 : nullptr};
+  L.p[1] = {dfpre, c.d_ff, c.d_ff, h1, c.d, c.d, R, g ? g->w1 : nullptr};
+  L.p[2] = {dx1b, c.d, c.d, o, HD, HD, R, g ? g->wo : nullptr};
+  L.p[3] = {acat, 3 * HD, HD, hin, c.d, c.d, R, g ? g->wq : nullptr};
+  L.p[4] = {kvg, 2 * HD, HD, ext, c.d, c.d, KR, g ? g->wk : nullptr};
+  L.p[5] = {kvg ? kvg + HD : nullptr, 2 * HD, HD, ext, c.d, c.d, KR, g ? g->wv : nullptr};
+  L.p[6] = {drb, HD, HD, st_rows, c.d, c.d, ML, g ? g->wr : nullptr};
+  return L;
 }
 
 // Workspace of the segment backward (one layer's intermediates, reused from
 // the top layer down).
 struct BwdWs {
   size_t g0, g1, dx2, dx2b, dh1, dx1, dx1b, dfpre, dout, kvg, drb, attn, attn_bytes, ext, acat, wcatT,
-      wT, st, pg, pb, part, total;
+      wT, st, pg, pb, part, part_floats, total;
 };
 
 BwdWs bwd_ws(const txl_stack_config &c) {
@@ -334,20 +344,12 @@ BwdWs bwd_ws(const txl_stack_config &c) {
   const size_t ln_blocks = ln_backward_blocks(static_cast<int>(rows), &rpb);
   w.pg = take(ln_blocks * c.d * 4);
   w.pb = take(ln_blocks * c.d * 4);
-  // the largest split-K partial set of the weight-gradient products
-  size_t part = 0;
-  auto need = [&](int r, int n, int k) {
-    const int s = dw_gemm_splits(r, n, k);
-    if (s > 1) part = std::max(part, static_cast<size_t>(s) * r * n);
-  };
-  const int R = static_cast<int>(rows), KR = static_cast<int>(krows), ML = static_cast<int>(ml);
-  need(c.d, c.d_ff, R);
-  need(c.d_ff, c.d, R);
-  need(c.d, HD, R);
-  need(HD, c.d, R);
-  need(HD, c.d, KR);
-  need(HD, c.d, ML);
-  w.part = take(part * 4);
+  // the split-K partials of a layer's weight-gradient batch
+  const LayerDw dw = layer_dw(c, static_cast<int>(rows), static_cast<int>(krows), static_cast<int>(ml),
+                              nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                              nullptr, nullptr, nullptr, nullptr, nullptr);
+  w.part_floats = dw_batch_part_floats(dw.p, 7);
+  w.part = take(w.part_floats * 4);
   w.total = off;
   return w;
 }
@@ -620,14 +622,10 @@ TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t 
     // LN2
     s = ln_bwd(tl.x2, lw.ln2_g, gin, dx2, dx2b, g.ln2_g, g.ln2_b);
     if (s != TXL_OK) return s;
-    // dW2 = dX2^T F
-    if ((s = dw_gemm(dx2b, c.d, c.d, tl.f, c.d_ff, c.d_ff, R, g.w2, part, stream)) != TXL_OK) return s;
     // dFpre = (dX2 W2) * GELU'(Fpre)
     GemmParams pf = dense(dx2b, c.d, R, c.d_ff, c.d, w2T, dfpre, c.d_ff);
     pf.pre_in = tl.fpre;
     if ((s = launch_gemm(pf, kEpiGeluGradBf16, stream)) != TXL_OK) return s;
-    // dW1 = dFpre^T H1
-    if ((s = dw_gemm(dfpre, c.d_ff, c.d_ff, tl.h1, c.d, c.d, R, g.w1, part, stream)) != TXL_OK) return s;
     // dH1 = dX2 + dFpre W1
     GemmParams ph = dense(dfpre, c.d_ff, R, c.d, c.d_ff, w1T, dh1, c.d);
     ph.res32 = dx2;
@@ -635,8 +633,7 @@ TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t 
     if ((s = launch_gemm(ph, kEpiResidualF32, stream)) != TXL_OK) return s;
     // LN1
     if ((s = ln_bwd(tl.x1, lw.ln1_g, dh1, dx1, dx1b, g.ln1_g, g.ln1_b)) != TXL_OK) return s;
-    // dW^O = dX1^T A;  dA = dX1 W^O
-    if ((s = dw_gemm(dx1b, c.d, c.d, tl.o, HD, HD, R, g.wo, part, stream)) != TXL_OK) return s;
+    // dA = dX1 W^O
     if ((s = launch_gemm(dense(dx1b, c.d, R, HD, c.d, woT, b16(w.dout), HD), kEpiStoreBf16, stream)) !=
         TXL_OK)
       return s;
@@ -692,15 +689,18 @@ TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t 
     rows.dr = drb;
     rows.dr_ld = HD;
     if ((s = rel_attn_bwd_impl(&a, &ag, &rows, base + w.attn, w.attn_bytes, stream)) != TXL_OK) return s;
-    // dW^Q = dQ^T H
-    if ((s = dw_gemm(acat, 3 * HD, HD, tl.hin, c.d, c.d, R, g.wq, part, stream)) != TXL_OK) return s;
-    // dW^K = dK^T [mem; H], dW^V = dV^T [mem; H] (slots a row does not hold read as 0)
+    // [memory; segment] rows for dW^K and dW^V (slots a row does not hold read as 0)
     if ((s = launch_gather_ext(tl.mem, tl.valid, tl.hin, c.B, c.M, c.L, c.d, ext, stream)) != TXL_OK)
       return s;
-    if ((s = dw_gemm(kvg, 2 * HD, HD, ext, c.d, c.d, KR, g.wk, part, stream)) != TXL_OK) return s;
-    if ((s = dw_gemm(kvg + HD, 2 * HD, HD, ext, c.d, c.d, KR, g.wv, part, stream)) != TXL_OK) return s;
+    // the layer's weight gradients in one batch (their inputs are all still
+    // in place): dW2 = dX2^T F, dW1 = dFpre^T H1, dW^O = dX1^T A,
+    // dW^Q = dQ^T H, dW^K = dK^T [mem; H], dW^V = dV^T [mem; H],
     // dW_R = dR^T S (R = S W_R^T for distances M+L-1 .. 0)
-    if ((s = dw_gemm(drb, HD, HD, st_rows, c.d, c.d, ML, g.wr, part, stream)) != TXL_OK) return s;
+    {
+      const LayerDw dw = layer_dw(c, R, KR, ML, dx2b, tl.f, dfpre, tl.h1, dx1b, tl.o, acat, tl.hin, kvg,
+                                  ext, drb, st_rows, &g);
+      if ((s = launch_dw_batch(dw.p, 7, part, w.part_floats, stream)) != TXL_OK) return s;
+    }
     // dH^(n-1) = dX1 + [dQ | dK_seg | dV_seg] [W^Q; W^K; W^V]
     GemmParams pi = dense(acat, 3 * HD, R, c.d, 3 * HD, wcatT, gout, c.d);
     pi.res32 = dx1;

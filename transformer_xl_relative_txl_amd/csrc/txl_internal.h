@@ -258,13 +258,26 @@ struct GemmParams {
 };
 txl_status launch_gemm(const GemmParams &p, int epi, hipStream_t s);
 // Weight gradients: out [rows, N] fp32 = X^T Y over the first k_rows rows of
-// X [*, ldx] bf16 (rows columns used) and Y [*, ldy] bf16 (N columns used),
-// split over k_splits contiguous K ranges whose fp32 results go to
-// out + s * split_stride (k_splits == 1: out). rows and N multiples of 64,
-// ldx, ldy and the base pointers 16-byte aligned in bf16 elements (x8).
-int dw_gemm_splits(int rows, int N, int k_rows);
-txl_status launch_dw_gemm(const void *x, int64_t ldx, int rows, const void *y, int64_t ldy, int N,
-                          int k_rows, int k_splits, float *out, int64_t split_stride, hipStream_t s);
+// X [*, ldx] bf16 (rows columns used) and Y [*, ldy] bf16 (N columns used);
+// rows and N multiples of 64, ldx and ldy multiples of 8, x and y 16-byte
+// aligned. A batch of such products runs in one launch per tile shape: each
+// product's K range is split so that the splits of the whole batch carry
+// about the same number of K slabs; a split product's fp32 partials go to
+// `part` and are summed into out in split order afterwards (deterministic).
+struct DwProblem {
+  const void *x;
+  int64_t ldx;
+  int rows;
+  const void *y;
+  int64_t ldy;
+  int N;
+  int k_rows;
+  float *out;
+};
+constexpr int kMaxDwProblems = 8;
+// fp32 elements of `part` that launch_dw_batch needs for these shapes
+size_t dw_batch_part_floats(const DwProblem *p, int n);
+txl_status launch_dw_batch(const DwProblem *p, int n, float *part, size_t part_floats, hipStream_t s);
 // y = LN(x) over rows of d, x = sum of n_parts fp32 buffers (part_stride
 // elements apart, added in order) plus the bf16 residual res (may be null)
 // x_out (may be null) receives the summed fp32 x (the LayerNorm's input)
