@@ -90,30 +90,6 @@ __global__ __launch_bounds__(256) void gather_ext_kernel(const u32x4 *__restrict
   y[e] = v;
 }
 
-// out[i] = sum_{s < S} part[s * stride + i], s ascending (4 floats a thread).
-// The parts are loaded eight at a time (the index clamped to the last part,
-// so the loads need no branch) before any of them is added: one load at a
-// time left a thread waiting a full memory round trip per part.
-constexpr int kPartBatch = 8;
-__global__ __launch_bounds__(256) void reduce_parts_kernel(const float *__restrict__ part, int S,
-                                                           int64_t stride, int64_t n4,
-                                                           float *__restrict__ out) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (e >= n4) return;
-  const f32x4 *p = reinterpret_cast<const f32x4 *>(part) + e;
-  const int64_t st4 = stride / 4;
-  f32x4 acc = p[0];
-  for (int s0 = 1; s0 < S; s0 += kPartBatch) {
-    f32x4 v[kPartBatch];
-#pragma unroll
-    for (int t = 0; t < kPartBatch; ++t) v[t] = p[(s0 + t < S ? s0 + t : S - 1) * st4];
-#pragma unroll
-    for (int t = 0; t < kPartBatch; ++t)
-      if (s0 + t < S) acc += v[t];
-  }
-  reinterpret_cast<f32x4 *>(out)[e] = acc;
-}
-
 // The same sum for many parts over few columns, for two part sets at once
 // (the LayerNorm gamma and beta partials: hundreds of parts, d columns):
 // blockIdx.y picks the set, a workgroup owns 8 columns, its 32 thread
@@ -346,19 +322,6 @@ txl_status launch_gather_ext(const void *mem, const int32_t *valid, const void *
                      static_cast<const u32x4 *>(mem), valid, static_cast<const u32x4 *>(seg), B, M, L, cpr,
                      static_cast<u32x4 *>(y));
   return check_launch("gather_ext_kernel");
-}
-
-txl_status launch_reduce_parts(const float *part, int S, int64_t stride, int64_t n, float *out,
-                               hipStream_t s) {
-  if (n == 0) return TXL_OK;
-  if (n % 4 || reinterpret_cast<uintptr_t>(part) % 16 || reinterpret_cast<uintptr_t>(out) % 16 ||
-      stride % 4)
-    return fail(TXL_ERR_UNSUPPORTED, "reduce_parts: n, stride multiples of 4, 16-byte aligned");
-  const int64_t n4 = n / 4;
-  (void)hipGetLastError();
-  hipLaunchKernelGGL(reduce_parts_kernel, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, s,
-                     part, S, stride, n4, out);
-  return check_launch("reduce_parts_kernel");
 }
 
 txl_status launch_reduce_cols2(const float *part0, float *out0, const float *part1, float *out1, int S,

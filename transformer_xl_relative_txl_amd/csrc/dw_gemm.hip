@@ -51,6 +51,20 @@ struct DwBatch {
   int n;
 };
 
+// The split products' partial sums, all in one launch: product j owns the
+// threads [e_begin, e_begin + n4) (e_begin a multiple of 256, so a
+// workgroup serves one product), four floats a thread.
+struct DwRed {
+  const float *part;
+  float *out;
+  int64_t n4, e_begin;
+  int S;
+};
+struct DwRedBatch {
+  DwRed job[kMaxDwProblems];
+  int n;
+};
+
 __device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
                                            static_cast<int>(bytes), 0x00020000);
@@ -231,6 +245,33 @@ __global__ __launch_bounds__(256, 2) void dw_kernel(DwBatch bt) {
     }
 }
 
+// out[i] = sum_{s < S} part[s * n + i] (n = 4 n4), s ascending. The parts
+// are loaded eight at a time (the index clamped to the last part, so the
+// loads need no branch) before any of them is added: one load at a time
+// left a thread waiting a full memory round trip per part.
+constexpr int kPartBatch = 8;
+__global__ __launch_bounds__(256) void dw_reduce_kernel(DwRedBatch rb) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int64_t gidx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  DwRed R = rb.job[0];
+#pragma unroll
+  for (int k = 1; k < kMaxDwProblems; ++k)
+    if (k < rb.n && gidx >= rb.job[k].e_begin) R = rb.job[k];
+  const int64_t e = gidx - R.e_begin;
+  if (e >= R.n4) return;
+  const f32x4 *p = reinterpret_cast<const f32x4 *>(R.part) + e;
+  f32x4 acc = p[0];
+  for (int s0 = 1; s0 < R.S; s0 += kPartBatch) {
+    f32x4 v[kPartBatch];
+#pragma unroll
+    for (int t = 0; t < kPartBatch; ++t) v[t] = p[(s0 + t < R.S ? s0 + t : R.S - 1) * R.n4];
+#pragma unroll
+    for (int t = 0; t < kPartBatch; ++t)
+      if (s0 + t < R.S) acc += v[t];
+  }
+  reinterpret_cast<f32x4 *>(R.out)[e] = acc;
+}
+
 }  // namespace
 
 // 128 x 128 tiles when the output divides into them, else 64 x 64.
@@ -329,16 +370,31 @@ txl_status launch_dw_batch(const DwProblem *p, int n, float *part, size_t part_f
     hipLaunchKernelGGL((dw_kernel<64, 64>), dim3(static_cast<unsigned>(wg_small)), dim3(256), 0, s, small);
   txl_status st = check_launch("dw_kernel");
   if (st != TXL_OK) return st;
-  // the split products' partials, each summed in split order
+  // the split products' partials, each summed in split order, one launch
+  DwRedBatch rb = {};
+  int64_t threads = 0;
   poff = 0;
   for (int j = 0; j < n; ++j) {
     const DwProblem &d = p[j];
     if (d.rows == 0 || d.N == 0 || sp[j] == 1) continue;
-    const int64_t stride = static_cast<int64_t>(d.rows) * d.N;
-    if ((st = launch_reduce_parts(part + poff, sp[j], stride, stride, d.out, s)) != TXL_OK) return st;
+    DwRed R;
+    R.part = part + poff;
+    R.out = d.out;
+    R.n4 = static_cast<int64_t>(d.rows) * d.N / 4;
+    R.S = sp[j];
+    R.e_begin = threads;
+    threads += (R.n4 + 255) / 256 * 256;
+    rb.job[rb.n++] = R;
     poff += static_cast<size_t>(sp[j]) * d.rows * d.N;
   }
-  return TXL_OK;
+  if (rb.n == 0) return TXL_OK;
+  if (reinterpret_cast<uintptr_t>(part) % 16)
+    return fail(TXL_ERR_UNSUPPORTED, "dw_batch: partials must be 16-byte aligned");
+  for (int j = 0; j < rb.n; ++j)
+    if (reinterpret_cast<uintptr_t>(rb.job[j].out) % 16)
+      return fail(TXL_ERR_UNSUPPORTED, "dw_batch: split product outputs must be 16-byte aligned");
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3(static_cast<unsigned>(threads / 256)), dim3(256), 0, s, rb);
+  return check_launch("dw_reduce_kernel");
 }
 
 }  // namespace txl
