@@ -90,20 +90,26 @@ __global__ __launch_bounds__(256) void gather_ext_kernel(const u32x4 *__restrict
   y[e] = v;
 }
 
-// The same sum for many parts over few columns, for two part sets at once
-// (the LayerNorm gamma and beta partials: hundreds of parts, d columns):
-// blockIdx.y picks the set, a workgroup owns 8 columns, its 32 thread
-// groups each add every 32nd part in order, and the 32 group sums are
-// added in group order.
-constexpr int kColGroups = 32, kColsPerBlock = 8;
-__global__ __launch_bounds__(256) void reduce_cols2_kernel(const float *__restrict__ part0,
-                                                           float *__restrict__ out0,
-                                                           const float *__restrict__ part1,
-                                                           float *__restrict__ out1, int S,
-                                                           int64_t stride, int64_t n) {
+// Column sums of many parts over few columns, for up to four part sets in
+// one launch (the LayerNorm gamma and beta partials of a layer's two
+// LayerNorms: hundreds of parts, d columns): blockIdx.y picks the set, a
+// workgroup owns 8 columns, its 32 thread groups each add every 32nd part in
+// order, and the 32 group sums are added in group order.
+constexpr int kColGroups = 32, kColsPerBlock = 8, kMaxColSets = 4;
+struct ColSets {
+  const float *part[kMaxColSets];
+  float *out[kMaxColSets];
+};
+__global__ __launch_bounds__(256) void reduce_cols_kernel(ColSets cs, int S, int64_t stride, int64_t n) {
   __shared__ float red[kColGroups][kColsPerBlock];
-  const float *part = blockIdx.y ? part1 : part0;
-  float *out = blockIdx.y ? out1 : out0;
+  const float *part = cs.part[0];
+  float *out = cs.out[0];
+#pragma unroll
+  for (int k = 1; k < kMaxColSets; ++k)
+    if (static_cast<int>(blockIdx.y) == k) {
+      part = cs.part[k];
+      out = cs.out[k];
+    }
   const int cl = threadIdx.x % kColsPerBlock, grp = threadIdx.x / kColsPerBlock;
   const int64_t col = static_cast<int64_t>(blockIdx.x) * kColsPerBlock + cl;
   float acc = 0.0f;
@@ -324,14 +330,21 @@ txl_status launch_gather_ext(const void *mem, const int32_t *valid, const void *
   return check_launch("gather_ext_kernel");
 }
 
-txl_status launch_reduce_cols2(const float *part0, float *out0, const float *part1, float *out1, int S,
-                               int64_t stride, int64_t n, hipStream_t s) {
-  if (n == 0) return TXL_OK;
+txl_status launch_reduce_cols(const float *const *parts, float *const *outs, int n_sets, int S,
+                              int64_t stride, int64_t n, hipStream_t s) {
+  if (n == 0 || n_sets == 0) return TXL_OK;
+  if (n_sets < 0 || n_sets > kMaxColSets)
+    return fail(TXL_ERR_INVALID_ARG, "reduce_cols: %d part sets (at most %d)", n_sets, kMaxColSets);
+  ColSets cs = {};
+  for (int k = 0; k < n_sets; ++k) {
+    cs.part[k] = parts[k];
+    cs.out[k] = outs[k];
+  }
   (void)hipGetLastError();
-  hipLaunchKernelGGL(reduce_cols2_kernel,
-                     dim3(static_cast<unsigned>((n + kColsPerBlock - 1) / kColsPerBlock), 2), dim3(256), 0,
-                     s, part0, out0, part1, out1, S, stride, n);
-  return check_launch("reduce_cols2_kernel");
+  hipLaunchKernelGGL(reduce_cols_kernel,
+                     dim3(static_cast<unsigned>((n + kColsPerBlock - 1) / kColsPerBlock), n_sets), dim3(256), 0,
+                     s, cs, S, stride, n);
+  return check_launch("reduce_cols_kernel");
 }
 
 // rows per workgroup of the LayerNorm backward: at least kLnBwdMinRows, about

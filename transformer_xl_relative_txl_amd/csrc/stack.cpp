@@ -305,7 +305,7 @@ LayerDw layer_dw(const txl_stack_config &c, int R, int KR, int ML, const __bf16 
 // the top layer down).
 struct BwdWs {
   size_t g0, g1, dx2, dx2b, dh1, dx1, dx1b, dfpre, dout, kvg, drb, attn, attn_bytes, ext, acat, wcatT,
-      wT, st, pg, pb, part, part_floats, total;
+      wT, st, pg, pb, pg1, pb1, part, part_floats, total;
 };
 
 BwdWs bwd_ws(const txl_stack_config &c) {
@@ -342,8 +342,10 @@ BwdWs bwd_ws(const txl_stack_config &c) {
   w.st = take(ml * c.d * 2);
   int rpb;
   const size_t ln_blocks = ln_backward_blocks(static_cast<int>(rows), &rpb);
-  w.pg = take(ln_blocks * c.d * 4);
+  w.pg = take(ln_blocks * c.d * 4);   // LN2's gamma / beta partials
   w.pb = take(ln_blocks * c.d * 4);
+  w.pg1 = take(ln_blocks * c.d * 4);  // LN1's (summed together at the layer's end)
+  w.pb1 = take(ln_blocks * c.d * 4);
   // the split-K partials of a layer's weight-gradient batch
   const LayerDw dw = layer_dw(c, static_cast<int>(rows), static_cast<int>(krows), static_cast<int>(ml),
                               nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
@@ -588,12 +590,11 @@ TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t 
   txl_status s = launch_sinusoid_rows(c.M, c.L, c.d, st_rows, stream);
   if (s != TXL_OK) return s;
 
+  // the LayerNorm backward; its gamma / beta partials (per workgroup) are
+  // summed for both LayerNorms of a layer in one launch at the layer's end
   auto ln_bwd = [&](const float *x, const void *gamma, const float *dyv, float *dx, __bf16 *dxb,
-                    float *dg, float *db) {
-    txl_status r = launch_ln_backward(x, gamma, dyv, dx, dxb, f32(w.pg), f32(w.pb), R, c.d,
-                                      c.ln_eps, stream);
-    if (r != TXL_OK) return r;
-    return launch_reduce_cols2(f32(w.pg), dg, f32(w.pb), db, ln_blocks, c.d, c.d, stream);
+                    float *pg, float *pb) {
+    return launch_ln_backward(x, gamma, dyv, dx, dxb, pg, pb, R, c.d, c.ln_eps, stream);
   };
 
   const float *gin = dy;
@@ -620,7 +621,7 @@ TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t 
         {lw.wv, c.d, HD, c.d, wcatT, 3 * HD, 2 * HD}};
     if ((s = launch_transpose_batch(jobs, 6, stream)) != TXL_OK) return s;
     // LN2
-    s = ln_bwd(tl.x2, lw.ln2_g, gin, dx2, dx2b, g.ln2_g, g.ln2_b);
+    s = ln_bwd(tl.x2, lw.ln2_g, gin, dx2, dx2b, f32(w.pg), f32(w.pb));
     if (s != TXL_OK) return s;
     // dFpre = (dX2 W2) * GELU'(Fpre)
     GemmParams pf = dense(dx2b, c.d, R, c.d_ff, c.d, w2T, dfpre, c.d_ff);
@@ -632,7 +633,7 @@ TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t 
     ph.ldres = c.d;
     if ((s = launch_gemm(ph, kEpiResidualF32, stream)) != TXL_OK) return s;
     // LN1
-    if ((s = ln_bwd(tl.x1, lw.ln1_g, dh1, dx1, dx1b, g.ln1_g, g.ln1_b)) != TXL_OK) return s;
+    if ((s = ln_bwd(tl.x1, lw.ln1_g, dh1, dx1, dx1b, f32(w.pg1), f32(w.pb1))) != TXL_OK) return s;
     // dA = dX1 W^O
     if ((s = launch_gemm(dense(dx1b, c.d, R, HD, c.d, woT, b16(w.dout), HD), kEpiStoreBf16, stream)) !=
         TXL_OK)
@@ -700,6 +701,11 @@ TXL_API txl_status txl_segment_backward(txl_stack *st, const void *tape, size_t 
       const LayerDw dw = layer_dw(c, R, KR, ML, dx2b, tl.f, dfpre, tl.h1, dx1b, tl.o, acat, tl.hin, kvg,
                                   ext, drb, st_rows, &g);
       if ((s = launch_dw_batch(dw.p, 7, part, w.part_floats, stream)) != TXL_OK) return s;
+    }
+    {
+      const float *parts[4] = {f32(w.pg), f32(w.pb), f32(w.pg1), f32(w.pb1)};
+      float *outs[4] = {g.ln2_g, g.ln2_b, g.ln1_g, g.ln1_b};
+      if ((s = launch_reduce_cols(parts, outs, 4, ln_blocks, c.d, c.d, stream)) != TXL_OK) return s;
     }
     // dH^(n-1) = dX1 + [dQ | dK_seg | dV_seg] [W^Q; W^K; W^V]
     GemmParams pi = dense(acat, 3 * HD, R, c.d, 3 * HD, wcatT, gout, c.d);

@@ -196,11 +196,11 @@ txl_status launch_transpose_batch(const TransposeJob *jobs, int n, hipStream_t s
 // y [B*(M+L), d] = [memory (logical order, unheld slots zero); segment] per batch row
 txl_status launch_gather_ext(const void *mem, const int32_t *valid, const void *seg, int B, int M, int L,
                              int d, void *y, hipStream_t s);
-// out0[i] = sum over s < S of part0[s*stride + i] in a fixed order, and the
-// same for out1 from part1, in one launch, for many parts over few columns
-// (any n, 4-byte aligned)
-txl_status launch_reduce_cols2(const float *part0, float *out0, const float *part1, float *out1, int S,
-                               int64_t stride, int64_t n, hipStream_t s);
+// outs[k][i] = sum over s < S of parts[k][s*stride + i] in a fixed order, for
+// up to four part sets in one launch, for many parts over few columns (any
+// n, 4-byte aligned)
+txl_status launch_reduce_cols(const float *const *parts, float *const *outs, int n_sets, int S,
+                              int64_t stride, int64_t n, hipStream_t s);
 int ln_backward_blocks(int rows, int *rpb);
 txl_status launch_ln_backward(const float *x, const void *gamma, const float *dy, float *dx,
                               void *dxb, float *part_g, float *part_b, int rows, int d, float eps,
