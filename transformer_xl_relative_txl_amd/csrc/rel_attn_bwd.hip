@@ -464,13 +464,14 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(AttnParams p, BwdParams 
 
 // ---------------------------------------------------------------------------
 // C[z][m][n] (+)= sum_k A_z(m, k) B_z(k, n), n < 64, over the visible part of
-// p or g only. Addressing and visibility by kind (jv = first valid key of
-// the batch row, c = key index of the element):
-//   0  A(m = key j', k = query i)  at a + k*lda + m        visible jv <= m <= M + k
-//   1  A(m = query i, k = key j')  at a + m*lda + k        visible jv <= k <= M + m
-//   2  A(m = query i, k = row t)   at a + m*lda + c, c = k + m - (L-1)
-//   3  A(m = row t, k = query i)   at a + k*lda + c, c = m + k - (L-1), batch row = outer k
-// (kinds 2 and 3 are the diagonal view: key c of query i has distance row t).
+// g only. A is g stored by key or by distance, element (i, c) of query i at
+// a + i*lda + c; addressing and visibility by kind (jv = first valid key of
+// the batch row):
+//   1  A(m = query i, k = key j')  = g_key(i, k)     visible jv <= k <= M + m
+//   2  A(m = query i, k = row t)   = g_dist(i, k)    key t + m - (L-1) visible
+//   3  A(m = row t, k = query i)   = g_dist(k, m)    key m + k - (L-1) visible
+// (kinds 2 and 3 are the diagonal view: distance row t of query i is key
+// t + i - (L-1)).
 constexpr int GT = 64;    // output rows per workgroup
 constexpr int GK = 64;    // k per slab
 constexpr int GS = GK + 8;
@@ -478,7 +479,6 @@ constexpr int GS = GK + 8;
 // One operand set of a product: C += A B over K, A addressed by kind.
 struct BgPhase {
   int kind, K;
-  int gs;         // kinds 2, 3: A stored by distance, element (i, t) at a + i*lda + t
   const __bf16 *a;
   int64_t lda, a_s1, a_s2;
   const __bf16 *b;
@@ -497,29 +497,22 @@ struct BgParams {
   int M, L;
 };
 
-// 16 consecutive bf16 of a buffer starting at any element offset off0 (zero
-// outside the buffer): three aligned 16-byte loads and a byte-align shift.
-__device__ inline void load16_unaligned(rsrc_t rs, int off0, bf16x8 &x0, bf16x8 &x1) {
-  const int o = off0 & 7, base8 = off0 - o;
-  const u32x4 w0 = bload(rs, 2 * base8), w1 = bload(rs, 2 * base8 + 16), w2 = bload(rs, 2 * base8 + 32);
-  const uint32_t win[12] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3],
-                            w2[0], w2[1], w2[2], w2[3]};
-  const int wsh = o >> 1, sub = (o & 1) * 2;
-  u32x4 pk0, pk1;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t lo = wsh == 0 ? win[j] : wsh == 1 ? win[j + 1] : wsh == 2 ? win[j + 2] : win[j + 3];
-    const uint32_t hi = wsh == 0 ? win[j + 1] : wsh == 1 ? win[j + 2] : wsh == 2 ? win[j + 3] : win[j + 4];
-    const uint32_t w = __builtin_amdgcn_alignbyte(hi, lo, sub);
-    if (j < 4) pk0[j] = w; else pk1[j - 4] = w;
-  }
-  x0 = __builtin_bit_cast(bf16x8, pk0);
-  x1 = __builtin_bit_cast(bf16x8, pk1);
+// k-major LDS tiles ([k][64], 128-byte rows): the 16-byte chunk c of row k
+// sits in slot c ^ (4 * ((k >> 1) & 1)), so that the transposing operand
+// read (four rows of 64 bytes for 32 lanes) covers every bank once
+__device__ inline int kmaj_off(int row, int col) {
+  return row * 64 + 8 * ((col >> 3) ^ (((row >> 1) & 1) << 2)) + (col & 7);
+}
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+// Transposing LDS read: within each 16-lane group, element k of lane j is the
+// 16-bit value at (address of lane 4k + j/4) + j % 4.
+__device__ inline v4i16 lds_read_tr(const __bf16 *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)p);
 }
 
 __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
-  __shared__ __attribute__((aligned(16))) __bf16 sa[GT * GS];
-  __shared__ __attribute__((aligned(16))) __bf16 sb[DH * GS];
+  __shared__ __attribute__((aligned(16))) __bf16 sa[GT * GS];   // [m][k] padded, or k-major
+  __shared__ __attribute__((aligned(16))) __bf16 sb[GK * DH];   // k-major
   __shared__ float scol[2][DH];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
@@ -549,7 +542,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
   }
   const int m0 = mt * GT;
   const int z1 = z / q.Z2, z2 = z - z1 * q.Z2;
-  const int M = q.M, L = q.L, ML = M + L;
+  const int M = q.M, L = q.L;
   int valid = q.valid ? q.valid[z1] : M;
   valid = valid < 0 ? 0 : (valid > M ? M : valid);
   const int jv = M - valid;
@@ -561,30 +554,43 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
   for (int x = 0; x < 16; ++x) acc[x] = 0.0f;
   float col_before = 0.0f;   // this lane's column sum before the phase
 
+  // Operand reads of the k-major tiles: lane 16g + 4kq + jq supplies the
+  // address of row 8(g >> 1) + kq (+ 16 per k-step, + 4 for the second four
+  // k) at column c0 + 16(g & 1) + 4jq, so that lane j of its group receives
+  // the column's four k in a row: a lane gets k = 8hh .. 8hh + 7 of column
+  // c0 + r, the operand layout of the MFMA (c0 = 32 wm for A, 32 wn for B).
+  int tr_a, tr_b;
+  {
+    const int g = lane >> 4, kq = (lane >> 2) & 3, jq = lane & 3;
+    tr_a = kmaj_off(8 * (g >> 1) + kq, 32 * wm + 16 * (g & 1) + 4 * jq);
+    tr_b = kmaj_off(8 * (g >> 1) + kq, 32 * wn + 16 * (g & 1) + 4 * jq);
+  }
+
   // two register sets: the slab being stored to LDS and the next one, so two
-  // slabs' loads are in flight while a slab is multiplied
-  bf16x8 ra[2][2], rb[2][2];
+  // slabs' loads are in flight while a slab is multiplied. The loads are
+  // issued unconditionally (A range-checked, B at a clamped row) and their
+  // registers are not read before the slab is stored two steps later, where
+  // the hidden entries are zeroed: so the compiler's count of loads in flight
+  // stays exact and a step waits only for the slab it stores.
+  u32x4 xa[2][2];
+  bf16x8 rb[2][2];
 
   for (int ph = 0; ph < q.n_phase; ++ph) {
     const BgPhase &P = q.ph[ph];
-    const bool trans = P.kind == 0 || P.kind == 3;
+    const bool trans = P.kind == 3;             // A read k-major (by query)
     const bool skew = P.kind >= 2;              // indexed by distance: key = t + i - (L-1)
-    const bool unaligned = skew && !P.gs;       // read along g's diagonals
-    // Each thread moves 16 consecutive elements of A and of B per slab. Where
-    // the tile is transposed on its way to LDS (A stored k-major, and every B)
-    // the 64 lanes of a wave take 64 consecutive k, so each 2-byte LDS store of
-    // the wave touches every bank once or twice.
-    const int a_mm = trans ? (tid >> 6) * 16 : tid >> 2;  // m offset in the tile
-    const int a_kk = trans ? tid & 63 : (tid & 3) * 16;   // k offset in the slab
-    const int b_kk = tid & 63, b_nc = (tid >> 6) * 16;
+    // Each thread moves 16 consecutive elements of one stored row of A and of
+    // B per slab (four threads per 128-byte row). A stored by query (kind 3)
+    // and every B are kept k-major in LDS and read through the transposing
+    // operand read; the others keep A m-major, read 16 bytes at a time.
+    const int a_mm = trans ? (tid & 3) * 16 : tid >> 2;   // m offset in the tile
+    const int a_kk = trans ? tid >> 2 : (tid & 3) * 16;   // k offset in the slab
+    const int b_kk = tid >> 2, b_nc = (tid & 3) * 16;
     const __bf16 *abase = P.a + z1 * P.a_s1 + z2 * P.a_s2;
     const __bf16 *bbase = P.b + z1 * P.b_s1 + z2 * P.b_s2;
     const rsrc_t ars = make_rsrc(abase, static_cast<uint32_t>(L * P.lda * 2));
     int k_lo = 0, k_hi = P.K;
-    if (P.kind == 0) {
-      k_lo = m0 - M;
-      if (m_last < jv) k_hi = 0;
-    } else if (P.kind == 1) {
+    if (P.kind == 1) {
       k_lo = jv;
       k_hi = M + m_last + 1 < P.K ? M + m_last + 1 : P.K;
     } else {
@@ -592,76 +598,85 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgParams q) {
     }
     k_lo = k_lo < 0 ? 0 : (k_lo & ~(GK - 1));
     const int n_slabs = k_hi > k_lo ? (k_hi - k_lo + GK - 1) / GK : 0;
+    const int k_last_slab = k_lo + (n_slabs > 0 ? n_slabs - 1 : 0) * GK;
 
+    // slabs past the last are read again as the last (cache hits, never stored)
     auto load = [&](int set, int k0) {
+      k0 = k0 < k_last_slab ? k0 : k_last_slab;
       const int m = m0 + a_mm, k = k0 + a_kk;
-      // row (query) of the stored matrix and first key / distance of the run
+      const int qi = trans ? k : m, t0 = trans ? m : k;
+      // rows at or past L fall outside the range and read as zeros; entries
+      // past M + L - 1 of a row are hidden and zeroed at the store
+      const int off = 2 * ((qi < L ? qi : L) * static_cast<int>(P.lda) + t0);
+      xa[set][0] = bload(ars, off);
+      xa[set][1] = bload(ars, off + 16);
+      const int kb = k0 + b_kk;
+      const __bf16 *bsrc = bbase + static_cast<int64_t>(kb < P.K ? kb : P.K - 1) * P.ldb + b_nc;
+      rb[set][0] = load8(bsrc);
+      rb[set][1] = load8(bsrc + 8);
+    };
+    auto store = [&](int set, int k0) {
+      const int m = m0 + a_mm, k = k0 + a_kk;
       const int qi = trans ? k : m, t0 = trans ? m : k;
       const int sh = skew ? qi - (L - 1) : 0;         // key = index + sh
-      bf16x8 x[2];
-      if (!unaligned) {
-        x[0] = x[1] = zero8();
-        if (qi < L) {
-          const __bf16 *src = abase + static_cast<int64_t>(qi) * P.lda + t0;
-          if (t0 < ML) x[0] = load8(src);
-          if (t0 + 8 < ML) x[1] = load8(src + 8);
-        }
-      } else {
-        load16_unaligned(ars, qi * static_cast<int>(P.lda) + t0 + sh, x[0], x[1]);
-      }
+      bf16x8 x[2] = {__builtin_bit_cast(bf16x8, xa[set][0]), __builtin_bit_cast(bf16x8, xa[set][1])};
       // visible keys of this query: [jv, M + qi]; indices stay below M + L
       const int k_first = t0 + sh, k_last = t0 + 15 + sh;
-      if (qi < L && k_first >= jv && k_last <= M + qi && t0 + 15 < ML) {
-        ra[set][0] = x[0];
-        ra[set][1] = x[1];
-      } else {
+      if (!(qi < L && k_first >= jv && k_last <= M + qi && t0 + 15 < M + L)) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int idx = t0 + 8 * c + e, key = idx + sh;
-            const bool ok = qi < L && idx < ML && key >= jv && key <= M + qi;
-            ra[set][c][e] = ok ? x[c][e] : static_cast<__bf16>(0.0f);
+            const bool ok = qi < L && idx < M + L && key >= jv && key <= M + qi;
+            x[c][e] = ok ? x[c][e] : static_cast<__bf16>(0.0f);
           }
       }
-      const int kb = k0 + b_kk;
-      const __bf16 *bsrc = bbase + static_cast<int64_t>(kb) * P.ldb + b_nc;
-      rb[set][0] = kb < P.K ? load8(bsrc) : zero8();
-      rb[set][1] = kb < P.K ? load8(bsrc + 8) : zero8();
-    };
-    auto store = [&](int set) {
       if (trans) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sa[(a_mm + 8 * c + e) * GS + a_kk] = ra[set][c][e];
+        *reinterpret_cast<bf16x8 *>(sa + kmaj_off(a_kk, a_mm)) = x[0];
+        *reinterpret_cast<bf16x8 *>(sa + kmaj_off(a_kk, a_mm + 8)) = x[1];
       } else {
-        *reinterpret_cast<bf16x8 *>(sa + a_mm * GS + a_kk) = ra[set][0];
-        *reinterpret_cast<bf16x8 *>(sa + a_mm * GS + a_kk + 8) = ra[set][1];
+        *reinterpret_cast<bf16x8 *>(sa + a_mm * GS + a_kk) = x[0];
+        *reinterpret_cast<bf16x8 *>(sa + a_mm * GS + a_kk + 8) = x[1];
       }
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sb[(b_nc + 8 * c + e) * GS + b_kk] = rb[set][c][e];
+      const bool b_ok = k0 + b_kk < P.K;
+      *reinterpret_cast<bf16x8 *>(sb + kmaj_off(b_kk, b_nc)) = b_ok ? rb[set][0] : zero8();
+      *reinterpret_cast<bf16x8 *>(sb + kmaj_off(b_kk, b_nc + 8)) = b_ok ? rb[set][1] : zero8();
     };
     auto step = [&](int set, int s) {
       __syncthreads();
-      store(set);
+      store(set, k_lo + s * GK);
       __syncthreads();
-      if (s + 2 < n_slabs) load(set, k_lo + (s + 2) * GK);
+      load(set, k_lo + (s + 2) * GK);
 #pragma unroll
       for (int kk = 0; kk < GK / 16; ++kk) {
-        const bf16x8 av = load8(sa + (wm * 32 + r) * GS + 16 * kk + 8 * hh);
-        const bf16x8 bv = load8(sb + (wn * 32 + r) * GS + 16 * kk + 8 * hh);
+        bf16x8 av;
+        if (trans) {
+          const v4i16 lo = lds_read_tr(sa + tr_a + 1024 * kk), hi = lds_read_tr(sa + tr_a + 1024 * kk + 256);
+          av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+          av = load8(sa + (wm * 32 + r) * GS + 16 * kk + 8 * hh);
+        }
+        const v4i16 lo = lds_read_tr(sb + tr_b + 1024 * kk), hi = lds_read_tr(sb + tr_b + 1024 * kk + 256);
+        // one cast of the whole vector (a per-element cast of the halves is
+        // folded wrongly by the compiler)
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc = mfma32(av, bv, acc);
       }
     };
 
-    if (n_slabs > 0) load(0, k_lo);
-    if (n_slabs > 1) load(1, k_lo + GK);
-    for (int s2 = 0; s2 < n_slabs; s2 += 2) {
-      step(0, s2);
-      if (s2 + 1 < n_slabs) step(1, s2 + 1);
+    // both steps of every iteration run (an odd slab count ends with one
+    // more step after the loop), and the loop is entered only after the two
+    // first loads, so every step is entered with the same loads in flight
+    if (n_slabs > 0) {
+      load(0, k_lo);
+      load(1, k_lo + GK);
+      int s2 = 0;
+      for (; s2 + 1 < n_slabs; s2 += 2) {
+        step(0, s2);
+        step(1, s2 + 1);
+      }
+      if (s2 < n_slabs) step(0, s2);
     }
 
     if (P.colsum) {   // (uniform) this phase's share of the column sums
@@ -804,7 +819,7 @@ txl_status launch_rel_attn_bwd(const AttnParams &p, const BwdParams &g, hipStrea
   q.ph[0].a = g.gm; q.ph[0].lda = g.ldp; q.ph[0].a_s1 = H * pz; q.ph[0].a_s2 = pz;
   q.ph[0].b = static_cast<const __bf16 *>(p.k); q.ph[0].ldb = p.kv_sl; q.ph[0].b_s1 = p.kv_sb;
   q.ph[0].b_s2 = p.kv_sh; q.ph[0].colsum = g.part_u;
-  q.ph[1].kind = 2; q.ph[1].K = ml; q.ph[1].gs = 1;
+  q.ph[1].kind = 2; q.ph[1].K = ml;
   q.ph[1].a = g.pm; q.ph[1].lda = g.ldp; q.ph[1].a_s1 = H * pz; q.ph[1].a_s2 = pz;
   q.ph[1].b = static_cast<const __bf16 *>(p.r); q.ph[1].ldb = p.r_sl; q.ph[1].b_s1 = 0;
   q.ph[1].b_s2 = p.r_sh; q.ph[1].colsum = g.part_v;
@@ -819,7 +834,7 @@ txl_status launch_rel_attn_bwd(const AttnParams &p, const BwdParams &g, hipStrea
   // batch rows by the reduction below
   q = BgParams{};
   q.rows = ml; q.n_phase = 1;
-  q.ph[0].kind = 3; q.ph[0].K = L; q.ph[0].gs = 1;
+  q.ph[0].kind = 3; q.ph[0].K = L;
   q.ph[0].a = g.pm; q.ph[0].lda = g.ldp; q.ph[0].a_s1 = H * pz; q.ph[0].a_s2 = pz;
   q.ph[0].b = g.qv; q.ph[0].ldb = DH; q.ph[0].b_s1 = static_cast<int64_t>(H) * L * DH;
   q.ph[0].b_s2 = static_cast<int64_t>(L) * DH;
