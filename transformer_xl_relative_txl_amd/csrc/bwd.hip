@@ -151,20 +151,33 @@ __global__ __launch_bounds__(256) void ln_backward_kernel(
     ab[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
   const int r_lo = blockIdx.x * rpb, r_hi = min(rows, r_lo + rpb);
-  for (int row = r_lo + wave; row < r_hi; row += 4) {
-    const float *xr = x + static_cast<int64_t>(row) * d;
-    const float *gr = dy + static_cast<int64_t>(row) * d;
-    // x, dy and gamma of the row are loaded before any arithmetic: one
-    // memory round trip per row
-    f32x4 xv[MAXC], gv[MAXC];
-    bf16x4 gmv[MAXC];
+  bf16x4 gmv[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c)
+    if (c < nch) gmv[c] = *reinterpret_cast<const bf16x4 *>(gamma + 256 * c + 4 * lane);
+  // x and dy of a wave's next row are loaded while its current row is
+  // computed (the last row's "next" is the row itself again, a cache hit)
+  f32x4 xn[MAXC], gn[MAXC];
+  auto load_row = [&](int rw) {
+    const float *xr = x + static_cast<int64_t>(rw) * d;
+    const float *gr = dy + static_cast<int64_t>(rw) * d;
 #pragma unroll
     for (int c = 0; c < MAXC; ++c)
       if (c < nch) {
-        xv[c] = *reinterpret_cast<const f32x4 *>(xr + 256 * c + 4 * lane);
-        gv[c] = *reinterpret_cast<const f32x4 *>(gr + 256 * c + 4 * lane);
-        gmv[c] = *reinterpret_cast<const bf16x4 *>(gamma + 256 * c + 4 * lane);
+        xn[c] = *reinterpret_cast<const f32x4 *>(xr + 256 * c + 4 * lane);
+        gn[c] = *reinterpret_cast<const f32x4 *>(gr + 256 * c + 4 * lane);
       }
+  };
+  if (r_lo + wave < r_hi) load_row(r_lo + wave);
+  for (int row = r_lo + wave; row < r_hi; row += 4) {
+    f32x4 xv[MAXC], gv[MAXC];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c)
+      if (c < nch) {
+        xv[c] = xn[c];
+        gv[c] = gn[c];
+      }
+    load_row(row + 4 < r_hi ? row + 4 : row);
     float s = 0.0f;
 #pragma unroll
     for (int c = 0; c < MAXC; ++c)
